@@ -1,0 +1,125 @@
+/*
+ * sf_gdn.h -- C ABI of the MI355X (gfx950) library for one pipeline chunk of
+ * the gated delta-rule recurrence (Gated DeltaNet), forward and backward.
+ *
+ * Source of the operation: "Pith review of StateFlow: Sequence Pipeline
+ * Parallelism for Long-Context Modeling with Linear Recurrence"
+ * (pith.science).
+ *   - "What carries the argument": a sequence is split into chunks
+ *     C_0 || ... || C_{N-1}; chunk C_i starts from its boundary state
+ *     S_i^in and emits S_i^out; forward chaining S_{i+1}^in = S_i^out
+ *     (Eq. 5) and backward chaining Sbar_i^out = Sbar_{i+1}^in (Eq. 7).
+ *   - "Referee Report", major comment 1: the layer is the gated delta rule
+ *     (Eq. (1)) with its auxiliary V_new path (Eq. (2)); the chunk backward
+ *     must rebuild the chunk's state trajectory, which this library does by
+ *     recomputing it from the chunk inputs.
+ * Per (batch b, head h) sequence, with a d_v x d_k state S:
+ *     S_t = alpha_t S_{t-1} (I - beta_t k_t k_t^T) + beta_t v_t k_t^T
+ *     o_t = S_t q_t
+ * alpha_t (decay, 0 < alpha <= 1) and beta_t (write strength) are scalars per
+ * token and head; there is no query scaling and no normalisation inside.
+ *
+ * Layouts (all contiguous, row-major):
+ *     q, k            [B, T, H, Dk]   dtype (bf16 or fp32)
+ *     v, o, dO        [B, T, H, Dv]   dtype
+ *     dq, dk, dv      like q, k, v    dtype
+ *     alpha, beta     [B, T, H]       fp32
+ *     dalpha, dbeta   [B, T, H]       fp32
+ *     S_in, S_out, dS_out, dS_in   [B, H, Dv, Dk] fp32  (o_t = S_t q_t)
+ * With B = 1 a pipeline chunk of a longer sequence is a pointer offset into
+ * the sequence tensors (rows t0 .. t0+T-1), so chaining needs no copies.
+ *
+ * Ownership: the caller owns every buffer, including the workspace.  The
+ * library allocates and frees no device memory and keeps no pointer after a
+ * call returns.  All work is enqueued on `stream` (a hipStream_t; NULL is the
+ * default stream) with no host synchronisation; results are ready when the
+ * stream reaches that point.  Calls are stateless and reentrant; results are
+ * bitwise deterministic for a given shape and seg_blocks.
+ *
+ * Errors: arguments are checked on the host before anything is enqueued; on
+ * failure nothing is enqueued and the status says why (details in
+ * sf_last_error_message(), per thread).  No exception or abort crosses the
+ * ABI.  Not checked (documented preconditions, checking would cost a pass over
+ * HBM): 0 < alpha <= 1, finite inputs.  NaN inputs propagate.
+ *
+ * Supported: Dk == Dv in {64, 128} for bf16, Dk == Dv == 64 for fp32; any
+ * T >= 0 (a partial last 64-token block is handled in the kernels).
+ */
+#ifndef SF_GDN_H
+#define SF_GDN_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  SF_OK = 0,
+  SF_ERR_INVALID_ARG = 1,  /* null pointer, bad dimension, misalignment, aliasing */
+  SF_ERR_UNSUPPORTED = 2,  /* valid request this build does not implement */
+  SF_ERR_WORKSPACE = 3,    /* workspace missing or smaller than required */
+  SF_ERR_HIP = 4           /* a HIP runtime call or kernel launch failed */
+} sf_status;
+
+typedef enum { SF_DTYPE_F32 = 0, SF_DTYPE_BF16 = 1 } sf_dtype;
+
+/* Problem description.  seg_blocks is the number of 64-token kernel blocks
+ * per segment of the in-chunk parallel scan; 0 picks a default from the
+ * shape.  Workspace sizes depend on it. */
+typedef struct {
+  int B, T, H, Dk, Dv;
+  int dtype;       /* sf_dtype of q, k, v, o, dO, dq, dk, dv */
+  int seg_blocks;  /* 0 = automatic */
+} sf_gdn_shape;
+
+/* Workspace bytes (256-byte aligned start required) for the calls below.
+ * Returns SF_OK and writes *bytes, or an error for an unsupported shape. */
+sf_status sf_gdn_chunk_fwd_workspace_size(const sf_gdn_shape* shape, size_t* bytes);
+sf_status sf_gdn_chunk_bwd_workspace_size(const sf_gdn_shape* shape, size_t* bytes);
+
+/* Forward of one chunk ("Fwd_i(S_i^in) -> S_i^out", Eq. 5 of the page).
+ *   S_in   entry state, NULL means zeros.
+ *   o      outputs (required when T > 0).
+ *   S_out  exit state, may be NULL when not wanted.
+ * Outputs must not overlap inputs or each other. */
+sf_status sf_gdn_chunk_fwd(const sf_gdn_shape* shape, const void* q, const void* k, const void* v,
+                           const float* alpha, const float* beta, const float* S_in, void* o,
+                           float* S_out, void* workspace, size_t ws_bytes, void* stream);
+
+/* Backward of one chunk ("Bwd_i(Sbar_i^out) -> Sbar_i^in", Eq. 7 of the
+ * page) of the loss L = <dO, o> + <dS_out, S_out>.  The inputs are the
+ * forward's inputs (the chunk's state trajectory is recomputed from them);
+ * dS_out NULL means zeros.  Writes dq, dk, dv (dtype), dalpha, dbeta (fp32,
+ * gradients with respect to alpha and beta themselves) and dS_in (fp32, may
+ * be NULL when not wanted). */
+sf_status sf_gdn_chunk_bwd(const sf_gdn_shape* shape, const void* q, const void* k, const void* v,
+                           const float* alpha, const float* beta, const float* S_in,
+                           const void* dO, const float* dS_out, void* dq, void* dk, void* dv,
+                           float* dalpha, float* dbeta, float* dS_in, void* workspace,
+                           size_t ws_bytes, void* stream);
+
+/* Static text for a status code. */
+const char* sf_status_string(int status);
+/* Detail of the calling thread's last non-OK status (static until the next
+ * failing call on this thread). */
+const char* sf_last_error_message(void);
+/* Library version string. */
+const char* sf_gdn_version(void);
+
+/* Per-kernel timing for measurement.  sf_gdn_profile_begin(capacity) makes
+ * every following launch (up to `capacity`) record a HIP event pair on its
+ * stream; sf_gdn_profile_end() waits for them and aggregates per kernel name.
+ * Results stay readable until the next begin.  Process-wide; calls are
+ * serialised internally. */
+sf_status sf_gdn_profile_begin(int capacity);
+sf_status sf_gdn_profile_end(void);
+int sf_gdn_profile_kernel_count(void);
+sf_status sf_gdn_profile_kernel(int index, const char** name, long long* launches,
+                                double* total_ms);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SF_GDN_H */

@@ -1,0 +1,224 @@
+"""ctypes binding of libsf_gdn.so (the C ABI in include/sf_gdn.h).
+
+Argument marshalling only: torch provides device memory and the stream, and
+every step of the computation runs in the library's HIP kernels.  There is no
+fallback: if the library is missing or fails, calls raise.
+"""
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libsf_gdn.so")
+
+SF_OK, SF_ERR_INVALID_ARG, SF_ERR_UNSUPPORTED, SF_ERR_WORKSPACE, SF_ERR_HIP = range(5)
+SF_DTYPE_F32, SF_DTYPE_BF16 = 0, 1
+
+_DTYPES = {torch.float32: SF_DTYPE_F32, torch.bfloat16: SF_DTYPE_BF16}
+
+# Every function the header declares, with (restype, argtypes).
+_vp, _cvp, _fp = ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p
+_sz = ctypes.c_size_t
+
+
+class Shape(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int), ("T", ctypes.c_int), ("H", ctypes.c_int),
+                ("Dk", ctypes.c_int), ("Dv", ctypes.c_int), ("dtype", ctypes.c_int),
+                ("seg_blocks", ctypes.c_int)]
+
+
+SIGNATURES = {
+    "sf_gdn_chunk_fwd_workspace_size": (ctypes.c_int, [ctypes.POINTER(Shape), ctypes.POINTER(_sz)]),
+    "sf_gdn_chunk_bwd_workspace_size": (ctypes.c_int, [ctypes.POINTER(Shape), ctypes.POINTER(_sz)]),
+    "sf_gdn_chunk_fwd": (ctypes.c_int, [ctypes.POINTER(Shape)] + [_vp] * 8 + [_vp, _sz, _vp]),
+    "sf_gdn_chunk_bwd": (ctypes.c_int, [ctypes.POINTER(Shape)] + [_vp] * 14 + [_vp, _sz, _vp]),
+    "sf_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "sf_last_error_message": (ctypes.c_char_p, []),
+    "sf_gdn_version": (ctypes.c_char_p, []),
+    "sf_gdn_profile_begin": (ctypes.c_int, [ctypes.c_int]),
+    "sf_gdn_profile_end": (ctypes.c_int, []),
+    "sf_gdn_profile_kernel_count": (ctypes.c_int, []),
+    "sf_gdn_profile_kernel": (ctypes.c_int, [ctypes.c_int, ctypes.POINTER(ctypes.c_char_p),
+                                             ctypes.POINTER(ctypes.c_longlong),
+                                             ctypes.POINTER(ctypes.c_double)]),
+}
+
+_lib = None
+
+
+class GDNError(RuntimeError):
+    def __init__(self, status, where, msg):
+        super().__init__("%s: %s (%s)" % (where, msg, status_string(status)))
+        self.status = status
+
+
+def load():
+    """Load the library (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError("libsf_gdn.so is not built; run "
+                           "`python -m linear_recurrence_chunked_gated_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    for name, (res, args) in SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def status_string(status):
+    return load().sf_status_string(int(status)).decode()
+
+
+def _check(status, where):
+    if status != SF_OK:
+        raise GDNError(status, where, load().sf_last_error_message().decode())
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def make_shape(B, T, H, Dk, Dv, dtype, seg_blocks=0):
+    if isinstance(dtype, torch.dtype):
+        if dtype not in _DTYPES:
+            raise TypeError("q/k/v must be bfloat16 or float32, got %s" % dtype)
+        dtype = _DTYPES[dtype]
+    return Shape(B, T, H, Dk, Dv, dtype, seg_blocks)
+
+
+def workspace_bytes(shape, backward=False):
+    n = ctypes.c_size_t(0)
+    fn = load().sf_gdn_chunk_bwd_workspace_size if backward else load().sf_gdn_chunk_fwd_workspace_size
+    _check(fn(ctypes.byref(shape), ctypes.byref(n)), "workspace_size")
+    return n.value
+
+
+def alloc_workspace(nbytes, device):
+    """A 256-byte aligned uint8 view of at least nbytes (None when 0)."""
+    if nbytes == 0:
+        return None
+    raw = torch.empty(nbytes + 256, dtype=torch.uint8, device=device)
+    off = (-raw.data_ptr()) % 256
+    return raw[off:off + nbytes]
+
+
+def _need(t, name, dtype, shape, device):
+    if t is None:
+        raise ValueError("%s is required" % name)
+    if t.device != device:
+        raise ValueError("%s is on %s, expected %s" % (name, t.device, device))
+    if t.dtype != dtype:
+        raise TypeError("%s has dtype %s, expected %s" % (name, t.dtype, dtype))
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError("%s has shape %s, expected %s" % (name, tuple(t.shape), tuple(shape)))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+
+
+def chunk_fwd(q, k, v, alpha, beta, S_in=None, o=None, S_out=None, seg_blocks=0,
+              workspace=None, stream=None):
+    """sf_gdn_chunk_fwd on torch tensors.  Returns (o, S_out)."""
+    B, T, H, Dk = q.shape
+    Dv = v.shape[3]
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("tensors must be on a GPU device")
+    _need(q, "q", q.dtype, (B, T, H, Dk), dev)
+    _need(k, "k", q.dtype, (B, T, H, Dk), dev)
+    _need(v, "v", q.dtype, (B, T, H, Dv), dev)
+    _need(alpha, "alpha", torch.float32, (B, T, H), dev)
+    _need(beta, "beta", torch.float32, (B, T, H), dev)
+    if S_in is not None:
+        _need(S_in, "S_in", torch.float32, (B, H, Dv, Dk), dev)
+    if o is None:
+        o = torch.empty((B, T, H, Dv), dtype=q.dtype, device=dev)
+    _need(o, "o", q.dtype, (B, T, H, Dv), dev)
+    if S_out is None:
+        S_out = torch.empty((B, H, Dv, Dk), dtype=torch.float32, device=dev)
+    _need(S_out, "S_out", torch.float32, (B, H, Dv, Dk), dev)
+    shape = make_shape(B, T, H, Dk, Dv, q.dtype, seg_blocks)
+    need = workspace_bytes(shape)
+    if workspace is None or workspace.numel() < need:
+        workspace = alloc_workspace(need, dev)
+    st = load().sf_gdn_chunk_fwd(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha),
+                                 _ptr(beta), _ptr(S_in), _ptr(o), _ptr(S_out), _ptr(workspace),
+                                 ctypes.c_size_t(0 if workspace is None else workspace.numel()),
+                                 _stream(stream))
+    _check(st, "sf_gdn_chunk_fwd")
+    return o, S_out
+
+
+def chunk_bwd(q, k, v, alpha, beta, S_in, dO, dS_out=None, grads=None, seg_blocks=0,
+              workspace=None, stream=None):
+    """sf_gdn_chunk_bwd on torch tensors.
+
+    Returns (dq, dk, dv, dalpha, dbeta, dS_in).  ``grads`` may supply
+    preallocated outputs in that order (dS_in may be None there)."""
+    B, T, H, Dk = q.shape
+    Dv = v.shape[3]
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("tensors must be on a GPU device")
+    for t, n, dt, shp in ((q, "q", q.dtype, (B, T, H, Dk)), (k, "k", q.dtype, (B, T, H, Dk)),
+                          (v, "v", q.dtype, (B, T, H, Dv)), (dO, "dO", q.dtype, (B, T, H, Dv)),
+                          (alpha, "alpha", torch.float32, (B, T, H)),
+                          (beta, "beta", torch.float32, (B, T, H))):
+        _need(t, n, dt, shp, dev)
+    if S_in is not None:
+        _need(S_in, "S_in", torch.float32, (B, H, Dv, Dk), dev)
+    if dS_out is not None:
+        _need(dS_out, "dS_out", torch.float32, (B, H, Dv, Dk), dev)
+    if grads is None:
+        grads = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v),
+                 torch.empty_like(alpha), torch.empty_like(beta),
+                 torch.empty((B, H, Dv, Dk), dtype=torch.float32, device=dev))
+    dq, dk, dv, da, db, dS_in = grads
+    shape = make_shape(B, T, H, Dk, Dv, q.dtype, seg_blocks)
+    need = workspace_bytes(shape, backward=True)
+    if workspace is None or workspace.numel() < need:
+        workspace = alloc_workspace(need, dev)
+    st = load().sf_gdn_chunk_bwd(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha),
+                                 _ptr(beta), _ptr(S_in), _ptr(dO), _ptr(dS_out), _ptr(dq),
+                                 _ptr(dk), _ptr(dv), _ptr(da), _ptr(db), _ptr(dS_in),
+                                 _ptr(workspace),
+                                 ctypes.c_size_t(0 if workspace is None else workspace.numel()),
+                                 _stream(stream))
+    _check(st, "sf_gdn_chunk_bwd")
+    return dq, dk, dv, da, db, dS_in
+
+
+class profile:
+    """Context manager: per-kernel HIP-event timing of the library's launches.
+
+    After exit, ``.results`` maps kernel name -> (launches, total_ms)."""
+
+    def __init__(self, capacity=65536):
+        self.capacity = capacity
+        self.results = {}
+
+    def __enter__(self):
+        _check(load().sf_gdn_profile_begin(int(self.capacity)), "sf_gdn_profile_begin")
+        return self
+
+    def __exit__(self, *exc):
+        lib = load()
+        _check(lib.sf_gdn_profile_end(), "sf_gdn_profile_end")
+        for i in range(lib.sf_gdn_profile_kernel_count()):
+            name = ctypes.c_char_p()
+            n = ctypes.c_longlong()
+            ms = ctypes.c_double()
+            _check(lib.sf_gdn_profile_kernel(i, ctypes.byref(name), ctypes.byref(n), ctypes.byref(ms)),
+                   "sf_gdn_profile_kernel")
+            self.results[name.value.decode()] = (n.value, ms.value)
+        return False

@@ -1,0 +1,67 @@
+// Kernel argument blocks and launch entry points shared by the forward and
+// backward translation units and the C-ABI layer.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+
+#include "gdn_block.hpp"
+
+namespace sfgdn {
+
+// One chunk call.  Token-major tensors are [B, T, H, D]; gates [B, T, H];
+// states [B, H, D, D] fp32 ([dv][dk] row-major).  The chunk's nblk blocks are
+// split into P segments of L blocks (the last one may be shorter).
+struct FwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* alpha;
+  const float* beta;
+  const float* S_in;   // may be null (zeros)
+  void* o;             // may be null for state-only passes
+  float* S_out;        // may be null
+  int B, T, H;
+  int nblk, L, P;
+  // workspace
+  float* Mseg;         // [B*H][P][D][D]  segment transition maps
+  float* Nseg;         // [B*H][P][D][D]  segment zero-entry exit states
+  const float* Sst;    // [B*H][sst_P][D][D] segment entry states (S_in when P == 1)
+  int sst_P;
+};
+
+struct ChainArgs {
+  const float* S_in;
+  const float* Mseg;
+  const float* Nseg;
+  float* Sst;
+  int P;
+};
+
+struct BwdArgs {
+  FwdArgs f;            // inputs, plan and forward workspace (o, S_out unused)
+  const void* dO;       // [B, T, H, D]
+  const float* dS_out;  // may be null (zeros)
+  void* dq;
+  void* dk;
+  void* dv;
+  float* dalpha;
+  float* dbeta;
+  float* dS_in;         // may be null
+  // workspace
+  float* NBseg;         // [B*H][P][D][D] segment state-gradient maps from a zero exit gradient
+  float* dSend;         // [B*H][P][D][D] state gradient at each segment's exit
+  void* hst;            // [B*H][nblk][D][D] block entry states (state storage type)
+  void* dhst;           // [B*H][nblk][D][D] gradient wrt each block's exit state
+};
+
+// Optional per-launch event timing (see sf_gdn_profile_* in the C ABI).
+struct Profiler;
+void prof_begin(Profiler* p, const char* name, hipStream_t st);
+void prof_end(Profiler* p, hipStream_t st);
+
+template <typename T, int D>
+hipError_t launch_fwd(const FwdArgs& a, hipStream_t st, Profiler* prof);
+template <typename T, int D>
+hipError_t launch_bwd(const BwdArgs& a, hipStream_t st, Profiler* prof);
+
+}  // namespace sfgdn

@@ -1,0 +1,392 @@
+// C ABI of the chunked gated delta-rule library: argument checks, the
+// segment plan, workspace carving and kernel launches on the caller's stream.
+#include <hip/hip_runtime.h>
+
+#include <mutex>
+#include <stdint.h>
+#include <stdio.h>
+#include <string>
+#include <vector>
+
+#include "../../include/sf_gdn.h"
+#include "gdn_kernels.hpp"
+
+namespace sfgdn {
+hipError_t launch_copy_state(float* dst, const float* src, size_t n, hipStream_t st);
+}
+
+using namespace sfgdn;
+
+namespace {
+
+thread_local std::string g_err;
+
+sf_status fail(sf_status s, const std::string& msg) {
+  g_err = msg;
+  return s;
+}
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+struct Plan {
+  int B, T, H, D, dtype;
+  int nblk, L, P;
+  size_t state_elem;  // bytes per stored per-block state element (bwd)
+};
+
+sf_status make_plan(const sf_gdn_shape* s, Plan& p) {
+  if (!s) return fail(SF_ERR_INVALID_ARG, "shape is NULL");
+  if (s->B <= 0 || s->H <= 0 || s->T < 0 || s->Dk <= 0 || s->Dv <= 0)
+    return fail(SF_ERR_INVALID_ARG, "dimensions must be positive (T may be 0)");
+  if (s->dtype != SF_DTYPE_F32 && s->dtype != SF_DTYPE_BF16)
+    return fail(SF_ERR_INVALID_ARG, "unknown dtype");
+  if (s->seg_blocks < 0) return fail(SF_ERR_INVALID_ARG, "seg_blocks must be >= 0");
+  if (s->Dk != s->Dv) return fail(SF_ERR_UNSUPPORTED, "Dk != Dv is not supported");
+  if (s->Dk != 64 && s->Dk != 128) return fail(SF_ERR_UNSUPPORTED, "Dk must be 64 or 128");
+  if (s->dtype == SF_DTYPE_F32 && s->Dk != 64)
+    return fail(SF_ERR_UNSUPPORTED, "fp32 inputs are supported for Dk = Dv = 64 only");
+  if ((long long)s->B * s->H > (1LL << 20))
+    return fail(SF_ERR_UNSUPPORTED, "B*H too large");
+  p.B = s->B;
+  p.T = s->T;
+  p.H = s->H;
+  p.D = s->Dk;
+  p.dtype = s->dtype;
+  p.nblk = (s->T + BLK - 1) / BLK;
+  if (p.nblk == 0) {
+    p.L = 1;
+    p.P = 0;
+  } else {
+    int L = s->seg_blocks;
+    if (L == 0) {
+      // Enough segments that B*H*P workgroups cover the 256 compute units.
+      const long long bh = (long long)s->B * s->H;
+      long long P0 = (256 + bh - 1) / bh;
+      if (P0 > p.nblk) P0 = p.nblk;
+      if (P0 < 1) P0 = 1;
+      L = (int)((p.nblk + P0 - 1) / P0);
+    }
+    if (L > p.nblk) L = p.nblk;
+    p.L = L;
+    p.P = (p.nblk + L - 1) / L;
+    if ((long long)p.B * p.H * p.P > (1LL << 30))
+      return fail(SF_ERR_UNSUPPORTED, "too many segments");
+  }
+  p.state_elem = (s->dtype == SF_DTYPE_BF16) ? 2 : 4;
+  return SF_OK;
+}
+
+size_t dd(const Plan& p) { return (size_t)p.D * p.D; }
+size_t seg_buf(const Plan& p) { return align_up((size_t)p.B * p.H * p.P * dd(p) * sizeof(float)); }
+size_t fwd_ws(const Plan& p) { return p.P > 1 ? 3 * seg_buf(p) : 0; }
+size_t blk_buf(const Plan& p) { return align_up((size_t)p.B * p.H * p.nblk * dd(p) * p.state_elem); }
+size_t bwd_ws(const Plan& p) {
+  if (p.P == 0) return 0;
+  return 3 * seg_buf(p) + 2 * seg_buf(p) + 2 * blk_buf(p);
+}
+
+size_t elem(const Plan& p) { return p.dtype == SF_DTYPE_BF16 ? 2 : 4; }
+
+struct Range {
+  const void* p;
+  size_t n;
+  const char* name;
+};
+
+bool overlap(const Range& a, const Range& b) {
+  if (!a.p || !b.p || a.n == 0 || b.n == 0) return false;
+  const uintptr_t a0 = (uintptr_t)a.p, b0 = (uintptr_t)b.p;
+  return a0 < b0 + b.n && b0 < a0 + a.n;
+}
+
+sf_status check_ptrs(const std::vector<Range>& in, const std::vector<Range>& out,
+                     const std::vector<const char*>& required) {
+  (void)required;
+  for (const Range& r : in)
+    if (r.p && ((uintptr_t)r.p % 16)) return fail(SF_ERR_INVALID_ARG, std::string(r.name) + " is not 16-byte aligned");
+  for (const Range& r : out)
+    if (r.p && ((uintptr_t)r.p % 16)) return fail(SF_ERR_INVALID_ARG, std::string(r.name) + " is not 16-byte aligned");
+  for (size_t i = 0; i < out.size(); ++i) {
+    for (const Range& r : in)
+      if (overlap(out[i], r))
+        return fail(SF_ERR_INVALID_ARG, std::string(out[i].name) + " overlaps input " + r.name);
+    for (size_t j = i + 1; j < out.size(); ++j)
+      if (overlap(out[i], out[j]))
+        return fail(SF_ERR_INVALID_ARG, std::string(out[i].name) + " overlaps output " + out[j].name);
+  }
+  return SF_OK;
+}
+
+// ------------------------------------------------------------ profiler ----
+struct ProfRec {
+  const char* name;
+  int ev;
+};
+
+}  // namespace
+
+namespace sfgdn {
+struct Profiler {
+  std::mutex mu;
+  bool on = false;
+  std::vector<hipEvent_t> ev;
+  std::vector<ProfRec> recs;
+  int open = -1;
+  std::vector<std::string> names;
+  std::vector<long long> counts;
+  std::vector<double> ms;
+};
+
+void prof_begin(Profiler* p, const char* name, hipStream_t st) {
+  if (!p) return;
+  p->open = -1;
+  const int idx = (int)p->recs.size() * 2;
+  if (idx + 2 > (int)p->ev.size()) return;
+  if (hipEventRecord(p->ev[idx], st) != hipSuccess) return;
+  p->recs.push_back(ProfRec{name, idx});
+  p->open = idx;
+}
+
+void prof_end(Profiler* p, hipStream_t st) {
+  if (!p || p->open < 0) return;
+  if (hipEventRecord(p->ev[p->open + 1], st) != hipSuccess) p->recs.pop_back();
+  p->open = -1;
+}
+}  // namespace sfgdn
+
+namespace {
+Profiler g_prof;
+
+Profiler* prof_if_on() { return g_prof.on ? &g_prof : nullptr; }
+
+template <typename F>
+sf_status run_locked(F f) {
+  if (g_prof.on) {
+    std::lock_guard<std::mutex> lk(g_prof.mu);
+    return f(prof_if_on());
+  }
+  return f(nullptr);
+}
+
+sf_status hip_fail(hipError_t e, const char* what) {
+  return fail(SF_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------- ABI ------
+extern "C" {
+
+sf_status sf_gdn_chunk_fwd_workspace_size(const sf_gdn_shape* shape, size_t* bytes) {
+  Plan p;
+  sf_status s = make_plan(shape, p);
+  if (s != SF_OK) return s;
+  if (!bytes) return fail(SF_ERR_INVALID_ARG, "bytes is NULL");
+  *bytes = fwd_ws(p);
+  return SF_OK;
+}
+
+sf_status sf_gdn_chunk_bwd_workspace_size(const sf_gdn_shape* shape, size_t* bytes) {
+  Plan p;
+  sf_status s = make_plan(shape, p);
+  if (s != SF_OK) return s;
+  if (!bytes) return fail(SF_ERR_INVALID_ARG, "bytes is NULL");
+  *bytes = bwd_ws(p);
+  return SF_OK;
+}
+
+sf_status sf_gdn_chunk_fwd(const sf_gdn_shape* shape, const void* q, const void* k, const void* v,
+                           const float* alpha, const float* beta, const float* S_in, void* o,
+                           float* S_out, void* workspace, size_t ws_bytes, void* stream) {
+  Plan p;
+  sf_status s = make_plan(shape, p);
+  if (s != SF_OK) return s;
+  const size_t ntok = (size_t)p.B * p.T * p.H;
+  const size_t nst = (size_t)p.B * p.H * dd(p);
+  if (p.T > 0 && (!q || !k || !v || !alpha || !beta || !o))
+    return fail(SF_ERR_INVALID_ARG, "q, k, v, alpha, beta and o are required");
+  std::vector<Range> in = {{q, ntok * p.D * elem(p), "q"},     {k, ntok * p.D * elem(p), "k"},
+                           {v, ntok * p.D * elem(p), "v"},     {alpha, ntok * 4, "alpha"},
+                           {beta, ntok * 4, "beta"},           {S_in, nst * 4, "S_in"},
+                           {workspace, ws_bytes, "workspace"}};
+  std::vector<Range> out = {{o, ntok * p.D * elem(p), "o"}, {S_out, nst * 4, "S_out"}};
+  if ((s = check_ptrs(in, out, {})) != SF_OK) return s;
+  const size_t need = fwd_ws(p);
+  if (need > 0 && (!workspace || ws_bytes < need))
+    return fail(SF_ERR_WORKSPACE, "forward workspace needs " + std::to_string(need) + " bytes");
+  if (workspace && ((uintptr_t)workspace % kAlign))
+    return fail(SF_ERR_INVALID_ARG, "workspace is not 256-byte aligned");
+  hipStream_t st = (hipStream_t)stream;
+
+  return run_locked([&](Profiler* prof) -> sf_status {
+    if (p.T == 0) {
+      if (S_out) {
+        hipError_t e = launch_copy_state(S_out, S_in, nst, st);
+        if (e != hipSuccess) return hip_fail(e, "state copy");
+      }
+      return SF_OK;
+    }
+    FwdArgs a{};
+    a.q = q; a.k = k; a.v = v; a.alpha = alpha; a.beta = beta; a.S_in = S_in;
+    a.o = o; a.S_out = S_out;
+    a.B = p.B; a.T = p.T; a.H = p.H; a.nblk = p.nblk; a.L = p.L; a.P = p.P;
+    char* ws = (char*)workspace;
+    if (p.P > 1) {
+      a.Mseg = (float*)ws;
+      a.Nseg = (float*)(ws + seg_buf(p));
+      a.Sst = (float*)(ws + 2 * seg_buf(p));
+      a.sst_P = p.P;
+    } else {
+      a.Sst = S_in;
+      a.sst_P = 1;
+    }
+    hipError_t e;
+    if (p.dtype == SF_DTYPE_BF16)
+      e = (p.D == 128) ? launch_fwd<bf16, 128>(a, st, prof) : launch_fwd<bf16, 64>(a, st, prof);
+    else
+      e = launch_fwd<float, 64>(a, st, prof);
+    if (e != hipSuccess) return hip_fail(e, "forward launch");
+    return SF_OK;
+  });
+}
+
+sf_status sf_gdn_chunk_bwd(const sf_gdn_shape* shape, const void* q, const void* k, const void* v,
+                           const float* alpha, const float* beta, const float* S_in,
+                           const void* dO, const float* dS_out, void* dq, void* dk, void* dv,
+                           float* dalpha, float* dbeta, float* dS_in, void* workspace,
+                           size_t ws_bytes, void* stream) {
+  Plan p;
+  sf_status s = make_plan(shape, p);
+  if (s != SF_OK) return s;
+  const size_t ntok = (size_t)p.B * p.T * p.H;
+  const size_t nst = (size_t)p.B * p.H * dd(p);
+  const size_t nt = ntok * p.D * elem(p);
+  if (p.T > 0 && (!q || !k || !v || !alpha || !beta || !dO || !dq || !dk || !dv || !dalpha || !dbeta))
+    return fail(SF_ERR_INVALID_ARG, "q, k, v, alpha, beta, dO, dq, dk, dv, dalpha and dbeta are required");
+  std::vector<Range> in = {{q, nt, "q"},          {k, nt, "k"},           {v, nt, "v"},
+                           {alpha, ntok * 4, "alpha"}, {beta, ntok * 4, "beta"}, {S_in, nst * 4, "S_in"},
+                           {dO, nt, "dO"},        {dS_out, nst * 4, "dS_out"},
+                           {workspace, ws_bytes, "workspace"}};
+  std::vector<Range> out = {{dq, nt, "dq"}, {dk, nt, "dk"}, {dv, nt, "dv"}, {dalpha, ntok * 4, "dalpha"},
+                            {dbeta, ntok * 4, "dbeta"}, {dS_in, nst * 4, "dS_in"}};
+  if ((s = check_ptrs(in, out, {})) != SF_OK) return s;
+  const size_t need = bwd_ws(p);
+  if (need > 0 && (!workspace || ws_bytes < need))
+    return fail(SF_ERR_WORKSPACE, "backward workspace needs " + std::to_string(need) + " bytes");
+  if (workspace && ((uintptr_t)workspace % kAlign))
+    return fail(SF_ERR_INVALID_ARG, "workspace is not 256-byte aligned");
+  hipStream_t st = (hipStream_t)stream;
+
+  return run_locked([&](Profiler* prof) -> sf_status {
+    if (p.T == 0) {
+      if (dS_in) {
+        hipError_t e = launch_copy_state(dS_in, dS_out, nst, st);
+        if (e != hipSuccess) return hip_fail(e, "state copy");
+      }
+      return SF_OK;
+    }
+    BwdArgs a{};
+    FwdArgs& f = a.f;
+    f.q = q; f.k = k; f.v = v; f.alpha = alpha; f.beta = beta; f.S_in = S_in;
+    f.o = nullptr; f.S_out = nullptr;
+    f.B = p.B; f.T = p.T; f.H = p.H; f.nblk = p.nblk; f.L = p.L; f.P = p.P;
+    char* ws = (char*)workspace;
+    const size_t sb = seg_buf(p), bb = blk_buf(p);
+    f.Mseg = (float*)ws;
+    f.Nseg = (float*)(ws + sb);
+    f.Sst = (float*)(ws + 2 * sb);
+    f.sst_P = p.P;
+    a.NBseg = (float*)(ws + 3 * sb);
+    a.dSend = (float*)(ws + 4 * sb);
+    a.hst = ws + 5 * sb;
+    a.dhst = ws + 5 * sb + bb;
+    a.dO = dO; a.dS_out = dS_out;
+    a.dq = dq; a.dk = dk; a.dv = dv; a.dalpha = dalpha; a.dbeta = dbeta; a.dS_in = dS_in;
+    hipError_t e;
+    if (p.dtype == SF_DTYPE_BF16)
+      e = (p.D == 128) ? launch_bwd<bf16, 128>(a, st, prof) : launch_bwd<bf16, 64>(a, st, prof);
+    else
+      e = launch_bwd<float, 64>(a, st, prof);
+    if (e == hipErrorNotSupported) return fail(SF_ERR_UNSUPPORTED, "backward not available");
+    if (e != hipSuccess) return hip_fail(e, "backward launch");
+    return SF_OK;
+  });
+}
+
+const char* sf_status_string(int status) {
+  switch (status) {
+    case SF_OK: return "SF_OK";
+    case SF_ERR_INVALID_ARG: return "SF_ERR_INVALID_ARG";
+    case SF_ERR_UNSUPPORTED: return "SF_ERR_UNSUPPORTED";
+    case SF_ERR_WORKSPACE: return "SF_ERR_WORKSPACE";
+    case SF_ERR_HIP: return "SF_ERR_HIP";
+    default: return "SF_ERR_UNKNOWN";
+  }
+}
+
+const char* sf_last_error_message(void) { return g_err.c_str(); }
+
+const char* sf_gdn_version(void) { return "sf_gdn 0.1 (gfx950)"; }
+
+sf_status sf_gdn_profile_begin(int capacity) {
+  if (capacity <= 0) return fail(SF_ERR_INVALID_ARG, "capacity must be positive");
+  std::lock_guard<std::mutex> lk(g_prof.mu);
+  for (hipEvent_t e : g_prof.ev) (void)hipEventDestroy(e);
+  g_prof.ev.clear();
+  g_prof.recs.clear();
+  g_prof.names.clear();
+  g_prof.counts.clear();
+  g_prof.ms.clear();
+  g_prof.ev.resize((size_t)capacity * 2);
+  for (auto& e : g_prof.ev) {
+    hipError_t r = hipEventCreate(&e);
+    if (r != hipSuccess) {
+      g_prof.ev.clear();
+      return hip_fail(r, "hipEventCreate");
+    }
+  }
+  g_prof.on = true;
+  return SF_OK;
+}
+
+sf_status sf_gdn_profile_end(void) {
+  std::lock_guard<std::mutex> lk(g_prof.mu);
+  g_prof.on = false;
+  for (const ProfRec& r : g_prof.recs) {
+    hipError_t e = hipEventSynchronize(g_prof.ev[r.ev + 1]);
+    if (e != hipSuccess) return hip_fail(e, "hipEventSynchronize");
+    float t = 0.f;
+    e = hipEventElapsedTime(&t, g_prof.ev[r.ev], g_prof.ev[r.ev + 1]);
+    if (e != hipSuccess) return hip_fail(e, "hipEventElapsedTime");
+    size_t i = 0;
+    while (i < g_prof.names.size() && g_prof.names[i] != r.name) ++i;
+    if (i == g_prof.names.size()) {
+      g_prof.names.push_back(r.name);
+      g_prof.counts.push_back(0);
+      g_prof.ms.push_back(0.0);
+    }
+    g_prof.counts[i] += 1;
+    g_prof.ms[i] += t;
+  }
+  g_prof.recs.clear();
+  return SF_OK;
+}
+
+int sf_gdn_profile_kernel_count(void) {
+  std::lock_guard<std::mutex> lk(g_prof.mu);
+  return (int)g_prof.names.size();
+}
+
+sf_status sf_gdn_profile_kernel(int index, const char** name, long long* launches,
+                                double* total_ms) {
+  std::lock_guard<std::mutex> lk(g_prof.mu);
+  if (index < 0 || index >= (int)g_prof.names.size())
+    return fail(SF_ERR_INVALID_ARG, "profile index out of range");
+  if (name) *name = g_prof.names[index].c_str();
+  if (launches) *launches = g_prof.counts[index];
+  if (total_ms) *total_ms = g_prof.ms[index];
+  return SF_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,113 @@
+"""Host-side checks that need no GPU: the C ABI library loads and exports
+every declared symbol, arguments are validated before anything is enqueued,
+and the chunk planner matches the oracle's search."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from linear_recurrence_chunked_gated_amd import _lib
+from linear_recurrence_chunked_gated_amd.plan import chunk_lengths
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sf_gdn.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"\b(sf_\w+)\s*\(", text)
+    return sorted(set(names))
+
+
+def test_header_declares_the_chunk_calls():
+    names = declared_functions()
+    for n in ("sf_gdn_chunk_fwd", "sf_gdn_chunk_bwd", "sf_gdn_chunk_fwd_workspace_size",
+              "sf_gdn_chunk_bwd_workspace_size", "sf_status_string", "sf_last_error_message"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(_lib.LIB_PATH)
+    missing = [n for n in declared_functions() if not hasattr(lib, n)]
+    assert not missing, missing
+    # the binding describes each declared function
+    assert set(declared_functions()) == set(_lib.SIGNATURES)
+
+
+def _shape(B=1, T=128, H=2, D=128, dtype=1, seg=0):
+    return _lib.Shape(B, T, H, D, D, dtype, seg)
+
+
+G = 1 << 30  # fake, never dereferenced: validation fails before any launch
+
+
+def _fwd(shape, q=1 * G, k=2 * G, v=3 * G, a=4 * G, b=5 * G, s_in=None,
+         o=6 * G, s_out=7 * G, ws=None, wsn=0):
+    L = _lib.load()
+    vp = lambda x: None if x is None else ctypes.c_void_p(x)
+    return L.sf_gdn_chunk_fwd(ctypes.byref(shape) if shape is not None else None,
+                              vp(q), vp(k), vp(v), vp(a), vp(b), vp(s_in), vp(o), vp(s_out),
+                              vp(ws), ctypes.c_size_t(wsn), None)
+
+
+def test_status_strings():
+    assert _lib.status_string(0) == "SF_OK"
+    assert _lib.status_string(3) == "SF_ERR_WORKSPACE"
+
+
+@pytest.mark.parametrize("shape,code", [
+    (_shape(B=0), _lib.SF_ERR_INVALID_ARG),
+    (_shape(T=-1), _lib.SF_ERR_INVALID_ARG),
+    (_shape(D=96), _lib.SF_ERR_UNSUPPORTED),
+    (_shape(dtype=0, D=128), _lib.SF_ERR_UNSUPPORTED),
+    (_shape(dtype=7), _lib.SF_ERR_INVALID_ARG),
+    (_shape(seg=-2), _lib.SF_ERR_INVALID_ARG),
+])
+def test_rejects_bad_shapes(shape, code):
+    assert _fwd(shape) == code
+    assert _lib.load().sf_last_error_message()
+
+
+def test_rejects_null_shape_and_missing_pointers():
+    assert _fwd(None) == _lib.SF_ERR_INVALID_ARG
+    assert _fwd(_shape(), q=None) == _lib.SF_ERR_INVALID_ARG
+    assert _fwd(_shape(), o=None) == _lib.SF_ERR_INVALID_ARG
+
+
+def test_rejects_misaligned_and_overlapping():
+    assert _fwd(_shape(), q=G + 2) == _lib.SF_ERR_INVALID_ARG
+    # o overlapping q
+    assert _fwd(_shape(), o=G + 64) == _lib.SF_ERR_INVALID_ARG
+    # S_out overlapping o
+    assert _fwd(_shape(), s_out=6 * G + 256) == _lib.SF_ERR_INVALID_ARG
+    msg = _lib.load().sf_last_error_message().decode()
+    assert "overlaps" in msg
+
+
+def test_rejects_small_workspace():
+    shape = _shape(T=8192, H=2)
+    need = _lib.workspace_bytes(shape)
+    assert need > 0
+    assert _fwd(shape, ws=16 * G, wsn=need - 1) == _lib.SF_ERR_WORKSPACE
+    assert _fwd(shape, ws=None, wsn=0) == _lib.SF_ERR_WORKSPACE
+    assert _fwd(shape, ws=16 * G + 16, wsn=need) == _lib.SF_ERR_INVALID_ARG  # not 256-aligned
+
+
+def test_workspace_sizes():
+    # one segment needs no forward workspace
+    assert _lib.workspace_bytes(_shape(T=64, H=1, seg=0)) >= 0
+    s = _shape(B=1, T=65536, H=16, D=128)
+    f = _lib.workspace_bytes(s)
+    b = _lib.workspace_bytes(s, backward=True)
+    assert b > f > 0
+    # explicit segment length changes the plan and the size
+    assert _lib.workspace_bytes(_shape(T=65536, H=16, seg=1)) > f
+
+
+@pytest.mark.parametrize("T,N,alpha", [(262144, 8, 0.5), (262144, 8, 0.0), (262144, 8, 1.0),
+                                       (131072, 4, 0.75), (65536, 16, 0.25)])
+def test_planner_matches_oracle_search(T, N, alpha):
+    from oracle import plan as op
+    assert chunk_lengths(T, N, alpha) == op.skewed_lengths(T, N, alpha, 1.0, 0.25, 64)

@@ -22,16 +22,6 @@
 
 namespace sfgdn {
 
-// Distribution of a (16*TM) x (16*TN) tile grid over the workgroup's waves:
-// each wave owns one 16-row m-tile and NJ consecutive n-tiles.
-template <int TM, int TN> struct Dist {
-  static constexpr int NJ = TM * TN / NWAVE;
-  static_assert(TM <= NWAVE && (TM * TN) % NWAVE == 0 && NJ >= 1 && TN % NJ == 0,
-                "tile grid does not split over the waves");
-  __device__ static __forceinline__ int m(int w) { return w % TM; }
-  __device__ static __forceinline__ int n0(int w) { return (w / TM) * NJ; }
-};
-
 // Block gate vectors in LDS.
 struct GateLds {
   float* g;     // block-local inclusive cumsum of log alpha
@@ -41,6 +31,12 @@ struct GateLds {
   float* dec;   // exp(g_C - g)
   float* gC;    // [0] = exp(g_C), [1] = g_C
 };
+constexpr size_t kGateBytes = 6 * BLK * sizeof(float) + 16;
+
+__device__ __forceinline__ GateLds gate_lds(unsigned char* base) {
+  float* f = reinterpret_cast<float*>(base);
+  return GateLds{f, f + BLK, f + 2 * BLK, f + 3 * BLK, f + 4 * BLK, f + 5 * BLK};
+}
 
 // Wave 0 only: lane r holds log(alpha_r) and beta_r of token r (0 and 0 for
 // rows past the end of the sequence, which then leave the state unchanged).
@@ -65,48 +61,60 @@ __device__ __forceinline__ void block_gates(float la, float be, const GateLds& G
   }
 }
 
-// A (fp32, row-major, strictly lower) and, when WITH_Q, the masked decayed
-// scores P[r][s] = (s <= r) Gamma_rs q_r.k_s (row-major, T).  Computed as
-// transposed products (K K^T and K Q^T) so each lane stores 4 consecutive s.
-template <typename T, int D, bool WITH_Q>
+// Scores of an NW-wave workgroup (NW = 4 or 8): wave w owns s-tile w % 4 and
+// r-tiles from (w / 4) * (16 / NW).
+//   Af[r][s] = (s < r) beta_r Gamma_rs k_r.k_s      (fp32, strictly lower)
+//   Pl[r][s] = (s <= r) Gamma_rs q_r.k_s            (operand type), if WITH_Q
+// Computed as K K^T and K Q^T with s on the accumulator's m index so each
+// lane stores 4 consecutive s.
+template <typename T, int D, int NW, bool WITH_Q>
 __device__ __forceinline__ void block_scores(const T* Qs, const T* Ks, int ldd, const GateLds& G,
                                              float* Af, int ldf, T* Pl, int ldc) {
-  typedef Dist<4, 4> DS;
+  constexpr int NJ = 16 / NW;
   const int w = wave_id(), lane = lane_id();
-  const int mt = DS::m(w), nt0 = DS::n0(w);
-  f32x4 accA[1][DS::NJ], accP[1][DS::NJ];
-  zero_acc(accA);
-  gemm_nt<T, 1, DS::NJ, D>(accA, Ks + 16 * mt * ldd, ldd, Ks + 16 * nt0 * ldd, ldd);
-  if (WITH_Q) {
-    zero_acc(accP);
-    gemm_nt<T, 1, DS::NJ, D>(accP, Ks + 16 * mt * ldd, ldd, Qs + 16 * nt0 * ldd, ldd);
-  }
-  const int s0 = 16 * mt + 4 * (lane >> 4);
+  const int st = w & 3, r0 = (w >> 2) * NJ;
+  f32x4 accA[NJ], accP[NJ];
 #pragma unroll
-  for (int j = 0; j < DS::NJ; ++j) {
-    const int r = 16 * (nt0 + j) + (lane & 15);
+  for (int j = 0; j < NJ; ++j) accA[j] = accP[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int s = 0; s < D / Mma<T>::KSTEP; ++s) {
+    const auto a = frag_row<T, STD>(Ks + 16 * st * ldd, ldd, s);
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      accA[j] = Mma<T>::mma(a, frag_row<T, STD>(Ks + 16 * (r0 + j) * ldd, ldd, s), accA[j]);
+      if constexpr (WITH_Q)
+        accP[j] = Mma<T>::mma(a, frag_row<T, STD>(Qs + 16 * (r0 + j) * ldd, ldd, s), accP[j]);
+    }
+  }
+  const int s0 = 16 * st + 4 * (lane >> 4);
+  float gs[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) gs[e] = G.g[s0 + e];
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    const int r = 16 * (r0 + j) + (lane & 15);
     const float gr = G.g[r], br = G.beta[r];
     float a[4], p[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int s = s0 + e;
-      const float gam = (s <= r) ? __expf(gr - G.g[s]) : 0.f;
-      a[e] = (s < r) ? br * gam * accA[0][j][e] : 0.f;
-      p[e] = gam * accP[0][j][e];
+      const float gam = (s <= r) ? __expf(gr - gs[e]) : 0.f;
+      a[e] = (s < r) ? br * gam * accA[j][e] : 0.f;
+      p[e] = gam * accP[j][e];
     }
     st4(Af + r * ldf + s0, a[0], a[1], a[2], a[3]);
-    if (WITH_Q) st4(Pl + r * ldc + s0, p[0], p[1], p[2], p[3]);
+    if constexpr (WITH_Q) st4(Pl + r * ldc + s0, p[0], p[1], p[2], p[3]);
   }
 }
 
-// T = (I + A)^{-1} for the strictly lower 64x64 A, in fp32.  The four 16x16
-// diagonal blocks are solved by forward substitution (one lane per column);
-// the off-diagonal blocks follow by block recursion on MFMA:
-//   T_ij = -T_ii (sum_k A_ik T_kj)
-// first for the sub-diagonal pairs (1,0), (3,2), then for rows 32..63 x cols
-// 0..31 at once.  Upper blocks of Tm are left unwritten (they are zero).
-// scratch needs 2*16*20 + 32*36 floats.  Ends with a workgroup barrier.
-__device__ __forceinline__ void block_solve(const float* Af, float* Tm, int ldf, float* scratch) {
+// T = (I + A)^{-1} for the strictly lower 64x64 A, in fp32 (needs >= 4 waves).
+// The four 16x16 diagonal blocks are solved by forward substitution (one lane
+// per column); the off-diagonal blocks follow by block recursion on MFMA,
+//   T_ij = -T_ii (sum_k A_ik T_kj),
+// first for the pairs (1,0) and (3,2), then for rows 32..63 x cols 0..31.
+// The upper blocks of Tm are never part of T; they serve as scratch here and
+// must be treated as zero by readers.  Ends with a workgroup barrier.
+__device__ __forceinline__ void block_solve(const float* Af, float* Tm, int ldf) {
   const int w = wave_id(), lane = lane_id();
   if (w == 0) {
     const int base = 16 * (lane >> 4), c = lane & 15;
@@ -121,23 +129,23 @@ __device__ __forceinline__ void block_solve(const float* Af, float* Tm, int ldf,
 #pragma unroll
     for (int r = 0; r < 16; ++r) Tm[(base + r) * ldf + base + c] = x[r];
   }
-  __syncthreads();
-  float* X = scratch;               // two 16 x 20 blocks
-  float* R = scratch + 2 * 16 * 20; // 32 x 36
+  lds_barrier();
+  float* X = Tm + 16;  // blocks (0,1) and (0,2) as scratch: X_w at column 16 (w + 1)
   if (w < 2) {
     const int ib = 2 * w + 1, jb = 2 * w;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     gemm_nn_f32<16>(acc, Af + 16 * ib * ldf + 16 * jb, ldf, Tm + 16 * jb * ldf + 16 * jb, ldf);
-    store_tile_N(acc, X + w * 16 * 20, 20, 0, 0);
+    store_tile_N(acc, X + 16 * w, ldf, 0, 0);
   }
-  __syncthreads();
+  lds_barrier();
   if (w < 2) {
     const int ib = 2 * w + 1, jb = 2 * w;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    gemm_nn_f32<16>(acc, Tm + 16 * ib * ldf + 16 * ib, ldf, X + w * 16 * 20, 20);
+    gemm_nn_f32<16>(acc, Tm + 16 * ib * ldf + 16 * ib, ldf, X + 16 * w, ldf);
     store_tile_N(acc, Tm + 16 * ib * ldf + 16 * jb, ldf, 0, 0, -1.f);
   }
-  __syncthreads();
+  lds_barrier();
+  float* R = Tm + 32;  // rows 0..31 x cols 32..63 (upper blocks) as scratch
   if (w < 4) {
     const int ib = 2 + (w >> 1), jb = w & 1;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -145,33 +153,37 @@ __device__ __forceinline__ void block_solve(const float* Af, float* Tm, int ldf,
       gemm_nn_f32<32>(acc, Af + 16 * ib * ldf, ldf, Tm, ldf);
     else          // A_{ib,1} T_{1,1}
       gemm_nn_f32<16>(acc, Af + 16 * ib * ldf + 16, ldf, Tm + 16 * ldf + 16, ldf);
-    store_tile_N(acc, R + (ib - 2) * 16 * 36 + 16 * jb, 36, 0, 0);
+    store_tile_N(acc, R + 16 * (ib - 2) * ldf + 16 * jb, ldf, 0, 0);
   }
-  __syncthreads();
+  lds_barrier();
   if (w < 4) {
     const int ib = 2 + (w >> 1), jb = w & 1;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     if (ib == 2)  // T_22 R_{2,jb}
-      gemm_nn_f32<16>(acc, Tm + 32 * ldf + 32, ldf, R + 16 * jb, 36);
+      gemm_nn_f32<16>(acc, Tm + 32 * ldf + 32, ldf, R + 16 * jb, ldf);
     else          // T_32 R_{2,jb} + T_33 R_{3,jb}
-      gemm_nn_f32<32>(acc, Tm + 48 * ldf + 32, ldf, R + 16 * jb, 36);
+      gemm_nn_f32<32>(acc, Tm + 48 * ldf + 32, ldf, R + 16 * jb, ldf);
     store_tile_N(acc, Tm + 16 * ib * ldf + 16 * jb, ldf, 0, 0, -1.f);
   }
-  __syncthreads();
+  lds_barrier();
 }
 
-// Tp = T diag(beta o gamma), Tpp = T diag(beta), in the operand type.
-template <typename T>
+// Tp = T diag(beta o gamma), Tpp = T diag(beta), in the operand type, by a
+// workgroup of NT threads.  Upper 16x16 blocks are written as zero.
+template <typename T, int NT>
 __device__ __forceinline__ void block_tprime(const float* Tm, int ldf, const GateLds& G, T* Tp,
                                              T* Tpp, int ldc) {
-  const int r = threadIdx.x >> 3, s0 = (threadIdx.x & 7) * 8;
-  const bool upper = (s0 >> 4) > (r >> 4);
+  constexpr int EPT = BLK * BLK / NT;   // elements per thread
+  constexpr int TPR = BLK / EPT;        // threads per row
+  static_assert(EPT % 4 == 0 && EPT <= 16, "tprime split");
+  const int r = threadIdx.x / TPR, s0 = (threadIdx.x % TPR) * EPT;
 #pragma unroll
-  for (int x = 0; x < 8; x += 4) {
+  for (int x = 0; x < EPT; x += 4) {
+    const int s = s0 + x;
+    const bool upper = (s >> 4) > (r >> 4);
     float t[4];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) t[e] = upper ? 0.f : Tm[r * ldf + s0 + x + e];
-    const int s = s0 + x;
+    for (int e = 0; e < 4; ++e) t[e] = upper ? 0.f : Tm[r * ldf + s + e];
     st4(Tp + r * ldc + s, t[0] * G.bg[s], t[1] * G.bg[s + 1], t[2] * G.bg[s + 2],
         t[3] * G.bg[s + 3]);
     st4(Tpp + r * ldc + s, t[0] * G.beta[s], t[1] * G.beta[s + 1], t[2] * G.beta[s + 2],
@@ -179,23 +191,126 @@ __device__ __forceinline__ void block_tprime(const float* Tm, int ldf, const Gat
   }
 }
 
-// Wn = -W (row-major [r][dk]) from W^T = K^T Tp^T, and the U accumulator
-// accU[m = s][n = dv] = (Tpp V)[s][dv] for this wave's tiles.
+// Wn = -W, row-major [r][dk], by a workgroup of D/16 waves (wave w: dk-tile
+// w): computed as W^T = K^T Tp^T with K^T read through the transpose read
+// from the row-major K tile.
 template <typename T, int D>
-__device__ __forceinline__ void block_wu(const T* KTs, const T* VTs, const T* Tp, const T* Tpp,
-                                         int ldc, T* Wn, int ldd,
-                                         f32x4 (&accU)[1][Dist<4, D / 16>::NJ]) {
-  typedef Dist<D / 16, 4> DW;
-  typedef Dist<4, D / 16> DU;
+__device__ __forceinline__ void block_w(const T* Ks, int ldd, const T* Tp, int ldc, T* Wn) {
   const int w = wave_id();
-  f32x4 accW[1][DW::NJ];
-  zero_acc(accW);
-  gemm_nt<T, 1, DW::NJ, BLK>(accW, KTs + 16 * DW::m(w) * ldc, ldc, Tp + 16 * DW::n0(w) * ldc, ldc);
+  f32x4 acc[4];
 #pragma unroll
-  for (int j = 0; j < DW::NJ; ++j)
-    store_tile_T(accW[0][j], Wn, ldd, 16 * DW::m(w), 16 * (DW::n0(w) + j), -1.f);
-  zero_acc(accU);
-  gemm_nt<T, 1, DU::NJ, BLK>(accU, Tpp + 16 * DU::m(w) * ldc, ldc, VTs + 16 * DU::n0(w) * ldc, ldc);
+  for (int j = 0; j < 4; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int s = 0; s < BLK / Mma<T>::KSTEP; ++s) {
+    const auto a = frag_tr<T, STD>(Ks + 16 * w, ldd, s);
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      acc[j] = Mma<T>::mma(a, frag_row<T, STD>(Tp + 16 * j * ldc, ldc, s), acc[j]);
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j) store_tile_T(acc[j], Wn, ldd, 16 * w, 16 * j, -1.f);
+}
+
+// U[s][dv] = (Tpp V)[s][dv] for this wave's dv-tiles dv0 .. dv0+NDV-1, into
+// register tiles u[dv-tile][s-tile] (s on the accumulator's m index).
+template <typename T, int NDV>
+__device__ __forceinline__ void block_u(const T* Tpp, int ldc, const T* Vs, int ldd, int dv0,
+                                        f32x4 (&u)[NDV][4]) {
+#pragma unroll
+  for (int b = 0; b < NDV; ++b)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) u[b][i] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int s = 0; s < BLK / Mma<T>::KSTEP; ++s) {
+    typename Mma<T>::frag bv[NDV];
+#pragma unroll
+    for (int b = 0; b < NDV; ++b) bv[b] = frag_tr<T, STD>(Vs + 16 * (dv0 + b), ldd, s);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const auto a = frag_row<T, STD>(Tpp + 16 * i * ldc, ldc, s);
+#pragma unroll
+      for (int b = 0; b < NDV; ++b) u[b][i] = Mma<T>::mma(a, bv[b], u[b][i]);
+    }
+  }
+}
+
+// acc[b][i] (m = s-tile i, n = dv-tile b) += X[s][:] . St[b]^T where the state
+// tiles St[b][a] hold S^T (m = dk-tile a, n = dv-tile b) in registers; X is a
+// row-major [s][dk] LDS tile (here -W).  Gives Vn = U - W S^T.
+template <typename T, int D, int NDV>
+__device__ __forceinline__ void block_x_st(const T* X, int ldd, const f32x4 (&St)[NDV][D / 16],
+                                           f32x4 (&acc)[NDV][4]) {
+#pragma unroll
+  for (int s = 0; s < D / Mma<T>::KSTEP; ++s) {
+    typename Mma<T>::frag bs[NDV];
+#pragma unroll
+    for (int b = 0; b < NDV; ++b) bs[b] = AccFrag<T>::get(St[b], s);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const auto a = frag_row<T, PERM>(X + 16 * i * ldd, ldd, s);
+#pragma unroll
+      for (int b = 0; b < NDV; ++b) acc[b][i] = Mma<T>::mma(a, bs[b], acc[b][i]);
+    }
+  }
+}
+
+// acc[b][j] (m = dv-tile b, n = r-tile j) += S[dv][:] . Y[r][:] with S from the
+// register state tiles and Y a row-major [r][dk] LDS tile (Q):  (S Y^T).
+template <typename T, int D, int NDV>
+__device__ __forceinline__ void block_s_yT(const f32x4 (&St)[NDV][D / 16], const T* Y, int ldd,
+                                           f32x4 (&acc)[NDV][4]) {
+#pragma unroll
+  for (int s = 0; s < D / Mma<T>::KSTEP; ++s) {
+    typename Mma<T>::frag bq[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) bq[j] = frag_row<T, PERM>(Y + 16 * j * ldd, ldd, s);
+#pragma unroll
+    for (int b = 0; b < NDV; ++b) {
+      const auto a = AccFrag<T>::get(St[b], s);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[b][j] = Mma<T>::mma(a, bq[j], acc[b][j]);
+    }
+  }
+}
+
+// acc[b][j] (m = dv-tile b, n = r-tile j) += Vn^T[dv][:] . P[r][:] with Vn in
+// register tiles vn[b][s-tile] and P a row-major [r][s] LDS tile.
+template <typename T, int NDV>
+__device__ __forceinline__ void block_vnT_pT(const f32x4 (&vn)[NDV][4], const T* Pl, int ldc,
+                                             f32x4 (&acc)[NDV][4]) {
+#pragma unroll
+  for (int s = 0; s < BLK / Mma<T>::KSTEP; ++s) {
+    typename Mma<T>::frag bp[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) bp[j] = frag_row<T, PERM>(Pl + 16 * j * ldc, ldc, s);
+#pragma unroll
+    for (int b = 0; b < NDV; ++b) {
+      const auto a = AccFrag<T>::get(vn[b], s);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[b][j] = Mma<T>::mma(a, bp[j], acc[b][j]);
+    }
+  }
+}
+
+// St[b][a] (m = dk-tile a, n = dv-tile b) += K^T[dk][:] . (D Vn)^T[dv][:]:
+// the state update's write term Vn^T D K, with K^T through the transpose read
+// from the row-major K tile and D Vn from the register tiles vn scaled by dsc.
+template <typename T, int D, int NDV>
+__device__ __forceinline__ void block_state_write(const T* Ks, int ldd, const f32x4 (&vn)[NDV][4],
+                                                  const f32x4 (&dsc)[4],
+                                                  f32x4 (&St)[NDV][D / 16]) {
+#pragma unroll
+  for (int s = 0; s < BLK / Mma<T>::KSTEP; ++s) {
+    typename Mma<T>::frag bv[NDV];
+#pragma unroll
+    for (int b = 0; b < NDV; ++b) bv[b] = AccFrag<T>::get_scaled(vn[b], dsc, s);
+#pragma unroll
+    for (int a = 0; a < D / 16; ++a) {
+      const auto ka = frag_tr<T, PERM>(Ks + 16 * a, ldd, s);
+#pragma unroll
+      for (int b = 0; b < NDV; ++b) St[b][a] = Mma<T>::mma(ka, bv[b], St[b][a]);
+    }
+  }
 }
 
 }  // namespace sfgdn

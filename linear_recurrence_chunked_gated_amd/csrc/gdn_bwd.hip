@@ -1,11 +1,833 @@
 // Backward kernels of one pipeline chunk of the gated delta rule.
+//
+// The chunk backward ("Bwd_i(Sbar_i^out) -> Sbar_i^in", Eq. 7 of the Pith
+// review of StateFlow, "What carries the argument") rebuilds the chunk's state
+// trajectory from its inputs (Referee Report, major comment 1: the backward
+// must reconstruct the same intra-chunk trajectory, including V_new) and runs
+// the state gradient backwards through it.  Per block, with dS' the gradient
+// with respect to the block's exit state,
+//   dVn = P^T dO + D K dS'^T
+//   dS  = gamma_C dS' + dO^T diag(gamma) Q - dVn^T W     (entry-state gradient)
+// which, like the forward, is affine: dS = dS' M_b^T + NB_b.  The launch
+// sequence is
+//   1. segment maps (M, N) of the forward                       [forward kernel]
+//   2. gdn_bwd_dscan<summary>: per segment, dS at its entry from a zero exit
+//      gradient (NB_seg)
+//   3. forward chain of entry states, reverse chain of exit gradients
+//   4. block entry states h_b of every block                    [forward kernel]
+//   5. gdn_bwd_dscan<main>: per segment from its true exit gradient, the exit
+//      gradient dS'_b of every block, and dS_in
+//   6. gdn_bwd_grads: per block, fully parallel, dq dk dv dalpha dbeta.
 #include "gdn_kernels.hpp"
 
 namespace sfgdn {
 
 template <typename T, int D>
-hipError_t launch_bwd(const BwdArgs&, hipStream_t, Profiler*) {
-  return hipErrorNotSupported;
+__device__ __forceinline__ const T* tok_base(const void* p, int T_, int H, int b, int h) {
+  return reinterpret_cast<const T*>(p) + ((size_t)b * T_ * H + h) * D;
+}
+
+// ------------------------------------------------------------------ LDS ----
+// dscan: RQ Q -> Tm -> Wn | RK K | RO dO | RA Af -> Tp,Tpp | RP P | RG gates
+template <typename T, int D> struct ScanLds {
+  static constexpr int LDD = D + Lay<T>::PAD;
+  static constexpr int LDC = BLK + Lay<T>::PAD;
+  static constexpr int LDF = BLK + 4;
+  static constexpr size_t cmax(size_t a, size_t b) { return a > b ? a : b; }
+  static constexpr size_t rowD = (size_t)BLK * LDD * sizeof(T);
+  static constexpr size_t f64x64 = (size_t)BLK * LDF * sizeof(float);
+  static constexpr size_t zQ = cmax(rowD, f64x64);
+  static constexpr size_t zA = cmax(f64x64, 2 * (size_t)BLK * LDC * sizeof(T));
+  static constexpr size_t zP = (size_t)BLK * LDC * sizeof(T);
+  static constexpr size_t oQ = 0, oK = oQ + zQ, oO = oK + rowD, oA = oO + rowD, oP = oA + zA,
+                          oG = oP + zP;
+  static constexpr size_t bytes = oG + kGateBytes;
+  static_assert(bytes <= 160 * 1024, "LDS budget");
+};
+
+// Per-block inputs of the reverse scan in flight (q, k, dO rows and gates).
+template <typename T, int D> struct ScanPrefetch {
+  typedef Tile<T, D, 4 * D> Tl;
+  uint4 rq[Tl::NCH], rk[Tl::NCH], ro[Tl::NCH];
+  float la = 0.f, be = 0.f;
+  __device__ __forceinline__ void fetch(const T* q, const T* k, const T* dO, const float* al,
+                                        const float* bt, size_t rs, int H, int t0, int nv) {
+    Tl::load(rq, q + (size_t)t0 * rs, rs, nv);
+    Tl::load(rk, k + (size_t)t0 * rs, rs, nv);
+    Tl::load(ro, dO + (size_t)t0 * rs, rs, nv);
+    if (wave_id() == 0) {
+      const int lane = lane_id();
+      const size_t idx = (size_t)(t0 + min(lane, nv - 1)) * H;
+      const float x = al[idx], y = bt[idx];
+      la = lane < nv ? __logf(x) : 0.f;
+      be = lane < nv ? y : 0.f;
+    }
+  }
+  __device__ __forceinline__ void stage(T* Qs, T* Ks, T* Os, int ld, int nv, const GateLds& G) {
+    Tl::to_lds(rq, Qs, ld, nv);
+    Tl::to_lds(rk, Ks, ld, nv);
+    Tl::to_lds(ro, Os, ld, nv);
+    if (wave_id() == 0) block_gates(la, be, G);
+  }
+};
+
+// B operand rows dv of gamma_r dO[r][dv] (k = r, STD order): the transpose read
+// of dO scaled per contraction element.
+template <typename T>
+__device__ __forceinline__ typename Mma<T>::frag frag_tr_gamma(const T* p, int ld, int s,
+                                                               const float* gam);
+template <>
+__device__ __forceinline__ bf16x8 frag_tr_gamma<bf16>(const bf16* p, int ld, int s,
+                                                      const float* gam) {
+  bf16x8 f = frag_tr<bf16, STD>(p, ld, s);
+  const int r0 = 32 * s + 8 * (lane_id() >> 4);
+#pragma unroll
+  for (int j = 0; j < 8; ++j) f[j] = (bf16)((float)f[j] * gam[r0 + j]);
+  return f;
+}
+template <>
+__device__ __forceinline__ float frag_tr_gamma<float>(const float* p, int ld, int s,
+                                                      const float* gam) {
+  return frag_tr<float, STD>(p, ld, s) * gam[4 * s + (lane_id() >> 4)];
+}
+
+// ------------------------------------------------------- reverse dS scan ---
+// Wave w owns dv-tile w of the state gradient dSv (tiles m = dk, n = dv, i.e.
+// dS^T).  Blocks of the segment are visited last to first.  MAIN: start from
+// the segment's exit gradient, store dS' of every block to dhst and dS_in from
+// segment 0.  Otherwise: start from zero and store the segment's NB map.
+template <typename T, int D, bool MAIN>
+__global__ __launch_bounds__(4 * D, 2) void gdn_bwd_dscan_kernel(BwdArgs a, int seg0, int nseg,
+                                                                 const float* dSend,
+                                                                 int dsend_P) {
+  typedef ScanLds<T, D> Lz;
+  constexpr int DKT = D / 16, NW = D / 16;
+  constexpr int LDD = Lz::LDD, LDC = Lz::LDC, LDF = Lz::LDF;
+  extern __shared__ __align__(16) unsigned char smem[];
+  T* Qs = reinterpret_cast<T*>(smem + Lz::oQ);
+  float* Tm = reinterpret_cast<float*>(smem + Lz::oQ);
+  T* Wn = reinterpret_cast<T*>(smem + Lz::oQ);
+  T* Ks = reinterpret_cast<T*>(smem + Lz::oK);
+  T* Os = reinterpret_cast<T*>(smem + Lz::oO);
+  float* Af = reinterpret_cast<float*>(smem + Lz::oA);
+  T* Tp = reinterpret_cast<T*>(smem + Lz::oA);
+  T* Tpp = Tp + BLK * LDC;
+  T* Pl = reinterpret_cast<T*>(smem + Lz::oP);
+  const GateLds G = gate_lds(smem + Lz::oG);
+
+  const FwdArgs& f = a.f;
+  const int w = wave_id(), lane = lane_id(), g4 = 4 * (lane >> 4), li = lane & 15;
+  const int seg = seg0 + blockIdx.x % nseg, bh = blockIdx.x / nseg;
+  const int b = bh / f.H, h = bh % f.H;
+  const int blk0 = seg * f.L, blk1 = min(f.nblk, blk0 + f.L);
+  const size_t rs = (size_t)f.H * D;
+  const T* q = tok_base<T, D>(f.q, f.T, f.H, b, h);
+  const T* k = tok_base<T, D>(f.k, f.T, f.H, b, h);
+  const T* dO = tok_base<T, D>(a.dO, f.T, f.H, b, h);
+  const float* al = f.alpha + (size_t)b * f.T * f.H + h;
+  const float* bt = f.beta + (size_t)b * f.T * f.H + h;
+
+  f32x4 dSv[DKT];
+  {
+    const float* G0 = (MAIN && dSend) ? dSend + ((size_t)bh * dsend_P + seg) * D * D : nullptr;
+#pragma unroll
+    for (int aa = 0; aa < DKT; ++aa)
+      dSv[aa] = G0 ? *reinterpret_cast<const f32x4*>(G0 + (size_t)(16 * w + li) * D + 16 * aa + g4)
+                   : f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  ScanPrefetch<T, D> pf;
+  {
+    const int t0 = (blk1 - 1) * BLK;
+    pf.fetch(q, k, dO, al, bt, rs, f.H, t0, min(BLK, f.T - t0));
+  }
+  for (int blk = blk1 - 1; blk >= blk0; --blk) {
+    const int t0 = blk * BLK, nv = min(BLK, f.T - t0);
+    pf.stage(Qs, Ks, Os, LDD, nv, G);
+    if constexpr (MAIN) {
+      float* gb = reinterpret_cast<float*>(a.dhst) + ((size_t)bh * f.nblk + blk) * D * D;
+#pragma unroll
+      for (int aa = 0; aa < DKT; ++aa)
+        *reinterpret_cast<f32x4*>(gb + (size_t)(16 * w + li) * D + 16 * aa + g4) = dSv[aa];
+    }
+    if (blk > blk0) pf.fetch(q, k, dO, al, bt, rs, f.H, t0 - BLK, BLK);
+    lds_barrier();
+    // scores and the dO^T diag(gamma) Q term (needs Q before its region is reused)
+    block_scores<T, D, NW, true>(Qs, Ks, LDD, G, Af, LDF, Pl, LDC);
+    f32x4 X2[DKT];
+#pragma unroll
+    for (int aa = 0; aa < DKT; ++aa) X2[aa] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < BLK / Mma<T>::KSTEP; ++s) {
+      const auto bo = frag_tr_gamma<T>(Os + 16 * w, LDD, s, G.gam);
+#pragma unroll
+      for (int aa = 0; aa < DKT; ++aa)
+        X2[aa] = Mma<T>::mma(frag_tr<T, STD>(Qs + 16 * aa, LDD, s), bo, X2[aa]);
+    }
+    lds_barrier();
+    block_solve(Af, Tm, LDF);
+    block_tprime<T, 64 * NW>(Tm, LDF, G, Tp, Tpp, LDC);
+    lds_barrier();
+    block_w<T, D>(Ks, LDD, Tp, LDC, Wn);
+    lds_barrier();
+    // dVn = P^T dO + D (K dS'^T)
+    f32x4 dvn[4], kd[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dvn[i] = kd[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < BLK / Mma<T>::KSTEP; ++s) {
+      const auto bo = frag_tr<T, STD>(Os + 16 * w, LDD, s);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) dvn[i] = Mma<T>::mma(frag_tr<T, STD>(Pl + 16 * i, LDC, s), bo, dvn[i]);
+    }
+#pragma unroll
+    for (int s = 0; s < D / Mma<T>::KSTEP; ++s) {
+      const auto bs = AccFrag<T>::get(dSv, s);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) kd[i] = Mma<T>::mma(frag_row<T, PERM>(Ks + 16 * i * LDD, LDD, s), bs, kd[i]);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) dvn[i][e] += G.dec[16 * i + g4 + e] * kd[i][e];
+    // dS = gamma_C dS' + dO^T diag(gamma) Q - dVn^T W   (Wn holds -W)
+    const float gc = G.gC[0];
+#pragma unroll
+    for (int aa = 0; aa < DKT; ++aa) dSv[aa] = gc * dSv[aa] + X2[aa];
+#pragma unroll
+    for (int s = 0; s < BLK / Mma<T>::KSTEP; ++s) {
+      const auto bv = AccFrag<T>::get(dvn, s);
+#pragma unroll
+      for (int aa = 0; aa < DKT; ++aa)
+        dSv[aa] = Mma<T>::mma(frag_tr<T, PERM>(Wn + 16 * aa, LDD, s), bv, dSv[aa]);
+    }
+    lds_barrier();
+  }
+
+  float* out = MAIN ? ((seg == 0 && a.dS_in) ? a.dS_in + (size_t)bh * D * D : nullptr)
+                    : a.NBseg + ((size_t)bh * f.P + seg) * D * D;
+  if (out) {
+#pragma unroll
+    for (int aa = 0; aa < DKT; ++aa)
+      *reinterpret_cast<f32x4*>(out + (size_t)(16 * w + li) * D + 16 * aa + g4) = dSv[aa];
+  }
+}
+
+// ------------------------------------------------------------ chain ---------
+// Exit gradients of all segments: dSend[P-1] = dS_out (or 0),
+// dSend[j-1] = dSend[j] M_j^T + NB_j.  Same layout as the forward chain.
+template <int D>
+__global__ __launch_bounds__(256) void gdn_chain_bwd_kernel(const float* dS_out, const float* Mseg,
+                                                            const float* NBseg, float* dSend,
+                                                            int P) {
+  constexpr int RT = D / 16, NT = D / 64, KS = D / 4, LDS_ = D + 4;
+  __shared__ __align__(16) float Sl[16 * LDS_];
+  const int w = wave_id(), lane = lane_id();
+  const int bh = blockIdx.x / RT, r0 = 16 * (blockIdx.x % RT);
+  const size_t DD = (size_t)D * D;
+  const float* G0 = dS_out ? dS_out + bh * DD : nullptr;
+  float* out = dSend + (size_t)bh * P * DD;
+  for (int i = threadIdx.x; i < 16 * D; i += 256) {
+    const int rr = i / D, cc = i % D;
+    const float x = G0 ? G0[(size_t)(r0 + rr) * D + cc] : 0.f;
+    Sl[rr * LDS_ + cc] = x;
+    out[(size_t)(P - 1) * DD + (size_t)(r0 + rr) * D + cc] = x;
+  }
+  float bm[NT][KS], nn[NT][4];
+  auto load_map = [&](int j, float (&m)[NT][KS], float (&n)[NT][4]) {
+    const float* M = Mseg + ((size_t)bh * P + j) * DD;
+    const float* N = NBseg + ((size_t)bh * P + j) * DD;
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const int col = 16 * (w * NT + t) + (lane & 15);
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) m[t][ks] = M[(size_t)col * D + 4 * ks + (lane >> 4)];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) n[t][e] = N[(size_t)(r0 + 4 * (lane >> 4) + e) * D + col];
+    }
+  };
+  if (P > 1) load_map(P - 1, bm, nn);
+  lds_barrier();
+  for (int j = P - 1; j >= 1; --j) {
+    float bm2[NT][KS], nn2[NT][4];
+    const bool more = j >= 2;
+    if (more) load_map(j - 1, bm2, nn2);
+    f32x4 acc[NT][2];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      acc[t][0] = f32x4{nn[t][0], nn[t][1], nn[t][2], nn[t][3]};
+      acc[t][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const float av = Sl[(lane & 15) * LDS_ + 4 * ks + (lane >> 4)];
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+        acc[t][ks & 1] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bm[t][ks], acc[t][ks & 1], 0, 0, 0);
+    }
+    lds_barrier();
+    float* Snext = out + (size_t)(j - 1) * DD;
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const int n = 16 * (w * NT + t) + (lane & 15);
+      const f32x4 x = acc[t][0] + acc[t][1];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int m = 4 * (lane >> 4) + e;
+        Sl[m * LDS_ + n] = x[e];
+        Snext[(size_t)(r0 + m) * D + n] = x[e];
+      }
+    }
+    if (more) {
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) bm[t][ks] = bm2[t][ks];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) nn[t][e] = nn2[t][e];
+      }
+    }
+    lds_barrier();
+  }
+}
+
+// -------------------------------------------------------- block gradients ---
+// Sums of a 16x16 accumulator tile C[m][n] (lane: m = 4 g + e, n = i):
+// over n for each m (result valid in lanes with i == 0, element e), and over
+// m for each n (result valid in lanes 0..15).
+__device__ __forceinline__ f32x4 tile_sum_over_n(f32x4 v) {
+#pragma unroll
+  for (int off = 1; off < 16; off <<= 1)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] += __shfl_xor(v[e], off, 64);
+  return v;
+}
+__device__ __forceinline__ float tile_sum_over_m(f32x4 v) {
+  float x = (v[0] + v[1]) + (v[2] + v[3]);
+  x += __shfl_xor(x, 16, 64);
+  x += __shfl_xor(x, 32, 64);
+  return x;
+}
+// part[m0 + m] += sum over n   (one writer lane per entry)
+__device__ __forceinline__ void add_rows(float* part, int m0, f32x4 v, float sign = 1.f) {
+  v = tile_sum_over_n(v);
+  const int lane = lane_id();
+  if ((lane & 15) == 0) {
+    float* p = part + m0 + 4 * (lane >> 4);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) p[e] += sign * v[e];
+  }
+}
+// part[n0 + n] += sum over m
+__device__ __forceinline__ void add_cols(float* part, int n0, f32x4 v, float sign = 1.f) {
+  const float x = tile_sum_over_m(v);
+  const int lane = lane_id();
+  if (lane < 16) part[n0 + lane] += sign * x;
+}
+
+// LDS plan of the gradient kernel (regions reused by phase):
+//   RQ Q | RK K | RV V -> Y | RO dO -> dW | RT Tm | RA Af -> Tp, Tpp (-> dVn, dKK
+//   for fp32) | RP P -> dPm | RW Wn -> Vn -> dT | RD dVn -> dKK (bf16) | gates,
+//   per-wave partial sums.
+template <typename T, int D> struct GradLds {
+  static constexpr int NW = D / 16;
+  static constexpr int LDD = D + Lay<T>::PAD;
+  static constexpr int LDC = BLK + Lay<T>::PAD;
+  static constexpr int LDF = BLK + 4;
+  static constexpr size_t cmax(size_t a, size_t b) { return a > b ? a : b; }
+  static constexpr size_t rowD = (size_t)BLK * LDD * sizeof(T);
+  static constexpr size_t f64x64 = (size_t)BLK * LDF * sizeof(float);
+  static constexpr size_t sq64 = (size_t)BLK * LDC * sizeof(T);
+  static constexpr bool DVN_IN_A = sizeof(T) == 4;  // dVn fits the Tpp half only for fp32
+  static constexpr size_t zR = cmax(rowD, f64x64);
+  static constexpr size_t zA = cmax(f64x64, 2 * sq64);
+  static constexpr size_t zW = cmax(rowD, f64x64);
+  static constexpr size_t zD = DVN_IN_A ? 0 : cmax(rowD, sq64);
+  static constexpr size_t zPart = (3 * NW * BLK + NW + 4) * sizeof(float);
+  static constexpr size_t oQ = 0, oK = oQ + zR, oV = oK + zR, oO = oV + zR, oT = oO + zR,
+                          oA = oT + f64x64, oP = oA + zA, oW = oP + sq64, oD = oW + zW,
+                          oG = oD + zD, oPart = oG + kGateBytes;
+  static constexpr size_t bytes = oPart + zPart;
+  static_assert(bytes <= 160 * 1024, "LDS budget");
+  static_assert(!DVN_IN_A || sq64 >= rowD, "dVn must fit the Tpp half");
+};
+
+template <typename T, int D>
+__global__ __launch_bounds__(4 * D, 2) void gdn_bwd_grads_kernel(BwdArgs a) {
+  typedef GradLds<T, D> Lz;
+  constexpr int NW = Lz::NW, DKT = D / 16;
+  constexpr int LDD = Lz::LDD, LDC = Lz::LDC, LDF = Lz::LDF;
+  constexpr int NJ = 16 / NW;  // 64x64 tiles per wave
+  extern __shared__ __align__(16) unsigned char smem[];
+  T* Qs = reinterpret_cast<T*>(smem + Lz::oQ);
+  T* Ks = reinterpret_cast<T*>(smem + Lz::oK);
+  T* Vs = reinterpret_cast<T*>(smem + Lz::oV);
+  float* Yf = reinterpret_cast<float*>(smem + Lz::oV);
+  T* Os = reinterpret_cast<T*>(smem + Lz::oO);
+  T* dWs = reinterpret_cast<T*>(smem + Lz::oO);
+  float* Tm = reinterpret_cast<float*>(smem + Lz::oT);
+  float* Af = reinterpret_cast<float*>(smem + Lz::oA);
+  T* Tp = reinterpret_cast<T*>(smem + Lz::oA);
+  T* Tpp = Tp + BLK * LDC;
+  T* Pl = reinterpret_cast<T*>(smem + Lz::oP);
+  T* Wn = reinterpret_cast<T*>(smem + Lz::oW);
+  T* Vns = reinterpret_cast<T*>(smem + Lz::oW);
+  float* dTf = reinterpret_cast<float*>(smem + Lz::oW);
+  T* dVns = Lz::DVN_IN_A ? Tpp : reinterpret_cast<T*>(smem + Lz::oD);
+  T* dKKs = dVns;
+  const GateLds G = gate_lds(smem + Lz::oG);
+  float* part = reinterpret_cast<float*>(smem + Lz::oPart);
+
+  const FwdArgs& f = a.f;
+  const int w = wave_id(), lane = lane_id(), g4 = 4 * (lane >> 4), li = lane & 15;
+  float* dgp = part + w * BLK;                // dg per token, this wave's share
+  float* dbp = part + NW * BLK + w * BLK;     // dbeta per token
+  float* ddp = part + 2 * NW * BLK + w * BLK; // dD per token
+  float* dgc = part + 3 * NW * BLK;           // per-wave <dS', S>
+  const int blk = blockIdx.x % f.nblk, bh = blockIdx.x / f.nblk;
+  const int b = bh / f.H, h = bh % f.H;
+  const int t0 = blk * BLK, nv = min(BLK, f.T - t0);
+  const size_t rs = (size_t)f.H * D;
+  const T* q = tok_base<T, D>(f.q, f.T, f.H, b, h) + (size_t)t0 * rs;
+  const T* k = tok_base<T, D>(f.k, f.T, f.H, b, h) + (size_t)t0 * rs;
+  const T* v = tok_base<T, D>(f.v, f.T, f.H, b, h) + (size_t)t0 * rs;
+  const T* dO = tok_base<T, D>(a.dO, f.T, f.H, b, h) + (size_t)t0 * rs;
+  T* dq = const_cast<T*>(tok_base<T, D>(a.dq, f.T, f.H, b, h)) + (size_t)t0 * rs;
+  T* dk = const_cast<T*>(tok_base<T, D>(a.dk, f.T, f.H, b, h)) + (size_t)t0 * rs;
+  T* dv = const_cast<T*>(tok_base<T, D>(a.dv, f.T, f.H, b, h)) + (size_t)t0 * rs;
+  const size_t gofs = (size_t)b * f.T * f.H + (size_t)t0 * f.H + h;
+  const float* hS = reinterpret_cast<const float*>(a.hst) + ((size_t)bh * f.nblk + blk) * D * D;
+  const float* hG = reinterpret_cast<const float*>(a.dhst) + ((size_t)bh * f.nblk + blk) * D * D;
+
+  // ---- A: inputs, states (by dv-tile), partial sums
+  {
+    typedef Tile<T, D, 4 * D> Tl;
+    uint4 r0[Tl::NCH], r1[Tl::NCH], r2[Tl::NCH], r3[Tl::NCH];
+    Tl::load(r0, q, rs, nv);
+    Tl::load(r1, k, rs, nv);
+    Tl::load(r2, v, rs, nv);
+    Tl::load(r3, dO, rs, nv);
+    float la = 0.f, be = 0.f;
+    if (w == 0) {
+      const size_t idx = (size_t)min(lane, nv - 1) * f.H;
+      const float x = f.alpha[gofs + idx], y = f.beta[gofs + idx];
+      la = lane < nv ? __logf(x) : 0.f;
+      be = lane < nv ? y : 0.f;
+    }
+    for (int i = threadIdx.x; i < 3 * NW * BLK + NW + 4; i += 64 * NW) part[i] = 0.f;
+    Tl::to_lds(r0, Qs, LDD, nv);
+    Tl::to_lds(r1, Ks, LDD, nv);
+    Tl::to_lds(r2, Vs, LDD, nv);
+    Tl::to_lds(r3, Os, LDD, nv);
+    if (w == 0) block_gates(la, be, G);
+  }
+  f32x4 Sx[DKT], dSx[DKT];  // by dv-tile: m = dk-tile, n = dv-tile w
+#pragma unroll
+  for (int aa = 0; aa < DKT; ++aa) {
+    const size_t off = (size_t)(16 * w + li) * D + 16 * aa + g4;
+    Sx[aa] = *reinterpret_cast<const f32x4*>(hS + off);
+    dSx[aa] = *reinterpret_cast<const f32x4*>(hG + off);
+  }
+  {
+    f32x4 p = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int aa = 0; aa < DKT; ++aa) p += Sx[aa] * dSx[aa];
+    float x = (p[0] + p[1]) + (p[2] + p[3]);
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) x += __shfl_xor(x, off, 64);
+    lds_barrier();  // partial arrays zeroed
+    if (lane == 0) dgc[w] = x;
+  }
+  lds_barrier();
+  // ---- B: scores
+  block_scores<T, D, NW, true>(Qs, Ks, LDD, G, Af, LDF, Pl, LDC);
+  lds_barrier();
+  // ---- C: T = (I + A)^{-1}, Tp, Tpp; zero Tm's upper blocks (solve scratch)
+  block_solve(Af, Tm, LDF);
+  block_tprime<T, 64 * NW>(Tm, LDF, G, Tp, Tpp, LDC);
+  lds_barrier();
+  for (int i = threadIdx.x; i < BLK * BLK; i += 64 * NW) {
+    const int r = i >> 6, s = i & 63;
+    if ((s >> 4) > (r >> 4)) Tm[r * LDF + s] = 0.f;
+  }
+  // ---- D: W, U
+  block_w<T, D>(Ks, LDD, Tp, LDC, Wn);
+  f32x4 U[1][4];
+  block_u<T, 1>(Tpp, LDC, Vs, LDD, w, U);
+  lds_barrier();
+  // ---- E: Vn = U - W S^T (registers), then to LDS
+  {
+    f32x4 Sv[1][DKT];
+#pragma unroll
+    for (int aa = 0; aa < DKT; ++aa) Sv[0][aa] = Sx[aa];
+    block_x_st<T, D, 1>(Wn, LDD, Sv, U);
+  }
+  lds_barrier();
+#pragma unroll
+  for (int i = 0; i < 4; ++i) store_tile_N(U[0][i], Vns, LDD, 16 * i, 16 * w);
+  // dVn = P^T dO + D (K dS'^T)
+  f32x4 dvn[4];
+  {
+    f32x4 kd[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dvn[i] = kd[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < BLK / Mma<T>::KSTEP; ++s) {
+      const auto bo = frag_tr<T, STD>(Os + 16 * w, LDD, s);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) dvn[i] = Mma<T>::mma(frag_tr<T, STD>(Pl + 16 * i, LDC, s), bo, dvn[i]);
+    }
+#pragma unroll
+    for (int s = 0; s < D / Mma<T>::KSTEP; ++s) {
+      const auto bs = AccFrag<T>::get(dSx, s);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) kd[i] = Mma<T>::mma(frag_row<T, PERM>(Ks + 16 * i * LDD, LDD, s), bs, kd[i]);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) dvn[i][e] += G.dec[16 * i + g4 + e] * kd[i][e];
+  }
+  // dV^T = dVn^T Tpp  (m = dv, n = s)
+  {
+    f32x4 acc[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < BLK / Mma<T>::KSTEP; ++s) {
+      const auto av = AccFrag<T>::get(dvn, s);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[j] = Mma<T>::mma(av, frag_tr<T, PERM>(Tpp + 16 * j, LDC, s), acc[j]);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int r = 16 * j + li;
+      if (r < nv) st4(dv + (size_t)r * rs + 16 * w + g4, acc[j][0], acc[j][1], acc[j][2], acc[j][3]);
+    }
+  }
+  lds_barrier();
+  // ---- F: dVn to LDS
+#pragma unroll
+  for (int i = 0; i < 4; ++i) store_tile_N(dvn[i], dVns, LDD, 16 * i, 16 * w);
+  lds_barrier();
+  // ---- G: dP^T (m = s, n = r) = Vn dO^T ; P-term of dg ; dPm = dP o Gamma o mask in place of P
+  {
+    const int st = w & 3, r0 = (w >> 2) * NJ;
+    f32x4 acc[NJ];
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < D / Mma<T>::KSTEP; ++s) {
+      const auto av = frag_row<T, STD>(Vns + 16 * st * LDD, LDD, s);
+#pragma unroll
+      for (int j = 0; j < NJ; ++j)
+        acc[j] = Mma<T>::mma(av, frag_row<T, STD>(Os + 16 * (r0 + j) * LDD, LDD, s), acc[j]);
+    }
+    const int s0 = 16 * st + g4;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const int r = 16 * (r0 + j) + li;
+      T* pp = Pl + r * LDC + s0;
+      f32x4 pg, dm;
+      const float gr = G.g[r];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int s = s0 + e;
+        const float p = (float)pp[e];
+        pg[e] = acc[j][e] * p;
+        dm[e] = (s <= r) ? acc[j][e] * __expf(gr - G.g[s]) : 0.f;
+      }
+      st4(pp, dm[0], dm[1], dm[2], dm[3]);
+      add_cols(dgp, 16 * (r0 + j), pg, 1.f);   // dg_r += sum_s
+      add_rows(dgp, 16 * st, pg, -1.f);        // dg_s -= sum_r
+    }
+  }
+  lds_barrier();
+  // ---- H: dQ^T = diag-scaled (S^T dO^T) + K^T dPm^T  (wave: dk-tile w); dK^T starts
+  f32x4 Sk[DKT];  // by dk-tile: m = dv-tile, n = dk-tile w
+#pragma unroll
+  for (int bb = 0; bb < DKT; ++bb)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) Sk[bb][e] = hS[(size_t)(16 * bb + g4 + e) * D + 16 * w + li];
+  f32x4 dKt[4];
+  {
+    f32x4 acc[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[j] = dKt[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < D / Mma<T>::KSTEP; ++s) {
+      const auto as = AccFrag<T>::get(Sk, s);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[j] = Mma<T>::mma(as, frag_row<T, PERM>(Os + 16 * j * LDD, LDD, s), acc[j]);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int r = 16 * j + li;
+      acc[j] *= G.gam[r];
+      // O-term of dg: dg_r += sum_dk Q[r][dk] dQ1[r][dk]
+      f32x4 qv;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) qv[e] = (float)Qs[r * LDD + 16 * w + g4 + e] * acc[j][e];
+      add_cols(dgp, 16 * j, qv, 1.f);
+    }
+#pragma unroll
+    for (int s = 0; s < BLK / Mma<T>::KSTEP; ++s) {
+      const auto ak = frag_tr<T, STD>(Ks + 16 * w, LDD, s);
+      const auto aq = frag_tr<T, STD>(Qs + 16 * w, LDD, s);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const auto bp = frag_tr<T, STD>(Pl + 16 * j, LDC, s);   // dPm^T rows
+        acc[j] = Mma<T>::mma(ak, frag_row<T, STD>(Pl + 16 * j * LDC, LDC, s), acc[j]);
+        dKt[j] = Mma<T>::mma(aq, bp, dKt[j]);                    // dK1 = Q^T dPm
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int r = 16 * j + li;
+      if (r < nv) st4(dq + (size_t)r * rs + 16 * w + g4, acc[j][0], acc[j][1], acc[j][2], acc[j][3]);
+    }
+  }
+  lds_barrier();  // dO reads done: its region takes dW
+  // ---- I: dW^T = -(S^T dVn^T) -> dW row-major ; dK2^T = dS'^T Vn^T scaled by D ; D-term
+  {
+    f32x4 dSk[DKT];
+#pragma unroll
+    for (int bb = 0; bb < DKT; ++bb)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) dSk[bb][e] = hG[(size_t)(16 * bb + g4 + e) * D + 16 * w + li];
+    f32x4 acc[4], x2[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[j] = x2[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < D / Mma<T>::KSTEP; ++s) {
+      const auto as = AccFrag<T>::get(Sk, s);
+      const auto ag = AccFrag<T>::get(dSk, s);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        acc[j] = Mma<T>::mma(as, frag_row<T, PERM>(dVns + 16 * j * LDD, LDD, s), acc[j]);
+        x2[j] = Mma<T>::mma(ag, frag_row<T, PERM>(Vns + 16 * j * LDD, LDD, s), x2[j]);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      store_tile_T(acc[j], dWs, LDD, 16 * w, 16 * j, -1.f);
+      const int s = 16 * j + li;
+      f32x4 kv;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) kv[e] = (float)Ks[s * LDD + 16 * w + g4 + e] * x2[j][e];
+      add_cols(ddp, 16 * j, kv, 1.f);
+      dKt[j] += G.dec[s] * x2[j];
+    }
+  }
+  lds_barrier();
+  // ---- J: dTp = dW K^T, dTpp = dVn V^T (m = r, n = s); dT; column terms
+  {
+    const int rt = w & 3, s0t = (w >> 2) * NJ;
+    f32x4 a1[NJ], a2[NJ];
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) a1[j] = a2[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < D / Mma<T>::KSTEP; ++s) {
+      const auto aw = frag_row<T, STD>(dWs + 16 * rt * LDD, LDD, s);
+      const auto au = frag_row<T, STD>(dVns + 16 * rt * LDD, LDD, s);
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        a1[j] = Mma<T>::mma(aw, frag_row<T, STD>(Ks + 16 * (s0t + j) * LDD, LDD, s), a1[j]);
+        a2[j] = Mma<T>::mma(au, frag_row<T, STD>(Vs + 16 * (s0t + j) * LDD, LDD, s), a2[j]);
+      }
+    }
+    lds_barrier();  // Vn (region RW) and V reads done before dT overwrites RW
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const int s = 16 * (s0t + j) + li;
+      const float bg = G.bg[s], bs = G.beta[s], gs = G.gam[s];
+      f32x4 dt, c1, c2;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = 16 * rt + g4 + e;
+        const bool low = s <= r;
+        const float tv = low ? Tm[r * LDF + s] : 0.f;
+        dt[e] = low ? a1[j][e] * bg + a2[j][e] * bs : 0.f;
+        c1[e] = a1[j][e] * tv;  // d(beta gamma)_s
+        c2[e] = a2[j][e] * tv;  // dbeta_s through Tpp
+      }
+      store_tile_N(dt, dTf, LDF, 16 * rt, 16 * (s0t + j));
+      const float sbg = tile_sum_over_m(c1), sb2 = tile_sum_over_m(c2);
+      if (lane < 16) {
+        dbp[s] += sb2 + gs * sbg;
+        dgp[s] += bs * gs * sbg;
+      }
+    }
+  }
+  lds_barrier();
+  // ---- K: Y = dT T^T (fp32)
+  {
+    const int rt = w & 3, s0t = (w >> 2) * NJ;
+    f32x4 acc[NJ];
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < BLK / 4; ++s) {
+      const float av = frag_row<float, STD>(dTf + 16 * rt * LDF, LDF, s);
+#pragma unroll
+      for (int j = 0; j < NJ; ++j)
+        acc[j] = Mma<float>::mma(av, frag_row<float, STD>(Tm + 16 * (s0t + j) * LDF, LDF, s), acc[j]);
+    }
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) store_tile_N(acc[j], Yf, LDF, 16 * rt, 16 * (s0t + j));
+  }
+  lds_barrier();
+  // ---- L: dA = -T^T Y (strictly lower); A-terms of dbeta, dg; dKK
+  {
+    const int rt = w & 3, s0t = (w >> 2) * NJ;
+    f32x4 acc[NJ], kk[NJ];
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) acc[j] = kk[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < BLK / 4; ++s) {
+      const float at = frag_tr<float, STD>(Tm + 16 * rt, LDF, s);
+#pragma unroll
+      for (int j = 0; j < NJ; ++j)
+        acc[j] = Mma<float>::mma(at, frag_tr<float, STD>(Yf + 16 * (s0t + j), LDF, s), acc[j]);
+    }
+#pragma unroll
+    for (int s = 0; s < D / Mma<T>::KSTEP; ++s) {
+      const auto ak = frag_row<T, STD>(Ks + 16 * rt * LDD, LDD, s);
+#pragma unroll
+      for (int j = 0; j < NJ; ++j)
+        kk[j] = Mma<T>::mma(ak, frag_row<T, STD>(Ks + 16 * (s0t + j) * LDD, LDD, s), kk[j]);
+    }
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const int s = 16 * (s0t + j) + li;
+      const float gs = G.g[s];
+      f32x4 db, dag, dkk;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = 16 * rt + g4 + e;
+        const bool low = s < r;
+        const float gam = low ? __expf(G.g[r] - gs) : 0.f;
+        const float da = low ? -acc[j][e] : 0.f;
+        const float br = G.beta[r];
+        db[e] = da * gam * kk[j][e];
+        dag[e] = br * db[e];
+        dkk[e] = da * br * gam;
+      }
+      store_tile_N(dkk, dKKs, LDC, 16 * rt, 16 * (s0t + j));
+      add_rows(dbp, 16 * rt, db, 1.f);
+      add_rows(dgp, 16 * rt, dag, 1.f);
+      add_cols(dgp, 16 * (s0t + j), dag, -1.f);
+    }
+  }
+  lds_barrier();
+  // ---- M: dK^T += K^T (dKK + dKK^T)^T-terms + dW^T Tp ; store dk
+  {
+#pragma unroll
+    for (int s = 0; s < BLK / Mma<T>::KSTEP; ++s) {
+      const auto ak = frag_tr<T, STD>(Ks + 16 * w, LDD, s);
+      const auto aw = frag_tr<T, STD>(dWs + 16 * w, LDD, s);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        dKt[j] = Mma<T>::mma(ak, frag_row<T, STD>(dKKs + 16 * j * LDC, LDC, s), dKt[j]);
+        dKt[j] = Mma<T>::mma(ak, frag_tr<T, STD>(dKKs + 16 * j, LDC, s), dKt[j]);
+        dKt[j] = Mma<T>::mma(aw, frag_tr<T, STD>(Tp + 16 * j, LDC, s), dKt[j]);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int s = 16 * j + li;
+      if (s < nv) st4(dk + (size_t)s * rs + 16 * w + g4, dKt[j][0], dKt[j][1], dKt[j][2], dKt[j][3]);
+    }
+  }
+  lds_barrier();
+  // ---- N: gate gradients
+  if (w == 0) {
+    const int j = lane;
+    float dg = 0.f, dbv = 0.f, dd = 0.f, gcs = 0.f;
+#pragma unroll
+    for (int ww = 0; ww < NW; ++ww) {
+      dg += part[ww * BLK + j];
+      dbv += part[NW * BLK + ww * BLK + j];
+      dd += part[2 * NW * BLK + ww * BLK + j];
+      gcs += dgc[ww];
+    }
+    const float dj = G.dec[j] * dd;
+    dg -= dj;
+    float tot = dj;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) tot += __shfl_xor(tot, off, 64);
+    const float dgC = tot + G.gC[0] * gcs;
+    if (j == BLK - 1) dg += dgC;
+    // reverse inclusive cumsum over the block: dlog alpha_j = sum_{r >= j} dg_r
+    float x = dg;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const float y = __shfl_down(x, off, 64);
+      if (j + off < 64) x += y;
+    }
+    if (j < nv) {
+      const size_t idx = gofs + (size_t)j * f.H;
+      a.dalpha[idx] = x / f.alpha[idx];
+      a.dbeta[idx] = dbv;
+    }
+  }
+}
+
+// ------------------------------------------------------------ launch -------
+static hipError_t set_lds(const void* fn, size_t bytes) {
+  return hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+}
+
+template <typename T, int D>
+hipError_t launch_bwd(const BwdArgs& a0, hipStream_t st, Profiler* prof) {
+  BwdArgs a = a0;
+  FwdArgs& f = a.f;
+  const int BH = f.B * f.H, P = f.P;
+  constexpr size_t scan_bytes = ScanLds<T, D>::bytes, grad_bytes = GradLds<T, D>::bytes;
+  hipError_t e;
+  float* hst = reinterpret_cast<float*>(a.hst);
+  const float* dSend = a.dS_out;
+  int dsend_P = 1;
+  if (P > 1) {
+    // 1. segment maps of the forward (all segments)
+    if ((e = launch_fwd_summary<T, D>(f, P, st, prof)) != hipSuccess) return e;
+    // 2. NB maps of segments 1..P-1
+    if ((e = set_lds((const void*)gdn_bwd_dscan_kernel<T, D, false>, ScanLds<T, D>::bytes)) != hipSuccess)
+      return e;
+    prof_begin(prof, "gdn_bwd_dscan_summary", st);
+    hipLaunchKernelGGL((gdn_bwd_dscan_kernel<T, D, false>), dim3(BH * (P - 1)), dim3(4 * D),
+                       scan_bytes, st, a, 1, P - 1, nullptr, 1);
+    prof_end(prof, st);
+    // 3. chains
+    ChainArgs c{f.S_in, f.Mseg, f.Nseg, const_cast<float*>(f.Sst), P};
+    if ((e = launch_chain_fwd<D>(c, BH, st, prof)) != hipSuccess) return e;
+    prof_begin(prof, "gdn_chain_bwd", st);
+    hipLaunchKernelGGL((gdn_chain_bwd_kernel<D>), dim3(BH * (D / 16)), dim3(256), 0, st, a.dS_out,
+                       f.Mseg, a.NBseg, a.dSend, P);
+    prof_end(prof, st);
+    dSend = a.dSend;
+    dsend_P = P;
+  } else {
+    f.Sst = f.S_in;
+    f.sst_P = 1;
+  }
+  // 4. block entry states
+  if ((e = launch_states<T, D>(f, hst, st, prof)) != hipSuccess) return e;
+  // 5. block exit gradients and dS_in
+  if ((e = set_lds((const void*)gdn_bwd_dscan_kernel<T, D, true>, ScanLds<T, D>::bytes)) != hipSuccess)
+    return e;
+  prof_begin(prof, "gdn_bwd_dscan", st);
+  hipLaunchKernelGGL((gdn_bwd_dscan_kernel<T, D, true>), dim3(BH * P), dim3(4 * D),
+                     scan_bytes, st, a, 0, P, dSend, dsend_P);
+  prof_end(prof, st);
+  // 6. per-block gradients
+  if ((e = set_lds((const void*)gdn_bwd_grads_kernel<T, D>, GradLds<T, D>::bytes)) != hipSuccess)
+    return e;
+  prof_begin(prof, "gdn_bwd_grads", st);
+  hipLaunchKernelGGL((gdn_bwd_grads_kernel<T, D>), dim3(BH * f.nblk), dim3(4 * D),
+                     grad_bytes, st, a);
+  prof_end(prof, st);
+  return hipGetLastError();
 }
 
 template hipError_t launch_bwd<bf16, 128>(const BwdArgs&, hipStream_t, Profiler*);

@@ -2,18 +2,28 @@
 //
 // Conventions used by every kernel in this library:
 //  * A kernel block is BLK = 64 consecutive tokens of one (batch, head)
-//    sequence ("kernel-level blocks b_{i,j} inside a pipeline chunk", Pith
-//    review of StateFlow, "Assumptions", domain assumption on kernel-level
-//    chunking).
-//  * Workgroups have NWAVE = 8 wave64s.  Matrix products run on MFMA
-//    16x16 tiles: v_mfma_f32_16x16x32_bf16 for bf16 operands and
-//    v_mfma_f32_16x16x4_f32 for fp32 operands, always accumulating in fp32.
-//  * Operands live in LDS as row-major tiles whose rows are contiguous along
-//    the contraction index ("NT" form: C[m][n] += sum_k A[m][k] B[n][k]).
-//    Rows are padded by 16 bytes to spread LDS banks.
-//  * An accumulator tile holds C[m][n] with m = 4*(lane/16) + e (e = 0..3)
-//    and n = lane % 16.  Storing it "transposed" (dst[n][m..m+3]) is one
-//    vector write per lane; storing it as-is is four scalar writes.
+//    sequence (the kernel-level blocks inside a pipeline chunk, Pith review of
+//    StateFlow, "Assumptions", domain assumption on kernel-level chunking).
+//  * Matrix products run on MFMA 16x16 tiles: v_mfma_f32_16x16x32_bf16 for
+//    bf16 operands and v_mfma_f32_16x16x4_f32 for fp32 operands, always
+//    accumulating in fp32.  Products are written C[m][n] += sum_k A[m][k] B[n][k].
+//  * An operand fragment gives lane l = 16 g + i row i of the operand (its m
+//    or n index) and, per instruction, KPL contraction elements whose k index
+//    depends on g.  Two k orders are used, and both operands of one product
+//    must use the same order:
+//      STD   k = 8 g + j                                 (bf16, j = 0..7)
+//            k = g                                       (fp32)
+//      PERM  k = 4 g + (j & 3) + 16 (j >> 2)             (bf16)
+//            k = 16 (s / 4) + 4 g + (s % 4) at step s    (fp32)
+//    PERM is the order in which an accumulator tile already holds its values
+//    (lane l owns C[m = 4 g + e][n = i]), so an accumulator can be fed back as
+//    an operand whose rows are its n index and whose contraction index is its
+//    m index, without leaving registers.
+//  * Operands in LDS are row-major tiles padded by 16 bytes per row.  A tile
+//    stored as X[k][n] (contraction index on rows) is read as an operand with
+//    rows n through the gfx950 transpose read ds_read_b64_tr_b16: within each
+//    16-lane group, input lane m addresses row m / 4, columns 4 (m % 4) .. +3,
+//    and output lane i receives column i of those 4 rows.
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -23,25 +33,29 @@ namespace sfgdn {
 typedef __bf16 bf16;
 typedef bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int BLK = 64;
-constexpr int NWAVE = 8;
-constexpr int NTHR = 64 * NWAVE;
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
 __device__ __forceinline__ int wave_id() {
   return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 }
 
+// Workgroup barrier for LDS hand-offs.  It waits only for this wave's LDS
+// (and scalar) operations; outstanding global loads and stores stay in
+// flight.  (__syncthreads() would also drain vmcnt.)
+__device__ __forceinline__ void lds_barrier() {
+  __asm__ __volatile__("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+enum KOrder { STD = 0, PERM = 1 };
+
 template <typename T> struct Mma;
 template <> struct Mma<bf16> {
   typedef bf16x8 frag;
-  static constexpr int KSTEP = 32;  // contraction depth of one instruction
-  static constexpr int KPL = 8;     // contraction elements held per lane
-  __device__ static __forceinline__ frag load(const bf16* p) {
-    return *reinterpret_cast<const bf16x8*>(p);
-  }
+  static constexpr int KSTEP = 32;
   __device__ static __forceinline__ f32x4 mma(frag a, frag b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
   }
@@ -49,17 +63,100 @@ template <> struct Mma<bf16> {
 template <> struct Mma<float> {
   typedef float frag;
   static constexpr int KSTEP = 4;
-  static constexpr int KPL = 1;
-  __device__ static __forceinline__ frag load(const float* p) { return *p; }
   __device__ static __forceinline__ f32x4 mma(frag a, frag b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
   }
 };
 
-// Elements per 16-byte chunk and padded leading dimensions.
 template <typename T> struct Lay {
-  static constexpr int VEC = 16 / sizeof(T);
-  static constexpr int PAD = VEC;
+  static constexpr int VEC = 16 / sizeof(T);  // elements per 16-byte chunk
+  static constexpr int PAD = VEC;             // row padding (elements)
+};
+
+// ---------------------------------------------------------------- frags ----
+// Operand rows from a row-major LDS tile: p points at the fragment's row 0
+// (the operand's m or n index), k runs along the row.  s is the k-step.
+template <typename T, int KO> __device__ __forceinline__ typename Mma<T>::frag
+frag_row(const T* p, int ld, int s);
+
+template <> __device__ __forceinline__ bf16x8 frag_row<bf16, STD>(const bf16* p, int ld, int s) {
+  const int l = lane_id();
+  return *reinterpret_cast<const bf16x8*>(p + (l & 15) * ld + 32 * s + 8 * (l >> 4));
+}
+template <> __device__ __forceinline__ bf16x8 frag_row<bf16, PERM>(const bf16* p, int ld, int s) {
+  const int l = lane_id();
+  const bf16* q = p + (l & 15) * ld + 32 * s + 4 * (l >> 4);
+  const bf16x4 lo = *reinterpret_cast<const bf16x4*>(q);
+  const bf16x4 hi = *reinterpret_cast<const bf16x4*>(q + 16);
+  return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+template <> __device__ __forceinline__ float frag_row<float, STD>(const float* p, int ld, int s) {
+  const int l = lane_id();
+  return p[(l & 15) * ld + 4 * s + (l >> 4)];
+}
+template <> __device__ __forceinline__ float frag_row<float, PERM>(const float* p, int ld, int s) {
+  const int l = lane_id();
+  return p[(l & 15) * ld + 16 * (s >> 2) + 4 * (l >> 4) + (s & 3)];
+}
+
+// Operand rows n0.. from a tile stored X[k][n] (k on rows): the operand is
+// X^T.  p points at X[0][n0].
+template <typename T, int KO> __device__ __forceinline__ typename Mma<T>::frag
+frag_tr(const T* p, int ld, int s);
+
+__device__ __forceinline__ bf16x4 ds_tr4(const bf16* p) {
+  typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+  const i16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_i16x4*)(const_cast<bf16*>(p)));
+  return __builtin_bit_cast(bf16x4, r);
+}
+// rows k0 .. k0+3 of X, columns n0 .. n0+15, delivered transposed.
+__device__ __forceinline__ bf16x4 tr_rows4(const bf16* p, int ld, int k0) {
+  const int i = lane_id() & 15;
+  return ds_tr4(p + (k0 + (i >> 2)) * ld + 4 * (i & 3));
+}
+template <> __device__ __forceinline__ bf16x8 frag_tr<bf16, STD>(const bf16* p, int ld, int s) {
+  const int g = lane_id() >> 4;
+  const bf16x4 lo = tr_rows4(p, ld, 32 * s + 8 * g);
+  const bf16x4 hi = tr_rows4(p, ld, 32 * s + 8 * g + 4);
+  return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+template <> __device__ __forceinline__ bf16x8 frag_tr<bf16, PERM>(const bf16* p, int ld, int s) {
+  const int g = lane_id() >> 4;
+  const bf16x4 lo = tr_rows4(p, ld, 32 * s + 4 * g);
+  const bf16x4 hi = tr_rows4(p, ld, 32 * s + 16 + 4 * g);
+  return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+template <> __device__ __forceinline__ float frag_tr<float, STD>(const float* p, int ld, int s) {
+  const int l = lane_id();
+  return p[(4 * s + (l >> 4)) * ld + (l & 15)];
+}
+template <> __device__ __forceinline__ float frag_tr<float, PERM>(const float* p, int ld, int s) {
+  const int l = lane_id();
+  return p[(16 * (s >> 2) + 4 * (l >> 4) + (s & 3)) * ld + (l & 15)];
+}
+
+// Operand from accumulator tiles acc[0 .. ] whose m index is the contraction
+// index (PERM order), each element scaled by sc[m-tile][e] when given.
+template <typename T> struct AccFrag;
+template <> struct AccFrag<bf16> {
+  // k-step s uses tiles 2s and 2s+1
+  __device__ static __forceinline__ bf16x8 get(const f32x4* t, int s) {
+    const f32x4 a = t[2 * s], b = t[2 * s + 1];
+    return bf16x8{(bf16)a[0], (bf16)a[1], (bf16)a[2], (bf16)a[3],
+                  (bf16)b[0], (bf16)b[1], (bf16)b[2], (bf16)b[3]};
+  }
+  __device__ static __forceinline__ bf16x8 get_scaled(const f32x4* t, const f32x4* sc, int s) {
+    const f32x4 a = t[2 * s] * sc[2 * s], b = t[2 * s + 1] * sc[2 * s + 1];
+    return bf16x8{(bf16)a[0], (bf16)a[1], (bf16)a[2], (bf16)a[3],
+                  (bf16)b[0], (bf16)b[1], (bf16)b[2], (bf16)b[3]};
+  }
+};
+template <> struct AccFrag<float> {
+  __device__ static __forceinline__ float get(const f32x4* t, int s) { return t[s >> 2][s & 3]; }
+  __device__ static __forceinline__ float get_scaled(const f32x4* t, const f32x4* sc, int s) {
+    return t[s >> 2][s & 3] * sc[s >> 2][s & 3];
+  }
 };
 
 template <int MI, int NJ>
@@ -76,27 +173,6 @@ __device__ __forceinline__ void scale_acc(f32x4 (&acc)[MI][NJ], float s) {
   for (int i = 0; i < MI; ++i)
 #pragma unroll
     for (int j = 0; j < NJ; ++j) acc[i][j] *= s;
-}
-
-// acc[i][j] += A[16i + m][:K] . B[16j + n][:K]; A and B point at the wave's
-// first row, both K-contiguous.
-template <typename T, int MI, int NJ, int K>
-__device__ __forceinline__ void gemm_nt(f32x4 (&acc)[MI][NJ], const T* A, int lda,
-                                        const T* B, int ldb) {
-  const int lane = lane_id();
-  const int r = lane & 15, kq = (lane >> 4) * Mma<T>::KPL;
-#pragma unroll
-  for (int k = 0; k < K; k += Mma<T>::KSTEP) {
-    typename Mma<T>::frag a[MI], b[NJ];
-#pragma unroll
-    for (int i = 0; i < MI; ++i) a[i] = Mma<T>::load(A + (16 * i + r) * lda + k + kq);
-#pragma unroll
-    for (int j = 0; j < NJ; ++j) b[j] = Mma<T>::load(B + (16 * j + r) * ldb + k + kq);
-#pragma unroll
-    for (int i = 0; i < MI; ++i)
-#pragma unroll
-      for (int j = 0; j < NJ; ++j) acc[i][j] = Mma<T>::mma(a[i], b[j], acc[i][j]);
-  }
 }
 
 // fp32 product with a row-major right operand: acc += A[m][:K] * B[:K][n].
@@ -120,8 +196,6 @@ __device__ __forceinline__ void st4(float* p, float a, float b, float c, float d
   *reinterpret_cast<f32x4*>(p) = f32x4{a, b, c, d};
 }
 
-__device__ __forceinline__ float to_f(bf16 x) { return (float)x; }
-__device__ __forceinline__ float to_f(float x) { return x; }
 template <typename T> __device__ __forceinline__ T from_f(float x) { return (T)x; }
 
 // dst[n][m..m+3] = scale * acc for the tile at (m0, n0).
@@ -144,70 +218,41 @@ __device__ __forceinline__ void store_tile_N(const f32x4& acc, T* dst, int ld, i
 }
 
 // ---------------------------------------------------------------------------
-// Moving 64-row tiles between HBM and LDS.  A tile is BLK rows of D elements
-// of type T; each thread moves NCH 16-byte chunks.  Within a group of 16 rows
-// the chunk index runs fastest over rows, so a wave touches 16 rows x 4
-// chunks (64 contiguous bytes per row) and the transposed LDS scatter hits
-// 16 consecutive columns.
+// Moving 64-row tiles from HBM to LDS.  A tile is BLK rows of D elements of
+// type T; each of NT threads moves NCH 16-byte chunks, consecutive threads
+// covering consecutive chunks of a row.  Loads are unconditional (rows past
+// the end of the sequence re-read its last row, which is in bounds) and the
+// tail rows are zeroed when the tile is written to LDS, so no branch sits
+// between a load and its use.
 // ---------------------------------------------------------------------------
-template <typename T, int D> struct Tile {
+template <typename T, int D, int NT> struct Tile {
   static constexpr int VEC = Lay<T>::VEC;
-  static constexpr int CPR = D / VEC;                 // chunks per row
-  static constexpr int NCHUNK = BLK * CPR;
-  static constexpr int NCH = NCHUNK / NTHR;           // chunks per thread
-  static_assert(NCHUNK % NTHR == 0, "tile must split evenly over the workgroup");
+  static constexpr int CPR = D / VEC;
+  static constexpr int NCH = BLK * CPR / NT;
+  static_assert((BLK * CPR) % NT == 0, "tile must split evenly over the workgroup");
 
-  __device__ static __forceinline__ void coords(int c, int& row, int& ch) {
-    const int slot = c % (16 * CPR);
-    row = 16 * (c / (16 * CPR)) + (slot & 15);
-    ch = slot >> 4;
-  }
-
-  // Rows >= nvalid read as zero.  row_stride is in elements.
   __device__ static __forceinline__ void load(uint4 (&r)[NCH], const T* g, size_t row_stride,
                                               int nvalid) {
 #pragma unroll
     for (int it = 0; it < NCH; ++it) {
-      int row, ch;
-      coords(threadIdx.x + NTHR * it, row, ch);
-      if (row < nvalid)
-        r[it] = *reinterpret_cast<const uint4*>(g + (size_t)row * row_stride + ch * VEC);
-      else
-        r[it] = uint4{0u, 0u, 0u, 0u};
+      const int c = threadIdx.x + NT * it;
+      const int row = min(c / CPR, nvalid - 1), ch = c % CPR;
+      r[it] = *reinterpret_cast<const uint4*>(g + (size_t)row * row_stride + ch * VEC);
     }
   }
 
-  __device__ static __forceinline__ void to_lds(const uint4 (&r)[NCH], T* s, int ld) {
+  __device__ static __forceinline__ void to_lds(const uint4 (&r)[NCH], T* s, int ld, int nvalid) {
 #pragma unroll
     for (int it = 0; it < NCH; ++it) {
-      int row, ch;
-      coords(threadIdx.x + NTHR * it, row, ch);
-      *reinterpret_cast<uint4*>(s + row * ld + ch * VEC) = r[it];
-    }
-  }
-
-  // sT[col][row] = tile[row][col]
-  __device__ static __forceinline__ void to_lds_T(const uint4 (&r)[NCH], T* sT, int ldT) {
-#pragma unroll
-    for (int it = 0; it < NCH; ++it) {
-      int row, ch;
-      coords(threadIdx.x + NTHR * it, row, ch);
-      const T* e = reinterpret_cast<const T*>(&r[it]);
-#pragma unroll
-      for (int x = 0; x < VEC; ++x) sT[(ch * VEC + x) * ldT + row] = e[x];
-    }
-  }
-
-  // Row-major LDS tile -> HBM rows < nvalid, coalesced along rows.
-  __device__ static __forceinline__ void store(const T* s, int ld, T* g, size_t row_stride,
-                                               int nvalid) {
-#pragma unroll
-    for (int it = 0; it < NCH; ++it) {
-      const int c = threadIdx.x + NTHR * it;
+      const int c = threadIdx.x + NT * it;
       const int row = c / CPR, ch = c % CPR;
-      if (row < nvalid)
-        *reinterpret_cast<uint4*>(g + (size_t)row * row_stride + ch * VEC) =
-            *reinterpret_cast<const uint4*>(s + row * ld + ch * VEC);
+      const bool ok = row < nvalid;
+      uint4 v = r[it];
+      v.x = ok ? v.x : 0u;
+      v.y = ok ? v.y : 0u;
+      v.z = ok ? v.z : 0u;
+      v.w = ok ? v.w : 0u;
+      *reinterpret_cast<uint4*>(s + row * ld + ch * VEC) = v;
     }
   }
 };

@@ -20,43 +20,32 @@
 namespace sfgdn {
 
 // ------------------------------------------------------------------ LDS ----
+// One workgroup = D/16 waves, one per 16-column slice of the state.  LDS
+// regions are reused by phase:
+//   RQ : Q (scores, S Q^T) -> Tm (solve) -> Wn (-W, for Vn)
+//   RK : K (row-major; K^T operands come from transpose reads)
+//   RV : V (row-major; V^T operands come from transpose reads)
+//   RA : Af (solve input) -> Tp, Tpp
+//   RP : P (masked decayed scores, for the output)
+//   RG : gate vectors
 template <typename T, int D> struct FwdLds {
   static constexpr int LDD = D + Lay<T>::PAD;
   static constexpr int LDC = BLK + Lay<T>::PAD;
   static constexpr int LDF = BLK + 4;
   static constexpr size_t cmax(size_t a, size_t b) { return a > b ? a : b; }
-  static constexpr size_t rowD = (size_t)BLK * LDD * sizeof(T);  // 64 rows of D
-  static constexpr size_t colD = (size_t)D * LDC * sizeof(T);    // D rows of 64
-  static constexpr size_t sqD = (size_t)D * LDD * sizeof(T);     // D rows of D
+  static constexpr size_t rowD = (size_t)BLK * LDD * sizeof(T);
   static constexpr size_t f64x64 = (size_t)BLK * LDF * sizeof(float);
-  static constexpr size_t solve_scratch = (2 * 16 * 20 + 32 * 36) * sizeof(float);
-  // region sizes
-  static constexpr size_t zK = cmax(rowD, f64x64);                    // Ks | Tm
-  static constexpr size_t zKT = colD;                                 // KTs
-  static constexpr size_t zVT = colD;                                 // VTs | VnDT
-  static constexpr size_t zA = cmax(f64x64, rowD);                    // Af | Wn | Ost
-  static constexpr size_t zTT = cmax(cmax(2 * (size_t)BLK * LDC * sizeof(T), colD),
-                                     solve_scratch);                  // Tp,Tpp | VnT | ZD | scratch
-  static constexpr size_t zQ = rowD;
+  static constexpr size_t zQ = cmax(rowD, f64x64);
+  static constexpr size_t zK = rowD;
+  static constexpr size_t zV = rowD;
+  static constexpr size_t zA = cmax(f64x64, 2 * (size_t)BLK * LDC * sizeof(T));
   static constexpr size_t zP = (size_t)BLK * LDC * sizeof(T);
-  static constexpr size_t zS = sqD;
-  static constexpr size_t zM = sqD;
-  static constexpr size_t zG = 6 * BLK * sizeof(float) + 16;
-  // offsets (out kernel)
-  static constexpr size_t oK = 0, oKT = oK + zK, oVT = oKT + zKT, oA = oVT + zVT, oTT = oA + zA,
-                          oS = oTT + zTT, oG = oS + zS, oQ = oG + zG, oP = oQ + zQ;
+  static constexpr size_t oQ = 0, oK = oQ + zQ, oV = oK + zK, oA = oV + zV, oG = oA + zA,
+                          oP = oG + kGateBytes;
   static constexpr size_t out_bytes = oP + zP;
-  // summary kernel: M replaces Q and P
-  static constexpr size_t oM = oG + zG;
-  static constexpr size_t sum_bytes = oM + zM;
-  static_assert(out_bytes <= 160 * 1024, "out kernel LDS budget");
-  static_assert(sum_bytes <= 160 * 1024, "summary kernel LDS budget");
+  static constexpr size_t sum_bytes = oG + kGateBytes;  // no P
+  static_assert(out_bytes <= 160 * 1024 && sum_bytes <= 160 * 1024, "LDS budget");
 };
-
-__device__ __forceinline__ GateLds gate_lds(unsigned char* base) {
-  float* f = reinterpret_cast<float*>(base);
-  return GateLds{f, f + BLK, f + 2 * BLK, f + 3 * BLK, f + 4 * BLK, f + 5 * BLK};
-}
 
 // Token rows of one (b, h) sequence: row t starts at base + t * H * D.
 template <typename T, int D>
@@ -64,34 +53,58 @@ __device__ __forceinline__ const T* seq_base(const void* p, const FwdArgs& a, in
   return reinterpret_cast<const T*>(p) + ((size_t)b * a.T * a.H + h) * D;
 }
 
-// --------------------------------------------------------- fused out -------
-template <typename T, int D>
-__global__ __launch_bounds__(NTHR) void gdn_fwd_out_kernel(FwdArgs a) {
-  typedef FwdLds<T, D> Lz;
-  typedef Tile<T, D> Tl;
-  typedef Dist<D / 16, D / 16> DS;   // state tiles  [dk][dv]
-  typedef Dist<4, D / 16> DU;        // value tiles  [s][dv]
-  typedef Dist<D / 16, 4> DO;        // output tiles [dv][r]
-  extern __shared__ __align__(16) unsigned char smem[];
-  T* Ks = reinterpret_cast<T*>(smem + Lz::oK);
-  float* Tm = reinterpret_cast<float*>(smem + Lz::oK);
-  T* KTs = reinterpret_cast<T*>(smem + Lz::oKT);
-  T* VTs = reinterpret_cast<T*>(smem + Lz::oVT);
-  T* VnDT = VTs;
-  float* Af = reinterpret_cast<float*>(smem + Lz::oA);
-  T* Wn = reinterpret_cast<T*>(smem + Lz::oA);
-  T* Ost = Wn;
-  T* Tp = reinterpret_cast<T*>(smem + Lz::oTT);
-  T* Tpp = Tp + BLK * Lz::LDC;
-  T* VnT = Tp;
-  float* scratch = reinterpret_cast<float*>(smem + Lz::oTT);
-  T* Sbf = reinterpret_cast<T*>(smem + Lz::oS);
-  const GateLds G = gate_lds(smem + Lz::oG);
-  T* Qs = reinterpret_cast<T*>(smem + Lz::oQ);
-  T* Pl = reinterpret_cast<T*>(smem + Lz::oP);
-  constexpr int LDD = Lz::LDD, LDC = Lz::LDC, LDF = Lz::LDF;
 
-  const int w = wave_id(), lane = lane_id();
+// Per-block inputs in flight: the next block's rows are loaded into registers
+// while the current block computes.
+template <typename T, int D, bool WITH_Q> struct Prefetch {
+  typedef Tile<T, D, 4 * D> Tl;
+  uint4 rq[WITH_Q ? Tl::NCH : 1], rk[Tl::NCH], rv[Tl::NCH];
+  float la = 0.f, be = 0.f;
+  __device__ __forceinline__ void fetch(const T* q, const T* k, const T* v, const float* al,
+                                        const float* bt, size_t rs, int H, int t0, int nv) {
+    if constexpr (WITH_Q) Tl::load(rq, q + (size_t)t0 * rs, rs, nv);
+    Tl::load(rk, k + (size_t)t0 * rs, rs, nv);
+    Tl::load(rv, v + (size_t)t0 * rs, rs, nv);
+    if (wave_id() == 0) {
+      const int lane = lane_id();
+      const size_t idx = (size_t)(t0 + min(lane, nv - 1)) * H;
+      const float x = al[idx], y = bt[idx];
+      la = lane < nv ? __logf(x) : 0.f;
+      be = lane < nv ? y : 0.f;
+    }
+  }
+  __device__ __forceinline__ void stage(T* Qs, T* Ks, T* Vs, int ld, int nv, const GateLds& G) {
+    if constexpr (WITH_Q) Tl::to_lds(rq, Qs, ld, nv);
+    Tl::to_lds(rk, Ks, ld, nv);
+    Tl::to_lds(rv, Vs, ld, nv);
+    if (wave_id() == 0) block_gates(la, be, G);
+  }
+};
+
+// --------------------------------------------------------- fused out -------
+// Wave w owns dv-tile w of the state: S^T, U/Vn and O^T for those 16 columns
+// live in its registers for the whole segment.  With STATES the kernel
+// computes no output; instead it stores each block's entry state (fp32,
+// [dv][dk]) to hst[b*H + h][block], which the backward pass consumes.
+template <typename T, int D, bool STATES>
+__global__ __launch_bounds__(4 * D, 2) void gdn_fwd_out_kernel(FwdArgs a, float* hst) {
+  typedef FwdLds<T, D> Lz;
+  constexpr int NW = D / 16, NDV = 1, DKT = D / 16;
+  constexpr int LDD = Lz::LDD, LDC = Lz::LDC, LDF = Lz::LDF;
+  extern __shared__ __align__(16) unsigned char smem[];
+  T* Qs = reinterpret_cast<T*>(smem + Lz::oQ);
+  float* Tm = reinterpret_cast<float*>(smem + Lz::oQ);
+  T* Wn = reinterpret_cast<T*>(smem + Lz::oQ);
+  T* Ks = reinterpret_cast<T*>(smem + Lz::oK);
+  T* Vs = reinterpret_cast<T*>(smem + Lz::oV);
+  float* Af = reinterpret_cast<float*>(smem + Lz::oA);
+  T* Tp = reinterpret_cast<T*>(smem + Lz::oA);
+  T* Tpp = Tp + BLK * LDC;
+  const GateLds G = gate_lds(smem + Lz::oG);
+  T* Pl = reinterpret_cast<T*>(smem + Lz::oP);
+
+  const int w = wave_id(), lane = lane_id(), g4 = 4 * (lane >> 4), li = lane & 15;
+  const int dv0 = NDV * w;
   const int seg = blockIdx.x % a.P, bh = blockIdx.x / a.P;
   const int b = bh / a.H, h = bh % a.H;
   const int blk0 = seg * a.L, blk1 = min(a.nblk, blk0 + a.L);
@@ -101,133 +114,129 @@ __global__ __launch_bounds__(NTHR) void gdn_fwd_out_kernel(FwdArgs a) {
   const T* v = seq_base<T, D>(a.v, a, b, h);
   T* o = const_cast<T*>(seq_base<T, D>(a.o, a, b, h));
   const float* al = a.alpha + (size_t)b * a.T * a.H + h;
-  const float* be = a.beta + (size_t)b * a.T * a.H + h;
+  const float* bt = a.beta + (size_t)b * a.T * a.H + h;
 
-  // Entry state (fp32, [dv][dk]) into the transposed accumulators.
-  f32x4 accS[1][DS::NJ];
+  // State S^T tiles: St[bb][aa] covers dk-tile aa, dv-tile dv0 + bb.
+  f32x4 St[NDV][DKT];
   {
     const float* S0 = a.Sst ? a.Sst + ((size_t)bh * a.sst_P + seg) * D * D : nullptr;
-    const int dk = 16 * DS::m(w) + 4 * (lane >> 4);
 #pragma unroll
-    for (int j = 0; j < DS::NJ; ++j) {
-      const int dv = 16 * (DS::n0(w) + j) + (lane & 15);
-      accS[0][j] = S0 ? *reinterpret_cast<const f32x4*>(S0 + (size_t)dv * D + dk)
-                      : f32x4{0.f, 0.f, 0.f, 0.f};
-      store_tile_T(accS[0][j], Sbf, LDD, 16 * DS::m(w), 16 * (DS::n0(w) + j));
-    }
+    for (int bb = 0; bb < NDV; ++bb)
+#pragma unroll
+      for (int aa = 0; aa < DKT; ++aa) {
+        const int dv = 16 * (dv0 + bb) + li, dk = 16 * aa + g4;
+        St[bb][aa] = S0 ? *reinterpret_cast<const f32x4*>(S0 + (size_t)dv * D + dk)
+                        : f32x4{0.f, 0.f, 0.f, 0.f};
+      }
   }
-  uint4 rq[Tl::NCH], rk[Tl::NCH], rv[Tl::NCH];
-  float ra = 0.f, rb = 0.f;
-  auto fetch = [&](int blk) {
-    const int t0 = blk * BLK, nv = min(BLK, a.T - t0);
-    Tl::load(rq, q + (size_t)t0 * rs, rs, nv);
-    Tl::load(rk, k + (size_t)t0 * rs, rs, nv);
-    Tl::load(rv, v + (size_t)t0 * rs, rs, nv);
-    if (w == 0) {
-      ra = lane < nv ? __logf(al[(size_t)(t0 + lane) * a.H]) : 0.f;
-      rb = lane < nv ? be[(size_t)(t0 + lane) * a.H] : 0.f;
-    }
+
+  Prefetch<T, D, !STATES> pf;
+  if (blk0 < blk1) pf.fetch(q, k, v, al, bt, rs, a.H, blk0 * BLK, min(BLK, a.T - blk0 * BLK));
+  f32x4 O[NDV][4];
+  int prev_t0 = -1, prev_nv = 0;
+  auto store_o = [&]() {
+#pragma unroll
+    for (int bb = 0; bb < NDV; ++bb)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int r = 16 * j + li;
+        if (r < prev_nv) {
+          const f32x4 x = O[bb][j];
+          st4(o + (size_t)(prev_t0 + r) * rs + 16 * (dv0 + bb) + g4, x[0], x[1], x[2], x[3]);
+        }
+      }
   };
-  auto stage = [&]() {
-    Tl::to_lds(rq, Qs, LDD);
-    Tl::to_lds(rk, Ks, LDD);
-    Tl::to_lds_T(rk, KTs, LDC);
-    Tl::to_lds_T(rv, VTs, LDC);
-  };
-  if (blk0 < blk1) {
-    fetch(blk0);
-    stage();
-  }
-  __syncthreads();
 
   for (int blk = blk0; blk < blk1; ++blk) {
-    const int nv = min(BLK, a.T - blk * BLK);
-    if (w == 0) block_gates(ra, rb, G);
-    if (blk + 1 < blk1) fetch(blk + 1);
-    __syncthreads();
-    block_scores<T, D, true>(Qs, Ks, LDD, G, Af, LDF, Pl, LDC);
-    __syncthreads();
-    block_solve(Af, Tm, LDF, scratch);
-    block_tprime(Tm, LDF, G, Tp, Tpp, LDC);
-    __syncthreads();
-    f32x4 accU[1][DU::NJ];
-    block_wu<T, D>(KTs, VTs, Tp, Tpp, LDC, Wn, LDD, accU);
-    __syncthreads();
-    // Vn = U - W S^T, stored as Vn^T and (D Vn)^T.
-    gemm_nt<T, 1, DU::NJ, D>(accU, Wn + 16 * DU::m(w) * LDD, LDD, Sbf + 16 * DU::n0(w) * LDD, LDD);
-    {
-      const int s = 16 * DU::m(w) + 4 * (lane >> 4);
-      const float d0 = G.dec[s], d1 = G.dec[s + 1], d2 = G.dec[s + 2], d3 = G.dec[s + 3];
+    const int t0 = blk * BLK, nv = min(BLK, a.T - t0);
+    pf.stage(Qs, Ks, Vs, LDD, nv, G);
+    if constexpr (STATES) {
+      float* hb = hst + ((size_t)bh * a.nblk + blk) * D * D;
 #pragma unroll
-      for (int j = 0; j < DU::NJ; ++j) {
-        const int dv = 16 * (DU::n0(w) + j) + (lane & 15);
-        const f32x4 x = accU[0][j];
-        st4(VnT + dv * LDC + s, x[0], x[1], x[2], x[3]);
-        st4(VnDT + dv * LDC + s, d0 * x[0], d1 * x[1], d2 * x[2], d3 * x[3]);
+      for (int aa = 0; aa < DKT; ++aa)
+        *reinterpret_cast<f32x4*>(hb + (size_t)(16 * dv0 + li) * D + 16 * aa + g4) = St[0][aa];
+    } else {
+      if (prev_t0 >= 0) store_o();
+    }
+    if (blk + 1 < blk1) pf.fetch(q, k, v, al, bt, rs, a.H, t0 + BLK, min(BLK, a.T - t0 - BLK));
+    lds_barrier();
+    // Pre: scores; Out, state part: O^T = diag(gamma) (S Q^T)
+    block_scores<T, D, NW, !STATES>(Qs, Ks, LDD, G, Af, LDF, Pl, LDC);
+    if constexpr (!STATES) {
+      zero_acc(O);
+      block_s_yT<T, D, NDV>(St, Qs, LDD, O);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float gr = G.gam[16 * j + li];
+#pragma unroll
+        for (int bb = 0; bb < NDV; ++bb) O[bb][j] *= gr;
       }
     }
-    __syncthreads();
-    // O^T = diag-scaled S Q^T + Vn^T P^T, and the state update.
-    {
-      f32x4 accO[1][DO::NJ];
-      zero_acc(accO);
-      gemm_nt<T, 1, DO::NJ, D>(accO, Sbf + 16 * DO::m(w) * LDD, LDD, Qs + 16 * DO::n0(w) * LDD, LDD);
+    lds_barrier();
+    // Pre: T = (I + A)^{-1}, W, U
+    block_solve(Af, Tm, LDF);
+    block_tprime<T, 64 * NW>(Tm, LDF, G, Tp, Tpp, LDC);
+    lds_barrier();
+    block_w<T, D>(Ks, LDD, Tp, LDC, Wn);
+    f32x4 U[NDV][4];
+    block_u<T, NDV>(Tpp, LDC, Vs, LDD, dv0, U);
+    lds_barrier();
+    // ST and Out: Vn = U - W S^T; O^T += Vn^T P^T; S' = gamma_C S + Vn^T D K
+    block_x_st<T, D, NDV>(Wn, LDD, St, U);
+    if constexpr (!STATES) block_vnT_pT<T, NDV>(U, Pl, LDC, O);
+    f32x4 dsc[4];
 #pragma unroll
-      for (int j = 0; j < DO::NJ; ++j) accO[0][j] *= G.gam[16 * (DO::n0(w) + j) + (lane & 15)];
-      gemm_nt<T, 1, DO::NJ, BLK>(accO, VnT + 16 * DO::m(w) * LDC, LDC, Pl + 16 * DO::n0(w) * LDC, LDC);
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < DO::NJ; ++j)
-        store_tile_T(accO[0][j], Ost, LDD, 16 * DO::m(w), 16 * (DO::n0(w) + j));
-      scale_acc(accS, G.gC[0]);
-      gemm_nt<T, 1, DS::NJ, BLK>(accS, KTs + 16 * DS::m(w) * LDC, LDC, VnDT + 16 * DS::n0(w) * LDC, LDC);
-    }
-    __syncthreads();
+      for (int e = 0; e < 4; ++e) dsc[i][e] = G.dec[16 * i + g4 + e];
+    const float gc = G.gC[0];
 #pragma unroll
-    for (int j = 0; j < DS::NJ; ++j)
-      store_tile_T(accS[0][j], Sbf, LDD, 16 * DS::m(w), 16 * (DS::n0(w) + j));
-    Tl::store(Ost, LDD, o + (size_t)blk * BLK * rs, rs, nv);
-    if (blk + 1 < blk1) stage();
-    __syncthreads();
+    for (int bb = 0; bb < NDV; ++bb)
+#pragma unroll
+      for (int aa = 0; aa < DKT; ++aa) St[bb][aa] *= gc;
+    block_state_write<T, D, NDV>(Ks, LDD, U, dsc, St);
+    prev_t0 = t0;
+    prev_nv = nv;
+    lds_barrier();
+  }
+  if constexpr (!STATES) {
+    if (prev_t0 >= 0) store_o();
   }
 
-  if (seg == a.P - 1 && a.S_out) {
+  if (!STATES && seg == a.P - 1 && a.S_out) {
     float* So = a.S_out + (size_t)bh * D * D;
-    const int dk = 16 * DS::m(w) + 4 * (lane >> 4);
 #pragma unroll
-    for (int j = 0; j < DS::NJ; ++j) {
-      const int dv = 16 * (DS::n0(w) + j) + (lane & 15);
-      *reinterpret_cast<f32x4*>(So + (size_t)dv * D + dk) = accS[0][j];
-    }
+    for (int bb = 0; bb < NDV; ++bb)
+#pragma unroll
+      for (int aa = 0; aa < DKT; ++aa)
+        *reinterpret_cast<f32x4*>(So + (size_t)(16 * (dv0 + bb) + li) * D + 16 * aa + g4) =
+            St[bb][aa];
   }
 }
 
 // ------------------------------------------------------ segment summary ----
 // Per segment: N = the exit state from a zero entry state and M = the product
-// of the block maps M_b, both fp32, row-major [D][D].
+// of the block maps M_b = gamma_C I - W^T D K, both fp32, row-major [D][D].
+// Wave w owns rows NDV*w .. of N (dv) and of M (i); the propagation
+//   M' = gamma_C M - (M W^T) D K
+// runs like the state update with M in place of S.
 template <typename T, int D>
-__global__ __launch_bounds__(NTHR) void gdn_fwd_summary_kernel(FwdArgs a, int nseg) {
+__global__ __launch_bounds__(4 * D, 2) void gdn_fwd_summary_kernel(FwdArgs a, int nseg) {
   typedef FwdLds<T, D> Lz;
-  typedef Tile<T, D> Tl;
-  typedef Dist<D / 16, D / 16> DS;
-  typedef Dist<4, D / 16> DU;
-  extern __shared__ __align__(16) unsigned char smem[];
-  T* Ks = reinterpret_cast<T*>(smem + Lz::oK);
-  float* Tm = reinterpret_cast<float*>(smem + Lz::oK);
-  T* KTs = reinterpret_cast<T*>(smem + Lz::oKT);
-  T* VTs = reinterpret_cast<T*>(smem + Lz::oVT);
-  T* VnDT = VTs;
-  float* Af = reinterpret_cast<float*>(smem + Lz::oA);
-  T* Wn = reinterpret_cast<T*>(smem + Lz::oA);
-  T* Tp = reinterpret_cast<T*>(smem + Lz::oTT);
-  T* Tpp = Tp + BLK * Lz::LDC;
-  T* ZD = Tp;
-  float* scratch = reinterpret_cast<float*>(smem + Lz::oTT);
-  T* Nbf = reinterpret_cast<T*>(smem + Lz::oS);
-  const GateLds G = gate_lds(smem + Lz::oG);
-  T* Mbf = reinterpret_cast<T*>(smem + Lz::oM);
+  constexpr int NW = D / 16, NDV = 1, DKT = D / 16;
   constexpr int LDD = Lz::LDD, LDC = Lz::LDC, LDF = Lz::LDF;
+  extern __shared__ __align__(16) unsigned char smem[];
+  float* Tm = reinterpret_cast<float*>(smem + Lz::oQ);
+  T* Wn = reinterpret_cast<T*>(smem + Lz::oQ);
+  T* Ks = reinterpret_cast<T*>(smem + Lz::oK);
+  T* Vs = reinterpret_cast<T*>(smem + Lz::oV);
+  float* Af = reinterpret_cast<float*>(smem + Lz::oA);
+  T* Tp = reinterpret_cast<T*>(smem + Lz::oA);
+  T* Tpp = Tp + BLK * LDC;
+  const GateLds G = gate_lds(smem + Lz::oG);
 
-  const int w = wave_id(), lane = lane_id();
+  const int w = wave_id(), lane = lane_id(), g4 = 4 * (lane >> 4), li = lane & 15;
+  const int dv0 = NDV * w;
   const int seg = blockIdx.x % nseg, bh = blockIdx.x / nseg;
   const int b = bh / a.H, h = bh % a.H;
   const int blk0 = seg * a.L, blk1 = min(a.nblk, blk0 + a.L);
@@ -235,108 +244,81 @@ __global__ __launch_bounds__(NTHR) void gdn_fwd_summary_kernel(FwdArgs a, int ns
   const T* k = seq_base<T, D>(a.k, a, b, h);
   const T* v = seq_base<T, D>(a.v, a, b, h);
   const float* al = a.alpha + (size_t)b * a.T * a.H + h;
-  const float* be = a.beta + (size_t)b * a.T * a.H + h;
+  const float* bt = a.beta + (size_t)b * a.T * a.H + h;
 
-  f32x4 accN[1][DS::NJ], accM[1][DS::NJ];
-  {
-    const int mrow = 16 * DS::m(w) + 4 * (lane >> 4);
+  f32x4 Nt[NDV][DKT], Mt[NDV][DKT];
 #pragma unroll
-    for (int j = 0; j < DS::NJ; ++j) {
-      const int n = 16 * (DS::n0(w) + j) + (lane & 15);
-      accN[0][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int bb = 0; bb < NDV; ++bb)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) accM[0][j][e] = (mrow + e == n) ? 1.f : 0.f;
-      store_tile_T(accN[0][j], Nbf, LDD, 16 * DS::m(w), 16 * (DS::n0(w) + j));
-      store_tile_T(accM[0][j], Mbf, LDD, 16 * DS::m(w), 16 * (DS::n0(w) + j));
+    for (int aa = 0; aa < DKT; ++aa) {
+      Nt[bb][aa] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) Mt[bb][aa][e] = (16 * aa + g4 + e == 16 * (dv0 + bb) + li) ? 1.f : 0.f;
     }
-  }
-  uint4 rk[Tl::NCH], rv[Tl::NCH];
-  float ra = 0.f, rb = 0.f;
-  auto fetch = [&](int blk) {
-    const int t0 = blk * BLK, nv = min(BLK, a.T - t0);
-    Tl::load(rk, k + (size_t)t0 * rs, rs, nv);
-    Tl::load(rv, v + (size_t)t0 * rs, rs, nv);
-    if (w == 0) {
-      ra = lane < nv ? __logf(al[(size_t)(t0 + lane) * a.H]) : 0.f;
-      rb = lane < nv ? be[(size_t)(t0 + lane) * a.H] : 0.f;
-    }
-  };
-  auto stage = [&]() {
-    Tl::to_lds(rk, Ks, LDD);
-    Tl::to_lds_T(rk, KTs, LDC);
-    Tl::to_lds_T(rv, VTs, LDC);
-  };
-  if (blk0 < blk1) {
-    fetch(blk0);
-    stage();
-  }
-  __syncthreads();
 
+  Prefetch<T, D, false> pf;
+  if (blk0 < blk1) pf.fetch(nullptr, k, v, al, bt, rs, a.H, blk0 * BLK, min(BLK, a.T - blk0 * BLK));
   for (int blk = blk0; blk < blk1; ++blk) {
-    if (w == 0) block_gates(ra, rb, G);
-    if (blk + 1 < blk1) fetch(blk + 1);
-    __syncthreads();
-    block_scores<T, D, false>(nullptr, Ks, LDD, G, Af, LDF, nullptr, LDC);
-    __syncthreads();
-    block_solve(Af, Tm, LDF, scratch);
-    block_tprime(Tm, LDF, G, Tp, Tpp, LDC);
-    __syncthreads();
-    f32x4 accU[1][DU::NJ];
-    block_wu<T, D>(KTs, VTs, Tp, Tpp, LDC, Wn, LDD, accU);
-    __syncthreads();
-    {
-      // Vn0 = U - W N^T -> (D Vn0)^T ;  -(W M^T) -> ZD[i][s] = -D_s (M W^T)[i][s]
-      gemm_nt<T, 1, DU::NJ, D>(accU, Wn + 16 * DU::m(w) * LDD, LDD, Nbf + 16 * DU::n0(w) * LDD, LDD);
-      f32x4 accZ[1][DU::NJ];
-      zero_acc(accZ);
-      gemm_nt<T, 1, DU::NJ, D>(accZ, Wn + 16 * DU::m(w) * LDD, LDD, Mbf + 16 * DU::n0(w) * LDD, LDD);
-      const int s = 16 * DU::m(w) + 4 * (lane >> 4);
-      const float d0 = G.dec[s], d1 = G.dec[s + 1], d2 = G.dec[s + 2], d3 = G.dec[s + 3];
+    const int t0 = blk * BLK, nv = min(BLK, a.T - t0);
+    pf.stage(nullptr, Ks, Vs, LDD, nv, G);
+    if (blk + 1 < blk1) pf.fetch(nullptr, k, v, al, bt, rs, a.H, t0 + BLK, min(BLK, a.T - t0 - BLK));
+    lds_barrier();
+    block_scores<T, D, NW, false>(nullptr, Ks, LDD, G, Af, LDF, nullptr, LDC);
+    lds_barrier();
+    block_solve(Af, Tm, LDF);
+    block_tprime<T, 64 * NW>(Tm, LDF, G, Tp, Tpp, LDC);
+    lds_barrier();
+    block_w<T, D>(Ks, LDD, Tp, LDC, Wn);
+    f32x4 X[NDV][4];
+    block_u<T, NDV>(Tpp, LDC, Vs, LDD, dv0, X);
+    lds_barrier();
+    f32x4 dsc[4];
 #pragma unroll
-      for (int j = 0; j < DU::NJ; ++j) {
-        const int n = 16 * (DU::n0(w) + j) + (lane & 15);
-        const f32x4 x = accU[0][j], z = accZ[0][j];
-        st4(VnDT + n * LDC + s, d0 * x[0], d1 * x[1], d2 * x[2], d3 * x[3]);
-        st4(ZD + n * LDC + s, d0 * z[0], d1 * z[1], d2 * z[2], d3 * z[3]);
-      }
-    }
-    __syncthreads();
-    {
-      const float gc = G.gC[0];
-      scale_acc(accN, gc);
-      scale_acc(accM, gc);
-      gemm_nt<T, 1, DS::NJ, BLK>(accN, KTs + 16 * DS::m(w) * LDC, LDC, VnDT + 16 * DS::n0(w) * LDC, LDC);
-      gemm_nt<T, 1, DS::NJ, BLK>(accM, KTs + 16 * DS::m(w) * LDC, LDC, ZD + 16 * DS::n0(w) * LDC, LDC);
-    }
-    __syncthreads();
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < DS::NJ; ++j) {
-      store_tile_T(accN[0][j], Nbf, LDD, 16 * DS::m(w), 16 * (DS::n0(w) + j));
-      store_tile_T(accM[0][j], Mbf, LDD, 16 * DS::m(w), 16 * (DS::n0(w) + j));
-    }
-    if (blk + 1 < blk1) stage();
-    __syncthreads();
+      for (int e = 0; e < 4; ++e) dsc[i][e] = G.dec[16 * i + g4 + e];
+    const float gc = G.gC[0];
+    // N: Vn0 = U - W N^T ; N' = gamma_C N + Vn0^T D K
+    block_x_st<T, D, NDV>(Wn, LDD, Nt, X);
+#pragma unroll
+    for (int bb = 0; bb < NDV; ++bb)
+#pragma unroll
+      for (int aa = 0; aa < DKT; ++aa) Nt[bb][aa] *= gc;
+    block_state_write<T, D, NDV>(Ks, LDD, X, dsc, Nt);
+    // M: Z = -(W M^T) ; M' = gamma_C M + (D Z)^T-term through K
+    zero_acc(X);
+    block_x_st<T, D, NDV>(Wn, LDD, Mt, X);
+#pragma unroll
+    for (int bb = 0; bb < NDV; ++bb)
+#pragma unroll
+      for (int aa = 0; aa < DKT; ++aa) Mt[bb][aa] *= gc;
+    block_state_write<T, D, NDV>(Ks, LDD, X, dsc, Mt);
+    lds_barrier();
   }
 
-  // accN holds N^T[dk][dv] -> N[dv][dk..]; accM holds M^T[j][i] -> M[i][j..].
+  // Nt holds N^T (m = dk, n = dv) -> N[dv][dk..]; Mt holds M^T (m = j, n = i) -> M[i][j..].
   float* Mo = a.Mseg + ((size_t)bh * a.P + seg) * D * D;
   float* No = a.Nseg + ((size_t)bh * a.P + seg) * D * D;
-  const int mrow = 16 * DS::m(w) + 4 * (lane >> 4);
 #pragma unroll
-  for (int j = 0; j < DS::NJ; ++j) {
-    const int n = 16 * (DS::n0(w) + j) + (lane & 15);
-    *reinterpret_cast<f32x4*>(No + (size_t)n * D + mrow) = accN[0][j];
-    *reinterpret_cast<f32x4*>(Mo + (size_t)n * D + mrow) = accM[0][j];
-  }
+  for (int bb = 0; bb < NDV; ++bb)
+#pragma unroll
+    for (int aa = 0; aa < DKT; ++aa) {
+      const size_t off = (size_t)(16 * (dv0 + bb) + li) * D + 16 * aa + g4;
+      *reinterpret_cast<f32x4*>(No + off) = Nt[bb][aa];
+      *reinterpret_cast<f32x4*>(Mo + off) = Mt[bb][aa];
+    }
 }
 
 // ------------------------------------------------------------ chain ---------
 // Entry states of all segments: Sst[0] = S_in (or 0), Sst[j+1] = Sst[j] M_j + N_j.
-// One workgroup of 4 waves per (b, h, 16 rows of S); fp32 MFMA.
+// One workgroup of 4 waves per (b, h, 16 rows of S); fp32 MFMA.  The next
+// segment's map is loaded into registers while the current product runs, so
+// each step costs one dependent chain of MFMAs, not a round trip to memory.
 template <int D>
 __global__ __launch_bounds__(256) void gdn_chain_fwd_kernel(ChainArgs c) {
   constexpr int RT = D / 16;        // row tiles per state
-  constexpr int NT = D / 16 / 4;    // column tiles per wave
+  constexpr int NT = D / 64;        // column tiles per wave
+  constexpr int KS = D / 4;         // MFMA steps along the contraction
   constexpr int LDS_ = D + 4;
   __shared__ __align__(16) float Sl[16 * LDS_];
   const int w = wave_id(), lane = lane_id();
@@ -350,74 +332,130 @@ __global__ __launch_bounds__(256) void gdn_chain_fwd_kernel(ChainArgs c) {
     Sl[rr * LDS_ + cc] = x;
     Sst[(size_t)(r0 + rr) * D + cc] = x;
   }
-  __syncthreads();
-  for (int j = 0; j + 1 < c.P; ++j) {
+  float bm[NT][KS], nn[NT][4];
+  auto load_map = [&](int j, float (&m)[NT][KS], float (&n)[NT][4]) {
     const float* M = c.Mseg + ((size_t)bh * c.P + j) * DD;
     const float* N = c.Nseg + ((size_t)bh * c.P + j) * DD;
-    f32x4 acc[NT];
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
-      const int n = 16 * (w * NT + t) + (lane & 15);
+      const int col = 16 * (w * NT + t) + (lane & 15);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) acc[t][e] = N[(size_t)(r0 + 4 * (lane >> 4) + e) * D + n];
-    }
-#pragma unroll 8
-    for (int kk = 0; kk < D; kk += 4) {
-      const float av = Sl[(lane & 15) * LDS_ + kk + (lane >> 4)];
+      for (int ks = 0; ks < KS; ++ks) m[t][ks] = M[(size_t)(4 * ks + (lane >> 4)) * D + col];
 #pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        const float bv = M[(size_t)(kk + (lane >> 4)) * D + 16 * (w * NT + t) + (lane & 15)];
-        acc[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bv, acc[t], 0, 0, 0);
-      }
+      for (int e = 0; e < 4; ++e) n[t][e] = N[(size_t)(r0 + 4 * (lane >> 4) + e) * D + col];
     }
-    __syncthreads();
+  };
+  if (c.P > 1) load_map(0, bm, nn);
+  lds_barrier();
+  for (int j = 0; j + 1 < c.P; ++j) {
+    float bm2[NT][KS], nn2[NT][4];
+    const bool more = j + 2 < c.P;
+    if (more) load_map(j + 1, bm2, nn2);
+    f32x4 acc[NT][2];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      acc[t][0] = f32x4{nn[t][0], nn[t][1], nn[t][2], nn[t][3]};
+      acc[t][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const float av = Sl[(lane & 15) * LDS_ + 4 * ks + (lane >> 4)];
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+        acc[t][ks & 1] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bm[t][ks], acc[t][ks & 1], 0, 0, 0);
+    }
+    lds_barrier();
     float* Snext = Sst + (size_t)(j + 1) * DD;
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
       const int n = 16 * (w * NT + t) + (lane & 15);
+      const f32x4 x = acc[t][0] + acc[t][1];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int m = 4 * (lane >> 4) + e;
-        Sl[m * LDS_ + n] = acc[t][e];
-        Snext[(size_t)(r0 + m) * D + n] = acc[t][e];
+        Sl[m * LDS_ + n] = x[e];
+        Snext[(size_t)(r0 + m) * D + n] = x[e];
       }
     }
-    __syncthreads();
+    if (more) {
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) bm[t][ks] = bm2[t][ks];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) nn[t][e] = nn2[t][e];
+      }
+    }
+    lds_barrier();
   }
 }
 
 // ------------------------------------------------------------ launch -------
-template <typename T, int D>
 static hipError_t set_lds(const void* fn, size_t bytes) {
   return hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+}
+
+template <typename T, int D>
+hipError_t launch_fwd_summary(const FwdArgs& a, int nseg, hipStream_t st, Profiler* prof) {
+  typedef FwdLds<T, D> Lz;
+  hipError_t e = set_lds((const void*)gdn_fwd_summary_kernel<T, D>, Lz::sum_bytes);
+  if (e != hipSuccess) return e;
+  prof_begin(prof, "gdn_fwd_summary", st);
+  hipLaunchKernelGGL((gdn_fwd_summary_kernel<T, D>), dim3(a.B * a.H * nseg), dim3(4 * D),
+                     Lz::sum_bytes, st, a, nseg);
+  prof_end(prof, st);
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_chain_fwd(const ChainArgs& c, int BH, hipStream_t st, Profiler* prof) {
+  prof_begin(prof, "gdn_chain_fwd", st);
+  hipLaunchKernelGGL((gdn_chain_fwd_kernel<D>), dim3(BH * (D / 16)), dim3(256), 0, st, c);
+  prof_end(prof, st);
+  return hipGetLastError();
+}
+
+template <typename T, int D>
+hipError_t launch_states(const FwdArgs& a, float* hst, hipStream_t st, Profiler* prof) {
+  typedef FwdLds<T, D> Lz;
+  hipError_t e = set_lds((const void*)gdn_fwd_out_kernel<T, D, true>, Lz::out_bytes);
+  if (e != hipSuccess) return e;
+  prof_begin(prof, "gdn_fwd_states", st);
+  hipLaunchKernelGGL((gdn_fwd_out_kernel<T, D, true>), dim3(a.B * a.H * a.P), dim3(4 * D),
+                     Lz::out_bytes, st, a, hst);
+  prof_end(prof, st);
+  return hipGetLastError();
 }
 
 template <typename T, int D>
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t st, Profiler* prof) {
   typedef FwdLds<T, D> Lz;
   hipError_t e;
-  if ((e = set_lds<T, D>((const void*)gdn_fwd_out_kernel<T, D>, Lz::out_bytes)) != hipSuccess) return e;
-  if ((e = set_lds<T, D>((const void*)gdn_fwd_summary_kernel<T, D>, Lz::sum_bytes)) != hipSuccess) return e;
   const int BH = a.B * a.H;
   if (a.P > 1) {
-    prof_begin(prof, "gdn_fwd_summary", st);
-    hipLaunchKernelGGL((gdn_fwd_summary_kernel<T, D>), dim3(BH * (a.P - 1)), dim3(NTHR),
-                       Lz::sum_bytes, st, a, a.P - 1);
-    prof_end(prof, st);
+    if ((e = launch_fwd_summary<T, D>(a, a.P - 1, st, prof)) != hipSuccess) return e;
     ChainArgs c{a.S_in, a.Mseg, a.Nseg, const_cast<float*>(a.Sst), a.P};
-    prof_begin(prof, "gdn_chain_fwd", st);
-    hipLaunchKernelGGL((gdn_chain_fwd_kernel<D>), dim3(BH * (D / 16)), dim3(256), 0, st, c);
-    prof_end(prof, st);
+    if ((e = launch_chain_fwd<D>(c, BH, st, prof)) != hipSuccess) return e;
   }
+  if ((e = set_lds((const void*)gdn_fwd_out_kernel<T, D, false>, Lz::out_bytes)) != hipSuccess)
+    return e;
   prof_begin(prof, "gdn_fwd_out", st);
-  hipLaunchKernelGGL((gdn_fwd_out_kernel<T, D>), dim3(BH * a.P), dim3(NTHR), Lz::out_bytes, st, a);
+  hipLaunchKernelGGL((gdn_fwd_out_kernel<T, D, false>), dim3(BH * a.P), dim3(4 * D),
+                     Lz::out_bytes, st, a, nullptr);
   prof_end(prof, st);
   return hipGetLastError();
 }
 
-template hipError_t launch_fwd<bf16, 128>(const FwdArgs&, hipStream_t, Profiler*);
-template hipError_t launch_fwd<bf16, 64>(const FwdArgs&, hipStream_t, Profiler*);
-template hipError_t launch_fwd<float, 64>(const FwdArgs&, hipStream_t, Profiler*);
+#define SF_INST(T, D)                                                                      \
+  template hipError_t launch_fwd<T, D>(const FwdArgs&, hipStream_t, Profiler*);          \
+  template hipError_t launch_fwd_summary<T, D>(const FwdArgs&, int, hipStream_t, Profiler*); \
+  template hipError_t launch_states<T, D>(const FwdArgs&, float*, hipStream_t, Profiler*);
+SF_INST(bf16, 128)
+SF_INST(bf16, 64)
+SF_INST(float, 64)
+#undef SF_INST
+template hipError_t launch_chain_fwd<128>(const ChainArgs&, int, hipStream_t, Profiler*);
+template hipError_t launch_chain_fwd<64>(const ChainArgs&, int, hipStream_t, Profiler*);
 
 }  // namespace sfgdn
 

@@ -61,6 +61,13 @@ void prof_end(Profiler* p, hipStream_t st);
 
 template <typename T, int D>
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t st, Profiler* prof);
+// Pieces of the forward reused by the backward.
+template <typename T, int D>
+hipError_t launch_fwd_summary(const FwdArgs& a, int nseg, hipStream_t st, Profiler* prof);
+template <int D>
+hipError_t launch_chain_fwd(const ChainArgs& c, int BH, hipStream_t st, Profiler* prof);
+template <typename T, int D>
+hipError_t launch_states(const FwdArgs& a, float* hst, hipStream_t st, Profiler* prof);
 template <typename T, int D>
 hipError_t launch_bwd(const BwdArgs& a, hipStream_t st, Profiler* prof);
 

@@ -73,7 +73,7 @@ sf_status make_plan(const sf_gdn_shape* s, Plan& p) {
     if ((long long)p.B * p.H * p.P > (1LL << 30))
       return fail(SF_ERR_UNSUPPORTED, "too many segments");
   }
-  p.state_elem = (s->dtype == SF_DTYPE_BF16) ? 2 : 4;
+  p.state_elem = 4;  // per-block states and state gradients are kept in fp32
   return SF_OK;
 }
 

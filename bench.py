@@ -1,0 +1,305 @@
+#!/usr/bin/env python3
+"""Throughput benchmark of the chunked gated delta rule on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+One step is the whole hot path over one batch: the chained forward over the
+pipeline chunks of the sequence (boundary state passed forward, Eq. 5 of the
+StateFlow page) followed by the chained backward (state gradient passed
+backward, Eq. 7).  The default workload is a 262,144-token sequence, 16 heads,
+d_k = d_v = 128, bf16, split into 8 chunks by the hybrid-cost plan
+c_i(alpha = 0.5) of Eq. 9 (a = 1, b = 0.25, literal token units).  Inputs are
+synthetic and resident in HBM before timing starts.
+
+Prints one JSON line with the metric, a roofline for the dominant kernel
+(per-launch times from HIP events recorded around every launch on the
+launching stream during the timed region) and for the whole path, and the
+fp64 CPU oracle timed on a bounded sample.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, HERE)
+
+METRIC = "tokens/sec chunked GDN fwd+bwd (H=16,d=128,1 GPU); % MFMA/HBM roofline"
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+PEAK_F32_TFLOPS = 157.3       # MI355X fp32 MFMA / vector
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+
+C = 64  # kernel block
+
+
+def kernel_flops_per_block(name, d):
+    """Algorithmic MFMA flops per 64-token block of one head, per kernel:
+    the sum of the matrix products the kernel's step of the method needs
+    (2 m n k each)."""
+    g = lambda m, n, k: 2.0 * m * n * k
+    pre = g(C, C, d) + g(C, C, d) + g(C, d, C) + g(C, d, C)   # K K^T, (Q K^T), W, U
+    if name == "gdn_fwd_out":
+        return pre + g(C, d, d) + g(C, d, d) + g(C, d, C) + g(d, d, C)   # Vn, QS^T, P Vn, S'
+    if name in ("gdn_fwd_summary", "gdn_bwd_summary"):
+        return (pre - g(C, C, d)) + g(C, d, d) + g(d, d, C) + g(C, d, d) + g(d, d, C)  # + M
+    if name == "gdn_fwd_states":
+        return (pre - g(C, C, d)) + g(C, d, d) + g(d, d, C)
+    if name in ("gdn_bwd_dscan", "gdn_bwd_dscan_summary"):
+        return (pre - g(C, d, C)) + g(d, d, C) + g(C, d, C) + g(C, d, d) + g(d, d, C)
+    if name == "gdn_bwd_grads":
+        return (pre + g(C, d, d)                       # recompute incl. Vn
+                + g(C, d, C) + g(C, d, d)              # dVn
+                + g(C, d, C) + g(C, C, d)              # dV, dP
+                + g(C, d, d) + g(C, d, C) + g(C, d, C)  # dQ, dK1
+                + 2 * g(C, d, d)                       # dW, dK2
+                + 2 * g(C, C, d)                       # dTp, dTpp
+                + 2 * g(C, C, C)                       # dA = -T^T dT T^T
+                + g(C, C, d) + 3 * g(C, d, C))         # kk, dK4 (two), dK3
+    return None
+
+
+def kernel_flops_per_launch(name, d, H, T, L, P):
+    """Algorithmic flops of one launch for one chunk of T tokens."""
+    nblk = (T + C - 1) // C
+    if name in ("gdn_chain_fwd", "gdn_chain_bwd"):
+        return H * max(P - 1, 0) * 2.0 * d * d * d
+    per = kernel_flops_per_block(name, d)
+    if per is None:
+        return None
+    if name == "gdn_fwd_summary":      # segments 0 .. P-2
+        return H * min(nblk, (P - 1) * L) * per
+    if name == "gdn_bwd_dscan_summary":
+        return H * max(nblk - min(L, nblk), 0) * per
+    return H * nblk * per
+
+
+def source_hash():
+    h = hashlib.sha256()
+    csrc = os.path.join(HERE, "linear_recurrence_chunked_gated_amd", "csrc")
+    for fn in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, fn), "rb") as f:
+            h.update(fn.encode())
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(kernel):
+    """HBM bytes per launch of `kernel` recorded from rocprofv3 counter runs
+    (profiles/traffic.json), or None when absent or taken on other sources."""
+    p = os.path.join(HERE, "profiles", "traffic.json")
+    if not os.path.exists(p):
+        return None
+    with open(p) as f:
+        rec = json.load(f)
+    if rec.get("source_hash") != source_hash():
+        return None
+    k = rec.get("kernels", {}).get(kernel)
+    return None if k is None else k.get("bytes_per_launch")
+
+
+def workload(name):
+    from linear_recurrence_chunked_gated_amd.plan import chunk_lengths
+    if name == "fwdbwd_h16_t262144_d128_8skew":
+        T = 262144
+        return dict(T=T, H=16, D=128, chunks=chunk_lengths(T, 8, 0.5), bwd=True, s_in_std=None,
+                    seed=20260004,
+                    desc="T=262144, H=16, d=128, bf16, 8 chunks by c_i(0.5) of Eq. 9 "
+                         "(a=1, b=0.25, token units), chained fwd then bwd")
+    if name == "fwdbwd_h16_t16384_d128":
+        return dict(T=16384, H=16, D=128, chunks=[16384], bwd=True, s_in_std=None, seed=20260003,
+                    desc="T=16384, H=16, d=128, bf16, one chunk fwd+bwd")
+    if name == "fwd_h16_t65536_d128":
+        return dict(T=65536, H=16, D=128, chunks=[65536], bwd=False, s_in_std=0.1, seed=20260102,
+                    desc="T=65536, H=16, d=128, bf16, one chunk fwd, S_in ~ N(0, 0.1)")
+    if name == "fwd_h32_t65536_d128":
+        return dict(T=65536, H=32, D=128, chunks=[65536], bwd=False, s_in_std=0.1, seed=20260002,
+                    desc="T=65536, H=32, d=128, bf16, one chunk fwd, S_in ~ N(0, 0.1)")
+    raise SystemExit("unknown workload %r" % name)
+
+
+def cpu_baseline(wl, seconds_target=7.0):
+    """The fp64 oracle on a bounded sample: the first n tokens of the same
+    sequence (all heads), one chunk forward and backward (or forward only)."""
+    import numpy as np
+    import oracle
+    from linear_recurrence_chunked_gated_amd.inputs import gdn_inputs, as_f64
+    oracle.build(force=False)
+    H, D = wl["H"], wl["D"]
+    n = 256
+    while True:
+        d = gdn_inputs(1, n, H, D, D, dtype="bf16", seed=wl["seed"], s_in_std=wl["s_in_std"],
+                       grads=wl["bwd"], device="cpu")
+        args = [as_f64(d[k]) for k in ("q", "k", "v", "alpha", "beta")] + [as_f64(d["S_in"])]
+        t0 = time.perf_counter()
+        _, _, nt = oracle.gdn_fwd(*args, return_threads=True)
+        if wl["bwd"]:
+            oracle.gdn_bwd(*args, as_f64(d["dO"]), as_f64(d["dS_out"]))
+        dt = time.perf_counter() - t0
+        if dt >= seconds_target or 2 * n > wl["T"]:
+            break
+        n *= 2
+    return {"value": n / dt, "unit": "tokens/s", "cores": int(nt), "kind": "oracle",
+            "sample": "first %d tokens x %d heads of the workload's sequence, one chunk, %s, "
+                      "fp64 token loop (%.1f s)" % (n, H, "fwd+bwd" if wl["bwd"] else "fwd", dt)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", default="fwdbwd_h16_t262144_d128_8skew")
+    ap.add_argument("--seg-blocks", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU; runs on several GPUs are not part of this build "
+              "(the chunk path shards by heads with no exchange, or along the sequence with one "
+              "boundary-state exchange per chunk)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import linear_recurrence_chunked_gated_amd as gdn
+    from linear_recurrence_chunked_gated_amd import _lib
+    from linear_recurrence_chunked_gated_amd.inputs import gdn_inputs
+
+    wl = workload(args.workload)
+    T, H, D, chunks = wl["T"], wl["H"], wl["D"], wl["chunks"]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    d = gdn_inputs(1, T, H, D, D, dtype="bf16", seed=wl["seed"], s_in_std=wl["s_in_std"],
+                   grads=wl["bwd"], device=dev)
+    q, k, v, al, be = d["q"], d["k"], d["v"], d["alpha"], d["beta"]
+    bounds = [0]
+    for n in chunks:
+        bounds.append(bounds[-1] + n)
+    # Preallocated outputs, boundary states and workspaces.
+    o = torch.empty_like(v)
+    states = [d["S_in"] if d["S_in"] is not None else torch.zeros(1, H, D, D, device=dev)]
+    states += [torch.empty(1, H, D, D, device=dev) for _ in chunks]
+    ws_f = max(_lib.workspace_bytes(_lib.make_shape(1, n, H, D, D, q.dtype, args.seg_blocks))
+               for n in chunks)
+    wsf = _lib.alloc_workspace(ws_f, dev)
+    if wl["bwd"]:
+        dO, dS_out = d["dO"], d["dS_out"]
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+        dal, dbe = torch.empty_like(al), torch.empty_like(be)
+        gst = [torch.empty(1, H, D, D, device=dev) for _ in range(len(chunks) + 1)]
+        ws_b = max(_lib.workspace_bytes(_lib.make_shape(1, n, H, D, D, q.dtype, args.seg_blocks),
+                                        backward=True) for n in chunks)
+        wsb = _lib.alloc_workspace(ws_b, dev)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        for i in range(len(chunks)):
+            sl = slice(bounds[i], bounds[i + 1])
+            _lib.chunk_fwd(q[:, sl], k[:, sl], v[:, sl], al[:, sl], be[:, sl], states[i],
+                           o=o[:, sl], S_out=states[i + 1], seg_blocks=args.seg_blocks,
+                           workspace=wsf, stream=stream)
+        if wl["bwd"]:
+            G = dS_out
+            for i in range(len(chunks) - 1, -1, -1):
+                sl = slice(bounds[i], bounds[i + 1])
+                _lib.chunk_bwd(q[:, sl], k[:, sl], v[:, sl], al[:, sl], be[:, sl], states[i],
+                               dO[:, sl], G, grads=(dq[:, sl], dk[:, sl], dv[:, sl], dal[:, sl],
+                                                    dbe[:, sl], gst[i]),
+                               seg_blocks=args.seg_blocks, workspace=wsb, stream=stream)
+                G = gst[i]
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    with _lib.profile(capacity=256 * args.steps * len(chunks) + 64) as prof:
+        torch.cuda.synchronize()
+        e0.record(stream)
+        wall0 = time.perf_counter()
+        for _ in range(args.steps):
+            step()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - wall0
+    ms = e0.elapsed_time(e1) / args.steps
+    tok_s = T / (ms * 1e-3)
+
+    # Per-kernel times over the timed region.
+    kern = {name: {"launches": n, "avg_us": tot / n * 1e3, "total_ms_per_step": tot / args.steps}
+            for name, (n, tot) in prof.results.items()}
+    dom = max(kern, key=lambda n: kern[n]["total_ms_per_step"])
+    # Algorithmic flops of the dominant kernel per launch (averaged over the
+    # chunk sizes of one step).
+    L_of = {}
+    for n in chunks:
+        nblk = (n + C - 1) // C
+        if args.seg_blocks:
+            L = args.seg_blocks
+        else:
+            P0 = min(nblk, max(1, -(-256 // H)))
+            L = -(-nblk // P0)
+        L = min(L, nblk)
+        L_of[n] = (L, -(-nblk // L))
+    fl = []
+    for n in chunks:
+        L, P = L_of[n]
+        f = kernel_flops_per_launch(dom, D, H, n, L, P)
+        if f is None:
+            fl = None
+            break
+        fl.append(f)
+    roofline = None
+    if fl:
+        per_launch = sum(fl) / len(fl)
+        achieved = per_launch / (kern[dom]["avg_us"] * 1e-6) / 1e12
+        traffic = load_traffic(dom)
+        roofline = {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 2),
+                    "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                    "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
+                    "flops_per_launch": per_launch}
+    # Whole-path roofline: algorithmic flops and bytes per token-head of the
+    # method (fwd 182,955 flop and 1,032 B; fwd+bwd 726,358 flop and 2,840 B at
+    # d = 128, block 64) plus the boundary states each chunk call moves.
+    fl_th = 726358.0 if wl["bwd"] else 182955.0
+    by_th = 2840.0 if wl["bwd"] else 1032.0
+    nst = (5 if wl["bwd"] else 2) * len(chunks) * H * D * D * 4
+    F = fl_th * T * H
+    Bytes = by_th * T * H + nst
+    t_roof = max(F / (PEAK_BF16_TFLOPS * 1e12), Bytes / (PEAK_HBM_GBS * 1e9))
+    path = {"bound": "hbm" if Bytes / (PEAK_HBM_GBS * 1e9) >= F / (PEAK_BF16_TFLOPS * 1e12) else "mfma",
+            "t_roof_ms": round(t_roof * 1e3, 4), "t_step_ms": round(ms, 4),
+            "frac": round(t_roof / (ms * 1e-3), 4),
+            "algorithmic_flops": F, "algorithmic_bytes": Bytes}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(wl)
+
+    line = {
+        "metric": METRIC,
+        "value": round(tok_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "description": wl["desc"], "B": 1, "T": T, "H": H,
+                   "d_k": D, "d_v": D, "block": C, "chunks": chunks,
+                   "seg_blocks": args.seg_blocks or "auto", "parallelism": "single GPU"},
+        "roofline": roofline,
+        "path_roofline": path,
+        "kernels": {n: {"avg_us": round(x["avg_us"], 2), "launches_per_step": x["launches"] // args.steps,
+                        "ms_per_step": round(x["total_ms_per_step"], 4)} for n, x in kern.items()},
+        "wall_s_timed": round(wall, 3),
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -790,7 +790,7 @@ hipError_t launch_bwd(const BwdArgs& a0, hipStream_t st, Profiler* prof) {
   int dsend_P = 1;
   if (P > 1) {
     // 1. segment maps of the forward (all segments)
-    if ((e = launch_fwd_summary<T, D>(f, P, st, prof)) != hipSuccess) return e;
+    if ((e = launch_fwd_summary<T, D>(f, P, st, prof, "gdn_bwd_summary")) != hipSuccess) return e;
     // 2. NB maps of segments 1..P-1
     if ((e = set_lds((const void*)gdn_bwd_dscan_kernel<T, D, false>, ScanLds<T, D>::bytes)) != hipSuccess)
       return e;

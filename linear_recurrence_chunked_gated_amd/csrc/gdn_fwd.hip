@@ -396,11 +396,12 @@ static hipError_t set_lds(const void* fn, size_t bytes) {
 }
 
 template <typename T, int D>
-hipError_t launch_fwd_summary(const FwdArgs& a, int nseg, hipStream_t st, Profiler* prof) {
+hipError_t launch_fwd_summary(const FwdArgs& a, int nseg, hipStream_t st, Profiler* prof,
+                              const char* name) {
   typedef FwdLds<T, D> Lz;
   hipError_t e = set_lds((const void*)gdn_fwd_summary_kernel<T, D>, Lz::sum_bytes);
   if (e != hipSuccess) return e;
-  prof_begin(prof, "gdn_fwd_summary", st);
+  prof_begin(prof, name, st);
   hipLaunchKernelGGL((gdn_fwd_summary_kernel<T, D>), dim3(a.B * a.H * nseg), dim3(4 * D),
                      Lz::sum_bytes, st, a, nseg);
   prof_end(prof, st);
@@ -433,7 +434,7 @@ hipError_t launch_fwd(const FwdArgs& a, hipStream_t st, Profiler* prof) {
   hipError_t e;
   const int BH = a.B * a.H;
   if (a.P > 1) {
-    if ((e = launch_fwd_summary<T, D>(a, a.P - 1, st, prof)) != hipSuccess) return e;
+    if ((e = launch_fwd_summary<T, D>(a, a.P - 1, st, prof, "gdn_fwd_summary")) != hipSuccess) return e;
     ChainArgs c{a.S_in, a.Mseg, a.Nseg, const_cast<float*>(a.Sst), a.P};
     if ((e = launch_chain_fwd<D>(c, BH, st, prof)) != hipSuccess) return e;
   }
@@ -448,7 +449,7 @@ hipError_t launch_fwd(const FwdArgs& a, hipStream_t st, Profiler* prof) {
 
 #define SF_INST(T, D)                                                                      \
   template hipError_t launch_fwd<T, D>(const FwdArgs&, hipStream_t, Profiler*);          \
-  template hipError_t launch_fwd_summary<T, D>(const FwdArgs&, int, hipStream_t, Profiler*); \
+  template hipError_t launch_fwd_summary<T, D>(const FwdArgs&, int, hipStream_t, Profiler*, const char*); \
   template hipError_t launch_states<T, D>(const FwdArgs&, float*, hipStream_t, Profiler*);
 SF_INST(bf16, 128)
 SF_INST(bf16, 64)

@@ -63,7 +63,8 @@ template <typename T, int D>
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t st, Profiler* prof);
 // Pieces of the forward reused by the backward.
 template <typename T, int D>
-hipError_t launch_fwd_summary(const FwdArgs& a, int nseg, hipStream_t st, Profiler* prof);
+hipError_t launch_fwd_summary(const FwdArgs& a, int nseg, hipStream_t st, Profiler* prof,
+                              const char* name);
 template <int D>
 hipError_t launch_chain_fwd(const ChainArgs& c, int BH, hipStream_t st, Profiler* prof);
 template <typename T, int D>

@@ -99,6 +99,73 @@ def load_traffic(kernel):
     return None if k is None else k.get("bytes_per_launch")
 
 
+def _read_counter_csv(path):
+    """Per-kernel mean of a rocprofv3 counter over dispatches: {kernel: value}."""
+    import csv
+    sums, counts = {}, {}
+    with open(path) as f:
+        for row in csv.DictReader(f):
+            name = row.get("Kernel_Name") or row.get("Kernel-Name") or row.get("KernelName")
+            val = row.get("Counter_Value") or row.get("Counter-Value")
+            if name is None or val is None:
+                continue
+            disp = row.get("Dispatch_Id") or row.get("Dispatch-Id") or str(len(counts))
+            key = (name, disp)
+            sums[key] = sums.get(key, 0.0) + float(val)   # sum over counter instances
+    per = {}
+    for (name, _), v in sums.items():
+        per.setdefault(name, []).append(v)
+    return {n: sum(v) / len(v) for n, v in per.items()}
+
+
+def write_traffic(fetch_csv, write_csv, calib_fetch_csv, calib_write_csv, calib_bytes):
+    """HBM bytes per launch of every library kernel from FETCH_SIZE and
+    WRITE_SIZE (KiB per dispatch), each scaled by what the same counter reads
+    for a plain device copy of calib_bytes."""
+    fetch = _read_counter_csv(fetch_csv)
+    write = _read_counter_csv(write_csv)
+    cf = _read_counter_csv(calib_fetch_csv)
+    cw = _read_counter_csv(calib_write_csv)
+    copy_f = max(cf.values())
+    copy_w = max(cw.values())
+    sf = calib_bytes / (copy_f * 1024.0)
+    sw = calib_bytes / (copy_w * 1024.0)
+    import re
+    out = {"source_hash": source_hash(),
+           "calibration": {"copy_bytes_each_way": calib_bytes,
+                           "fetch_kib_per_copy": copy_f, "write_kib_per_copy": copy_w,
+                           "fetch_scale": sf, "write_scale": sw},
+           "kernels": {}}
+    for name in sorted(set(fetch) | set(write)):
+        m = re.search(r"(gdn_\w+?)_kernel", name)
+        if not m:
+            continue
+        short = m.group(1)
+        if "Lb1E" in name and short == "gdn_fwd_out":
+            short = "gdn_fwd_states"
+        if short == "gdn_bwd_dscan" and "Lb0E" in name:
+            short = "gdn_bwd_dscan_summary"
+        fb = fetch.get(name, 0.0) * 1024.0 * sf
+        wb = write.get(name, 0.0) * 1024.0 * sw
+        out["kernels"][short] = {"fetch_bytes": fb, "write_bytes": wb, "bytes_per_launch": fb + wb}
+    path = os.path.join(HERE, "profiles", "traffic.json")
+    with open(path, "w") as f:
+        json.dump(out, f, indent=1)
+    print(json.dumps(out, indent=1))
+
+
+def copy_calibration(nbytes=1 << 30, reps=4):
+    """A plain device copy of known size, for scaling HBM byte counters."""
+    import torch
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_each_way": nbytes, "reps": reps}))
+
+
 def workload(name):
     from linear_recurrence_chunked_gated_amd.plan import chunk_lengths
     if name == "fwdbwd_h16_t262144_d128_8skew":
@@ -153,7 +220,18 @@ def main():
     ap.add_argument("--workload", default="fwdbwd_h16_t262144_d128_8skew")
     ap.add_argument("--seg-blocks", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run a plain 1 GiB device copy (for rocprofv3 counter scaling) and exit")
+    ap.add_argument("--write-traffic", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "CALIB_FETCH_CSV",
+                                                         "CALIB_WRITE_CSV"),
+                    help="turn rocprofv3 FETCH_SIZE/WRITE_SIZE runs into profiles/traffic.json")
     args = ap.parse_args()
+    if args.write_traffic:
+        write_traffic(*args.write_traffic, calib_bytes=1 << 30)
+        return
+    if args.copy_calibration:
+        copy_calibration()
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU; runs on several GPUs are not part of this build "
               "(the chunk path shards by heads with no exchange, or along the sequence with one "

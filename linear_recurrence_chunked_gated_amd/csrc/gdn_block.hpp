@@ -191,24 +191,31 @@ __device__ __forceinline__ void block_tprime(const float* Tm, int ldf, const Gat
   }
 }
 
-// Wn = -W, row-major [r][dk], by a workgroup of D/16 waves (wave w: dk-tile
-// w): computed as W^T = K^T Tp^T with K^T read through the transpose read
-// from the row-major K tile.
-template <typename T, int D>
+// Wn = -W, row-major [r][dk], by a workgroup of NW waves (wave w: dk-tiles
+// NDK*w ..): computed as W^T = K^T Tp^T with K^T read through the transpose
+// read from the row-major K tile.
+template <typename T, int D, int NW>
 __device__ __forceinline__ void block_w(const T* Ks, int ldd, const T* Tp, int ldc, T* Wn) {
+  constexpr int NDK = D / 16 / NW;
   const int w = wave_id();
-  f32x4 acc[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  f32x4 acc[NDK][4];
+  zero_acc(acc);
 #pragma unroll
   for (int s = 0; s < BLK / Mma<T>::KSTEP; ++s) {
-    const auto a = frag_tr<T, STD>(Ks + 16 * w, ldd, s);
+    typename Mma<T>::frag bt[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      acc[j] = Mma<T>::mma(a, frag_row<T, STD>(Tp + 16 * j * ldc, ldc, s), acc[j]);
+    for (int j = 0; j < 4; ++j) bt[j] = frag_row<T, STD>(Tp + 16 * j * ldc, ldc, s);
+#pragma unroll
+    for (int i = 0; i < NDK; ++i) {
+      const auto a = frag_tr<T, STD>(Ks + 16 * (NDK * w + i), ldd, s);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[i][j] = Mma<T>::mma(a, bt[j], acc[i][j]);
+    }
   }
 #pragma unroll
-  for (int j = 0; j < 4; ++j) store_tile_T(acc[j], Wn, ldd, 16 * w, 16 * j, -1.f);
+  for (int i = 0; i < NDK; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) store_tile_T(acc[i][j], Wn, ldd, 16 * (NDK * w + i), 16 * j, -1.f);
 }
 
 // U[s][dv] = (Tpp V)[s][dv] for this wave's dv-tiles dv0 .. dv0+NDV-1, into

@@ -168,7 +168,7 @@ __global__ __launch_bounds__(4 * D, 2) void gdn_bwd_dscan_kernel(BwdArgs a, int 
     block_solve(Af, Tm, LDF);
     block_tprime<T, 64 * NW>(Tm, LDF, G, Tp, Tpp, LDC);
     lds_barrier();
-    block_w<T, D>(Ks, LDD, Tp, LDC, Wn);
+    block_w<T, D, NW>(Ks, LDD, Tp, LDC, Wn);
     lds_barrier();
     // dVn = P^T dO + D (K dS'^T)
     f32x4 dvn[4], kd[4];
@@ -451,7 +451,7 @@ __global__ __launch_bounds__(4 * D, 2) void gdn_bwd_grads_kernel(BwdArgs a) {
     if ((s >> 4) > (r >> 4)) Tm[r * LDF + s] = 0.f;
   }
   // ---- D: W, U
-  block_w<T, D>(Ks, LDD, Tp, LDC, Wn);
+  block_w<T, D, NW>(Ks, LDD, Tp, LDC, Wn);
   f32x4 U[1][4];
   block_u<T, 1>(Tpp, LDC, Vs, LDD, w, U);
   lds_barrier();

@@ -56,8 +56,12 @@ __device__ __forceinline__ const T* seq_base(const void* p, const FwdArgs& a, in
 
 // Per-block inputs in flight: the next block's rows are loaded into registers
 // while the current block computes.
+// Waves per workgroup of the forward kernels: one per 16-column tile of the
+// state.
+template <int D> constexpr int fwd_nw() { return D / 16; }
+
 template <typename T, int D, bool WITH_Q> struct Prefetch {
-  typedef Tile<T, D, 4 * D> Tl;
+  typedef Tile<T, D, 64 * fwd_nw<D>()> Tl;
   uint4 rq[WITH_Q ? Tl::NCH : 1], rk[Tl::NCH], rv[Tl::NCH];
   float la = 0.f, be = 0.f;
   __device__ __forceinline__ void fetch(const T* q, const T* k, const T* v, const float* al,
@@ -82,14 +86,14 @@ template <typename T, int D, bool WITH_Q> struct Prefetch {
 };
 
 // --------------------------------------------------------- fused out -------
-// Wave w owns dv-tile w of the state: S^T, U/Vn and O^T for those 16 columns
-// live in its registers for the whole segment.  With STATES the kernel
+// Wave w owns dv-tiles NDV*w .. of the state: S^T, U/Vn and O^T for those
+// columns live in its registers for the whole segment.  With STATES the kernel
 // computes no output; instead it stores each block's entry state (fp32,
 // [dv][dk]) to hst[b*H + h][block], which the backward pass consumes.
 template <typename T, int D, bool STATES>
-__global__ __launch_bounds__(4 * D, 2) void gdn_fwd_out_kernel(FwdArgs a, float* hst) {
+__global__ __launch_bounds__(64 * fwd_nw<D>(), 2) void gdn_fwd_out_kernel(FwdArgs a, float* hst) {
   typedef FwdLds<T, D> Lz;
-  constexpr int NW = D / 16, NDV = 1, DKT = D / 16;
+  constexpr int NW = fwd_nw<D>(), NDV = D / 16 / NW, DKT = D / 16;
   constexpr int LDD = Lz::LDD, LDC = Lz::LDC, LDF = Lz::LDF;
   extern __shared__ __align__(16) unsigned char smem[];
   T* Qs = reinterpret_cast<T*>(smem + Lz::oQ);
@@ -153,12 +157,14 @@ __global__ __launch_bounds__(4 * D, 2) void gdn_fwd_out_kernel(FwdArgs a, float*
     if constexpr (STATES) {
       float* hb = hst + ((size_t)bh * a.nblk + blk) * D * D;
 #pragma unroll
-      for (int aa = 0; aa < DKT; ++aa)
-        *reinterpret_cast<f32x4*>(hb + (size_t)(16 * dv0 + li) * D + 16 * aa + g4) = St[0][aa];
+      for (int bb = 0; bb < NDV; ++bb)
+#pragma unroll
+        for (int aa = 0; aa < DKT; ++aa)
+          *reinterpret_cast<f32x4*>(hb + (size_t)(16 * (dv0 + bb) + li) * D + 16 * aa + g4) =
+              St[bb][aa];
     } else {
       if (prev_t0 >= 0) store_o();
     }
-    if (blk + 1 < blk1) pf.fetch(q, k, v, al, bt, rs, a.H, t0 + BLK, min(BLK, a.T - t0 - BLK));
     lds_barrier();
     // Pre: scores; Out, state part: O^T = diag(gamma) (S Q^T)
     block_scores<T, D, NW, !STATES>(Qs, Ks, LDD, G, Af, LDF, Pl, LDC);
@@ -177,7 +183,7 @@ __global__ __launch_bounds__(4 * D, 2) void gdn_fwd_out_kernel(FwdArgs a, float*
     block_solve(Af, Tm, LDF);
     block_tprime<T, 64 * NW>(Tm, LDF, G, Tp, Tpp, LDC);
     lds_barrier();
-    block_w<T, D>(Ks, LDD, Tp, LDC, Wn);
+    block_w<T, D, NW>(Ks, LDD, Tp, LDC, Wn);
     f32x4 U[NDV][4];
     block_u<T, NDV>(Tpp, LDC, Vs, LDD, dv0, U);
     lds_barrier();
@@ -197,6 +203,9 @@ __global__ __launch_bounds__(4 * D, 2) void gdn_fwd_out_kernel(FwdArgs a, float*
     block_state_write<T, D, NDV>(Ks, LDD, U, dsc, St);
     prev_t0 = t0;
     prev_nv = nv;
+    // The next block's rows: issued here so that they add no register pressure
+    // to the phases above; the other workgroup on the CU covers the latency.
+    if (blk + 1 < blk1) pf.fetch(q, k, v, al, bt, rs, a.H, t0 + BLK, min(BLK, a.T - t0 - BLK));
     lds_barrier();
   }
   if constexpr (!STATES) {
@@ -221,9 +230,9 @@ __global__ __launch_bounds__(4 * D, 2) void gdn_fwd_out_kernel(FwdArgs a, float*
 //   M' = gamma_C M - (M W^T) D K
 // runs like the state update with M in place of S.
 template <typename T, int D>
-__global__ __launch_bounds__(4 * D, 2) void gdn_fwd_summary_kernel(FwdArgs a, int nseg) {
+__global__ __launch_bounds__(64 * fwd_nw<D>(), 2) void gdn_fwd_summary_kernel(FwdArgs a, int nseg) {
   typedef FwdLds<T, D> Lz;
-  constexpr int NW = D / 16, NDV = 1, DKT = D / 16;
+  constexpr int NW = fwd_nw<D>(), NDV = D / 16 / NW, DKT = D / 16;
   constexpr int LDD = Lz::LDD, LDC = Lz::LDC, LDF = Lz::LDF;
   extern __shared__ __align__(16) unsigned char smem[];
   float* Tm = reinterpret_cast<float*>(smem + Lz::oQ);
@@ -261,14 +270,13 @@ __global__ __launch_bounds__(4 * D, 2) void gdn_fwd_summary_kernel(FwdArgs a, in
   for (int blk = blk0; blk < blk1; ++blk) {
     const int t0 = blk * BLK, nv = min(BLK, a.T - t0);
     pf.stage(nullptr, Ks, Vs, LDD, nv, G);
-    if (blk + 1 < blk1) pf.fetch(nullptr, k, v, al, bt, rs, a.H, t0 + BLK, min(BLK, a.T - t0 - BLK));
     lds_barrier();
     block_scores<T, D, NW, false>(nullptr, Ks, LDD, G, Af, LDF, nullptr, LDC);
     lds_barrier();
     block_solve(Af, Tm, LDF);
     block_tprime<T, 64 * NW>(Tm, LDF, G, Tp, Tpp, LDC);
     lds_barrier();
-    block_w<T, D>(Ks, LDD, Tp, LDC, Wn);
+    block_w<T, D, NW>(Ks, LDD, Tp, LDC, Wn);
     f32x4 X[NDV][4];
     block_u<T, NDV>(Tpp, LDC, Vs, LDD, dv0, X);
     lds_barrier();
@@ -293,6 +301,7 @@ __global__ __launch_bounds__(4 * D, 2) void gdn_fwd_summary_kernel(FwdArgs a, in
 #pragma unroll
       for (int aa = 0; aa < DKT; ++aa) Mt[bb][aa] *= gc;
     block_state_write<T, D, NDV>(Ks, LDD, X, dsc, Mt);
+    if (blk + 1 < blk1) pf.fetch(nullptr, k, v, al, bt, rs, a.H, t0 + BLK, min(BLK, a.T - t0 - BLK));
     lds_barrier();
   }
 
@@ -402,7 +411,7 @@ hipError_t launch_fwd_summary(const FwdArgs& a, int nseg, hipStream_t st, Profil
   hipError_t e = set_lds((const void*)gdn_fwd_summary_kernel<T, D>, Lz::sum_bytes);
   if (e != hipSuccess) return e;
   prof_begin(prof, name, st);
-  hipLaunchKernelGGL((gdn_fwd_summary_kernel<T, D>), dim3(a.B * a.H * nseg), dim3(4 * D),
+  hipLaunchKernelGGL((gdn_fwd_summary_kernel<T, D>), dim3(a.B * a.H * nseg), dim3(64 * fwd_nw<D>()),
                      Lz::sum_bytes, st, a, nseg);
   prof_end(prof, st);
   return hipGetLastError();
@@ -422,7 +431,7 @@ hipError_t launch_states(const FwdArgs& a, float* hst, hipStream_t st, Profiler*
   hipError_t e = set_lds((const void*)gdn_fwd_out_kernel<T, D, true>, Lz::out_bytes);
   if (e != hipSuccess) return e;
   prof_begin(prof, "gdn_fwd_states", st);
-  hipLaunchKernelGGL((gdn_fwd_out_kernel<T, D, true>), dim3(a.B * a.H * a.P), dim3(4 * D),
+  hipLaunchKernelGGL((gdn_fwd_out_kernel<T, D, true>), dim3(a.B * a.H * a.P), dim3(64 * fwd_nw<D>()),
                      Lz::out_bytes, st, a, hst);
   prof_end(prof, st);
   return hipGetLastError();
@@ -441,7 +450,7 @@ hipError_t launch_fwd(const FwdArgs& a, hipStream_t st, Profiler* prof) {
   if ((e = set_lds((const void*)gdn_fwd_out_kernel<T, D, false>, Lz::out_bytes)) != hipSuccess)
     return e;
   prof_begin(prof, "gdn_fwd_out", st);
-  hipLaunchKernelGGL((gdn_fwd_out_kernel<T, D, false>), dim3(BH * a.P), dim3(4 * D),
+  hipLaunchKernelGGL((gdn_fwd_out_kernel<T, D, false>), dim3(BH * a.P), dim3(64 * fwd_nw<D>()),
                      Lz::out_bytes, st, a, nullptr);
   prof_end(prof, st);
   return hipGetLastError();

@@ -40,7 +40,7 @@ def kernel_flops_per_block(name, d):
     (2 m n k each)."""
     g = lambda m, n, k: 2.0 * m * n * k
     pre = g(C, C, d) + g(C, C, d) + g(C, d, C) + g(C, d, C)   # K K^T, (Q K^T), W, U
-    if name == "gdn_fwd_out":
+    if name in ("gdn_fwd_out", "gdn_fwd_out_save"):
         return pre + g(C, d, d) + g(C, d, d) + g(C, d, C) + g(d, d, C)   # Vn, QS^T, P Vn, S'
     if name in ("gdn_fwd_summary", "gdn_bwd_summary"):
         return (pre - g(C, C, d)) + g(C, d, d) + g(d, d, C) + g(C, d, d) + g(d, d, C)  # + M
@@ -60,16 +60,17 @@ def kernel_flops_per_block(name, d):
     return None
 
 
-def kernel_flops_per_launch(name, d, H, T, L, P):
-    """Algorithmic flops of one launch for one chunk of T tokens."""
+def kernel_flops_per_launch(name, d, H, T, L, P, save=False):
+    """Algorithmic flops of one launch for one chunk of T tokens (``save``:
+    the saving forward, whose summary covers every segment)."""
     nblk = (T + C - 1) // C
     if name in ("gdn_chain_fwd", "gdn_chain_bwd"):
         return H * max(P - 1, 0) * 2.0 * d * d * d
     per = kernel_flops_per_block(name, d)
     if per is None:
         return None
-    if name == "gdn_fwd_summary":      # segments 0 .. P-2
-        return H * min(nblk, (P - 1) * L) * per
+    if name == "gdn_fwd_summary":      # segments 0 .. P-2, or all when saving
+        return H * (nblk if save else min(nblk, (P - 1) * L)) * per
     if name == "gdn_bwd_dscan_summary":
         return H * max(nblk - min(L, nblk), 0) * per
     return H * nblk * per
@@ -118,6 +119,27 @@ def _read_counter_csv(path):
     return {n: sum(v) / len(v) for n, v in per.items()}
 
 
+def kernel_label(name):
+    """The library's launch label of a kernel as a profiler names it
+    (demangled or mangled), or None for other kernels."""
+    import re
+    m = re.search(r"(gdn_\w+?)_kernel", name)
+    if not m:
+        return None
+    base = m.group(1)
+    d = re.search(r"_kernel<([^<>]*)>", name)
+    if d:
+        last = d.group(1).split(",")[-1].strip()
+    else:
+        mm = re.search(r"L[ib](\d+)EEE", name)
+        last = mm.group(1) if mm else ""
+    if base == "gdn_fwd_out":
+        return {"0": "gdn_fwd_out", "1": "gdn_fwd_states", "2": "gdn_fwd_out_save"}.get(last, base)
+    if base == "gdn_bwd_dscan":
+        return "gdn_bwd_dscan" if last in ("1", "true") else "gdn_bwd_dscan_summary"
+    return base
+
+
 def write_traffic(fetch_csv, write_csv, calib_fetch_csv, calib_write_csv, calib_bytes):
     """HBM bytes per launch of every library kernel from FETCH_SIZE and
     WRITE_SIZE (KiB per dispatch), each scaled by what the same counter reads
@@ -137,14 +159,9 @@ def write_traffic(fetch_csv, write_csv, calib_fetch_csv, calib_write_csv, calib_
                            "fetch_scale": sf, "write_scale": sw},
            "kernels": {}}
     for name in sorted(set(fetch) | set(write)):
-        m = re.search(r"(gdn_\w+?)_kernel", name)
-        if not m:
+        short = kernel_label(name)
+        if short is None:
             continue
-        short = m.group(1)
-        if "Lb1E" in name and short == "gdn_fwd_out":
-            short = "gdn_fwd_states"
-        if short == "gdn_bwd_dscan" and "Lb0E" in name:
-            short = "gdn_bwd_dscan_summary"
         fb = fetch.get(name, 0.0) * 1024.0 * sf
         wb = write.get(name, 0.0) * 1024.0 * sw
         out["kernels"][short] = {"fetch_bytes": fb, "write_bytes": wb, "bytes_per_launch": fb + wb}
@@ -220,6 +237,9 @@ def main():
     ap.add_argument("--workload", default="fwdbwd_h16_t262144_d128_8skew")
     ap.add_argument("--seg-blocks", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--recompute", action="store_true",
+                    help="backward recomputes the forward's block states instead of reading the "
+                         "saving forward's buffer")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run a plain 1 GiB device copy (for rocprofv3 counter scaling) and exit")
     ap.add_argument("--write-traffic", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "CALIB_FETCH_CSV",
@@ -268,6 +288,12 @@ def main():
         ws_b = max(_lib.workspace_bytes(_lib.make_shape(1, n, H, D, D, q.dtype, args.seg_blocks),
                                         backward=True) for n in chunks)
         wsb = _lib.alloc_workspace(ws_b, dev)
+    save = wl["bwd"] and not args.recompute
+    saved = [None] * len(chunks)
+    if save:
+        saved = [_lib.alloc_workspace(_lib.saved_bytes(_lib.make_shape(1, n, H, D, D, q.dtype,
+                                                                       args.seg_blocks)), dev)
+                 for n in chunks]
     stream = torch.cuda.current_stream()
 
     def step():
@@ -275,15 +301,17 @@ def main():
             sl = slice(bounds[i], bounds[i + 1])
             _lib.chunk_fwd(q[:, sl], k[:, sl], v[:, sl], al[:, sl], be[:, sl], states[i],
                            o=o[:, sl], S_out=states[i + 1], seg_blocks=args.seg_blocks,
-                           workspace=wsf, stream=stream)
+                           workspace=wsf, stream=stream, saved=saved[i])
         if wl["bwd"]:
             G = dS_out
             for i in range(len(chunks) - 1, -1, -1):
                 sl = slice(bounds[i], bounds[i + 1])
-                _lib.chunk_bwd(q[:, sl], k[:, sl], v[:, sl], al[:, sl], be[:, sl], states[i],
+                _lib.chunk_bwd(q[:, sl], k[:, sl], v[:, sl], al[:, sl], be[:, sl],
+                               None if save else states[i],
                                dO[:, sl], G, grads=(dq[:, sl], dk[:, sl], dv[:, sl], dal[:, sl],
                                                     dbe[:, sl], gst[i]),
-                               seg_blocks=args.seg_blocks, workspace=wsb, stream=stream)
+                               seg_blocks=args.seg_blocks, workspace=wsb, stream=stream,
+                               saved=saved[i])
                 G = gst[i]
 
     for _ in range(args.warmup):
@@ -321,7 +349,7 @@ def main():
     fl = []
     for n in chunks:
         L, P = L_of[n]
-        f = kernel_flops_per_launch(dom, D, H, n, L, P)
+        f = kernel_flops_per_launch(dom, D, H, n, L, P, save)
         if f is None:
             fl = None
             break
@@ -368,7 +396,9 @@ def main():
         "data": "synthetic",
         "config": {"workload": args.workload, "description": wl["desc"], "B": 1, "T": T, "H": H,
                    "d_k": D, "d_v": D, "block": C, "chunks": chunks,
-                   "seg_blocks": args.seg_blocks or "auto", "parallelism": "single GPU"},
+                   "seg_blocks": args.seg_blocks or "auto", "parallelism": "single GPU",
+                   "backward_states": "saved by the forward" if save else
+                   ("recomputed" if wl["bwd"] else None)},
         "roofline": roofline,
         "path_roofline": path,
         "kernels": {n: {"avg_us": round(x["avg_us"], 2), "launches_per_step": x["launches"] // args.steps,

@@ -99,6 +99,33 @@ sf_status sf_gdn_chunk_bwd(const sf_gdn_shape* shape, const void* q, const void*
                            float* dalpha, float* dbeta, float* dS_in, void* workspace,
                            size_t ws_bytes, void* stream);
 
+/* Saving forward and saved backward (no recompute of the forward scan).
+ *
+ * The backward above rebuilds the chunk's state trajectory from the inputs,
+ * as the page's per-chunk activation release implies ("What carries the
+ * argument"; Referee Report, major comment 1).  When memory allows keeping a
+ * chunk's block states until its backward, sf_gdn_chunk_fwd_save also writes
+ *   - the entry state of every 64-token block, fp32 [B, H, ceil(T/64), Dv, Dk]
+ *   - the segment transition maps of the in-chunk scan, fp32 [B, H, P, Dk, Dk]
+ * into the caller's `saved` buffer (size from sf_gdn_chunk_saved_size for
+ * the same shape, 256-byte aligned; opaque otherwise), and
+ * sf_gdn_chunk_bwd_saved computes the same gradients as sf_gdn_chunk_bwd from
+ * it without S_in.  Results are bitwise those of the recompute path for the
+ * same shape.  The workspaces are those of sf_gdn_chunk_fwd and
+ * sf_gdn_chunk_bwd.  `saved` must not overlap any other argument. */
+sf_status sf_gdn_chunk_saved_size(const sf_gdn_shape* shape, size_t* bytes);
+sf_status sf_gdn_chunk_fwd_save(const sf_gdn_shape* shape, const void* q, const void* k,
+                                const void* v, const float* alpha, const float* beta,
+                                const float* S_in, void* o, float* S_out, void* saved,
+                                size_t saved_bytes, void* workspace, size_t ws_bytes,
+                                void* stream);
+sf_status sf_gdn_chunk_bwd_saved(const sf_gdn_shape* shape, const void* q, const void* k,
+                                 const void* v, const float* alpha, const float* beta,
+                                 const void* saved, size_t saved_bytes, const void* dO,
+                                 const float* dS_out, void* dq, void* dk, void* dv, float* dalpha,
+                                 float* dbeta, float* dS_in, void* workspace, size_t ws_bytes,
+                                 void* stream);
+
 /* Static text for a status code. */
 const char* sf_status_string(int status);
 /* Detail of the calling thread's last non-OK status (static until the next

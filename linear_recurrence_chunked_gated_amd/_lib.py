@@ -33,6 +33,10 @@ SIGNATURES = {
     "sf_gdn_chunk_bwd_workspace_size": (ctypes.c_int, [ctypes.POINTER(Shape), ctypes.POINTER(_sz)]),
     "sf_gdn_chunk_fwd": (ctypes.c_int, [ctypes.POINTER(Shape)] + [_vp] * 8 + [_vp, _sz, _vp]),
     "sf_gdn_chunk_bwd": (ctypes.c_int, [ctypes.POINTER(Shape)] + [_vp] * 14 + [_vp, _sz, _vp]),
+    "sf_gdn_chunk_saved_size": (ctypes.c_int, [ctypes.POINTER(Shape), ctypes.POINTER(_sz)]),
+    "sf_gdn_chunk_fwd_save": (ctypes.c_int, [ctypes.POINTER(Shape)] + [_vp] * 9 + [_sz, _vp, _sz, _vp]),
+    "sf_gdn_chunk_bwd_saved": (ctypes.c_int, [ctypes.POINTER(Shape)] + [_vp] * 6 + [_sz] + [_vp] * 8
+                               + [_vp, _sz, _vp]),
     "sf_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "sf_last_error_message": (ctypes.c_char_p, []),
     "sf_gdn_version": (ctypes.c_char_p, []),
@@ -126,9 +130,19 @@ def _need(t, name, dtype, shape, device):
         raise ValueError("%s must be contiguous" % name)
 
 
+def saved_bytes(shape):
+    n = ctypes.c_size_t(0)
+    _check(load().sf_gdn_chunk_saved_size(ctypes.byref(shape), ctypes.byref(n)), "saved_size")
+    return n.value
+
+
 def chunk_fwd(q, k, v, alpha, beta, S_in=None, o=None, S_out=None, seg_blocks=0,
-              workspace=None, stream=None):
-    """sf_gdn_chunk_fwd on torch tensors.  Returns (o, S_out)."""
+              workspace=None, stream=None, saved=None):
+    """sf_gdn_chunk_fwd on torch tensors.  Returns (o, S_out).
+
+    With ``saved`` (a uint8 tensor of at least ``saved_bytes`` bytes, 256-byte
+    aligned, or True to allocate one) the saving forward runs and the return
+    value is (o, S_out, saved)."""
     B, T, H, Dk = q.shape
     Dv = v.shape[3]
     dev = q.device
@@ -151,17 +165,29 @@ def chunk_fwd(q, k, v, alpha, beta, S_in=None, o=None, S_out=None, seg_blocks=0,
     need = workspace_bytes(shape)
     if workspace is None or workspace.numel() < need:
         workspace = alloc_workspace(need, dev)
-    st = load().sf_gdn_chunk_fwd(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha),
-                                 _ptr(beta), _ptr(S_in), _ptr(o), _ptr(S_out), _ptr(workspace),
-                                 ctypes.c_size_t(0 if workspace is None else workspace.numel()),
-                                 _stream(stream))
-    _check(st, "sf_gdn_chunk_fwd")
-    return o, S_out
+    wsn = ctypes.c_size_t(0 if workspace is None else workspace.numel())
+    if saved is None:
+        st = load().sf_gdn_chunk_fwd(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha),
+                                     _ptr(beta), _ptr(S_in), _ptr(o), _ptr(S_out),
+                                     _ptr(workspace), wsn, _stream(stream))
+        _check(st, "sf_gdn_chunk_fwd")
+        return o, S_out
+    if saved is True:
+        n = saved_bytes(shape)
+        saved = (alloc_workspace(n, dev) if n else
+                 torch.empty(0, dtype=torch.uint8, device=dev))
+    st = load().sf_gdn_chunk_fwd_save(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha),
+                                      _ptr(beta), _ptr(S_in), _ptr(o), _ptr(S_out), _ptr(saved),
+                                      ctypes.c_size_t(0 if saved is None else saved.numel()),
+                                      _ptr(workspace), wsn, _stream(stream))
+    _check(st, "sf_gdn_chunk_fwd_save")
+    return o, S_out, saved
 
 
 def chunk_bwd(q, k, v, alpha, beta, S_in, dO, dS_out=None, grads=None, seg_blocks=0,
-              workspace=None, stream=None):
-    """sf_gdn_chunk_bwd on torch tensors.
+              workspace=None, stream=None, saved=None):
+    """sf_gdn_chunk_bwd on torch tensors (sf_gdn_chunk_bwd_saved when
+    ``saved`` holds the buffer of a saving forward; S_in is then unused).
 
     Returns (dq, dk, dv, dalpha, dbeta, dS_in).  ``grads`` may supply
     preallocated outputs in that order (dS_in may be None there)."""
@@ -175,7 +201,7 @@ def chunk_bwd(q, k, v, alpha, beta, S_in, dO, dS_out=None, grads=None, seg_block
                           (alpha, "alpha", torch.float32, (B, T, H)),
                           (beta, "beta", torch.float32, (B, T, H))):
         _need(t, n, dt, shp, dev)
-    if S_in is not None:
+    if S_in is not None and saved is None:
         _need(S_in, "S_in", torch.float32, (B, H, Dv, Dk), dev)
     if dS_out is not None:
         _need(dS_out, "dS_out", torch.float32, (B, H, Dv, Dk), dev)
@@ -188,13 +214,20 @@ def chunk_bwd(q, k, v, alpha, beta, S_in, dO, dS_out=None, grads=None, seg_block
     need = workspace_bytes(shape, backward=True)
     if workspace is None or workspace.numel() < need:
         workspace = alloc_workspace(need, dev)
-    st = load().sf_gdn_chunk_bwd(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha),
-                                 _ptr(beta), _ptr(S_in), _ptr(dO), _ptr(dS_out), _ptr(dq),
-                                 _ptr(dk), _ptr(dv), _ptr(da), _ptr(db), _ptr(dS_in),
-                                 _ptr(workspace),
-                                 ctypes.c_size_t(0 if workspace is None else workspace.numel()),
-                                 _stream(stream))
-    _check(st, "sf_gdn_chunk_bwd")
+    wsn = ctypes.c_size_t(0 if workspace is None else workspace.numel())
+    if saved is None:
+        st = load().sf_gdn_chunk_bwd(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha),
+                                     _ptr(beta), _ptr(S_in), _ptr(dO), _ptr(dS_out), _ptr(dq),
+                                     _ptr(dk), _ptr(dv), _ptr(da), _ptr(db), _ptr(dS_in),
+                                     _ptr(workspace), wsn, _stream(stream))
+        _check(st, "sf_gdn_chunk_bwd")
+    else:
+        st = load().sf_gdn_chunk_bwd_saved(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v),
+                                           _ptr(alpha), _ptr(beta), _ptr(saved),
+                                           ctypes.c_size_t(saved.numel()), _ptr(dO), _ptr(dS_out),
+                                           _ptr(dq), _ptr(dk), _ptr(dv), _ptr(da), _ptr(db),
+                                           _ptr(dS_in), _ptr(workspace), wsn, _stream(stream))
+        _check(st, "sf_gdn_chunk_bwd_saved")
     return dq, dk, dv, da, db, dS_in
 
 

@@ -22,10 +22,13 @@ def _bounds(lengths, T):
     return b
 
 
-def chain_fwd(q, k, v, alpha, beta, S_in, lengths, o=None, seg_blocks=0, stream=None):
+def chain_fwd(q, k, v, alpha, beta, S_in, lengths, o=None, seg_blocks=0, stream=None,
+              save=False):
     """Forward over consecutive chunks.  Returns (o, states) where states[i]
     is chunk i's entry state ([B,H,Dv,Dk] fp32; states[0] is S_in or zeros)
-    and states[-1] the final state."""
+    and states[-1] the final state.  With ``save`` every chunk runs the saving
+    forward and the return value is (o, states, saved), saved[i] being chunk
+    i's buffer for the saved backward."""
     B, T, H, Dk = q.shape
     Dv = v.shape[3]
     if B != 1:
@@ -35,21 +38,26 @@ def chain_fwd(q, k, v, alpha, beta, S_in, lengths, o=None, seg_blocks=0, stream=
         o = torch.empty((B, T, H, Dv), dtype=q.dtype, device=q.device)
     states = [S_in if S_in is not None else
               torch.zeros((B, H, Dv, Dk), dtype=torch.float32, device=q.device)]
+    saved = []
     for i in range(len(lengths)):
         sl = slice(bnd[i], bnd[i + 1])
         S_next = torch.empty((B, H, Dv, Dk), dtype=torch.float32, device=q.device)
-        _lib.chunk_fwd(q[:, sl], k[:, sl], v[:, sl], alpha[:, sl], beta[:, sl], states[i],
-                       o=o[:, sl], S_out=S_next, seg_blocks=seg_blocks, stream=stream)
+        r = _lib.chunk_fwd(q[:, sl], k[:, sl], v[:, sl], alpha[:, sl], beta[:, sl], states[i],
+                           o=o[:, sl], S_out=S_next, seg_blocks=seg_blocks, stream=stream,
+                           saved=True if save else None)
+        if save:
+            saved.append(r[2])
         states.append(S_next)
-    return o, states
+    return (o, states, saved) if save else (o, states)
 
 
 def chain_bwd(q, k, v, alpha, beta, dO, dS_out, lengths, states, grads=None, seg_blocks=0,
-              stream=None):
+              stream=None, saved=None):
     """Backward over consecutive chunks, last chunk first, each chunk's
     entry-state gradient feeding the previous chunk's exit gradient.
-    ``states`` are the entry states from chain_fwd.  Returns
-    (dq, dk, dv, dalpha, dbeta, dS_in)."""
+    ``states`` are the entry states from chain_fwd; ``saved`` the per-chunk
+    buffers of a saving chain_fwd (the recompute backward runs without them;
+    ``states`` may then be None).  Returns (dq, dk, dv, dalpha, dbeta, dS_in)."""
     B, T, H, Dk = q.shape
     Dv = v.shape[3]
     if B != 1:
@@ -63,9 +71,11 @@ def chain_bwd(q, k, v, alpha, beta, dO, dS_out, lengths, states, grads=None, seg
     for i in range(len(lengths) - 1, -1, -1):
         sl = slice(bnd[i], bnd[i + 1])
         G_prev = torch.empty((B, H, Dv, Dk), dtype=torch.float32, device=q.device)
-        _lib.chunk_bwd(q[:, sl], k[:, sl], v[:, sl], alpha[:, sl], beta[:, sl], states[i],
+        _lib.chunk_bwd(q[:, sl], k[:, sl], v[:, sl], alpha[:, sl], beta[:, sl],
+                       None if saved is not None else states[i],
                        dO[:, sl], G, grads=(dq[:, sl], dk[:, sl], dv[:, sl], da[:, sl],
                                             db[:, sl], G_prev),
-                       seg_blocks=seg_blocks, stream=stream)
+                       seg_blocks=seg_blocks, stream=stream,
+                       saved=None if saved is None else saved[i])
         G = G_prev
     return dq, dk, dv, da, db, G

@@ -779,7 +779,7 @@ static hipError_t set_lds(const void* fn, size_t bytes) {
 }
 
 template <typename T, int D>
-hipError_t launch_bwd(const BwdArgs& a0, hipStream_t st, Profiler* prof) {
+hipError_t launch_bwd(const BwdArgs& a0, bool saved, hipStream_t st, Profiler* prof) {
   BwdArgs a = a0;
   FwdArgs& f = a.f;
   const int BH = f.B * f.H, P = f.P;
@@ -790,7 +790,8 @@ hipError_t launch_bwd(const BwdArgs& a0, hipStream_t st, Profiler* prof) {
   int dsend_P = 1;
   if (P > 1) {
     // 1. segment maps of the forward (all segments)
-    if ((e = launch_fwd_summary<T, D>(f, P, st, prof, "gdn_bwd_summary")) != hipSuccess) return e;
+    if (!saved && (e = launch_fwd_summary<T, D>(f, P, st, prof, "gdn_bwd_summary")) != hipSuccess)
+      return e;
     // 2. NB maps of segments 1..P-1
     if ((e = set_lds((const void*)gdn_bwd_dscan_kernel<T, D, false>, ScanLds<T, D>::bytes)) != hipSuccess)
       return e;
@@ -799,8 +800,10 @@ hipError_t launch_bwd(const BwdArgs& a0, hipStream_t st, Profiler* prof) {
                        scan_bytes, st, a, 1, P - 1, nullptr, 1);
     prof_end(prof, st);
     // 3. chains
-    ChainArgs c{f.S_in, f.Mseg, f.Nseg, const_cast<float*>(f.Sst), P};
-    if ((e = launch_chain_fwd<D>(c, BH, st, prof)) != hipSuccess) return e;
+    if (!saved) {
+      ChainArgs c{f.S_in, f.Mseg, f.Nseg, const_cast<float*>(f.Sst), P};
+      if ((e = launch_chain_fwd<D>(c, BH, st, prof)) != hipSuccess) return e;
+    }
     prof_begin(prof, "gdn_chain_bwd", st);
     hipLaunchKernelGGL((gdn_chain_bwd_kernel<D>), dim3(BH * (D / 16)), dim3(256), 0, st, a.dS_out,
                        f.Mseg, a.NBseg, a.dSend, P);
@@ -812,7 +815,7 @@ hipError_t launch_bwd(const BwdArgs& a0, hipStream_t st, Profiler* prof) {
     f.sst_P = 1;
   }
   // 4. block entry states
-  if ((e = launch_states<T, D>(f, hst, st, prof)) != hipSuccess) return e;
+  if (!saved && (e = launch_states<T, D>(f, hst, st, prof)) != hipSuccess) return e;
   // 5. block exit gradients and dS_in
   if ((e = set_lds((const void*)gdn_bwd_dscan_kernel<T, D, true>, ScanLds<T, D>::bytes)) != hipSuccess)
     return e;
@@ -830,8 +833,8 @@ hipError_t launch_bwd(const BwdArgs& a0, hipStream_t st, Profiler* prof) {
   return hipGetLastError();
 }
 
-template hipError_t launch_bwd<bf16, 128>(const BwdArgs&, hipStream_t, Profiler*);
-template hipError_t launch_bwd<bf16, 64>(const BwdArgs&, hipStream_t, Profiler*);
-template hipError_t launch_bwd<float, 64>(const BwdArgs&, hipStream_t, Profiler*);
+template hipError_t launch_bwd<bf16, 128>(const BwdArgs&, bool, hipStream_t, Profiler*);
+template hipError_t launch_bwd<bf16, 64>(const BwdArgs&, bool, hipStream_t, Profiler*);
+template hipError_t launch_bwd<float, 64>(const BwdArgs&, bool, hipStream_t, Profiler*);
 
 }  // namespace sfgdn

@@ -87,14 +87,18 @@ template <typename T, int D, bool WITH_Q> struct Prefetch {
 
 // --------------------------------------------------------- fused out -------
 // Wave w owns dv-tiles NDV*w .. of the state: S^T, U/Vn and O^T for those
-// columns live in its registers for the whole segment.  With STATES the kernel
-// computes no output; instead it stores each block's entry state (fp32,
-// [dv][dk]) to hst[b*H + h][block], which the backward pass consumes.
-template <typename T, int D, bool STATES>
+// columns live in its registers for the whole segment.  MODE selects what is
+// written: OUT_ONLY the outputs o (and S_out); STATES_ONLY each block's entry
+// state (fp32, [dv][dk]) to hst[b*H + h][block] and no output; OUT_AND_STATES
+// both.  The backward consumes the stored states.
+enum FwdMode { OUT_ONLY = 0, STATES_ONLY = 1, OUT_AND_STATES = 2 };
+
+template <typename T, int D, int MODE>
 __global__ __launch_bounds__(64 * fwd_nw<D>(), 2) void gdn_fwd_out_kernel(FwdArgs a, float* hst) {
   typedef FwdLds<T, D> Lz;
   constexpr int NW = fwd_nw<D>(), NDV = D / 16 / NW, DKT = D / 16;
   constexpr int LDD = Lz::LDD, LDC = Lz::LDC, LDF = Lz::LDF;
+  constexpr bool STATES = MODE != OUT_ONLY, OUT = MODE != STATES_ONLY;
   extern __shared__ __align__(16) unsigned char smem[];
   T* Qs = reinterpret_cast<T*>(smem + Lz::oQ);
   float* Tm = reinterpret_cast<float*>(smem + Lz::oQ);
@@ -134,7 +138,7 @@ __global__ __launch_bounds__(64 * fwd_nw<D>(), 2) void gdn_fwd_out_kernel(FwdArg
       }
   }
 
-  Prefetch<T, D, !STATES> pf;
+  Prefetch<T, D, OUT> pf;
   if (blk0 < blk1) pf.fetch(q, k, v, al, bt, rs, a.H, blk0 * BLK, min(BLK, a.T - blk0 * BLK));
   f32x4 O[NDV][4];
   int prev_t0 = -1, prev_nv = 0;
@@ -162,13 +166,14 @@ __global__ __launch_bounds__(64 * fwd_nw<D>(), 2) void gdn_fwd_out_kernel(FwdArg
         for (int aa = 0; aa < DKT; ++aa)
           *reinterpret_cast<f32x4*>(hb + (size_t)(16 * (dv0 + bb) + li) * D + 16 * aa + g4) =
               St[bb][aa];
-    } else {
+    }
+    if constexpr (OUT) {
       if (prev_t0 >= 0) store_o();
     }
     lds_barrier();
     // Pre: scores; Out, state part: O^T = diag(gamma) (S Q^T)
-    block_scores<T, D, NW, !STATES>(Qs, Ks, LDD, G, Af, LDF, Pl, LDC);
-    if constexpr (!STATES) {
+    block_scores<T, D, NW, OUT>(Qs, Ks, LDD, G, Af, LDF, Pl, LDC);
+    if constexpr (OUT) {
       zero_acc(O);
       block_s_yT<T, D, NDV>(St, Qs, LDD, O);
 #pragma unroll
@@ -189,7 +194,7 @@ __global__ __launch_bounds__(64 * fwd_nw<D>(), 2) void gdn_fwd_out_kernel(FwdArg
     lds_barrier();
     // ST and Out: Vn = U - W S^T; O^T += Vn^T P^T; S' = gamma_C S + Vn^T D K
     block_x_st<T, D, NDV>(Wn, LDD, St, U);
-    if constexpr (!STATES) block_vnT_pT<T, NDV>(U, Pl, LDC, O);
+    if constexpr (OUT) block_vnT_pT<T, NDV>(U, Pl, LDC, O);
     f32x4 dsc[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -208,11 +213,11 @@ __global__ __launch_bounds__(64 * fwd_nw<D>(), 2) void gdn_fwd_out_kernel(FwdArg
     if (blk + 1 < blk1) pf.fetch(q, k, v, al, bt, rs, a.H, t0 + BLK, min(BLK, a.T - t0 - BLK));
     lds_barrier();
   }
-  if constexpr (!STATES) {
+  if constexpr (OUT) {
     if (prev_t0 >= 0) store_o();
   }
 
-  if (!STATES && seg == a.P - 1 && a.S_out) {
+  if (OUT && seg == a.P - 1 && a.S_out) {
     float* So = a.S_out + (size_t)bh * D * D;
 #pragma unroll
     for (int bb = 0; bb < NDV; ++bb)
@@ -428,36 +433,50 @@ hipError_t launch_chain_fwd(const ChainArgs& c, int BH, hipStream_t st, Profiler
 template <typename T, int D>
 hipError_t launch_states(const FwdArgs& a, float* hst, hipStream_t st, Profiler* prof) {
   typedef FwdLds<T, D> Lz;
-  hipError_t e = set_lds((const void*)gdn_fwd_out_kernel<T, D, true>, Lz::out_bytes);
+  hipError_t e = set_lds((const void*)gdn_fwd_out_kernel<T, D, STATES_ONLY>, Lz::out_bytes);
   if (e != hipSuccess) return e;
   prof_begin(prof, "gdn_fwd_states", st);
-  hipLaunchKernelGGL((gdn_fwd_out_kernel<T, D, true>), dim3(a.B * a.H * a.P), dim3(64 * fwd_nw<D>()),
+  hipLaunchKernelGGL((gdn_fwd_out_kernel<T, D, STATES_ONLY>), dim3(a.B * a.H * a.P), dim3(64 * fwd_nw<D>()),
                      Lz::out_bytes, st, a, hst);
   prof_end(prof, st);
   return hipGetLastError();
 }
 
+// hsave: when not null, every block's entry state is stored there and the
+// segment maps M are computed for all P segments (a.Mseg then points into the
+// caller's saved buffer), so that the backward can skip its recompute.
 template <typename T, int D>
-hipError_t launch_fwd(const FwdArgs& a, hipStream_t st, Profiler* prof) {
+hipError_t launch_fwd(const FwdArgs& a, float* hsave, hipStream_t st, Profiler* prof) {
   typedef FwdLds<T, D> Lz;
   hipError_t e;
   const int BH = a.B * a.H;
   if (a.P > 1) {
-    if ((e = launch_fwd_summary<T, D>(a, a.P - 1, st, prof, "gdn_fwd_summary")) != hipSuccess) return e;
+    const int nseg = hsave ? a.P : a.P - 1;
+    if ((e = launch_fwd_summary<T, D>(a, nseg, st, prof, "gdn_fwd_summary")) != hipSuccess) return e;
     ChainArgs c{a.S_in, a.Mseg, a.Nseg, const_cast<float*>(a.Sst), a.P};
     if ((e = launch_chain_fwd<D>(c, BH, st, prof)) != hipSuccess) return e;
   }
-  if ((e = set_lds((const void*)gdn_fwd_out_kernel<T, D, false>, Lz::out_bytes)) != hipSuccess)
+  if (hsave) {
+    if ((e = set_lds((const void*)gdn_fwd_out_kernel<T, D, OUT_AND_STATES>, Lz::out_bytes)) !=
+        hipSuccess)
+      return e;
+    prof_begin(prof, "gdn_fwd_out_save", st);
+    hipLaunchKernelGGL((gdn_fwd_out_kernel<T, D, OUT_AND_STATES>), dim3(BH * a.P),
+                       dim3(64 * fwd_nw<D>()), Lz::out_bytes, st, a, hsave);
+    prof_end(prof, st);
+    return hipGetLastError();
+  }
+  if ((e = set_lds((const void*)gdn_fwd_out_kernel<T, D, OUT_ONLY>, Lz::out_bytes)) != hipSuccess)
     return e;
   prof_begin(prof, "gdn_fwd_out", st);
-  hipLaunchKernelGGL((gdn_fwd_out_kernel<T, D, false>), dim3(BH * a.P), dim3(64 * fwd_nw<D>()),
+  hipLaunchKernelGGL((gdn_fwd_out_kernel<T, D, OUT_ONLY>), dim3(BH * a.P), dim3(64 * fwd_nw<D>()),
                      Lz::out_bytes, st, a, nullptr);
   prof_end(prof, st);
   return hipGetLastError();
 }
 
 #define SF_INST(T, D)                                                                      \
-  template hipError_t launch_fwd<T, D>(const FwdArgs&, hipStream_t, Profiler*);          \
+  template hipError_t launch_fwd<T, D>(const FwdArgs&, float*, hipStream_t, Profiler*);  \
   template hipError_t launch_fwd_summary<T, D>(const FwdArgs&, int, hipStream_t, Profiler*, const char*); \
   template hipError_t launch_states<T, D>(const FwdArgs&, float*, hipStream_t, Profiler*);
 SF_INST(bf16, 128)

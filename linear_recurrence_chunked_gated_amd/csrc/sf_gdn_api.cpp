@@ -196,9 +196,21 @@ sf_status sf_gdn_chunk_bwd_workspace_size(const sf_gdn_shape* shape, size_t* byt
   return SF_OK;
 }
 
-sf_status sf_gdn_chunk_fwd(const sf_gdn_shape* shape, const void* q, const void* k, const void* v,
-                           const float* alpha, const float* beta, const float* S_in, void* o,
-                           float* S_out, void* workspace, size_t ws_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+size_t saved_bytes(const Plan& p) {
+  if (p.P == 0) return 0;
+  return blk_buf(p) + (p.P > 1 ? seg_buf(p) : 0);
+}
+
+// Forward; with `saved` it also stores the per-block entry states and all
+// segment maps (layout: [B*H*nblk][D][D] states, then [B*H*P][D][D] maps).
+sf_status fwd_impl(const sf_gdn_shape* shape, const void* q, const void* k, const void* v,
+                   const float* alpha, const float* beta, const float* S_in, void* o,
+                   float* S_out, void* saved, size_t sv_bytes, void* workspace, size_t ws_bytes,
+                   void* stream, bool save) {
   Plan p;
   sf_status s = make_plan(shape, p);
   if (s != SF_OK) return s;
@@ -211,7 +223,15 @@ sf_status sf_gdn_chunk_fwd(const sf_gdn_shape* shape, const void* q, const void*
                            {beta, ntok * 4, "beta"},           {S_in, nst * 4, "S_in"},
                            {workspace, ws_bytes, "workspace"}};
   std::vector<Range> out = {{o, ntok * p.D * elem(p), "o"}, {S_out, nst * 4, "S_out"}};
+  if (save) out.push_back({saved, sv_bytes, "saved"});
   if ((s = check_ptrs(in, out, {})) != SF_OK) return s;
+  if (save) {
+    const size_t sneed = saved_bytes(p);
+    if (sneed > 0 && (!saved || sv_bytes < sneed))
+      return fail(SF_ERR_INVALID_ARG, "saved buffer needs " + std::to_string(sneed) + " bytes");
+    if (saved && ((uintptr_t)saved % kAlign))
+      return fail(SF_ERR_INVALID_ARG, "saved buffer is not 256-byte aligned");
+  }
   const size_t need = fwd_ws(p);
   if (need > 0 && (!workspace || ws_bytes < need))
     return fail(SF_ERR_WORKSPACE, "forward workspace needs " + std::to_string(need) + " bytes");
@@ -232,8 +252,9 @@ sf_status sf_gdn_chunk_fwd(const sf_gdn_shape* shape, const void* q, const void*
     a.o = o; a.S_out = S_out;
     a.B = p.B; a.T = p.T; a.H = p.H; a.nblk = p.nblk; a.L = p.L; a.P = p.P;
     char* ws = (char*)workspace;
+    float* hsave = save ? (float*)saved : nullptr;
     if (p.P > 1) {
-      a.Mseg = (float*)ws;
+      a.Mseg = save ? (float*)((char*)saved + blk_buf(p)) : (float*)ws;
       a.Nseg = (float*)(ws + seg_buf(p));
       a.Sst = (float*)(ws + 2 * seg_buf(p));
       a.sst_P = p.P;
@@ -243,19 +264,22 @@ sf_status sf_gdn_chunk_fwd(const sf_gdn_shape* shape, const void* q, const void*
     }
     hipError_t e;
     if (p.dtype == SF_DTYPE_BF16)
-      e = (p.D == 128) ? launch_fwd<bf16, 128>(a, st, prof) : launch_fwd<bf16, 64>(a, st, prof);
+      e = (p.D == 128) ? launch_fwd<bf16, 128>(a, hsave, st, prof)
+                       : launch_fwd<bf16, 64>(a, hsave, st, prof);
     else
-      e = launch_fwd<float, 64>(a, st, prof);
+      e = launch_fwd<float, 64>(a, hsave, st, prof);
     if (e != hipSuccess) return hip_fail(e, "forward launch");
     return SF_OK;
   });
 }
 
-sf_status sf_gdn_chunk_bwd(const sf_gdn_shape* shape, const void* q, const void* k, const void* v,
-                           const float* alpha, const float* beta, const float* S_in,
-                           const void* dO, const float* dS_out, void* dq, void* dk, void* dv,
-                           float* dalpha, float* dbeta, float* dS_in, void* workspace,
-                           size_t ws_bytes, void* stream) {
+// Backward; with `saved` (from fwd_impl with save) the forward recompute is
+// skipped and S_in is not needed.
+sf_status bwd_impl(const sf_gdn_shape* shape, const void* q, const void* k, const void* v,
+                   const float* alpha, const float* beta, const float* S_in, const void* saved,
+                   size_t sv_bytes, const void* dO, const float* dS_out, void* dq, void* dk,
+                   void* dv, float* dalpha, float* dbeta, float* dS_in, void* workspace,
+                   size_t ws_bytes, void* stream, bool use_saved) {
   Plan p;
   sf_status s = make_plan(shape, p);
   if (s != SF_OK) return s;
@@ -268,9 +292,17 @@ sf_status sf_gdn_chunk_bwd(const sf_gdn_shape* shape, const void* q, const void*
                            {alpha, ntok * 4, "alpha"}, {beta, ntok * 4, "beta"}, {S_in, nst * 4, "S_in"},
                            {dO, nt, "dO"},        {dS_out, nst * 4, "dS_out"},
                            {workspace, ws_bytes, "workspace"}};
+  if (use_saved) in.push_back({saved, sv_bytes, "saved"});
   std::vector<Range> out = {{dq, nt, "dq"}, {dk, nt, "dk"}, {dv, nt, "dv"}, {dalpha, ntok * 4, "dalpha"},
                             {dbeta, ntok * 4, "dbeta"}, {dS_in, nst * 4, "dS_in"}};
   if ((s = check_ptrs(in, out, {})) != SF_OK) return s;
+  if (use_saved) {
+    const size_t sneed = saved_bytes(p);
+    if (sneed > 0 && (!saved || sv_bytes < sneed))
+      return fail(SF_ERR_INVALID_ARG, "saved buffer needs " + std::to_string(sneed) + " bytes");
+    if (saved && ((uintptr_t)saved % kAlign))
+      return fail(SF_ERR_INVALID_ARG, "saved buffer is not 256-byte aligned");
+  }
   const size_t need = bwd_ws(p);
   if (need > 0 && (!workspace || ws_bytes < need))
     return fail(SF_ERR_WORKSPACE, "backward workspace needs " + std::to_string(need) + " bytes");
@@ -301,17 +333,70 @@ sf_status sf_gdn_chunk_bwd(const sf_gdn_shape* shape, const void* q, const void*
     a.dSend = (float*)(ws + 4 * sb);
     a.hst = ws + 5 * sb;
     a.dhst = ws + 5 * sb + bb;
+    if (use_saved) {
+      a.hst = const_cast<void*>(saved);
+      if (p.P > 1) f.Mseg = (float*)((char*)const_cast<void*>(saved) + bb);
+    }
     a.dO = dO; a.dS_out = dS_out;
     a.dq = dq; a.dk = dk; a.dv = dv; a.dalpha = dalpha; a.dbeta = dbeta; a.dS_in = dS_in;
     hipError_t e;
     if (p.dtype == SF_DTYPE_BF16)
-      e = (p.D == 128) ? launch_bwd<bf16, 128>(a, st, prof) : launch_bwd<bf16, 64>(a, st, prof);
+      e = (p.D == 128) ? launch_bwd<bf16, 128>(a, use_saved, st, prof)
+                       : launch_bwd<bf16, 64>(a, use_saved, st, prof);
     else
-      e = launch_bwd<float, 64>(a, st, prof);
+      e = launch_bwd<float, 64>(a, use_saved, st, prof);
     if (e == hipErrorNotSupported) return fail(SF_ERR_UNSUPPORTED, "backward not available");
     if (e != hipSuccess) return hip_fail(e, "backward launch");
     return SF_OK;
   });
+}
+
+}  // namespace
+
+extern "C" {
+
+sf_status sf_gdn_chunk_fwd(const sf_gdn_shape* shape, const void* q, const void* k, const void* v,
+                           const float* alpha, const float* beta, const float* S_in, void* o,
+                           float* S_out, void* workspace, size_t ws_bytes, void* stream) {
+  return fwd_impl(shape, q, k, v, alpha, beta, S_in, o, S_out, nullptr, 0, workspace, ws_bytes,
+                  stream, false);
+}
+
+sf_status sf_gdn_chunk_bwd(const sf_gdn_shape* shape, const void* q, const void* k, const void* v,
+                           const float* alpha, const float* beta, const float* S_in,
+                           const void* dO, const float* dS_out, void* dq, void* dk, void* dv,
+                           float* dalpha, float* dbeta, float* dS_in, void* workspace,
+                           size_t ws_bytes, void* stream) {
+  return bwd_impl(shape, q, k, v, alpha, beta, S_in, nullptr, 0, dO, dS_out, dq, dk, dv, dalpha,
+                  dbeta, dS_in, workspace, ws_bytes, stream, false);
+}
+
+sf_status sf_gdn_chunk_saved_size(const sf_gdn_shape* shape, size_t* bytes) {
+  Plan p;
+  sf_status s = make_plan(shape, p);
+  if (s != SF_OK) return s;
+  if (!bytes) return fail(SF_ERR_INVALID_ARG, "bytes is NULL");
+  *bytes = saved_bytes(p);
+  return SF_OK;
+}
+
+sf_status sf_gdn_chunk_fwd_save(const sf_gdn_shape* shape, const void* q, const void* k,
+                                const void* v, const float* alpha, const float* beta,
+                                const float* S_in, void* o, float* S_out, void* saved,
+                                size_t saved_bytes_, void* workspace, size_t ws_bytes,
+                                void* stream) {
+  return fwd_impl(shape, q, k, v, alpha, beta, S_in, o, S_out, saved, saved_bytes_, workspace,
+                  ws_bytes, stream, true);
+}
+
+sf_status sf_gdn_chunk_bwd_saved(const sf_gdn_shape* shape, const void* q, const void* k,
+                                 const void* v, const float* alpha, const float* beta,
+                                 const void* saved, size_t saved_bytes_, const void* dO,
+                                 const float* dS_out, void* dq, void* dk, void* dv, float* dalpha,
+                                 float* dbeta, float* dS_in, void* workspace, size_t ws_bytes,
+                                 void* stream) {
+  return bwd_impl(shape, q, k, v, alpha, beta, nullptr, saved, saved_bytes_, dO, dS_out, dq, dk,
+                  dv, dalpha, dbeta, dS_in, workspace, ws_bytes, stream, true);
 }
 
 const char* sf_status_string(int status) {

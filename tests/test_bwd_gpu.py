@@ -141,3 +141,70 @@ def test_bwd_empty_chunk_passes_gradient():
                       d["dS_out"])
     torch.cuda.synchronize()
     assert torch.equal(r[5], d["dS_out"])
+
+
+@pytest.mark.parametrize("B,T,H,D,dtype,seg,decay", [
+    (1, 256, 2, 64, "f32", 1, 0.01),
+    (2, 333, 2, 64, "f32", 2, 0.01),      # ragged, B = 2
+    (1, 1000, 3, 128, "bf16", 0, 0.01),   # ragged, several segments
+    (1, 640, 2, 128, "bf16", 100, 0.01),  # one segment
+    (1, 1, 2, 128, "bf16", 0, 1.0),       # single token (as in the oracle test above)
+    (2, 2048, 2, 128, "bf16", 5, 0.01),
+])
+def test_saved_path_bitwise_equals_recompute(oracle_mod, B, T, H, D, dtype, seg, decay):
+    """The saving forward returns the plain forward's o and S_out, and the
+    saved backward the recompute backward's gradients, bit for bit; both
+    also against the oracle."""
+    d = inputs(B, T, H, D, dtype, seed=3000 + T, s_in_std=0.1, grads=True, decay=decay)
+    dd = to_dev(d)
+    fa = (dd["q"], dd["k"], dd["v"], dd["alpha"], dd["beta"], dd["S_in"])
+    o1, S1 = gdn.chunk_fwd(*fa, seg_blocks=seg)
+    o2, S2, saved = gdn.chunk_fwd(*fa, seg_blocks=seg, saved=True)
+    g1 = gdn.chunk_bwd(*fa, dd["dO"], dd["dS_out"], seg_blocks=seg)
+    g2 = gdn.chunk_bwd(*fa[:5], None, dd["dO"], dd["dS_out"], seg_blocks=seg, saved=saved)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(S1, S2)
+    for name, x, y in zip(NAMES, g1, g2):
+        assert torch.equal(x, y), name
+    check_all([f64(x) for x in g2], oracle_bwd(oracle_mod, d), TOL[dtype])
+
+
+def test_saved_buffer_reused_across_shapes():
+    """One saved buffer sized for the larger chunk serves a smaller one."""
+    big = to_dev(inputs(1, 4096, 2, 128, "bf16", seed=31, s_in_std=0.1, grads=True))
+    small = to_dev(inputs(1, 700, 2, 128, "bf16", seed=32, s_in_std=0.1, grads=True))
+    _, _, saved = gdn.chunk_fwd(big["q"], big["k"], big["v"], big["alpha"], big["beta"],
+                                big["S_in"], saved=True)
+    for dd in (small, big):
+        fa = (dd["q"], dd["k"], dd["v"], dd["alpha"], dd["beta"], dd["S_in"])
+        gdn.chunk_fwd(*fa, saved=saved)
+        g1 = gdn.chunk_bwd(*fa, dd["dO"], dd["dS_out"])
+        g2 = gdn.chunk_bwd(*fa[:5], None, dd["dO"], dd["dS_out"], saved=saved)
+        torch.cuda.synchronize()
+        for name, x, y in zip(NAMES, g1, g2):
+            assert torch.equal(x, y), name
+
+
+def test_saved_chain_nonuniform_fwd_bwd(oracle_mod):
+    """The skewed eight-chunk chain of the test above through the saving
+    forward and the saved backward."""
+    T = 16384
+    lengths = chunk_lengths(T, 8, 0.5)
+    d = inputs(1, T, 4, 128, "bf16", seed=20260004, grads=True, decay=0.01)
+    dd = to_dev(d)
+    o, states, saved = gdn.chain_fwd(dd["q"], dd["k"], dd["v"], dd["alpha"], dd["beta"], None,
+                                     lengths, save=True)
+    g = gdn.chain_bwd(dd["q"], dd["k"], dd["v"], dd["alpha"], dd["beta"], dd["dO"],
+                      dd["dS_out"], lengths, None, saved=saved)
+    torch.cuda.synchronize()
+    check_all([f64(x) for x in g], oracle_bwd(oracle_mod, d), TOL["bf16"])
+
+
+def test_saved_bwd_empty_chunk():
+    d = to_dev(inputs(1, 0, 2, 64, "bf16", seed=10, s_in_std=0.1, grads=True))
+    fa = (d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["S_in"])
+    o, S, saved = gdn.chunk_fwd(*fa, saved=True)
+    r = gdn.chunk_bwd(*fa[:5], None, d["dO"], d["dS_out"], saved=saved)
+    torch.cuda.synchronize()
+    assert torch.equal(S, d["S_in"])
+    assert torch.equal(r[5], d["dS_out"])

@@ -95,6 +95,44 @@ def test_rejects_small_workspace():
     assert _fwd(shape, ws=16 * G + 16, wsn=need) == _lib.SF_ERR_INVALID_ARG  # not 256-aligned
 
 
+def _fwd_save(shape, saved=20 * G, svn=None, ws=24 * G, wsn=None):
+    L = _lib.load()
+    vp = lambda x: None if x is None else ctypes.c_void_p(x)
+    svn = _lib.saved_bytes(shape) if svn is None else svn
+    wsn = _lib.workspace_bytes(shape) if wsn is None else wsn
+    return L.sf_gdn_chunk_fwd_save(ctypes.byref(shape), vp(1 * G), vp(2 * G), vp(3 * G),
+                                   vp(4 * G), vp(5 * G), None, vp(6 * G), vp(7 * G), vp(saved),
+                                   ctypes.c_size_t(svn), vp(ws), ctypes.c_size_t(wsn), None)
+
+
+def _bwd_saved(shape, saved=20 * G, svn=None, ws=24 * G, wsn=None, dq=8 * G):
+    L = _lib.load()
+    vp = lambda x: None if x is None else ctypes.c_void_p(x)
+    svn = _lib.saved_bytes(shape) if svn is None else svn
+    wsn = _lib.workspace_bytes(shape, backward=True) if wsn is None else wsn
+    return L.sf_gdn_chunk_bwd_saved(ctypes.byref(shape), vp(1 * G), vp(2 * G), vp(3 * G),
+                                    vp(4 * G), vp(5 * G), vp(saved), ctypes.c_size_t(svn),
+                                    vp(6 * G), None, vp(dq), vp(9 * G), vp(10 * G), vp(11 * G),
+                                    vp(12 * G), None, vp(ws), ctypes.c_size_t(wsn), None)
+
+
+def test_saved_buffer_validation():
+    shape = _shape(T=8192, H=2)
+    need = _lib.saved_bytes(shape)
+    # per-block fp32 entry states at least
+    assert need >= 2 * (8192 // 64) * 128 * 128 * 4
+    for call in (_fwd_save, _bwd_saved):
+        assert call(shape, svn=need - 1) == _lib.SF_ERR_INVALID_ARG
+        assert "saved" in _lib.load().sf_last_error_message().decode()
+        assert call(shape, saved=None, svn=0) == _lib.SF_ERR_INVALID_ARG
+        assert call(shape, saved=20 * G + 64) == _lib.SF_ERR_INVALID_ARG  # not 256-aligned
+    # the saving forward writes it: it must not overlap an input
+    assert _fwd_save(shape, saved=3 * G + 256) == _lib.SF_ERR_INVALID_ARG
+    assert _bwd_saved(shape, dq=20 * G + 4096) == _lib.SF_ERR_INVALID_ARG  # dq overlaps saved
+    # an empty chunk needs no saved buffer
+    assert _lib.saved_bytes(_shape(T=0)) == 0
+
+
 def test_workspace_sizes():
     # one segment needs no forward workspace
     assert _lib.workspace_bytes(_shape(T=64, H=1, seg=0)) >= 0

@@ -105,7 +105,8 @@ sf_status sf_gdn_chunk_bwd(const sf_gdn_shape* shape, const void* q, const void*
  * as the page's per-chunk activation release implies ("What carries the
  * argument"; Referee Report, major comment 1).  When memory allows keeping a
  * chunk's block states until its backward, sf_gdn_chunk_fwd_save also writes
- *   - the entry state of every 64-token block, fp32 [B, H, ceil(T/64), Dv, Dk]
+ *   - the entry state of every 64-token block, [B, H, ceil(T/64), Dv, Dk] in
+ *     the q/k/v dtype (each state enters the backward's products in it)
  *   - the segment transition maps of the in-chunk scan, fp32 [B, H, P, Dk, Dk]
  * into the caller's `saved` buffer (size from sf_gdn_chunk_saved_size for
  * the same shape, 256-byte aligned; opaque otherwise), and

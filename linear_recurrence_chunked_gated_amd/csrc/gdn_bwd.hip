@@ -49,25 +49,26 @@ template <typename T, int D> struct ScanLds {
 template <typename T, int D> struct ScanPrefetch {
   typedef Tile<T, D, 4 * D> Tl;
   uint4 rq[Tl::NCH], rk[Tl::NCH], ro[Tl::NCH];
-  float la = 0.f, be = 0.f;
+  float ra = 1.f, rb = 0.f;  // raw gates of the next block (wave 0)
   __device__ __forceinline__ void fetch(const T* q, const T* k, const T* dO, const float* al,
                                         const float* bt, size_t rs, int H, int t0, int nv) {
+    if (wave_id() == 0) {
+      const size_t idx = (size_t)(t0 + min(lane_id(), nv - 1)) * H;
+      ra = al[idx];
+      rb = bt[idx];
+    }
     Tl::load(rq, q + (size_t)t0 * rs, rs, nv);
     Tl::load(rk, k + (size_t)t0 * rs, rs, nv);
     Tl::load(ro, dO + (size_t)t0 * rs, rs, nv);
-    if (wave_id() == 0) {
-      const int lane = lane_id();
-      const size_t idx = (size_t)(t0 + min(lane, nv - 1)) * H;
-      const float x = al[idx], y = bt[idx];
-      la = lane < nv ? __logf(x) : 0.f;
-      be = lane < nv ? y : 0.f;
-    }
   }
   __device__ __forceinline__ void stage(T* Qs, T* Ks, T* Os, int ld, int nv, const GateLds& G) {
     Tl::to_lds(rq, Qs, ld, nv);
     Tl::to_lds(rk, Ks, ld, nv);
     Tl::to_lds(ro, Os, ld, nv);
-    if (wave_id() == 0) block_gates(la, be, G);
+    if (wave_id() == 0) {
+      const bool ok = lane_id() < nv;
+      block_gates(ok ? __logf(ra) : 0.f, ok ? rb : 0.f, G);
+    }
   }
 };
 
@@ -145,10 +146,12 @@ __global__ __launch_bounds__(4 * D, 2) void gdn_bwd_dscan_kernel(BwdArgs a, int 
     const int t0 = blk * BLK, nv = min(BLK, f.T - t0);
     pf.stage(Qs, Ks, Os, LDD, nv, G);
     if constexpr (MAIN) {
-      float* gb = reinterpret_cast<float*>(a.dhst) + ((size_t)bh * f.nblk + blk) * D * D;
+      T* gb = reinterpret_cast<T*>(a.dhst) + ((size_t)bh * f.nblk + blk) * D * D;
 #pragma unroll
-      for (int aa = 0; aa < DKT; ++aa)
-        *reinterpret_cast<f32x4*>(gb + (size_t)(16 * w + li) * D + 16 * aa + g4) = dSv[aa];
+      for (int aa = 0; aa < DKT; ++aa) {
+        const f32x4 x = dSv[aa];
+        st4(gb + (size_t)(16 * w + li) * D + 16 * aa + g4, x[0], x[1], x[2], x[3]);
+      }
     }
     if (blk > blk0) pf.fetch(q, k, dO, al, bt, rs, f.H, t0 - BLK, BLK);
     lds_barrier();
@@ -396,8 +399,8 @@ __global__ __launch_bounds__(4 * D, 2) void gdn_bwd_grads_kernel(BwdArgs a) {
   T* dk = const_cast<T*>(tok_base<T, D>(a.dk, f.T, f.H, b, h)) + (size_t)t0 * rs;
   T* dv = const_cast<T*>(tok_base<T, D>(a.dv, f.T, f.H, b, h)) + (size_t)t0 * rs;
   const size_t gofs = (size_t)b * f.T * f.H + (size_t)t0 * f.H + h;
-  const float* hS = reinterpret_cast<const float*>(a.hst) + ((size_t)bh * f.nblk + blk) * D * D;
-  const float* hG = reinterpret_cast<const float*>(a.dhst) + ((size_t)bh * f.nblk + blk) * D * D;
+  const T* hS = reinterpret_cast<const T*>(a.hst) + ((size_t)bh * f.nblk + blk) * D * D;
+  const T* hG = reinterpret_cast<const T*>(a.dhst) + ((size_t)bh * f.nblk + blk) * D * D;
 
   // ---- A: inputs, states (by dv-tile), partial sums
   {
@@ -425,8 +428,8 @@ __global__ __launch_bounds__(4 * D, 2) void gdn_bwd_grads_kernel(BwdArgs a) {
 #pragma unroll
   for (int aa = 0; aa < DKT; ++aa) {
     const size_t off = (size_t)(16 * w + li) * D + 16 * aa + g4;
-    Sx[aa] = *reinterpret_cast<const f32x4*>(hS + off);
-    dSx[aa] = *reinterpret_cast<const f32x4*>(hG + off);
+    Sx[aa] = ld4f(hS + off);
+    dSx[aa] = ld4f(hG + off);
   }
   {
     f32x4 p = {0.f, 0.f, 0.f, 0.f};
@@ -548,7 +551,7 @@ __global__ __launch_bounds__(4 * D, 2) void gdn_bwd_grads_kernel(BwdArgs a) {
 #pragma unroll
   for (int bb = 0; bb < DKT; ++bb)
 #pragma unroll
-    for (int e = 0; e < 4; ++e) Sk[bb][e] = hS[(size_t)(16 * bb + g4 + e) * D + 16 * w + li];
+    for (int e = 0; e < 4; ++e) Sk[bb][e] = (float)hS[(size_t)(16 * bb + g4 + e) * D + 16 * w + li];
   f32x4 dKt[4];
   {
     f32x4 acc[4];
@@ -594,7 +597,7 @@ __global__ __launch_bounds__(4 * D, 2) void gdn_bwd_grads_kernel(BwdArgs a) {
 #pragma unroll
     for (int bb = 0; bb < DKT; ++bb)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) dSk[bb][e] = hG[(size_t)(16 * bb + g4 + e) * D + 16 * w + li];
+      for (int e = 0; e < 4; ++e) dSk[bb][e] = (float)hG[(size_t)(16 * bb + g4 + e) * D + 16 * w + li];
     f32x4 acc[4], x2[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[j] = x2[j] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -785,7 +788,6 @@ hipError_t launch_bwd(const BwdArgs& a0, bool saved, hipStream_t st, Profiler* p
   const int BH = f.B * f.H, P = f.P;
   constexpr size_t scan_bytes = ScanLds<T, D>::bytes, grad_bytes = GradLds<T, D>::bytes;
   hipError_t e;
-  float* hst = reinterpret_cast<float*>(a.hst);
   const float* dSend = a.dS_out;
   int dsend_P = 1;
   if (P > 1) {
@@ -815,7 +817,7 @@ hipError_t launch_bwd(const BwdArgs& a0, bool saved, hipStream_t st, Profiler* p
     f.sst_P = 1;
   }
   // 4. block entry states
-  if (!saved && (e = launch_states<T, D>(f, hst, st, prof)) != hipSuccess) return e;
+  if (!saved && (e = launch_states<T, D>(f, a.hst, st, prof)) != hipSuccess) return e;
   // 5. block exit gradients and dS_in
   if ((e = set_lds((const void*)gdn_bwd_dscan_kernel<T, D, true>, ScanLds<T, D>::bytes)) != hipSuccess)
     return e;

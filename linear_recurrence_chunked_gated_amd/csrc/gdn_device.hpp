@@ -198,6 +198,13 @@ __device__ __forceinline__ void st4(float* p, float a, float b, float c, float d
 
 template <typename T> __device__ __forceinline__ T from_f(float x) { return (T)x; }
 
+// Four consecutive elements as fp32.
+__device__ __forceinline__ f32x4 ld4f(const bf16* p) {
+  const bf16x4 v = *reinterpret_cast<const bf16x4*>(p);
+  return f32x4{(float)v[0], (float)v[1], (float)v[2], (float)v[3]};
+}
+__device__ __forceinline__ f32x4 ld4f(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
+
 // dst[n][m..m+3] = scale * acc for the tile at (m0, n0).
 template <typename T>
 __device__ __forceinline__ void store_tile_T(const f32x4& acc, T* dst, int ld, int m0, int n0,

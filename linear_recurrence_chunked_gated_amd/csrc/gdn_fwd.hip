@@ -63,25 +63,26 @@ template <int D> constexpr int fwd_nw() { return D / 16; }
 template <typename T, int D, bool WITH_Q> struct Prefetch {
   typedef Tile<T, D, 64 * fwd_nw<D>()> Tl;
   uint4 rq[WITH_Q ? Tl::NCH : 1], rk[Tl::NCH], rv[Tl::NCH];
-  float la = 0.f, be = 0.f;
+  float ra = 1.f, rb = 0.f;  // raw gates of the next block (wave 0)
   __device__ __forceinline__ void fetch(const T* q, const T* k, const T* v, const float* al,
                                         const float* bt, size_t rs, int H, int t0, int nv) {
+    if (wave_id() == 0) {
+      const size_t idx = (size_t)(t0 + min(lane_id(), nv - 1)) * H;
+      ra = al[idx];
+      rb = bt[idx];
+    }
     if constexpr (WITH_Q) Tl::load(rq, q + (size_t)t0 * rs, rs, nv);
     Tl::load(rk, k + (size_t)t0 * rs, rs, nv);
     Tl::load(rv, v + (size_t)t0 * rs, rs, nv);
-    if (wave_id() == 0) {
-      const int lane = lane_id();
-      const size_t idx = (size_t)(t0 + min(lane, nv - 1)) * H;
-      const float x = al[idx], y = bt[idx];
-      la = lane < nv ? __logf(x) : 0.f;
-      be = lane < nv ? y : 0.f;
-    }
   }
   __device__ __forceinline__ void stage(T* Qs, T* Ks, T* Vs, int ld, int nv, const GateLds& G) {
     if constexpr (WITH_Q) Tl::to_lds(rq, Qs, ld, nv);
     Tl::to_lds(rk, Ks, ld, nv);
     Tl::to_lds(rv, Vs, ld, nv);
-    if (wave_id() == 0) block_gates(la, be, G);
+    if (wave_id() == 0) {
+      const bool ok = lane_id() < nv;
+      block_gates(ok ? __logf(ra) : 0.f, ok ? rb : 0.f, G);
+    }
   }
 };
 
@@ -89,12 +90,13 @@ template <typename T, int D, bool WITH_Q> struct Prefetch {
 // Wave w owns dv-tiles NDV*w .. of the state: S^T, U/Vn and O^T for those
 // columns live in its registers for the whole segment.  MODE selects what is
 // written: OUT_ONLY the outputs o (and S_out); STATES_ONLY each block's entry
-// state (fp32, [dv][dk]) to hst[b*H + h][block] and no output; OUT_AND_STATES
-// both.  The backward consumes the stored states.
+// state ([dv][dk], rounded to the operand type T, which is the precision the
+// state has wherever it enters a product) to hst[b*H + h][block] and no
+// output; OUT_AND_STATES both.  The backward consumes the stored states.
 enum FwdMode { OUT_ONLY = 0, STATES_ONLY = 1, OUT_AND_STATES = 2 };
 
 template <typename T, int D, int MODE>
-__global__ __launch_bounds__(64 * fwd_nw<D>(), 2) void gdn_fwd_out_kernel(FwdArgs a, float* hst) {
+__global__ __launch_bounds__(64 * fwd_nw<D>(), 2) void gdn_fwd_out_kernel(FwdArgs a, T* hst) {
   typedef FwdLds<T, D> Lz;
   constexpr int NW = fwd_nw<D>(), NDV = D / 16 / NW, DKT = D / 16;
   constexpr int LDD = Lz::LDD, LDC = Lz::LDC, LDF = Lz::LDF;
@@ -159,13 +161,14 @@ __global__ __launch_bounds__(64 * fwd_nw<D>(), 2) void gdn_fwd_out_kernel(FwdArg
     const int t0 = blk * BLK, nv = min(BLK, a.T - t0);
     pf.stage(Qs, Ks, Vs, LDD, nv, G);
     if constexpr (STATES) {
-      float* hb = hst + ((size_t)bh * a.nblk + blk) * D * D;
+      T* hb = hst + ((size_t)bh * a.nblk + blk) * D * D;
 #pragma unroll
       for (int bb = 0; bb < NDV; ++bb)
 #pragma unroll
-        for (int aa = 0; aa < DKT; ++aa)
-          *reinterpret_cast<f32x4*>(hb + (size_t)(16 * (dv0 + bb) + li) * D + 16 * aa + g4) =
-              St[bb][aa];
+        for (int aa = 0; aa < DKT; ++aa) {
+          const f32x4 x = St[bb][aa];
+          st4(hb + (size_t)(16 * (dv0 + bb) + li) * D + 16 * aa + g4, x[0], x[1], x[2], x[3]);
+        }
     }
     if constexpr (OUT) {
       if (prev_t0 >= 0) store_o();
@@ -431,13 +434,13 @@ hipError_t launch_chain_fwd(const ChainArgs& c, int BH, hipStream_t st, Profiler
 }
 
 template <typename T, int D>
-hipError_t launch_states(const FwdArgs& a, float* hst, hipStream_t st, Profiler* prof) {
+hipError_t launch_states(const FwdArgs& a, void* hst, hipStream_t st, Profiler* prof) {
   typedef FwdLds<T, D> Lz;
   hipError_t e = set_lds((const void*)gdn_fwd_out_kernel<T, D, STATES_ONLY>, Lz::out_bytes);
   if (e != hipSuccess) return e;
   prof_begin(prof, "gdn_fwd_states", st);
   hipLaunchKernelGGL((gdn_fwd_out_kernel<T, D, STATES_ONLY>), dim3(a.B * a.H * a.P), dim3(64 * fwd_nw<D>()),
-                     Lz::out_bytes, st, a, hst);
+                     Lz::out_bytes, st, a, reinterpret_cast<T*>(hst));
   prof_end(prof, st);
   return hipGetLastError();
 }
@@ -446,7 +449,7 @@ hipError_t launch_states(const FwdArgs& a, float* hst, hipStream_t st, Profiler*
 // segment maps M are computed for all P segments (a.Mseg then points into the
 // caller's saved buffer), so that the backward can skip its recompute.
 template <typename T, int D>
-hipError_t launch_fwd(const FwdArgs& a, float* hsave, hipStream_t st, Profiler* prof) {
+hipError_t launch_fwd(const FwdArgs& a, void* hsave, hipStream_t st, Profiler* prof) {
   typedef FwdLds<T, D> Lz;
   hipError_t e;
   const int BH = a.B * a.H;
@@ -462,7 +465,7 @@ hipError_t launch_fwd(const FwdArgs& a, float* hsave, hipStream_t st, Profiler* 
       return e;
     prof_begin(prof, "gdn_fwd_out_save", st);
     hipLaunchKernelGGL((gdn_fwd_out_kernel<T, D, OUT_AND_STATES>), dim3(BH * a.P),
-                       dim3(64 * fwd_nw<D>()), Lz::out_bytes, st, a, hsave);
+                       dim3(64 * fwd_nw<D>()), Lz::out_bytes, st, a, reinterpret_cast<T*>(hsave));
     prof_end(prof, st);
     return hipGetLastError();
   }
@@ -470,15 +473,15 @@ hipError_t launch_fwd(const FwdArgs& a, float* hsave, hipStream_t st, Profiler* 
     return e;
   prof_begin(prof, "gdn_fwd_out", st);
   hipLaunchKernelGGL((gdn_fwd_out_kernel<T, D, OUT_ONLY>), dim3(BH * a.P), dim3(64 * fwd_nw<D>()),
-                     Lz::out_bytes, st, a, nullptr);
+                     Lz::out_bytes, st, a, (T*)nullptr);
   prof_end(prof, st);
   return hipGetLastError();
 }
 
 #define SF_INST(T, D)                                                                      \
-  template hipError_t launch_fwd<T, D>(const FwdArgs&, float*, hipStream_t, Profiler*);  \
+  template hipError_t launch_fwd<T, D>(const FwdArgs&, void*, hipStream_t, Profiler*);  \
   template hipError_t launch_fwd_summary<T, D>(const FwdArgs&, int, hipStream_t, Profiler*, const char*); \
-  template hipError_t launch_states<T, D>(const FwdArgs&, float*, hipStream_t, Profiler*);
+  template hipError_t launch_states<T, D>(const FwdArgs&, void*, hipStream_t, Profiler*);
 SF_INST(bf16, 128)
 SF_INST(bf16, 64)
 SF_INST(float, 64)

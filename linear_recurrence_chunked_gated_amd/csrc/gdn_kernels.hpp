@@ -61,7 +61,7 @@ void prof_end(Profiler* p, hipStream_t st);
 
 // hsave: optional per-block entry-state output (see launch_fwd).
 template <typename T, int D>
-hipError_t launch_fwd(const FwdArgs& a, float* hsave, hipStream_t st, Profiler* prof);
+hipError_t launch_fwd(const FwdArgs& a, void* hsave, hipStream_t st, Profiler* prof);
 // Pieces of the forward reused by the backward.
 template <typename T, int D>
 hipError_t launch_fwd_summary(const FwdArgs& a, int nseg, hipStream_t st, Profiler* prof,
@@ -69,7 +69,7 @@ hipError_t launch_fwd_summary(const FwdArgs& a, int nseg, hipStream_t st, Profil
 template <int D>
 hipError_t launch_chain_fwd(const ChainArgs& c, int BH, hipStream_t st, Profiler* prof);
 template <typename T, int D>
-hipError_t launch_states(const FwdArgs& a, float* hst, hipStream_t st, Profiler* prof);
+hipError_t launch_states(const FwdArgs& a, void* hst, hipStream_t st, Profiler* prof);
 // saved: a.hst already holds every block's entry state and a.f.Mseg every
 // segment's map (from a saving forward), so the forward recompute is skipped.
 template <typename T, int D>

@@ -73,7 +73,9 @@ sf_status make_plan(const sf_gdn_shape* s, Plan& p) {
     if ((long long)p.B * p.H * p.P > (1LL << 30))
       return fail(SF_ERR_UNSUPPORTED, "too many segments");
   }
-  p.state_elem = 4;  // per-block states and state gradients are kept in fp32
+  // per-block states and state gradients are stored in the operand type (the
+  // precision in which they enter every product that reads them)
+  p.state_elem = p.dtype == SF_DTYPE_BF16 ? 2 : 4;
   return SF_OK;
 }
 
@@ -252,7 +254,7 @@ sf_status fwd_impl(const sf_gdn_shape* shape, const void* q, const void* k, cons
     a.o = o; a.S_out = S_out;
     a.B = p.B; a.T = p.T; a.H = p.H; a.nblk = p.nblk; a.L = p.L; a.P = p.P;
     char* ws = (char*)workspace;
-    float* hsave = save ? (float*)saved : nullptr;
+    void* hsave = save ? saved : nullptr;
     if (p.P > 1) {
       a.Mseg = save ? (float*)((char*)saved + blk_buf(p)) : (float*)ws;
       a.Nseg = (float*)(ws + seg_buf(p));

@@ -63,11 +63,11 @@ __device__ __forceinline__ void block_gates(float la, float be, const GateLds& G
 
 // Scores of an NW-wave workgroup (NW = 4 or 8): wave w owns s-tile w % 4 and
 // r-tiles from (w / 4) * (16 / NW).
-//   Af[r][s] = (s < r) beta_r Gamma_rs k_r.k_s      (fp32, strictly lower)
+//   Af[r][s] = (s < r) beta_r Gamma_rs k_r.k_s      (fp32, strictly lower), if WITH_A
 //   Pl[r][s] = (s <= r) Gamma_rs q_r.k_s            (operand type), if WITH_Q
 // Computed as K K^T and K Q^T with s on the accumulator's m index so each
 // lane stores 4 consecutive s.
-template <typename T, int D, int NW, bool WITH_Q>
+template <typename T, int D, int NW, bool WITH_Q, bool WITH_A = true>
 __device__ __forceinline__ void block_scores(const T* Qs, const T* Ks, int ldd, const GateLds& G,
                                              float* Af, int ldf, T* Pl, int ldc) {
   constexpr int NJ = 16 / NW;
@@ -81,7 +81,8 @@ __device__ __forceinline__ void block_scores(const T* Qs, const T* Ks, int ldd, 
     const auto a = frag_row<T, STD>(Ks + 16 * st * ldd, ldd, s);
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
-      accA[j] = Mma<T>::mma(a, frag_row<T, STD>(Ks + 16 * (r0 + j) * ldd, ldd, s), accA[j]);
+      if constexpr (WITH_A)
+        accA[j] = Mma<T>::mma(a, frag_row<T, STD>(Ks + 16 * (r0 + j) * ldd, ldd, s), accA[j]);
       if constexpr (WITH_Q)
         accP[j] = Mma<T>::mma(a, frag_row<T, STD>(Qs + 16 * (r0 + j) * ldd, ldd, s), accP[j]);
     }
@@ -102,7 +103,7 @@ __device__ __forceinline__ void block_scores(const T* Qs, const T* Ks, int ldd, 
       a[e] = (s < r) ? br * gam * accA[j][e] : 0.f;
       p[e] = gam * accP[j][e];
     }
-    st4(Af + r * ldf + s0, a[0], a[1], a[2], a[3]);
+    if constexpr (WITH_A) st4(Af + r * ldf + s0, a[0], a[1], a[2], a[3]);
     if constexpr (WITH_Q) st4(Pl + r * ldc + s0, p[0], p[1], p[2], p[3]);
   }
 }

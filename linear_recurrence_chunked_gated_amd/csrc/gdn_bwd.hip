@@ -10,6 +10,7 @@
 //   dS  = gamma_C dS' + dO^T diag(gamma) Q - dVn^T W     (entry-state gradient)
 // which, like the forward, is affine: dS = dS' M_b^T + NB_b.  The launch
 // sequence is
+//   0. per-block Tp, Tpp                                  [forward Pre kernel]
 //   1. segment maps (M, N) of the forward                       [forward kernel]
 //   2. gdn_bwd_dscan<summary>: per segment, dS at its entry from a zero exit
 //      gradient (NB_seg)
@@ -28,40 +29,41 @@ __device__ __forceinline__ const T* tok_base(const void* p, int T_, int H, int b
 }
 
 // ------------------------------------------------------------------ LDS ----
-// dscan: RQ Q -> Tm -> Wn | RK K | RO dO | RA Af -> Tp,Tpp | RP P | RG gates
+// dscan: RQ Q | RK K | RO dO | RW Wn | RT Tp | RP P | RG gates
 template <typename T, int D> struct ScanLds {
   static constexpr int LDD = D + Lay<T>::PAD;
   static constexpr int LDC = BLK + Lay<T>::PAD;
-  static constexpr int LDF = BLK + 4;
-  static constexpr size_t cmax(size_t a, size_t b) { return a > b ? a : b; }
   static constexpr size_t rowD = (size_t)BLK * LDD * sizeof(T);
-  static constexpr size_t f64x64 = (size_t)BLK * LDF * sizeof(float);
-  static constexpr size_t zQ = cmax(rowD, f64x64);
-  static constexpr size_t zA = cmax(f64x64, 2 * (size_t)BLK * LDC * sizeof(T));
-  static constexpr size_t zP = (size_t)BLK * LDC * sizeof(T);
-  static constexpr size_t oQ = 0, oK = oQ + zQ, oO = oK + rowD, oA = oO + rowD, oP = oA + zA,
-                          oG = oP + zP;
+  static constexpr size_t sq = (size_t)BLK * LDC * sizeof(T);
+  static constexpr size_t oQ = 0, oK = oQ + rowD, oO = oK + rowD, oW = oO + rowD, oT = oW + rowD,
+                          oP = oT + sq, oG = oP + sq;
   static constexpr size_t bytes = oG + kGateBytes;
   static_assert(bytes <= 160 * 1024, "LDS budget");
 };
 
-// Per-block inputs of the reverse scan in flight (q, k, dO rows and gates).
+// Per-block inputs of the reverse scan in flight (q, k, dO rows, Tp from the
+// Pre kernel and gates).
 template <typename T, int D> struct ScanPrefetch {
   typedef Tile<T, D, 4 * D> Tl;
-  uint4 rq[Tl::NCH], rk[Tl::NCH], ro[Tl::NCH];
+  typedef Tile<T, BLK, 4 * D> Tt;
+  uint4 rq[Tl::NCH], rk[Tl::NCH], ro[Tl::NCH], rp[Tt::NCH];
   float ra = 1.f, rb = 0.f;  // raw gates of the next block (wave 0)
   __device__ __forceinline__ void fetch(const T* q, const T* k, const T* dO, const float* al,
-                                        const float* bt, size_t rs, int H, int t0, int nv) {
+                                        const float* bt, const T* tp, size_t rs, int H, int t0,
+                                        int nv) {
     if (wave_id() == 0) {
       const size_t idx = (size_t)(t0 + min(lane_id(), nv - 1)) * H;
       ra = al[idx];
       rb = bt[idx];
     }
+    Tt::load(rp, tp, BLK, BLK);
     Tl::load(rq, q + (size_t)t0 * rs, rs, nv);
     Tl::load(rk, k + (size_t)t0 * rs, rs, nv);
     Tl::load(ro, dO + (size_t)t0 * rs, rs, nv);
   }
-  __device__ __forceinline__ void stage(T* Qs, T* Ks, T* Os, int ld, int nv, const GateLds& G) {
+  __device__ __forceinline__ void stage(T* Qs, T* Ks, T* Os, T* Tp, int ld, int ldc, int nv,
+                                        const GateLds& G) {
+    Tt::to_lds(rp, Tp, ldc, BLK);
     Tl::to_lds(rq, Qs, ld, nv);
     Tl::to_lds(rk, Ks, ld, nv);
     Tl::to_lds(ro, Os, ld, nv);
@@ -71,6 +73,12 @@ template <typename T, int D> struct ScanPrefetch {
     }
   }
 };
+
+// Tp of block blk of sequence bh (the first of its [2][64][64] pair).
+template <typename T>
+__device__ __forceinline__ const T* tp_block(const void* tw, int nblk, int bh, int blk) {
+  return reinterpret_cast<const T*>(tw) + ((size_t)bh * nblk + blk) * 2 * BLK * BLK;
+}
 
 // B operand rows dv of gamma_r dO[r][dv] (k = r, STD order): the transpose read
 // of dO scaled per contraction element.
@@ -103,16 +111,13 @@ __global__ __launch_bounds__(4 * D, 2) void gdn_bwd_dscan_kernel(BwdArgs a, int 
                                                                  int dsend_P) {
   typedef ScanLds<T, D> Lz;
   constexpr int DKT = D / 16, NW = D / 16;
-  constexpr int LDD = Lz::LDD, LDC = Lz::LDC, LDF = Lz::LDF;
+  constexpr int LDD = Lz::LDD, LDC = Lz::LDC;
   extern __shared__ __align__(16) unsigned char smem[];
   T* Qs = reinterpret_cast<T*>(smem + Lz::oQ);
-  float* Tm = reinterpret_cast<float*>(smem + Lz::oQ);
-  T* Wn = reinterpret_cast<T*>(smem + Lz::oQ);
+  T* Wn = reinterpret_cast<T*>(smem + Lz::oW);
   T* Ks = reinterpret_cast<T*>(smem + Lz::oK);
   T* Os = reinterpret_cast<T*>(smem + Lz::oO);
-  float* Af = reinterpret_cast<float*>(smem + Lz::oA);
-  T* Tp = reinterpret_cast<T*>(smem + Lz::oA);
-  T* Tpp = Tp + BLK * LDC;
+  T* Tp = reinterpret_cast<T*>(smem + Lz::oT);
   T* Pl = reinterpret_cast<T*>(smem + Lz::oP);
   const GateLds G = gate_lds(smem + Lz::oG);
 
@@ -140,11 +145,12 @@ __global__ __launch_bounds__(4 * D, 2) void gdn_bwd_dscan_kernel(BwdArgs a, int 
   ScanPrefetch<T, D> pf;
   {
     const int t0 = (blk1 - 1) * BLK;
-    pf.fetch(q, k, dO, al, bt, rs, f.H, t0, min(BLK, f.T - t0));
+    pf.fetch(q, k, dO, al, bt, tp_block<T>(f.tw, f.nblk, bh, blk1 - 1), rs, f.H, t0,
+             min(BLK, f.T - t0));
   }
   for (int blk = blk1 - 1; blk >= blk0; --blk) {
     const int t0 = blk * BLK, nv = min(BLK, f.T - t0);
-    pf.stage(Qs, Ks, Os, LDD, nv, G);
+    pf.stage(Qs, Ks, Os, Tp, LDD, LDC, nv, G);
     if constexpr (MAIN) {
       T* gb = reinterpret_cast<T*>(a.dhst) + ((size_t)bh * f.nblk + blk) * D * D;
 #pragma unroll
@@ -153,10 +159,11 @@ __global__ __launch_bounds__(4 * D, 2) void gdn_bwd_dscan_kernel(BwdArgs a, int 
         st4(gb + (size_t)(16 * w + li) * D + 16 * aa + g4, x[0], x[1], x[2], x[3]);
       }
     }
-    if (blk > blk0) pf.fetch(q, k, dO, al, bt, rs, f.H, t0 - BLK, BLK);
+    if (blk > blk0)
+      pf.fetch(q, k, dO, al, bt, tp_block<T>(f.tw, f.nblk, bh, blk - 1), rs, f.H, t0 - BLK, BLK);
     lds_barrier();
-    // scores and the dO^T diag(gamma) Q term (needs Q before its region is reused)
-    block_scores<T, D, NW, true>(Qs, Ks, LDD, G, Af, LDF, Pl, LDC);
+    // P scores, the dO^T diag(gamma) Q term and Wn = -Tp K
+    block_scores<T, D, NW, true, false>(Qs, Ks, LDD, G, nullptr, 0, Pl, LDC);
     f32x4 X2[DKT];
 #pragma unroll
     for (int aa = 0; aa < DKT; ++aa) X2[aa] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -167,10 +174,6 @@ __global__ __launch_bounds__(4 * D, 2) void gdn_bwd_dscan_kernel(BwdArgs a, int 
       for (int aa = 0; aa < DKT; ++aa)
         X2[aa] = Mma<T>::mma(frag_tr<T, STD>(Qs + 16 * aa, LDD, s), bo, X2[aa]);
     }
-    lds_barrier();
-    block_solve(Af, Tm, LDF);
-    block_tprime<T, 64 * NW>(Tm, LDF, G, Tp, Tpp, LDC);
-    lds_barrier();
     block_w<T, D, NW>(Ks, LDD, Tp, LDC, Wn);
     lds_barrier();
     // dVn = P^T dO + D (K dS'^T)
@@ -788,6 +791,8 @@ hipError_t launch_bwd(const BwdArgs& a0, bool saved, hipStream_t st, Profiler* p
   const int BH = f.B * f.H, P = f.P;
   constexpr size_t scan_bytes = ScanLds<T, D>::bytes, grad_bytes = GradLds<T, D>::bytes;
   hipError_t e;
+  // 0. per-block Tp, Tpp (Pre)
+  if (!saved && (e = launch_prep<T, D>(f, st, prof)) != hipSuccess) return e;
   const float* dSend = a.dS_out;
   int dsend_P = 1;
   if (P > 1) {

@@ -4,13 +4,16 @@
 // The blocks are grouped into P segments of L blocks.  Each block maps the
 // state affinely, S' = S M_b + N_b with M_b = gamma_C I - W^T D K and
 // N_b = U^T D K, so a segment is an affine map too.  The forward runs
+//   0. gdn_prep:        per block, fully parallel, the state-free part of
+//      Pre: T = (I + A)^{-1} and its scaled copies Tp, Tpp (the only serial
+//      step inside a block, so it is kept out of the scan kernels);
 //   1. gdn_fwd_summary: per segment (except the last), its map (M, N) from
 //      the identity and a zero state, fully parallel;
 //   2. gdn_chain_fwd:   segment entry states S_{j+1} = S_j M_j + N_j, a short
 //      serial chain that starts from S_in;
 //   3. gdn_fwd_out:     per segment, from its true entry state, the fused
-//      Pre/ST/Out pass over its blocks: outputs o, and S_out from the last
-//      segment.
+//      W/U, ST and Out pass over its blocks: outputs o, and S_out from the
+//      last segment.
 // This is the page's boundary-state chain (Eq. 5, Pith review of StateFlow,
 // "What carries the argument") applied inside one chunk so that the low
 // parallelism of the state transition (Figure 2 caption; "grid-size tuning")
@@ -20,31 +23,36 @@
 namespace sfgdn {
 
 // ------------------------------------------------------------------ LDS ----
-// One workgroup = D/16 waves, one per 16-column slice of the state.  LDS
-// regions are reused by phase:
-//   RQ : Q (scores, S Q^T) -> Tm (solve) -> Wn (-W, for Vn)
+// Scan kernels: one workgroup = D/16 waves, one per 16-column slice of the
+// state.  Regions:
+//   RQ : Q (P scores, S Q^T)
 //   RK : K (row-major; K^T operands come from transpose reads)
 //   RV : V (row-major; V^T operands come from transpose reads)
-//   RA : Af (solve input) -> Tp, Tpp
+//   RW : Wn = -W (for Vn)
+//   RT : Tp, Tpp (from the Pre kernel)
 //   RP : P (masked decayed scores, for the output)
 //   RG : gate vectors
 template <typename T, int D> struct FwdLds {
   static constexpr int LDD = D + Lay<T>::PAD;
   static constexpr int LDC = BLK + Lay<T>::PAD;
+  static constexpr size_t rowD = (size_t)BLK * LDD * sizeof(T);
+  static constexpr size_t sq = (size_t)BLK * LDC * sizeof(T);
+  static constexpr size_t oQ = 0, oK = oQ + rowD, oV = oK + rowD, oW = oV + rowD,
+                          oT = oW + rowD, oP = oT + 2 * sq, oG = oP + sq;
+  static constexpr size_t out_bytes = oG + kGateBytes;
+  static_assert(out_bytes <= 160 * 1024, "LDS budget");
+};
+
+// Pre kernel: RK K -> Tm (fp32 T, solve scratch; K is dead once A is formed)
+// | RA Af (fp32 A) | RG gates.  About 36 KB, so four workgroups share a CU.
+template <typename T, int D> struct PrepLds {
+  static constexpr int LDD = D + Lay<T>::PAD;
   static constexpr int LDF = BLK + 4;
   static constexpr size_t cmax(size_t a, size_t b) { return a > b ? a : b; }
   static constexpr size_t rowD = (size_t)BLK * LDD * sizeof(T);
   static constexpr size_t f64x64 = (size_t)BLK * LDF * sizeof(float);
-  static constexpr size_t zQ = cmax(rowD, f64x64);
-  static constexpr size_t zK = rowD;
-  static constexpr size_t zV = rowD;
-  static constexpr size_t zA = cmax(f64x64, 2 * (size_t)BLK * LDC * sizeof(T));
-  static constexpr size_t zP = (size_t)BLK * LDC * sizeof(T);
-  static constexpr size_t oQ = 0, oK = oQ + zQ, oV = oK + zK, oA = oV + zV, oG = oA + zA,
-                          oP = oG + kGateBytes;
-  static constexpr size_t out_bytes = oP + zP;
-  static constexpr size_t sum_bytes = oG + kGateBytes;  // no P
-  static_assert(out_bytes <= 160 * 1024 && sum_bytes <= 160 * 1024, "LDS budget");
+  static constexpr size_t oK = 0, oT = 0, oA = cmax(rowD, f64x64), oG = oA + f64x64;
+  static constexpr size_t bytes = oG + kGateBytes;
 };
 
 // Token rows of one (b, h) sequence: row t starts at base + t * H * D.
@@ -54,28 +62,42 @@ __device__ __forceinline__ const T* seq_base(const void* p, const FwdArgs& a, in
 }
 
 
-// Per-block inputs in flight: the next block's rows are loaded into registers
-// while the current block computes.
+// Per-block inputs in flight: the next block's rows (q, k, v), its Tp and
+// Tpp from the Pre kernel and its gates are loaded into registers while the
+// current block computes.
 // Waves per workgroup of the forward kernels: one per 16-column tile of the
 // state.
 template <int D> constexpr int fwd_nw() { return D / 16; }
 
+// Tp, Tpp of block blk of sequence bh: [2][64][64] row-major.
+template <typename T>
+__device__ __forceinline__ const T* tw_block(const void* tw, int nblk, int bh, int blk) {
+  return reinterpret_cast<const T*>(tw) + ((size_t)bh * nblk + blk) * 2 * BLK * BLK;
+}
+
 template <typename T, int D, bool WITH_Q> struct Prefetch {
   typedef Tile<T, D, 64 * fwd_nw<D>()> Tl;
-  uint4 rq[WITH_Q ? Tl::NCH : 1], rk[Tl::NCH], rv[Tl::NCH];
+  typedef Tile<T, BLK, 64 * fwd_nw<D>()> Tt;
+  uint4 rq[WITH_Q ? Tl::NCH : 1], rk[Tl::NCH], rv[Tl::NCH], rp[Tt::NCH], rpp[Tt::NCH];
   float ra = 1.f, rb = 0.f;  // raw gates of the next block (wave 0)
   __device__ __forceinline__ void fetch(const T* q, const T* k, const T* v, const float* al,
-                                        const float* bt, size_t rs, int H, int t0, int nv) {
+                                        const float* bt, const T* tw, size_t rs, int H, int t0,
+                                        int nv) {
     if (wave_id() == 0) {
       const size_t idx = (size_t)(t0 + min(lane_id(), nv - 1)) * H;
       ra = al[idx];
       rb = bt[idx];
     }
+    Tt::load(rp, tw, BLK, BLK);
+    Tt::load(rpp, tw + BLK * BLK, BLK, BLK);
     if constexpr (WITH_Q) Tl::load(rq, q + (size_t)t0 * rs, rs, nv);
     Tl::load(rk, k + (size_t)t0 * rs, rs, nv);
     Tl::load(rv, v + (size_t)t0 * rs, rs, nv);
   }
-  __device__ __forceinline__ void stage(T* Qs, T* Ks, T* Vs, int ld, int nv, const GateLds& G) {
+  __device__ __forceinline__ void stage(T* Qs, T* Ks, T* Vs, T* Tp, T* Tpp, int ld, int ldc,
+                                        int nv, const GateLds& G) {
+    Tt::to_lds(rp, Tp, ldc, BLK);
+    Tt::to_lds(rpp, Tpp, ldc, BLK);
     if constexpr (WITH_Q) Tl::to_lds(rq, Qs, ld, nv);
     Tl::to_lds(rk, Ks, ld, nv);
     Tl::to_lds(rv, Vs, ld, nv);
@@ -85,6 +107,47 @@ template <typename T, int D, bool WITH_Q> struct Prefetch {
     }
   }
 };
+
+// ------------------------------------------------------------ Pre ----------
+// One workgroup of 4 waves per 64-token block, every block of every sequence
+// in parallel: gates, A = strict lower part of diag(beta) (K K^T o Gamma),
+// T = (I + A)^{-1} (fp32), then Tp = T diag(beta o gamma) and
+// Tpp = T diag(beta) in the operand type to tw[b*H + h][block][2][64][64].
+template <typename T, int D>
+__global__ __launch_bounds__(256) void gdn_prep_kernel(FwdArgs a) {
+  typedef PrepLds<T, D> Lz;
+  constexpr int LDD = Lz::LDD, LDF = Lz::LDF;
+  extern __shared__ __align__(16) unsigned char smem[];
+  T* Ks = reinterpret_cast<T*>(smem + Lz::oK);
+  float* Af = reinterpret_cast<float*>(smem + Lz::oA);
+  float* Tm = reinterpret_cast<float*>(smem + Lz::oT);
+  const GateLds G = gate_lds(smem + Lz::oG);
+
+  const int blk = blockIdx.x % a.nblk, bh = blockIdx.x / a.nblk;
+  const int b = bh / a.H, h = bh % a.H;
+  const int t0 = blk * BLK, nv = min(BLK, a.T - t0);
+  const size_t rs = (size_t)a.H * D;
+  typedef Tile<T, D, 256> Tl;
+  uint4 rk[Tl::NCH];
+  Tl::load(rk, seq_base<T, D>(a.k, a, b, h) + (size_t)t0 * rs, rs, nv);
+  float ra = 1.f, rb = 0.f;
+  if (wave_id() == 0) {
+    const size_t idx = (size_t)b * a.T * a.H + (size_t)(t0 + min(lane_id(), nv - 1)) * a.H + h;
+    ra = a.alpha[idx];
+    rb = a.beta[idx];
+  }
+  Tl::to_lds(rk, Ks, LDD, nv);
+  if (wave_id() == 0) {
+    const bool ok = lane_id() < nv;
+    block_gates(ok ? __logf(ra) : 0.f, ok ? rb : 0.f, G);
+  }
+  lds_barrier();
+  block_scores<T, D, 4, false>(nullptr, Ks, LDD, G, Af, LDF, nullptr, 0);
+  lds_barrier();
+  block_solve(Af, Tm, LDF);
+  T* out = const_cast<T*>(tw_block<T>(a.tw, a.nblk, bh, blk));
+  block_tprime<T, 256>(Tm, LDF, G, out, out + BLK * BLK, BLK);
+}
 
 // --------------------------------------------------------- fused out -------
 // Wave w owns dv-tiles NDV*w .. of the state: S^T, U/Vn and O^T for those
@@ -99,19 +162,17 @@ template <typename T, int D, int MODE>
 __global__ __launch_bounds__(64 * fwd_nw<D>(), 2) void gdn_fwd_out_kernel(FwdArgs a, T* hst) {
   typedef FwdLds<T, D> Lz;
   constexpr int NW = fwd_nw<D>(), NDV = D / 16 / NW, DKT = D / 16;
-  constexpr int LDD = Lz::LDD, LDC = Lz::LDC, LDF = Lz::LDF;
+  constexpr int LDD = Lz::LDD, LDC = Lz::LDC;
   constexpr bool STATES = MODE != OUT_ONLY, OUT = MODE != STATES_ONLY;
   extern __shared__ __align__(16) unsigned char smem[];
   T* Qs = reinterpret_cast<T*>(smem + Lz::oQ);
-  float* Tm = reinterpret_cast<float*>(smem + Lz::oQ);
-  T* Wn = reinterpret_cast<T*>(smem + Lz::oQ);
   T* Ks = reinterpret_cast<T*>(smem + Lz::oK);
   T* Vs = reinterpret_cast<T*>(smem + Lz::oV);
-  float* Af = reinterpret_cast<float*>(smem + Lz::oA);
-  T* Tp = reinterpret_cast<T*>(smem + Lz::oA);
+  T* Wn = reinterpret_cast<T*>(smem + Lz::oW);
+  T* Tp = reinterpret_cast<T*>(smem + Lz::oT);
   T* Tpp = Tp + BLK * LDC;
-  const GateLds G = gate_lds(smem + Lz::oG);
   T* Pl = reinterpret_cast<T*>(smem + Lz::oP);
+  const GateLds G = gate_lds(smem + Lz::oG);
 
   const int w = wave_id(), lane = lane_id(), g4 = 4 * (lane >> 4), li = lane & 15;
   const int dv0 = NDV * w;
@@ -141,7 +202,9 @@ __global__ __launch_bounds__(64 * fwd_nw<D>(), 2) void gdn_fwd_out_kernel(FwdArg
   }
 
   Prefetch<T, D, OUT> pf;
-  if (blk0 < blk1) pf.fetch(q, k, v, al, bt, rs, a.H, blk0 * BLK, min(BLK, a.T - blk0 * BLK));
+  if (blk0 < blk1)
+    pf.fetch(q, k, v, al, bt, tw_block<T>(a.tw, a.nblk, bh, blk0), rs, a.H, blk0 * BLK,
+             min(BLK, a.T - blk0 * BLK));
   f32x4 O[NDV][4];
   int prev_t0 = -1, prev_nv = 0;
   auto store_o = [&]() {
@@ -159,7 +222,7 @@ __global__ __launch_bounds__(64 * fwd_nw<D>(), 2) void gdn_fwd_out_kernel(FwdArg
 
   for (int blk = blk0; blk < blk1; ++blk) {
     const int t0 = blk * BLK, nv = min(BLK, a.T - t0);
-    pf.stage(Qs, Ks, Vs, LDD, nv, G);
+    pf.stage(Qs, Ks, Vs, Tp, Tpp, LDD, LDC, nv, G);
     if constexpr (STATES) {
       T* hb = hst + ((size_t)bh * a.nblk + blk) * D * D;
 #pragma unroll
@@ -174,9 +237,9 @@ __global__ __launch_bounds__(64 * fwd_nw<D>(), 2) void gdn_fwd_out_kernel(FwdArg
       if (prev_t0 >= 0) store_o();
     }
     lds_barrier();
-    // Pre: scores; Out, state part: O^T = diag(gamma) (S Q^T)
-    block_scores<T, D, NW, OUT>(Qs, Ks, LDD, G, Af, LDF, Pl, LDC);
+    // P = masked Q K^T o Gamma; O^T = diag(gamma) S Q^T; Wn = -Tp K; U = Tpp V
     if constexpr (OUT) {
+      block_scores<T, D, NW, true, false>(Qs, Ks, LDD, G, nullptr, 0, Pl, LDC);
       zero_acc(O);
       block_s_yT<T, D, NDV>(St, Qs, LDD, O);
 #pragma unroll
@@ -186,11 +249,6 @@ __global__ __launch_bounds__(64 * fwd_nw<D>(), 2) void gdn_fwd_out_kernel(FwdArg
         for (int bb = 0; bb < NDV; ++bb) O[bb][j] *= gr;
       }
     }
-    lds_barrier();
-    // Pre: T = (I + A)^{-1}, W, U
-    block_solve(Af, Tm, LDF);
-    block_tprime<T, 64 * NW>(Tm, LDF, G, Tp, Tpp, LDC);
-    lds_barrier();
     block_w<T, D, NW>(Ks, LDD, Tp, LDC, Wn);
     f32x4 U[NDV][4];
     block_u<T, NDV>(Tpp, LDC, Vs, LDD, dv0, U);
@@ -211,9 +269,11 @@ __global__ __launch_bounds__(64 * fwd_nw<D>(), 2) void gdn_fwd_out_kernel(FwdArg
     block_state_write<T, D, NDV>(Ks, LDD, U, dsc, St);
     prev_t0 = t0;
     prev_nv = nv;
-    // The next block's rows: issued here so that they add no register pressure
-    // to the phases above; the other workgroup on the CU covers the latency.
-    if (blk + 1 < blk1) pf.fetch(q, k, v, al, bt, rs, a.H, t0 + BLK, min(BLK, a.T - t0 - BLK));
+    // The next block's inputs: issued here so that they add no register
+    // pressure to the phases above.
+    if (blk + 1 < blk1)
+      pf.fetch(q, k, v, al, bt, tw_block<T>(a.tw, a.nblk, bh, blk + 1), rs, a.H, t0 + BLK,
+               min(BLK, a.T - t0 - BLK));
     lds_barrier();
   }
   if constexpr (OUT) {
@@ -241,14 +301,12 @@ template <typename T, int D>
 __global__ __launch_bounds__(64 * fwd_nw<D>(), 2) void gdn_fwd_summary_kernel(FwdArgs a, int nseg) {
   typedef FwdLds<T, D> Lz;
   constexpr int NW = fwd_nw<D>(), NDV = D / 16 / NW, DKT = D / 16;
-  constexpr int LDD = Lz::LDD, LDC = Lz::LDC, LDF = Lz::LDF;
+  constexpr int LDD = Lz::LDD, LDC = Lz::LDC;
   extern __shared__ __align__(16) unsigned char smem[];
-  float* Tm = reinterpret_cast<float*>(smem + Lz::oQ);
-  T* Wn = reinterpret_cast<T*>(smem + Lz::oQ);
+  T* Wn = reinterpret_cast<T*>(smem + Lz::oW);
   T* Ks = reinterpret_cast<T*>(smem + Lz::oK);
   T* Vs = reinterpret_cast<T*>(smem + Lz::oV);
-  float* Af = reinterpret_cast<float*>(smem + Lz::oA);
-  T* Tp = reinterpret_cast<T*>(smem + Lz::oA);
+  T* Tp = reinterpret_cast<T*>(smem + Lz::oT);
   T* Tpp = Tp + BLK * LDC;
   const GateLds G = gate_lds(smem + Lz::oG);
 
@@ -274,15 +332,12 @@ __global__ __launch_bounds__(64 * fwd_nw<D>(), 2) void gdn_fwd_summary_kernel(Fw
     }
 
   Prefetch<T, D, false> pf;
-  if (blk0 < blk1) pf.fetch(nullptr, k, v, al, bt, rs, a.H, blk0 * BLK, min(BLK, a.T - blk0 * BLK));
+  if (blk0 < blk1)
+    pf.fetch(nullptr, k, v, al, bt, tw_block<T>(a.tw, a.nblk, bh, blk0), rs, a.H, blk0 * BLK,
+             min(BLK, a.T - blk0 * BLK));
   for (int blk = blk0; blk < blk1; ++blk) {
     const int t0 = blk * BLK, nv = min(BLK, a.T - t0);
-    pf.stage(nullptr, Ks, Vs, LDD, nv, G);
-    lds_barrier();
-    block_scores<T, D, NW, false>(nullptr, Ks, LDD, G, Af, LDF, nullptr, LDC);
-    lds_barrier();
-    block_solve(Af, Tm, LDF);
-    block_tprime<T, 64 * NW>(Tm, LDF, G, Tp, Tpp, LDC);
+    pf.stage(nullptr, Ks, Vs, Tp, Tpp, LDD, LDC, nv, G);
     lds_barrier();
     block_w<T, D, NW>(Ks, LDD, Tp, LDC, Wn);
     f32x4 X[NDV][4];
@@ -309,7 +364,9 @@ __global__ __launch_bounds__(64 * fwd_nw<D>(), 2) void gdn_fwd_summary_kernel(Fw
 #pragma unroll
       for (int aa = 0; aa < DKT; ++aa) Mt[bb][aa] *= gc;
     block_state_write<T, D, NDV>(Ks, LDD, X, dsc, Mt);
-    if (blk + 1 < blk1) pf.fetch(nullptr, k, v, al, bt, rs, a.H, t0 + BLK, min(BLK, a.T - t0 - BLK));
+    if (blk + 1 < blk1)
+      pf.fetch(nullptr, k, v, al, bt, tw_block<T>(a.tw, a.nblk, bh, blk + 1), rs, a.H, t0 + BLK,
+               min(BLK, a.T - t0 - BLK));
     lds_barrier();
   }
 
@@ -416,11 +473,22 @@ template <typename T, int D>
 hipError_t launch_fwd_summary(const FwdArgs& a, int nseg, hipStream_t st, Profiler* prof,
                               const char* name) {
   typedef FwdLds<T, D> Lz;
-  hipError_t e = set_lds((const void*)gdn_fwd_summary_kernel<T, D>, Lz::sum_bytes);
+  hipError_t e = set_lds((const void*)gdn_fwd_summary_kernel<T, D>, Lz::out_bytes);
   if (e != hipSuccess) return e;
   prof_begin(prof, name, st);
   hipLaunchKernelGGL((gdn_fwd_summary_kernel<T, D>), dim3(a.B * a.H * nseg), dim3(64 * fwd_nw<D>()),
-                     Lz::sum_bytes, st, a, nseg);
+                     Lz::out_bytes, st, a, nseg);
+  prof_end(prof, st);
+  return hipGetLastError();
+}
+
+template <typename T, int D>
+hipError_t launch_prep(const FwdArgs& a, hipStream_t st, Profiler* prof) {
+  typedef PrepLds<T, D> Lz;
+  hipError_t e = set_lds((const void*)gdn_prep_kernel<T, D>, Lz::bytes);
+  if (e != hipSuccess) return e;
+  prof_begin(prof, "gdn_prep", st);
+  hipLaunchKernelGGL((gdn_prep_kernel<T, D>), dim3(a.B * a.H * a.nblk), dim3(256), Lz::bytes, st, a);
   prof_end(prof, st);
   return hipGetLastError();
 }
@@ -453,6 +521,7 @@ hipError_t launch_fwd(const FwdArgs& a, void* hsave, hipStream_t st, Profiler* p
   typedef FwdLds<T, D> Lz;
   hipError_t e;
   const int BH = a.B * a.H;
+  if ((e = launch_prep<T, D>(a, st, prof)) != hipSuccess) return e;
   if (a.P > 1) {
     const int nseg = hsave ? a.P : a.P - 1;
     if ((e = launch_fwd_summary<T, D>(a, nseg, st, prof, "gdn_fwd_summary")) != hipSuccess) return e;
@@ -481,7 +550,8 @@ hipError_t launch_fwd(const FwdArgs& a, void* hsave, hipStream_t st, Profiler* p
 #define SF_INST(T, D)                                                                      \
   template hipError_t launch_fwd<T, D>(const FwdArgs&, void*, hipStream_t, Profiler*);  \
   template hipError_t launch_fwd_summary<T, D>(const FwdArgs&, int, hipStream_t, Profiler*, const char*); \
-  template hipError_t launch_states<T, D>(const FwdArgs&, void*, hipStream_t, Profiler*);
+  template hipError_t launch_states<T, D>(const FwdArgs&, void*, hipStream_t, Profiler*);  \
+  template hipError_t launch_prep<T, D>(const FwdArgs&, hipStream_t, Profiler*);
 SF_INST(bf16, 128)
 SF_INST(bf16, 64)
 SF_INST(float, 64)

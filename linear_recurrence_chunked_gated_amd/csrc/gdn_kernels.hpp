@@ -27,6 +27,7 @@ struct FwdArgs {
   float* Nseg;         // [B*H][P][D][D]  segment zero-entry exit states
   const float* Sst;    // [B*H][sst_P][D][D] segment entry states (S_in when P == 1)
   int sst_P;
+  void* tw;            // [B*H][nblk][2][64][64] per-block Tp, Tpp (operand type), by the Pre kernel
 };
 
 struct ChainArgs {
@@ -66,12 +67,15 @@ hipError_t launch_fwd(const FwdArgs& a, void* hsave, hipStream_t st, Profiler* p
 template <typename T, int D>
 hipError_t launch_fwd_summary(const FwdArgs& a, int nseg, hipStream_t st, Profiler* prof,
                               const char* name);
+template <typename T, int D>
+hipError_t launch_prep(const FwdArgs& a, hipStream_t st, Profiler* prof);
 template <int D>
 hipError_t launch_chain_fwd(const ChainArgs& c, int BH, hipStream_t st, Profiler* prof);
 template <typename T, int D>
 hipError_t launch_states(const FwdArgs& a, void* hst, hipStream_t st, Profiler* prof);
-// saved: a.hst already holds every block's entry state and a.f.Mseg every
-// segment's map (from a saving forward), so the forward recompute is skipped.
+// saved: a.hst already holds every block's entry state, a.f.Mseg every
+// segment's map and a.f.tw every block's Tp, Tpp (from a saving forward), so
+// the forward recompute is skipped.
 template <typename T, int D>
 hipError_t launch_bwd(const BwdArgs& a, bool saved, hipStream_t st, Profiler* prof);
 

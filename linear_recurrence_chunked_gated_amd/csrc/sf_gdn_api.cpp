@@ -81,14 +81,18 @@ sf_status make_plan(const sf_gdn_shape* s, Plan& p) {
 
 size_t dd(const Plan& p) { return (size_t)p.D * p.D; }
 size_t seg_buf(const Plan& p) { return align_up((size_t)p.B * p.H * p.P * dd(p) * sizeof(float)); }
-size_t fwd_ws(const Plan& p) { return p.P > 1 ? 3 * seg_buf(p) : 0; }
+size_t elem(const Plan& p) { return p.dtype == SF_DTYPE_BF16 ? 2 : 4; }
+// per-block Tp, Tpp of the Pre kernel: [B*H][nblk][2][64][64] in the operand type
+size_t tw_buf(const Plan& p) {
+  return align_up((size_t)p.B * p.H * p.nblk * 2 * BLK * BLK * elem(p));
+}
+size_t fwd_seg(const Plan& p) { return p.P > 1 ? 3 * seg_buf(p) : 0; }
+size_t fwd_ws(const Plan& p) { return fwd_seg(p) + tw_buf(p); }
 size_t blk_buf(const Plan& p) { return align_up((size_t)p.B * p.H * p.nblk * dd(p) * p.state_elem); }
 size_t bwd_ws(const Plan& p) {
   if (p.P == 0) return 0;
-  return 3 * seg_buf(p) + 2 * seg_buf(p) + 2 * blk_buf(p);
+  return 3 * seg_buf(p) + 2 * seg_buf(p) + 2 * blk_buf(p) + tw_buf(p);
 }
-
-size_t elem(const Plan& p) { return p.dtype == SF_DTYPE_BF16 ? 2 : 4; }
 
 struct Range {
   const void* p;
@@ -202,13 +206,17 @@ sf_status sf_gdn_chunk_bwd_workspace_size(const sf_gdn_shape* shape, size_t* byt
 
 namespace {
 
+// Layout: per-block entry states [B*H*nblk][D][D], the segment maps
+// [B*H*P][D][D] (P > 1), then the Pre kernel's per-block Tp, Tpp.
+size_t saved_maps_off(const Plan& p) { return blk_buf(p); }
+size_t saved_tw_off(const Plan& p) { return blk_buf(p) + (p.P > 1 ? seg_buf(p) : 0); }
 size_t saved_bytes(const Plan& p) {
   if (p.P == 0) return 0;
-  return blk_buf(p) + (p.P > 1 ? seg_buf(p) : 0);
+  return saved_tw_off(p) + tw_buf(p);
 }
 
-// Forward; with `saved` it also stores the per-block entry states and all
-// segment maps (layout: [B*H*nblk][D][D] states, then [B*H*P][D][D] maps).
+// Forward; with `saved` it also stores the per-block entry states, all
+// segment maps and the per-block Tp, Tpp there.
 sf_status fwd_impl(const sf_gdn_shape* shape, const void* q, const void* k, const void* v,
                    const float* alpha, const float* beta, const float* S_in, void* o,
                    float* S_out, void* saved, size_t sv_bytes, void* workspace, size_t ws_bytes,
@@ -255,8 +263,9 @@ sf_status fwd_impl(const sf_gdn_shape* shape, const void* q, const void* k, cons
     a.B = p.B; a.T = p.T; a.H = p.H; a.nblk = p.nblk; a.L = p.L; a.P = p.P;
     char* ws = (char*)workspace;
     void* hsave = save ? saved : nullptr;
+    a.tw = save ? (char*)saved + saved_tw_off(p) : ws + fwd_seg(p);
     if (p.P > 1) {
-      a.Mseg = save ? (float*)((char*)saved + blk_buf(p)) : (float*)ws;
+      a.Mseg = save ? (float*)((char*)saved + saved_maps_off(p)) : (float*)ws;
       a.Nseg = (float*)(ws + seg_buf(p));
       a.Sst = (float*)(ws + 2 * seg_buf(p));
       a.sst_P = p.P;
@@ -335,9 +344,12 @@ sf_status bwd_impl(const sf_gdn_shape* shape, const void* q, const void* k, cons
     a.dSend = (float*)(ws + 4 * sb);
     a.hst = ws + 5 * sb;
     a.dhst = ws + 5 * sb + bb;
+    f.tw = ws + 5 * sb + 2 * bb;
     if (use_saved) {
-      a.hst = const_cast<void*>(saved);
-      if (p.P > 1) f.Mseg = (float*)((char*)const_cast<void*>(saved) + bb);
+      char* sv = (char*)const_cast<void*>(saved);
+      a.hst = sv;
+      if (p.P > 1) f.Mseg = (float*)(sv + saved_maps_off(p));
+      f.tw = sv + saved_tw_off(p);
     }
     a.dO = dO; a.dS_out = dS_out;
     a.dq = dq; a.dk = dk; a.dv = dv; a.dalpha = dalpha; a.dbeta = dbeta; a.dS_in = dS_in;

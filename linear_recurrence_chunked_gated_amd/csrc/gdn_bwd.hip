@@ -301,18 +301,42 @@ __global__ __launch_bounds__(256) void gdn_chain_bwd_kernel(const float* dS_out,
 // Sums of a 16x16 accumulator tile C[m][n] (lane: m = 4 g + e, n = i):
 // over n for each m (result valid in lanes with i == 0, element e), and over
 // m for each n (result valid in lanes 0..15).
+// Cross-lane sums without an LDS round trip: DPP within a 16-lane row, and
+// the gfx950 lane swaps (v_permlane16/32_swap) across rows.  Every lane of a
+// group ends with the same total.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+// sum over the 16 lanes of a row (quad_perm [1,0,3,2], [2,3,0,1], half-row
+// mirror, row mirror)
+__device__ __forceinline__ float sum_row16(float x) {
+  x += dpp_f<0xB1>(x);
+  x += dpp_f<0x4E>(x);
+  x += dpp_f<0x141>(x);
+  x += dpp_f<0x140>(x);
+  return x;
+}
+// sum over the 4 rows (lanes l, l^16, l^32, l^48)
+__device__ __forceinline__ float sum_rows4(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
 __device__ __forceinline__ f32x4 tile_sum_over_n(f32x4 v) {
 #pragma unroll
-  for (int off = 1; off < 16; off <<= 1)
-#pragma unroll
-    for (int e = 0; e < 4; ++e) v[e] += __shfl_xor(v[e], off, 64);
+  for (int e = 0; e < 4; ++e) v[e] = sum_row16(v[e]);
   return v;
 }
 __device__ __forceinline__ float tile_sum_over_m(f32x4 v) {
-  float x = (v[0] + v[1]) + (v[2] + v[3]);
-  x += __shfl_xor(x, 16, 64);
-  x += __shfl_xor(x, 32, 64);
-  return x;
+  return sum_rows4((v[0] + v[1]) + (v[2] + v[3]));
+}
+// *p += x in LDS without waiting for the old value (ds_add_f32).  The partial
+// arrays are per wave, so the order of the additions is this wave's program
+// order and the sums stay deterministic.
+__device__ __forceinline__ void lds_add(float* p, float x) {
+  __hip_atomic_fetch_add(p, x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
 }
 // part[m0 + m] += sum over n   (one writer lane per entry)
 __device__ __forceinline__ void add_rows(float* part, int m0, f32x4 v, float sign = 1.f) {
@@ -321,14 +345,14 @@ __device__ __forceinline__ void add_rows(float* part, int m0, f32x4 v, float sig
   if ((lane & 15) == 0) {
     float* p = part + m0 + 4 * (lane >> 4);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) p[e] += sign * v[e];
+    for (int e = 0; e < 4; ++e) lds_add(p + e, sign * v[e]);
   }
 }
 // part[n0 + n] += sum over m
 __device__ __forceinline__ void add_cols(float* part, int n0, f32x4 v, float sign = 1.f) {
   const float x = tile_sum_over_m(v);
   const int lane = lane_id();
-  if (lane < 16) part[n0 + lane] += sign * x;
+  if (lane < 16) lds_add(part + n0 + lane, sign * x);
 }
 
 // LDS plan of the gradient kernel (regions reused by phase):
@@ -405,27 +429,24 @@ __global__ __launch_bounds__(4 * D, 2) void gdn_bwd_grads_kernel(BwdArgs a) {
   const T* hS = reinterpret_cast<const T*>(a.hst) + ((size_t)bh * f.nblk + blk) * D * D;
   const T* hG = reinterpret_cast<const T*>(a.dhst) + ((size_t)bh * f.nblk + blk) * D * D;
 
-  // ---- A: inputs, states (by dv-tile), partial sums
+  // ---- A: inputs, states (by dv-tile), partial sums.  Q, K and the gates
+  // are staged now; V and dO (first used after the solve) stay in flight in
+  // registers until then.
+  typedef Tile<T, D, 4 * D> Tl;
+  uint4 r2[Tl::NCH], r3[Tl::NCH];
   {
-    typedef Tile<T, D, 4 * D> Tl;
-    uint4 r0[Tl::NCH], r1[Tl::NCH], r2[Tl::NCH], r3[Tl::NCH];
+    // issue order = wait order (vmcnt counts in order): gates, q, k, then v, dO
+    const size_t gidx = gofs + (size_t)min(lane, nv - 1) * f.H;
+    const float ra = f.alpha[gidx], rb = f.beta[gidx];
+    uint4 r0[Tl::NCH], r1[Tl::NCH];
     Tl::load(r0, q, rs, nv);
     Tl::load(r1, k, rs, nv);
     Tl::load(r2, v, rs, nv);
     Tl::load(r3, dO, rs, nv);
-    float la = 0.f, be = 0.f;
-    if (w == 0) {
-      const size_t idx = (size_t)min(lane, nv - 1) * f.H;
-      const float x = f.alpha[gofs + idx], y = f.beta[gofs + idx];
-      la = lane < nv ? __logf(x) : 0.f;
-      be = lane < nv ? y : 0.f;
-    }
     for (int i = threadIdx.x; i < 3 * NW * BLK + NW + 4; i += 64 * NW) part[i] = 0.f;
     Tl::to_lds(r0, Qs, LDD, nv);
     Tl::to_lds(r1, Ks, LDD, nv);
-    Tl::to_lds(r2, Vs, LDD, nv);
-    Tl::to_lds(r3, Os, LDD, nv);
-    if (w == 0) block_gates(la, be, G);
+    if (w == 0) block_gates(lane < nv ? __logf(ra) : 0.f, lane < nv ? rb : 0.f, G);
   }
   f32x4 Sx[DKT], dSx[DKT];  // by dv-tile: m = dk-tile, n = dv-tile w
 #pragma unroll
@@ -434,16 +455,6 @@ __global__ __launch_bounds__(4 * D, 2) void gdn_bwd_grads_kernel(BwdArgs a) {
     Sx[aa] = ld4f(hS + off);
     dSx[aa] = ld4f(hG + off);
   }
-  {
-    f32x4 p = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int aa = 0; aa < DKT; ++aa) p += Sx[aa] * dSx[aa];
-    float x = (p[0] + p[1]) + (p[2] + p[3]);
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) x += __shfl_xor(x, off, 64);
-    lds_barrier();  // partial arrays zeroed
-    if (lane == 0) dgc[w] = x;
-  }
   lds_barrier();
   // ---- B: scores
   block_scores<T, D, NW, true>(Qs, Ks, LDD, G, Af, LDF, Pl, LDC);
@@ -451,6 +462,8 @@ __global__ __launch_bounds__(4 * D, 2) void gdn_bwd_grads_kernel(BwdArgs a) {
   // ---- C: T = (I + A)^{-1}, Tp, Tpp; zero Tm's upper blocks (solve scratch)
   block_solve(Af, Tm, LDF);
   block_tprime<T, 64 * NW>(Tm, LDF, G, Tp, Tpp, LDC);
+  Tl::to_lds(r2, Vs, LDD, nv);
+  Tl::to_lds(r3, Os, LDD, nv);
   lds_barrier();
   for (int i = threadIdx.x; i < BLK * BLK; i += 64 * NW) {
     const int r = i >> 6, s = i & 63;
@@ -461,7 +474,17 @@ __global__ __launch_bounds__(4 * D, 2) void gdn_bwd_grads_kernel(BwdArgs a) {
   f32x4 U[1][4];
   block_u<T, 1>(Tpp, LDC, Vs, LDD, w, U);
   lds_barrier();
-  // ---- E: Vn = U - W S^T (registers), then to LDS
+  // ---- E: <dS', S> of this wave's rows (for the gate of the block end);
+  // Vn = U - W S^T (registers), then to LDS
+  {
+    f32x4 p = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int aa = 0; aa < DKT; ++aa) p += Sx[aa] * dSx[aa];
+    float x = (p[0] + p[1]) + (p[2] + p[3]);
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) x += __shfl_xor(x, off, 64);
+    if (lane == 0) dgc[w] = x;
+  }
   {
     f32x4 Sv[1][DKT];
 #pragma unroll
@@ -660,8 +683,8 @@ __global__ __launch_bounds__(4 * D, 2) void gdn_bwd_grads_kernel(BwdArgs a) {
       store_tile_N(dt, dTf, LDF, 16 * rt, 16 * (s0t + j));
       const float sbg = tile_sum_over_m(c1), sb2 = tile_sum_over_m(c2);
       if (lane < 16) {
-        dbp[s] += sb2 + gs * sbg;
-        dgp[s] += bs * gs * sbg;
+        lds_add(dbp + s, sb2 + gs * sbg);
+        lds_add(dgp + s, bs * gs * sbg);
       }
     }
   }

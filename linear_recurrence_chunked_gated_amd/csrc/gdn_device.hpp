@@ -71,6 +71,7 @@ template <> struct Mma<float> {
 template <typename T> struct Lay {
   static constexpr int VEC = 16 / sizeof(T);  // elements per 16-byte chunk
   static constexpr int PAD = VEC;             // row padding (elements)
+  typedef T pack4 __attribute__((ext_vector_type(4)));
 };
 
 // ---------------------------------------------------------------- frags ----

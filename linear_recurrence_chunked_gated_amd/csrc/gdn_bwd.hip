@@ -223,7 +223,7 @@ __global__ __launch_bounds__(4 * D, 2) void gdn_bwd_dscan_kernel(BwdArgs a, int 
 // Exit gradients of all segments: dSend[P-1] = dS_out (or 0),
 // dSend[j-1] = dSend[j] M_j^T + NB_j.  Same layout as the forward chain.
 template <int D>
-__global__ __launch_bounds__(256) void gdn_chain_bwd_kernel(const float* dS_out, const float* Mseg,
+__global__ __launch_bounds__(256) void gdn_chain_bwd_kernel(const float* dS_out, const float* MTseg,
                                                             const float* NBseg, float* dSend,
                                                             int P) {
   constexpr int RT = D / 16, NT = D / 64, KS = D / 4, LDS_ = D + 4;
@@ -241,13 +241,13 @@ __global__ __launch_bounds__(256) void gdn_chain_bwd_kernel(const float* dS_out,
   }
   float bm[NT][KS], nn[NT][4];
   auto load_map = [&](int j, float (&m)[NT][KS], float (&n)[NT][4]) {
-    const float* M = Mseg + ((size_t)bh * P + j) * DD;
+    const float* MT = MTseg + ((size_t)bh * P + j) * DD;  // MT[k][n] = M[n][k]
     const float* N = NBseg + ((size_t)bh * P + j) * DD;
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
       const int col = 16 * (w * NT + t) + (lane & 15);
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) m[t][ks] = M[(size_t)col * D + 4 * ks + (lane >> 4)];
+      for (int ks = 0; ks < KS; ++ks) m[t][ks] = MT[(size_t)(4 * ks + (lane >> 4)) * D + col];
 #pragma unroll
       for (int e = 0; e < 4; ++e) n[t][e] = N[(size_t)(r0 + 4 * (lane >> 4) + e) * D + col];
     }
@@ -836,7 +836,7 @@ hipError_t launch_bwd(const BwdArgs& a0, bool saved, hipStream_t st, Profiler* p
     }
     prof_begin(prof, "gdn_chain_bwd", st);
     hipLaunchKernelGGL((gdn_chain_bwd_kernel<D>), dim3(BH * (D / 16)), dim3(256), 0, st, a.dS_out,
-                       f.Mseg, a.NBseg, a.dSend, P);
+                       f.MTseg, a.NBseg, a.dSend, P);
     prof_end(prof, st);
     dSend = a.dSend;
     dsend_P = P;

@@ -373,6 +373,7 @@ __global__ __launch_bounds__(64 * fwd_nw<D>(), 2) void gdn_fwd_summary_kernel(Fw
   // Nt holds N^T (m = dk, n = dv) -> N[dv][dk..]; Mt holds M^T (m = j, n = i) -> M[i][j..].
   float* Mo = a.Mseg + ((size_t)bh * a.P + seg) * D * D;
   float* No = a.Nseg + ((size_t)bh * a.P + seg) * D * D;
+  float* MTo = a.MTseg ? a.MTseg + ((size_t)bh * a.P + seg) * D * D : nullptr;
 #pragma unroll
   for (int bb = 0; bb < NDV; ++bb)
 #pragma unroll
@@ -380,6 +381,11 @@ __global__ __launch_bounds__(64 * fwd_nw<D>(), 2) void gdn_fwd_summary_kernel(Fw
       const size_t off = (size_t)(16 * (dv0 + bb) + li) * D + 16 * aa + g4;
       *reinterpret_cast<f32x4*>(No + off) = Nt[bb][aa];
       *reinterpret_cast<f32x4*>(Mo + off) = Mt[bb][aa];
+      if (MTo) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          MTo[(size_t)(16 * aa + g4 + e) * D + 16 * (dv0 + bb) + li] = Mt[bb][aa][e];
+      }
     }
 }
 

@@ -24,6 +24,7 @@ struct FwdArgs {
   int nblk, L, P;
   // workspace
   float* Mseg;         // [B*H][P][D][D]  segment transition maps
+  float* MTseg;        // [B*H][P][D][D]  the same maps transposed (for the backward), or null
   float* Nseg;         // [B*H][P][D][D]  segment zero-entry exit states
   const float* Sst;    // [B*H][sst_P][D][D] segment entry states (S_in when P == 1)
   int sst_P;
@@ -73,9 +74,9 @@ template <int D>
 hipError_t launch_chain_fwd(const ChainArgs& c, int BH, hipStream_t st, Profiler* prof);
 template <typename T, int D>
 hipError_t launch_states(const FwdArgs& a, void* hst, hipStream_t st, Profiler* prof);
-// saved: a.hst already holds every block's entry state, a.f.Mseg every
-// segment's map and a.f.tw every block's Tp, Tpp (from a saving forward), so
-// the forward recompute is skipped.
+// saved: a.hst already holds every block's entry state, a.f.MTseg every
+// segment's transposed map and a.f.tw every block's Tp, Tpp (from a saving
+// forward), so the forward recompute is skipped.
 template <typename T, int D>
 hipError_t launch_bwd(const BwdArgs& a, bool saved, hipStream_t st, Profiler* prof);
 

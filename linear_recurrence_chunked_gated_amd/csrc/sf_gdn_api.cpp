@@ -91,7 +91,7 @@ size_t fwd_ws(const Plan& p) { return fwd_seg(p) + tw_buf(p); }
 size_t blk_buf(const Plan& p) { return align_up((size_t)p.B * p.H * p.nblk * dd(p) * p.state_elem); }
 size_t bwd_ws(const Plan& p) {
   if (p.P == 0) return 0;
-  return 3 * seg_buf(p) + 2 * seg_buf(p) + 2 * blk_buf(p) + tw_buf(p);
+  return 3 * seg_buf(p) + 3 * seg_buf(p) + 2 * blk_buf(p) + tw_buf(p);
 }
 
 struct Range {
@@ -206,8 +206,8 @@ sf_status sf_gdn_chunk_bwd_workspace_size(const sf_gdn_shape* shape, size_t* byt
 
 namespace {
 
-// Layout: per-block entry states [B*H*nblk][D][D], the segment maps
-// [B*H*P][D][D] (P > 1), then the Pre kernel's per-block Tp, Tpp.
+// Layout: per-block entry states [B*H*nblk][D][D], the transposed segment
+// maps [B*H*P][D][D] (P > 1), then the Pre kernel's per-block Tp, Tpp.
 size_t saved_maps_off(const Plan& p) { return blk_buf(p); }
 size_t saved_tw_off(const Plan& p) { return blk_buf(p) + (p.P > 1 ? seg_buf(p) : 0); }
 size_t saved_bytes(const Plan& p) {
@@ -265,7 +265,8 @@ sf_status fwd_impl(const sf_gdn_shape* shape, const void* q, const void* k, cons
     void* hsave = save ? saved : nullptr;
     a.tw = save ? (char*)saved + saved_tw_off(p) : ws + fwd_seg(p);
     if (p.P > 1) {
-      a.Mseg = save ? (float*)((char*)saved + saved_maps_off(p)) : (float*)ws;
+      a.Mseg = (float*)ws;
+      a.MTseg = save ? (float*)((char*)saved + saved_maps_off(p)) : nullptr;
       a.Nseg = (float*)(ws + seg_buf(p));
       a.Sst = (float*)(ws + 2 * seg_buf(p));
       a.sst_P = p.P;
@@ -345,10 +346,11 @@ sf_status bwd_impl(const sf_gdn_shape* shape, const void* q, const void* k, cons
     a.hst = ws + 5 * sb;
     a.dhst = ws + 5 * sb + bb;
     f.tw = ws + 5 * sb + 2 * bb;
+    f.MTseg = (float*)(ws + 5 * sb + 2 * bb + tw_buf(p));
     if (use_saved) {
       char* sv = (char*)const_cast<void*>(saved);
       a.hst = sv;
-      if (p.P > 1) f.Mseg = (float*)(sv + saved_maps_off(p));
+      if (p.P > 1) f.MTseg = (float*)(sv + saved_maps_off(p));
       f.tw = sv + saved_tw_off(p);
     }
     a.dO = dO; a.dS_out = dS_out;

@@ -380,6 +380,9 @@ template <typename T, int D> struct GradLds {
   static constexpr size_t bytes = oPart + zPart;
   static_assert(bytes <= 160 * 1024, "LDS budget");
   static_assert(!DVN_IN_A || sq64 >= rowD, "dVn must fit the Tpp half");
+  // a [D][LDD] copy of the state fits V+dO and W+dVn (adjacent regions)
+  static constexpr size_t zS = (size_t)D * LDD * sizeof(T);
+  static_assert(oO + zR - oV >= zS && (oD + zD) - oW >= zS, "state copies");
 };
 
 template <typename T, int D>
@@ -459,9 +462,29 @@ __global__ __launch_bounds__(4 * D, 2) void gdn_bwd_grads_kernel(BwdArgs a) {
   // ---- B: scores
   block_scores<T, D, NW, true>(Qs, Ks, LDD, G, Af, LDF, Pl, LDC);
   lds_barrier();
-  // ---- C: T = (I + A)^{-1}, Tp, Tpp; zero Tm's upper blocks (solve scratch)
-  block_solve(Af, Tm, LDF);
+  // ---- C: T = (I + A)^{-1}, Tp, Tpp; zero Tm's upper blocks (solve scratch).
+  // Meanwhile S and dS' go through LDS once, so that every wave also holds
+  // them by dk-tile (S^T, dS'^T rows 16 w .. as operands over dv, for dQ, dW
+  // and dK2): copies [dv][dk] in the V/dO and W/dVn regions, which are free
+  // until V, dO are staged and W is formed.
+  T* Sc = reinterpret_cast<T*>(smem + Lz::oV);
+  T* Gc = reinterpret_cast<T*>(smem + Lz::oW);
+#pragma unroll
+  for (int aa = 0; aa < DKT; ++aa) {
+    const int off = (16 * w + li) * LDD + 16 * aa + g4;
+    st4(Sc + off, Sx[aa][0], Sx[aa][1], Sx[aa][2], Sx[aa][3]);
+    st4(Gc + off, dSx[aa][0], dSx[aa][1], dSx[aa][2], dSx[aa][3]);
+  }
+  block_solve(Af, Tm, LDF);  // its first barrier publishes the copies
+  constexpr int KST = D / Mma<T>::KSTEP;
+  typename Mma<T>::frag skf[KST], gkf[KST];
+#pragma unroll
+  for (int s = 0; s < KST; ++s) {
+    skf[s] = frag_tr<T, PERM>(Sc + 16 * w, LDD, s);
+    gkf[s] = frag_tr<T, PERM>(Gc + 16 * w, LDD, s);
+  }
   block_tprime<T, 64 * NW>(Tm, LDF, G, Tp, Tpp, LDC);
+  lds_barrier();  // copies read before V and dO replace them
   Tl::to_lds(r2, Vs, LDD, nv);
   Tl::to_lds(r3, Os, LDD, nv);
   lds_barrier();
@@ -573,11 +596,6 @@ __global__ __launch_bounds__(4 * D, 2) void gdn_bwd_grads_kernel(BwdArgs a) {
   }
   lds_barrier();
   // ---- H: dQ^T = diag-scaled (S^T dO^T) + K^T dPm^T  (wave: dk-tile w); dK^T starts
-  f32x4 Sk[DKT];  // by dk-tile: m = dv-tile, n = dk-tile w
-#pragma unroll
-  for (int bb = 0; bb < DKT; ++bb)
-#pragma unroll
-    for (int e = 0; e < 4; ++e) Sk[bb][e] = (float)hS[(size_t)(16 * bb + g4 + e) * D + 16 * w + li];
   f32x4 dKt[4];
   {
     f32x4 acc[4];
@@ -585,9 +603,9 @@ __global__ __launch_bounds__(4 * D, 2) void gdn_bwd_grads_kernel(BwdArgs a) {
     for (int j = 0; j < 4; ++j) acc[j] = dKt[j] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int s = 0; s < D / Mma<T>::KSTEP; ++s) {
-      const auto as = AccFrag<T>::get(Sk, s);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) acc[j] = Mma<T>::mma(as, frag_row<T, PERM>(Os + 16 * j * LDD, LDD, s), acc[j]);
+      for (int j = 0; j < 4; ++j)
+        acc[j] = Mma<T>::mma(skf[s], frag_row<T, PERM>(Os + 16 * j * LDD, LDD, s), acc[j]);
     }
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -619,22 +637,15 @@ __global__ __launch_bounds__(4 * D, 2) void gdn_bwd_grads_kernel(BwdArgs a) {
   lds_barrier();  // dO reads done: its region takes dW
   // ---- I: dW^T = -(S^T dVn^T) -> dW row-major ; dK2^T = dS'^T Vn^T scaled by D ; D-term
   {
-    f32x4 dSk[DKT];
-#pragma unroll
-    for (int bb = 0; bb < DKT; ++bb)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) dSk[bb][e] = (float)hG[(size_t)(16 * bb + g4 + e) * D + 16 * w + li];
     f32x4 acc[4], x2[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[j] = x2[j] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int s = 0; s < D / Mma<T>::KSTEP; ++s) {
-      const auto as = AccFrag<T>::get(Sk, s);
-      const auto ag = AccFrag<T>::get(dSk, s);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        acc[j] = Mma<T>::mma(as, frag_row<T, PERM>(dVns + 16 * j * LDD, LDD, s), acc[j]);
-        x2[j] = Mma<T>::mma(ag, frag_row<T, PERM>(Vns + 16 * j * LDD, LDD, s), x2[j]);
+        acc[j] = Mma<T>::mma(skf[s], frag_row<T, PERM>(dVns + 16 * j * LDD, LDD, s), acc[j]);
+        x2[j] = Mma<T>::mma(gkf[s], frag_row<T, PERM>(Vns + 16 * j * LDD, LDD, s), x2[j]);
       }
     }
 #pragma unroll

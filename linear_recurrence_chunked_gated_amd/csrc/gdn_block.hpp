@@ -245,19 +245,44 @@ __device__ __forceinline__ void block_u(const T* Tpp, int ldc, const T* Vs, int 
 // acc[b][i] (m = s-tile i, n = dv-tile b) += X[s][:] . St[b]^T where the state
 // tiles St[b][a] hold S^T (m = dk-tile a, n = dv-tile b) in registers; X is a
 // row-major [s][dk] LDS tile (here -W).  Gives Vn = U - W S^T.
-template <typename T, int D, int NDV>
+// PF: load the next k-step's operands before the current step's products
+// (a scheduling barrier keeps the order), for kernels with registers to spare.
+template <typename T, int D, int NDV, bool PF = false>
 __device__ __forceinline__ void block_x_st(const T* X, int ldd, const f32x4 (&St)[NDV][D / 16],
                                            f32x4 (&acc)[NDV][4]) {
+  constexpr int KS = D / Mma<T>::KSTEP;
+  if constexpr (PF) {
+    typename Mma<T>::frag a[2][4];
 #pragma unroll
-  for (int s = 0; s < D / Mma<T>::KSTEP; ++s) {
-    typename Mma<T>::frag bs[NDV];
+    for (int i = 0; i < 4; ++i) a[0][i] = frag_row<T, PERM>(X + 16 * i * ldd, ldd, 0);
 #pragma unroll
-    for (int b = 0; b < NDV; ++b) bs[b] = AccFrag<T>::get(St[b], s);
+    for (int s = 0; s < KS; ++s) {
+      if (s + 1 < KS) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const auto a = frag_row<T, PERM>(X + 16 * i * ldd, ldd, s);
+        for (int i = 0; i < 4; ++i)
+          a[(s + 1) & 1][i] = frag_row<T, PERM>(X + 16 * i * ldd, ldd, s + 1);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      typename Mma<T>::frag bs[NDV];
 #pragma unroll
-      for (int b = 0; b < NDV; ++b) acc[b][i] = Mma<T>::mma(a, bs[b], acc[b][i]);
+      for (int b = 0; b < NDV; ++b) bs[b] = AccFrag<T>::get(St[b], s);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int b = 0; b < NDV; ++b) acc[b][i] = Mma<T>::mma(a[s & 1][i], bs[b], acc[b][i]);
+    }
+  } else {
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      typename Mma<T>::frag bs[NDV];
+#pragma unroll
+      for (int b = 0; b < NDV; ++b) bs[b] = AccFrag<T>::get(St[b], s);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const auto a = frag_row<T, PERM>(X + 16 * i * ldd, ldd, s);
+#pragma unroll
+        for (int b = 0; b < NDV; ++b) acc[b][i] = Mma<T>::mma(a, bs[b], acc[b][i]);
+      }
     }
   }
 }
@@ -283,40 +308,82 @@ __device__ __forceinline__ void block_s_yT(const f32x4 (&St)[NDV][D / 16], const
 
 // acc[b][j] (m = dv-tile b, n = r-tile j) += Vn^T[dv][:] . P[r][:] with Vn in
 // register tiles vn[b][s-tile] and P a row-major [r][s] LDS tile.
-template <typename T, int NDV>
+template <typename T, int NDV, bool PF = false>
 __device__ __forceinline__ void block_vnT_pT(const f32x4 (&vn)[NDV][4], const T* Pl, int ldc,
                                              f32x4 (&acc)[NDV][4]) {
+  constexpr int KS = BLK / Mma<T>::KSTEP;
+  typename Mma<T>::frag bp[KS][4];
 #pragma unroll
-  for (int s = 0; s < BLK / Mma<T>::KSTEP; ++s) {
-    typename Mma<T>::frag bp[4];
+  for (int s = 0; s < KS; ++s) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) bp[j] = frag_row<T, PERM>(Pl + 16 * j * ldc, ldc, s);
+    for (int j = 0; j < 4; ++j) bp[s][j] = frag_row<T, PERM>(Pl + 16 * j * ldc, ldc, s);
+    if constexpr (!PF) {
 #pragma unroll
-    for (int b = 0; b < NDV; ++b) {
-      const auto a = AccFrag<T>::get(vn[b], s);
+      for (int b = 0; b < NDV; ++b) {
+        const auto a = AccFrag<T>::get(vn[b], s);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) acc[b][j] = Mma<T>::mma(a, bp[j], acc[b][j]);
+        for (int j = 0; j < 4; ++j) acc[b][j] = Mma<T>::mma(a, bp[s][j], acc[b][j]);
+      }
     }
+  }
+  if constexpr (PF) {
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int s = 0; s < KS; ++s)
+#pragma unroll
+      for (int b = 0; b < NDV; ++b) {
+        const auto a = AccFrag<T>::get(vn[b], s);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[b][j] = Mma<T>::mma(a, bp[s][j], acc[b][j]);
+      }
   }
 }
 
 // St[b][a] (m = dk-tile a, n = dv-tile b) += K^T[dk][:] . (D Vn)^T[dv][:]:
 // the state update's write term Vn^T D K, with K^T through the transpose read
 // from the row-major K tile and D Vn from the register tiles vn scaled by dsc.
-template <typename T, int D, int NDV>
+template <typename T, int D, int NDV, bool PF = false>
 __device__ __forceinline__ void block_state_write(const T* Ks, int ldd, const f32x4 (&vn)[NDV][4],
                                                   const f32x4 (&dsc)[4],
                                                   f32x4 (&St)[NDV][D / 16]) {
+  constexpr int KS = BLK / Mma<T>::KSTEP, NA = D / 16, HA = NA / 2;
+  if constexpr (PF) {
+    // K^T operands in two halves of the dk-tiles, the next half loading while
+    // the current one multiplies
+    typename Mma<T>::frag ka[2][HA];
 #pragma unroll
-  for (int s = 0; s < BLK / Mma<T>::KSTEP; ++s) {
-    typename Mma<T>::frag bv[NDV];
+    for (int a = 0; a < HA; ++a) ka[0][a] = frag_tr<T, PERM>(Ks + 16 * a, ldd, 0);
 #pragma unroll
-    for (int b = 0; b < NDV; ++b) bv[b] = AccFrag<T>::get_scaled(vn[b], dsc, s);
+    for (int st = 0; st < 2 * KS; ++st) {
+      const int s = st >> 1, half = st & 1;
+      if (st + 1 < 2 * KS) {
+        const int s1 = (st + 1) >> 1, h1 = (st + 1) & 1;
 #pragma unroll
-    for (int a = 0; a < D / 16; ++a) {
-      const auto ka = frag_tr<T, PERM>(Ks + 16 * a, ldd, s);
+        for (int a = 0; a < HA; ++a)
+          ka[(st + 1) & 1][a] = frag_tr<T, PERM>(Ks + 16 * (h1 * HA + a), ldd, s1);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      typename Mma<T>::frag bv[NDV];
 #pragma unroll
-      for (int b = 0; b < NDV; ++b) St[b][a] = Mma<T>::mma(ka, bv[b], St[b][a]);
+      for (int b = 0; b < NDV; ++b) bv[b] = AccFrag<T>::get_scaled(vn[b], dsc, s);
+#pragma unroll
+      for (int a = 0; a < HA; ++a)
+#pragma unroll
+        for (int b = 0; b < NDV; ++b)
+          St[b][half * HA + a] = Mma<T>::mma(ka[st & 1][a], bv[b], St[b][half * HA + a]);
+    }
+  } else {
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      typename Mma<T>::frag bv[NDV];
+#pragma unroll
+      for (int b = 0; b < NDV; ++b) bv[b] = AccFrag<T>::get_scaled(vn[b], dsc, s);
+#pragma unroll
+      for (int a = 0; a < NA; ++a) {
+        const auto ka = frag_tr<T, PERM>(Ks + 16 * a, ldd, s);
+#pragma unroll
+        for (int b = 0; b < NDV; ++b) St[b][a] = Mma<T>::mma(ka, bv[b], St[b][a]);
+      }
     }
   }
 }

@@ -512,7 +512,7 @@ __global__ __launch_bounds__(4 * D, 2) void gdn_bwd_grads_kernel(BwdArgs a) {
     f32x4 Sv[1][DKT];
 #pragma unroll
     for (int aa = 0; aa < DKT; ++aa) Sv[0][aa] = Sx[aa];
-    block_x_st<T, D, 1>(Wn, LDD, Sv, U);
+    block_x_st<T, D, 1, true>(Wn, LDD, Sv, U);
   }
   lds_barrier();
 #pragma unroll

@@ -254,8 +254,8 @@ __global__ __launch_bounds__(64 * fwd_nw<D>(), 2) void gdn_fwd_out_kernel(FwdArg
     block_u<T, NDV>(Tpp, LDC, Vs, LDD, dv0, U);
     lds_barrier();
     // ST and Out: Vn = U - W S^T; O^T += Vn^T P^T; S' = gamma_C S + Vn^T D K
-    block_x_st<T, D, NDV>(Wn, LDD, St, U);
-    if constexpr (OUT) block_vnT_pT<T, NDV>(U, Pl, LDC, O);
+    block_x_st<T, D, NDV, true>(Wn, LDD, St, U);
+    if constexpr (OUT) block_vnT_pT<T, NDV, true>(U, Pl, LDC, O);
     f32x4 dsc[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -266,7 +266,7 @@ __global__ __launch_bounds__(64 * fwd_nw<D>(), 2) void gdn_fwd_out_kernel(FwdArg
     for (int bb = 0; bb < NDV; ++bb)
 #pragma unroll
       for (int aa = 0; aa < DKT; ++aa) St[bb][aa] *= gc;
-    block_state_write<T, D, NDV>(Ks, LDD, U, dsc, St);
+    block_state_write<T, D, NDV, true>(Ks, LDD, U, dsc, St);
     prev_t0 = t0;
     prev_nv = nv;
     // The next block's inputs: issued here so that they add no register

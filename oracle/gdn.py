@@ -25,7 +25,7 @@ def build(force=True):
         return _LIB
     tmp = _LIB + ".tmp%d" % os.getpid()
     cmd = ["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared", "-Wall",
-           "-o", tmp, _SRC]
+           "-o", tmp, _SRC, "-lm"]
     subprocess.run(cmd, check=True)
     os.replace(tmp, _LIB)
     return _LIB
@@ -45,6 +45,10 @@ def _load():
     lib.oracle_gdn_bwd.restype = i
     lib.oracle_gdn_bwd.argtypes = [i, i, i, i, i, dp, dp, dp, dp, dp, dp, dp, dp,
                                    dp, dp, dp, dp, dp, dp, i]
+    lib.oracle_shortconv_fwd.restype = None
+    lib.oracle_shortconv_fwd.argtypes = [i, i, i, i, i, dp, dp, dp, dp, dp]
+    lib.oracle_shortconv_bwd.restype = None
+    lib.oracle_shortconv_bwd.argtypes = [i, i, i, i, i, dp, dp, dp, dp, dp, dp, dp, dp]
     _lib = lib
     return lib
 
@@ -151,3 +155,33 @@ def gdn_bwd_chained(q, k, v, alpha, beta, S_in, dO, dS_out, lengths, nthreads=0)
         dq[:, sl], dk[:, sl], dv[:, sl], da[:, sl], db[:, sl] = r[:5]
         G = r[5]
     return dq, dk, dv, da, db, G
+
+
+def shortconv_fwd(x, w, conv_in=None, act=0):
+    """Causal depthwise convolution of one chunk with its boundary state.
+    x: [B,T,C]; w: [C,W]; conv_in: [B,W-1,C] or None (zeros).
+    Returns (y [B,T,C], conv_out [B,W-1,C]) as float64."""
+    x, w = _f64(x), _f64(w)
+    cin = None if conv_in is None else _f64(conv_in)
+    B, T, C = x.shape
+    W = w.shape[1]
+    y = np.zeros((B, T, C), np.float64)
+    cout = np.zeros((B, W - 1, C), np.float64)
+    _load().oracle_shortconv_fwd(B, T, C, W, int(act), _ptr(x), _ptr(w), _ptr(cin), _ptr(y),
+                                 _ptr(cout))
+    return y, cout
+
+
+def shortconv_bwd(x, w, conv_in, dy, dconv_out=None, act=0):
+    """Gradients of <dy, y> + <dconv_out, conv_out>: (dx, dw, dconv_in)."""
+    x, w, dy = _f64(x), _f64(w), _f64(dy)
+    cin = None if conv_in is None else _f64(conv_in)
+    dco = None if dconv_out is None else _f64(dconv_out)
+    B, T, C = x.shape
+    W = w.shape[1]
+    dx = np.zeros((B, T, C), np.float64)
+    dw = np.zeros((C, W), np.float64)
+    dcin = np.zeros((B, W - 1, C), np.float64)
+    _load().oracle_shortconv_bwd(B, T, C, W, int(act), _ptr(x), _ptr(w), _ptr(cin), _ptr(dy),
+                                 _ptr(dco), _ptr(dx), _ptr(dw), _ptr(dcin))
+    return dx, dw, dcin

@@ -33,6 +33,7 @@
  */
 #include <stdlib.h>
 #include <string.h>
+#include <math.h>
 #ifdef _OPENMP
 #include <omp.h>
 #endif
@@ -271,4 +272,95 @@ int oracle_gdn_bwd(int B, int T, int H, int Dk, int Dv,
         free(ckpt); free(seg); free(G); free(u); free(y); free(Gk); free(S);
     }
     return err ? -2 : nt;
+}
+
+/* ------------------------------------------------------------------------
+ * Short causal depthwise convolution with a boundary state (TEST
+ * INFRASTRUCTURE, like the rest of this file).
+ *
+ * Source: Pith review of StateFlow, "What carries the argument" (each chunk
+ * also carries auxiliary local-convolution states across its boundary) and
+ * "Referee Report", major comment 1 (the short-convolution boundary states
+ * must be reconstructed for the chunked backward to be exact).  The pages do
+ * not print the convolution; the plainest reading, used here, is the usual
+ * causal depthwise 1-D convolution of width W over the token axis, per
+ * channel, applied to a chunk's inputs with the previous chunk's last W-1
+ * inputs in front of them:
+ *     xe = [conv_in (W-1 rows) ; x (T rows)]          per (b, channel c)
+ *     z_t[c] = sum_{j=0}^{W-1} w[c][j] * xe[t + W-1 - j][c]
+ *     y_t[c] = z_t[c]            (act = 0)
+ *     y_t[c] = z_t / (1 + e^-z)  (act = 1, SiLU)
+ *     conv_out = the last W-1 rows of xe (the next chunk's conv_in).
+ * Tap j multiplies the input j tokens back.  conv_in NULL means zeros (the
+ * start of a sequence).
+ * Layouts (fp64, C-contiguous): x, y, dy, dx [B, T, C]; w, dw [C, W];
+ * conv_in, conv_out, dconv_in, dconv_out [B, W-1, C].
+ * ---------------------------------------------------------------------- */
+static double xe_at(const double *x, const double *cin, int b, int u, int T, int C, int W,
+                    int c)
+{
+    if (u < W - 1)
+        return cin ? cin[((size_t)b * (W - 1) + u) * C + c] : 0.0;
+    return x[((size_t)b * T + (u - (W - 1))) * C + c];
+}
+
+void oracle_shortconv_fwd(int B, int T, int C, int W, int act, const double *x, const double *w,
+                          const double *conv_in, double *y, double *conv_out)
+{
+    for (int b = 0; b < B; ++b)
+        for (int t = 0; t < T; ++t)
+            for (int c = 0; c < C; ++c) {
+                double z = 0.0;
+                for (int j = 0; j < W; ++j)
+                    z += w[(size_t)c * W + j] * xe_at(x, conv_in, b, t + W - 1 - j, T, C, W, c);
+                y[((size_t)b * T + t) * C + c] = act ? z / (1.0 + exp(-z)) : z;
+            }
+    if (conv_out)
+        for (int b = 0; b < B; ++b)
+            for (int m = 0; m < W - 1; ++m)
+                for (int c = 0; c < C; ++c)
+                    conv_out[((size_t)b * (W - 1) + m) * C + c] =
+                        xe_at(x, conv_in, b, T + m, T, C, W, c);
+}
+
+/* Backward of the loss L = <dy, y> + <dconv_out, conv_out>.  Writes dx, dw
+ * (summed over b and t) and dconv_in (NULL dconv_out means zeros). */
+void oracle_shortconv_bwd(int B, int T, int C, int W, int act, const double *x, const double *w,
+                          const double *conv_in, const double *dy, const double *dconv_out,
+                          double *dx, double *dw, double *dconv_in)
+{
+    const int U = T + W - 1;                   /* rows of xe */
+    double *dxe = (double *)calloc((size_t)U * C, sizeof(double));
+    memset(dw, 0, sizeof(double) * (size_t)C * W);
+    for (int b = 0; b < B; ++b) {
+        memset(dxe, 0, sizeof(double) * (size_t)U * C);
+        for (int t = 0; t < T; ++t)
+            for (int c = 0; c < C; ++c) {
+                double z = 0.0;
+                for (int j = 0; j < W; ++j)
+                    z += w[(size_t)c * W + j] * xe_at(x, conv_in, b, t + W - 1 - j, T, C, W, c);
+                double g = dy[((size_t)b * T + t) * C + c];
+                if (act) {
+                    const double s = 1.0 / (1.0 + exp(-z));
+                    g *= s * (1.0 + z * (1.0 - s));    /* d/dz of z * sigmoid(z) */
+                }
+                for (int j = 0; j < W; ++j) {
+                    const int u = t + W - 1 - j;
+                    dxe[(size_t)u * C + c] += w[(size_t)c * W + j] * g;
+                    dw[(size_t)c * W + j] += g * xe_at(x, conv_in, b, u, T, C, W, c);
+                }
+            }
+        if (dconv_out)                            /* conv_out = xe rows T .. T+W-2 */
+            for (int m = 0; m < W - 1; ++m)
+                for (int c = 0; c < C; ++c)
+                    dxe[(size_t)(T + m) * C + c] += dconv_out[((size_t)b * (W - 1) + m) * C + c];
+        for (int t = 0; t < T; ++t)
+            for (int c = 0; c < C; ++c)
+                dx[((size_t)b * T + t) * C + c] = dxe[(size_t)(t + W - 1) * C + c];
+        if (dconv_in)
+            for (int m = 0; m < W - 1; ++m)
+                for (int c = 0; c < C; ++c)
+                    dconv_in[((size_t)b * (W - 1) + m) * C + c] = dxe[(size_t)m * C + c];
+    }
+    free(dxe);
 }

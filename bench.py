@@ -123,7 +123,7 @@ def kernel_label(name):
     """The library's launch label of a kernel as a profiler names it
     (demangled or mangled), or None for other kernels."""
     import re
-    m = re.search(r"(gdn_\w+?)_kernel", name)
+    m = re.search(r"((?:gdn|conv)_\w+?)_kernel", name)
     if not m:
         return None
     base = m.group(1)
@@ -203,6 +203,110 @@ def workload(name):
     raise SystemExit("unknown workload %r" % name)
 
 
+def bench_conv(args):
+    """The short causal convolution (the chunk's auxiliary local-convolution
+    state) over q, k and v of a GDN layer: C = 3 * H * d channels, width 4,
+    SiLU, chained through the 8 skewed chunks of the main workload, forward
+    then backward.  Bound by HBM: per token, the forward reads x and writes y,
+    the backward reads x and dy and writes dx (bf16 each)."""
+    import torch
+    from linear_recurrence_chunked_gated_amd import _lib
+    from linear_recurrence_chunked_gated_amd.inputs import conv_inputs
+    from linear_recurrence_chunked_gated_amd.plan import chunk_lengths
+    T, H, D, W = 262144, 16, 128, 4
+    C = 3 * H * D
+    chunks = chunk_lengths(T, 8, 0.5)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    d = conv_inputs(1, T, C, W, "bf16", seed=20260104, state_std=None, grads=True, device=dev)
+    x, w, dy = d["x"], d["w"], d["dy"]
+    bounds = [0]
+    for n in chunks:
+        bounds.append(bounds[-1] + n)
+    y, dx = torch.empty_like(x), torch.empty_like(x)
+    states = [None] + [torch.empty(1, W - 1, C, dtype=x.dtype, device=dev) for _ in chunks]
+    gst = [torch.empty(1, W - 1, C, dtype=x.dtype, device=dev) for _ in range(len(chunks) + 1)]
+    dws = [torch.empty_like(w) for _ in chunks]
+    wsb = _lib.alloc_workspace(max(_lib.shortconv_bwd_workspace_bytes(
+        _lib.conv_shape(1, n, C, W, x.dtype, 1)) for n in chunks), dev)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        for i in range(len(chunks)):
+            sl = slice(bounds[i], bounds[i + 1])
+            _lib.shortconv_fwd(x[:, sl], w, states[i], 1, y=y[:, sl], conv_out=states[i + 1],
+                               stream=stream)
+        g = None
+        for i in range(len(chunks) - 1, -1, -1):
+            sl = slice(bounds[i], bounds[i + 1])
+            _, _, g = _lib.shortconv_bwd(x[:, sl], w, states[i], dy[:, sl], g, 1, dx=dx[:, sl],
+                                         dw=dws[i], workspace=wsb, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    with _lib.profile(capacity=64 * args.steps * len(chunks) + 64) as prof:
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(args.steps):
+            step()
+        e1.record(stream)
+        torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    kern = {n: {"avg_us": tot / k * 1e3, "ms_per_step": tot / args.steps, "launches": k}
+            for n, (k, tot) in prof.results.items()}
+    dom = max(kern, key=lambda n: kern[n]["ms_per_step"])
+    per_tok = {"conv_fwd": 4 * C, "conv_bwd": 6 * C}
+    by = per_tok[dom] * T / len(chunks)  # average chunk
+    achieved = by / (kern[dom]["avg_us"] * 1e-6) / 1e9
+    Bytes = 10 * C * T
+    t_roof = Bytes / (PEAK_HBM_GBS * 1e9)
+    cpu = None
+    if not args.no_cpu_baseline:
+        import numpy as np
+        import oracle
+        from linear_recurrence_chunked_gated_amd.inputs import as_f64
+        oracle.build(force=False)
+        hd = conv_inputs(1, T, C, W, "bf16", seed=20260104, state_std=None, grads=True)
+        n, el = 16, 0.0
+        while True:
+            xs, dys = as_f64(hd["x"][:, :n]), as_f64(hd["dy"][:, :n])
+            ws = as_f64(hd["w"])
+            t0 = time.perf_counter()
+            oracle.shortconv_fwd(xs, ws, None, 1)
+            oracle.shortconv_bwd(xs, ws, None, dys, None, 1)
+            el = time.perf_counter() - t0
+            if el >= 5.0 or 2 * n > T:
+                break
+            n *= 2
+        cpu = {"value": round(n / el, 1), "unit": "tokens/s", "cores": 1, "kind": "oracle",
+               "sample": "first %d tokens x %d channels of the workload, one chunk, fwd+bwd, "
+                         "fp64 loop (%.1f s)" % (n, C, el)}
+    line = {
+        "metric": "tokens/sec short causal conv fwd+bwd over q,k,v (H=16,d=128,W=4,1 GPU); "
+                  "% HBM roofline",
+        "value": round(T / (ms * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "B": 1, "T": T, "C": C, "W": W, "act": "silu",
+                   "chunks": chunks, "parallelism": "single GPU"},
+        "roofline": {"kernel": dom, "bound": "hbm", "achieved": round(achieved, 1),
+                     "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": load_traffic(dom),
+                     "bytes_per_launch": by},
+        "path_roofline": {"bound": "hbm", "t_roof_ms": round(t_roof * 1e3, 4),
+                          "t_step_ms": round(ms, 4), "frac": round(t_roof / (ms * 1e-3), 4),
+                          "algorithmic_bytes": Bytes},
+        "kernels": {n: {"avg_us": round(v["avg_us"], 2),
+                        "launches_per_step": v["launches"] // args.steps,
+                        "ms_per_step": round(v["ms_per_step"], 4)} for n, v in kern.items()},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
 def cpu_baseline(wl, seconds_target=7.0):
     """The fp64 oracle on a bounded sample: the first n tokens of the same
     sequence (all heads), one chunk forward and backward (or forward only)."""
@@ -234,7 +338,10 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=2)
-    ap.add_argument("--workload", default="fwdbwd_h16_t262144_d128_8skew")
+    ap.add_argument("--workload", default="fwdbwd_h16_t262144_d128_8skew",
+                    help="fwdbwd_h16_t262144_d128_8skew (default), fwdbwd_h16_t16384_d128, "
+                         "fwd_h16_t65536_d128, fwd_h32_t65536_d128, or "
+                         "conv_qkv_h16_t262144_d128_8skew (the short convolution)")
     ap.add_argument("--seg-blocks", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--recompute", action="store_true",
@@ -257,6 +364,10 @@ def main():
               "(the chunk path shards by heads with no exchange, or along the sequence with one "
               "boundary-state exchange per chunk)", file=sys.stderr)
         sys.exit(2)
+
+    if args.workload.startswith("conv_"):
+        bench_conv(args)
+        return
 
     import torch
     import linear_recurrence_chunked_gated_amd as gdn

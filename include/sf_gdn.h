@@ -131,6 +131,39 @@ sf_status sf_gdn_chunk_bwd_saved(const sf_gdn_shape* shape, const void* q, const
                                  float* dbeta, float* dS_in, void* workspace, size_t ws_bytes,
                                  void* stream);
 
+/* Short causal depthwise convolution of one chunk, with its boundary state
+ * ("auxiliary local-convolution states" of a chunk: Pith review of StateFlow,
+ * "What carries the argument"; their reconstruction in the chunked backward:
+ * Referee Report, major comment 1).  The pages do not print the operation;
+ * this is the usual causal depthwise 1-D convolution of width W along the
+ * tokens, per channel c, over the chunk's inputs preceded by the previous
+ * chunk's last W-1 inputs:
+ *     xe = [conv_in (W-1 rows); x (T rows)]
+ *     z_t = sum_{j<W} w[c][j] xe[t + W-1 - j][c]     (tap j = j tokens back)
+ *     y_t = z_t (act = 0) or z_t * sigmoid(z_t) (act = 1, SiLU)
+ *     conv_out = the last W-1 rows of xe (the next chunk's conv_in).
+ * Chaining chunks through conv_out -> conv_in gives the unchunked result.
+ * Layouts: x, y, dy, dx [B, T, C] and conv_in, conv_out, dconv_in, dconv_out
+ * [B, W-1, C] in `dtype`; w, dw [C, W] fp32.  NULL conv_in / dconv_out mean
+ * zeros; NULL conv_out / dconv_in mean not wanted.  1 <= W <= 8, C a
+ * multiple of 8, pointers 16-byte aligned, outputs not overlapping inputs.
+ * The backward writes dx, dconv_in and dw (the weight gradient summed over b
+ * and t, not accumulated into dw's old contents) for the loss
+ * <dy, y> + <dconv_out, conv_out>; its workspace (256-byte aligned) holds
+ * per-run partial weight gradients, summed in a fixed order. */
+typedef struct {
+  int B, T, C, W;
+  int dtype;  /* sf_dtype of x, y, conv states and their gradients */
+  int act;    /* 0: none, 1: SiLU */
+} sf_conv_shape;
+sf_status sf_gdn_shortconv_fwd(const sf_conv_shape* shape, const void* x, const float* w,
+                               const void* conv_in, void* y, void* conv_out, void* stream);
+sf_status sf_gdn_shortconv_bwd_workspace_size(const sf_conv_shape* shape, size_t* bytes);
+sf_status sf_gdn_shortconv_bwd(const sf_conv_shape* shape, const void* x, const float* w,
+                               const void* conv_in, const void* dy, const void* dconv_out,
+                               void* dx, float* dw, void* dconv_in, void* workspace,
+                               size_t ws_bytes, void* stream);
+
 /* Static text for a status code. */
 const char* sf_status_string(int status);
 /* Detail of the calling thread's last non-OK status (static until the next

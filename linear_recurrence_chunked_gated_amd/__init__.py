@@ -6,15 +6,18 @@ in include/sf_gdn.h.
     chunk_bwd(q, k, v, alpha, beta, S_in, dO, dS_out)
                                  -> (dq, dk, dv, dalpha, dbeta, dS_in)
     chain_fwd / chain_bwd: consecutive chunks through their boundary states.
+    shortconv_fwd(x, w, conv_in)                     -> (y, conv_out)
+    shortconv_bwd(x, w, conv_in, dy, dconv_out)      -> (dx, dw, dconv_in)
 
 Imports are lazy so that the input generator and the planner load without the
 HIP library.
 """
-__all__ = ["chunk_fwd", "chunk_bwd", "chain_fwd", "chain_bwd", "profile", "GDNError"]
+__all__ = ["chunk_fwd", "chunk_bwd", "chain_fwd", "chain_bwd", "shortconv_fwd", "shortconv_bwd",
+           "profile", "GDNError"]
 
 
 def __getattr__(name):
-    if name in ("chunk_fwd", "chunk_bwd", "profile", "GDNError"):
+    if name in ("chunk_fwd", "chunk_bwd", "shortconv_fwd", "shortconv_bwd", "profile", "GDNError"):
         from . import _lib
         return getattr(_lib, name)
     if name in ("chain_fwd", "chain_bwd"):

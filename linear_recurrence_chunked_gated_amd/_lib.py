@@ -28,6 +28,11 @@ class Shape(ctypes.Structure):
                 ("seg_blocks", ctypes.c_int)]
 
 
+class ConvShape(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int), ("T", ctypes.c_int), ("C", ctypes.c_int),
+                ("W", ctypes.c_int), ("dtype", ctypes.c_int), ("act", ctypes.c_int)]
+
+
 SIGNATURES = {
     "sf_gdn_chunk_fwd_workspace_size": (ctypes.c_int, [ctypes.POINTER(Shape), ctypes.POINTER(_sz)]),
     "sf_gdn_chunk_bwd_workspace_size": (ctypes.c_int, [ctypes.POINTER(Shape), ctypes.POINTER(_sz)]),
@@ -37,6 +42,10 @@ SIGNATURES = {
     "sf_gdn_chunk_fwd_save": (ctypes.c_int, [ctypes.POINTER(Shape)] + [_vp] * 9 + [_sz, _vp, _sz, _vp]),
     "sf_gdn_chunk_bwd_saved": (ctypes.c_int, [ctypes.POINTER(Shape)] + [_vp] * 6 + [_sz] + [_vp] * 8
                                + [_vp, _sz, _vp]),
+    "sf_gdn_shortconv_fwd": (ctypes.c_int, [ctypes.POINTER(ConvShape)] + [_vp] * 6),
+    "sf_gdn_shortconv_bwd_workspace_size": (ctypes.c_int, [ctypes.POINTER(ConvShape),
+                                                           ctypes.POINTER(_sz)]),
+    "sf_gdn_shortconv_bwd": (ctypes.c_int, [ctypes.POINTER(ConvShape)] + [_vp] * 9 + [_sz, _vp]),
     "sf_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "sf_last_error_message": (ctypes.c_char_p, []),
     "sf_gdn_version": (ctypes.c_char_p, []),
@@ -229,6 +238,79 @@ def chunk_bwd(q, k, v, alpha, beta, S_in, dO, dS_out=None, grads=None, seg_block
                                            _ptr(dS_in), _ptr(workspace), wsn, _stream(stream))
         _check(st, "sf_gdn_chunk_bwd_saved")
     return dq, dk, dv, da, db, dS_in
+
+
+def conv_shape(B, T, C, W, dtype, act=0):
+    if isinstance(dtype, torch.dtype):
+        if dtype not in _DTYPES:
+            raise TypeError("x must be bfloat16 or float32, got %s" % dtype)
+        dtype = _DTYPES[dtype]
+    return ConvShape(B, T, C, W, dtype, int(act))
+
+
+def shortconv_bwd_workspace_bytes(shape):
+    n = ctypes.c_size_t(0)
+    _check(load().sf_gdn_shortconv_bwd_workspace_size(ctypes.byref(shape), ctypes.byref(n)),
+           "shortconv_bwd_workspace_size")
+    return n.value
+
+
+def shortconv_fwd(x, w, conv_in=None, act=0, y=None, conv_out=None, want_state=True,
+                  stream=None):
+    """sf_gdn_shortconv_fwd on torch tensors: x [B,T,C], w [C,W] fp32,
+    conv_in [B,W-1,C] or None.  Returns (y, conv_out); conv_out is None when
+    want_state is False."""
+    B, T, C = x.shape
+    W = w.shape[1]
+    dev = x.device
+    if dev.type != "cuda":
+        raise ValueError("tensors must be on a GPU device")
+    _need(x, "x", x.dtype, (B, T, C), dev)
+    _need(w, "w", torch.float32, (C, W), dev)
+    if conv_in is not None:
+        _need(conv_in, "conv_in", x.dtype, (B, W - 1, C), dev)
+    if y is None:
+        y = torch.empty_like(x)
+    _need(y, "y", x.dtype, (B, T, C), dev)
+    if want_state and conv_out is None and W > 1:
+        conv_out = torch.empty((B, W - 1, C), dtype=x.dtype, device=dev)
+    shape = conv_shape(B, T, C, W, x.dtype, act)
+    _check(load().sf_gdn_shortconv_fwd(ctypes.byref(shape), _ptr(x), _ptr(w), _ptr(conv_in),
+                                       _ptr(y), _ptr(conv_out) if W > 1 else None,
+                                       _stream(stream)), "sf_gdn_shortconv_fwd")
+    return y, conv_out
+
+
+def shortconv_bwd(x, w, conv_in, dy, dconv_out=None, act=0, dx=None, dw=None, want_state=True,
+                  workspace=None, stream=None):
+    """sf_gdn_shortconv_bwd on torch tensors.  Returns (dx, dw, dconv_in)."""
+    B, T, C = x.shape
+    W = w.shape[1]
+    dev = x.device
+    if dev.type != "cuda":
+        raise ValueError("tensors must be on a GPU device")
+    _need(x, "x", x.dtype, (B, T, C), dev)
+    _need(dy, "dy", x.dtype, (B, T, C), dev)
+    _need(w, "w", torch.float32, (C, W), dev)
+    for t, n in ((conv_in, "conv_in"), (dconv_out, "dconv_out")):
+        if t is not None:
+            _need(t, n, x.dtype, (B, W - 1, C), dev)
+    if dx is None:
+        dx = torch.empty_like(x)
+    if dw is None:
+        dw = torch.empty_like(w)
+    dci = (torch.empty((B, W - 1, C), dtype=x.dtype, device=dev)
+           if want_state and W > 1 else None)
+    shape = conv_shape(B, T, C, W, x.dtype, act)
+    need = shortconv_bwd_workspace_bytes(shape)
+    if workspace is None or workspace.numel() < need:
+        workspace = alloc_workspace(need, dev)
+    _check(load().sf_gdn_shortconv_bwd(ctypes.byref(shape), _ptr(x), _ptr(w), _ptr(conv_in),
+                                       _ptr(dy), _ptr(dconv_out), _ptr(dx), _ptr(dw), _ptr(dci),
+                                       _ptr(workspace),
+                                       ctypes.c_size_t(0 if workspace is None else workspace.numel()),
+                                       _stream(stream)), "sf_gdn_shortconv_bwd")
+    return dx, dw, dci
 
 
 class profile:

@@ -14,7 +14,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libsf_gdn.so")
-SOURCES = ["gdn_fwd.hip", "gdn_bwd.hip", "sf_gdn_api.cpp"]
+SOURCES = ["gdn_fwd.hip", "gdn_bwd.hip", "gdn_conv.hip", "sf_gdn_api.cpp"]
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

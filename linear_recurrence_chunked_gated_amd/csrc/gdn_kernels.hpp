@@ -56,6 +56,23 @@ struct BwdArgs {
   void* dhst;           // [B*H][nblk][D][D] gradient wrt each block's exit state
 };
 
+// Short causal convolution of one chunk (see gdn_conv.hip).  Token tensors
+// [B, T, C] and boundary states [B, W-1, C] in the operand type; weights and
+// their gradient [C, W] fp32.  Null conv states mean zeros / not wanted.
+struct ConvArgs {
+  const void* x;
+  const float* w;
+  const void* cin;
+  void* y;
+  void* cout;
+  const void* dy;
+  const void* dcout;
+  void* dx;
+  float* dw;
+  void* dcin;
+  int B, T, C, W, act;
+};
+
 // Optional per-launch event timing (see sf_gdn_profile_* in the C ABI).
 struct Profiler;
 void prof_begin(Profiler* p, const char* name, hipStream_t st);
@@ -79,5 +96,11 @@ hipError_t launch_states(const FwdArgs& a, void* hst, hipStream_t st, Profiler* 
 // forward), so the forward recompute is skipped.
 template <typename T, int D>
 hipError_t launch_bwd(const BwdArgs& a, bool saved, hipStream_t st, Profiler* prof);
+// Short convolution: GR tokens per backward run; dwp holds the B * ceil(T/GR)
+// partial weight gradients [C][W] fp32 and room for their group sums.
+template <typename T>
+hipError_t launch_conv_fwd(const ConvArgs& a, hipStream_t st, Profiler* prof);
+template <typename T>
+hipError_t launch_conv_bwd(const ConvArgs& a, int GR, float* dwp, hipStream_t st, Profiler* prof);
 
 }  // namespace sfgdn

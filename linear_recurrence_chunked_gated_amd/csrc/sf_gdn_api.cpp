@@ -369,6 +369,46 @@ sf_status bwd_impl(const sf_gdn_shape* shape, const void* q, const void* k, cons
 
 }  // namespace
 
+namespace {
+
+// ------------------------------------------------------- short convolution
+struct ConvPlan {
+  int B, T, C, W, dtype, act;
+  int GR, nrun;  // backward: tokens per run, runs per sequence
+};
+
+sf_status make_conv_plan(const sf_conv_shape* s, ConvPlan& p) {
+  if (!s) return fail(SF_ERR_INVALID_ARG, "shape is NULL");
+  if (s->B <= 0 || s->T < 0 || s->C <= 0)
+    return fail(SF_ERR_INVALID_ARG, "B and C must be positive and T >= 0");
+  if (s->dtype != SF_DTYPE_F32 && s->dtype != SF_DTYPE_BF16)
+    return fail(SF_ERR_INVALID_ARG, "unknown dtype");
+  if (s->W < 1 || s->W > 8) return fail(SF_ERR_UNSUPPORTED, "W must be in 1..8");
+  if (s->act != 0 && s->act != 1) return fail(SF_ERR_INVALID_ARG, "act must be 0 or 1");
+  if (s->C % 8) return fail(SF_ERR_UNSUPPORTED, "C must be a multiple of 8");
+  if ((long long)s->B * s->T * s->C > (1LL << 40)) return fail(SF_ERR_UNSUPPORTED, "too large");
+  p.B = s->B; p.T = s->T; p.C = s->C; p.W = s->W; p.dtype = s->dtype; p.act = s->act;
+  // Backward runs: enough (channel group, run, b) workgroups to fill the GPU
+  // several times over, at least 32 tokens each (the weight-gradient
+  // partials are per run).
+  const long long gx = (s->C / (s->dtype == SF_DTYPE_BF16 ? 4 : 2) + 255) / 256;
+  long long want = (2048 + gx * s->B - 1) / (gx * s->B);
+  if (want < 1) want = 1;
+  long long GR = s->T > 0 ? (s->T + want - 1) / want : 16;
+  GR = (GR + 15) / 16 * 16;
+  if (GR < 32) GR = 32;
+  p.GR = (int)GR;
+  p.nrun = s->T > 0 ? (int)((s->T + GR - 1) / GR) : 0;
+  return SF_OK;
+}
+
+size_t conv_bwd_ws(const ConvPlan& p) {
+  const size_t np = (size_t)p.B * p.nrun, ng = (np + 31) / 32;  // partials, group sums
+  return align_up((np + ng) * p.C * p.W * sizeof(float));
+}
+
+}  // namespace
+
 extern "C" {
 
 sf_status sf_gdn_chunk_fwd(const sf_gdn_shape* shape, const void* q, const void* k, const void* v,
@@ -488,6 +528,76 @@ sf_status sf_gdn_profile_kernel(int index, const char** name, long long* launche
   if (launches) *launches = g_prof.counts[index];
   if (total_ms) *total_ms = g_prof.ms[index];
   return SF_OK;
+}
+
+
+sf_status sf_gdn_shortconv_fwd(const sf_conv_shape* shape, const void* x, const float* w,
+                               const void* conv_in, void* y, void* conv_out, void* stream) {
+  ConvPlan p;
+  sf_status s = make_conv_plan(shape, p);
+  if (s != SF_OK) return s;
+  const size_t es = p.dtype == SF_DTYPE_BF16 ? 2 : 4;
+  const size_t ntok = (size_t)p.B * p.T * p.C * es, nst = (size_t)p.B * (p.W - 1) * p.C * es;
+  if (!w) return fail(SF_ERR_INVALID_ARG, "w is required");
+  if (p.T > 0 && (!x || !y)) return fail(SF_ERR_INVALID_ARG, "x and y are required");
+  std::vector<Range> in = {{x, ntok, "x"}, {w, (size_t)p.C * p.W * 4, "w"}, {conv_in, nst, "conv_in"}};
+  std::vector<Range> out = {{y, ntok, "y"}, {conv_out, nst, "conv_out"}};
+  if ((s = check_ptrs(in, out, {})) != SF_OK) return s;
+  hipStream_t st = (hipStream_t)stream;
+  return run_locked([&](Profiler* prof) -> sf_status {
+    ConvArgs a{};
+    a.x = x; a.w = w; a.cin = conv_in; a.y = y; a.cout = conv_out;
+    a.B = p.B; a.T = p.T; a.C = p.C; a.W = p.W; a.act = p.act;
+    hipError_t e = p.dtype == SF_DTYPE_BF16 ? launch_conv_fwd<bf16>(a, st, prof)
+                                           : launch_conv_fwd<float>(a, st, prof);
+    if (e != hipSuccess) return hip_fail(e, "convolution launch");
+    return SF_OK;
+  });
+}
+
+sf_status sf_gdn_shortconv_bwd_workspace_size(const sf_conv_shape* shape, size_t* bytes) {
+  ConvPlan p;
+  sf_status s = make_conv_plan(shape, p);
+  if (s != SF_OK) return s;
+  if (!bytes) return fail(SF_ERR_INVALID_ARG, "bytes is NULL");
+  *bytes = conv_bwd_ws(p);
+  return SF_OK;
+}
+
+sf_status sf_gdn_shortconv_bwd(const sf_conv_shape* shape, const void* x, const float* w,
+                               const void* conv_in, const void* dy, const void* dconv_out,
+                               void* dx, float* dw, void* dconv_in, void* workspace,
+                               size_t ws_bytes, void* stream) {
+  ConvPlan p;
+  sf_status s = make_conv_plan(shape, p);
+  if (s != SF_OK) return s;
+  const size_t es = p.dtype == SF_DTYPE_BF16 ? 2 : 4;
+  const size_t ntok = (size_t)p.B * p.T * p.C * es, nst = (size_t)p.B * (p.W - 1) * p.C * es;
+  if (!w || !dw) return fail(SF_ERR_INVALID_ARG, "w and dw are required");
+  if (p.T > 0 && (!x || !dy || !dx)) return fail(SF_ERR_INVALID_ARG, "x, dy and dx are required");
+  std::vector<Range> in = {{x, ntok, "x"}, {w, (size_t)p.C * p.W * 4, "w"}, {conv_in, nst, "conv_in"},
+                           {dy, ntok, "dy"}, {dconv_out, nst, "dconv_out"},
+                           {workspace, ws_bytes, "workspace"}};
+  std::vector<Range> out = {{dx, ntok, "dx"}, {dw, (size_t)p.C * p.W * 4, "dw"},
+                            {dconv_in, nst, "dconv_in"}};
+  if ((s = check_ptrs(in, out, {})) != SF_OK) return s;
+  const size_t need = conv_bwd_ws(p);
+  if (need > 0 && (!workspace || ws_bytes < need))
+    return fail(SF_ERR_WORKSPACE, "convolution backward workspace needs " + std::to_string(need) + " bytes");
+  if (workspace && ((uintptr_t)workspace % kAlign))
+    return fail(SF_ERR_INVALID_ARG, "workspace is not 256-byte aligned");
+  hipStream_t st = (hipStream_t)stream;
+  return run_locked([&](Profiler* prof) -> sf_status {
+    ConvArgs a{};
+    a.x = x; a.w = w; a.cin = conv_in; a.dy = dy; a.dcout = dconv_out;
+    a.dx = dx; a.dw = dw; a.dcin = dconv_in;
+    a.B = p.B; a.T = p.T; a.C = p.C; a.W = p.W; a.act = p.act;
+    hipError_t e = p.dtype == SF_DTYPE_BF16
+                       ? launch_conv_bwd<bf16>(a, p.GR, (float*)workspace, st, prof)
+                       : launch_conv_bwd<float>(a, p.GR, (float*)workspace, st, prof);
+    if (e != hipSuccess) return hip_fail(e, "convolution launch");
+    return SF_OK;
+  });
 }
 
 }  // extern "C"

@@ -88,6 +88,38 @@ def gdn_inputs(B, T, H, Dk, Dv, dtype="bf16", seed=0, s_in_std=None, grads=False
     return out
 
 
+def conv_inputs(B, T, C, W, dtype="bf16", seed=0, state_std=1.0, grads=False, device="cpu"):
+    """Seeded inputs for the short causal convolution of one chunk.
+
+    Draw order: x ~ N(0, 1) [B,T,C]; w ~ N(0, 1) / W [C,W] (fp32);
+    conv_in ~ N(0, state_std) [B,W-1,C] (None when state_std is None); with
+    grads, dy ~ N(0, 1) [B,T,C] and dconv_out ~ N(0, 1) [B,W-1,C].  x, the
+    states and dy are rounded to the run dtype; w stays fp32.  Same
+    generators as gdn_inputs (numpy PCG64 on the CPU, torch on a device)."""
+    tdt = _TORCH_DTYPES[dtype]
+    dev = torch.device(device)
+    if dev.type == "cpu":
+        rng = np.random.Generator(np.random.PCG64(seed))
+
+        def normal(shape, std=1.0):
+            return torch.from_numpy(rng.standard_normal(shape, dtype=np.float32) * np.float32(std))
+    else:
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(seed)
+
+        def normal(shape, std=1.0):
+            return torch.randn(shape, generator=gen, device=dev, dtype=torch.float32) * std
+
+    out = {"x": normal((B, T, C)).to(tdt).contiguous(),
+           "w": (normal((C, W)) / W).contiguous(),
+           "conv_in": None if state_std is None else
+           normal((B, W - 1, C), state_std).to(tdt).contiguous()}
+    if grads:
+        out["dy"] = normal((B, T, C)).to(tdt).contiguous()
+        out["dconv_out"] = normal((B, W - 1, C)).to(tdt).contiguous()
+    return {k: (None if v is None else v.to(dev)) for k, v in out.items()}
+
+
 def as_f64(t):
     """Exact float64 copy (numpy) of a tensor's stored values, for the oracle."""
     if t is None:

@@ -149,3 +149,45 @@ def test_workspace_sizes():
 def test_planner_matches_oracle_search(T, N, alpha):
     from oracle import plan as op
     assert chunk_lengths(T, N, alpha) == op.skewed_lengths(T, N, alpha, 1.0, 0.25, 64)
+
+
+def _cshape(B=1, T=128, C=64, W=4, dtype=1, act=0):
+    return _lib.ConvShape(B, T, C, W, dtype, act)
+
+
+def _conv_fwd(shape, x=1 * G, w=2 * G, cin=None, y=3 * G, cout=4 * G):
+    L = _lib.load()
+    vp = lambda p: None if p is None else ctypes.c_void_p(p)
+    return L.sf_gdn_shortconv_fwd(ctypes.byref(shape), vp(x), vp(w), vp(cin), vp(y), vp(cout),
+                                  None)
+
+
+@pytest.mark.parametrize("shape,code", [
+    (_cshape(W=0), _lib.SF_ERR_UNSUPPORTED),
+    (_cshape(W=9), _lib.SF_ERR_UNSUPPORTED),
+    (_cshape(C=12), _lib.SF_ERR_UNSUPPORTED),
+    (_cshape(act=2), _lib.SF_ERR_INVALID_ARG),
+    (_cshape(B=0), _lib.SF_ERR_INVALID_ARG),
+    (_cshape(T=-1), _lib.SF_ERR_INVALID_ARG),
+    (_cshape(dtype=5), _lib.SF_ERR_INVALID_ARG),
+])
+def test_conv_rejects_bad_shapes(shape, code):
+    assert _conv_fwd(shape) == code
+
+
+def test_conv_rejects_missing_overlapping_and_small_workspace():
+    assert _conv_fwd(_cshape(), x=None) == _lib.SF_ERR_INVALID_ARG
+    assert _conv_fwd(_cshape(), w=None) == _lib.SF_ERR_INVALID_ARG
+    assert _conv_fwd(_cshape(), y=G + 64) == _lib.SF_ERR_INVALID_ARG        # y overlaps x
+    assert _conv_fwd(_cshape(), cout=3 * G + 64) == _lib.SF_ERR_INVALID_ARG  # overlaps y
+    assert _conv_fwd(_cshape(), x=G + 8) == _lib.SF_ERR_INVALID_ARG         # misaligned
+    shape = _cshape(T=4096, C=256)
+    need = _lib.shortconv_bwd_workspace_bytes(shape)
+    assert need > 0
+    L = _lib.load()
+    vp = lambda p: None if p is None else ctypes.c_void_p(p)
+    args = [vp(1 * G), vp(2 * G), None, vp(3 * G), None, vp(4 * G), vp(5 * G), vp(6 * G)]
+    assert L.sf_gdn_shortconv_bwd(ctypes.byref(shape), *args, vp(8 * G), ctypes.c_size_t(need - 1),
+                                  None) == _lib.SF_ERR_WORKSPACE
+    assert L.sf_gdn_shortconv_bwd(ctypes.byref(shape), *args, None, ctypes.c_size_t(0),
+                                  None) == _lib.SF_ERR_WORKSPACE

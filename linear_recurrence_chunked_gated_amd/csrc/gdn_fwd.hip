@@ -43,6 +43,20 @@ template <typename T, int D> struct FwdLds {
   static_assert(out_bytes <= 160 * 1024, "LDS budget");
 };
 
+// Fused out kernel, two blocks in flight: block b's state work reads K, W, P
+// and gates of buffer b % 2 while block b+1's state-free work fills the other
+// buffer.  Q, V, Tp, Tpp are single (consumed within one phase).
+template <typename T, int D> struct OutLds {
+  static constexpr int LDD = D + Lay<T>::PAD;
+  static constexpr int LDC = BLK + Lay<T>::PAD;
+  static constexpr size_t rowD = (size_t)BLK * LDD * sizeof(T);
+  static constexpr size_t sq = (size_t)BLK * LDC * sizeof(T);
+  static constexpr size_t oQ = 0, oV = oQ + rowD, oT = oV + rowD, oK = oT + 2 * sq,
+                          oW = oK + 2 * rowD, oP = oW + 2 * rowD, oG = oP + 2 * sq;
+  static constexpr size_t bytes = oG + 2 * kGateBytes;
+  static constexpr bool fits = bytes <= 160 * 1024;
+};
+
 // Pre kernel: RK K -> Tm (fp32 T, solve scratch; K is dead once A is formed)
 // | RA Af (fp32 A) | RG gates.  About 36 KB, so four workgroups share a CU.
 template <typename T, int D> struct PrepLds {
@@ -164,6 +178,7 @@ __global__ __launch_bounds__(64 * fwd_nw<D>(), 2) void gdn_fwd_out_kernel(FwdArg
   constexpr int NW = fwd_nw<D>(), NDV = D / 16 / NW, DKT = D / 16;
   constexpr int LDD = Lz::LDD, LDC = Lz::LDC;
   constexpr bool STATES = MODE != OUT_ONLY, OUT = MODE != STATES_ONLY;
+  constexpr bool PFQ = sizeof(T) == 2;  // operand prefetch: registers allow it for bf16
   extern __shared__ __align__(16) unsigned char smem[];
   T* Qs = reinterpret_cast<T*>(smem + Lz::oQ);
   T* Ks = reinterpret_cast<T*>(smem + Lz::oK);
@@ -254,8 +269,8 @@ __global__ __launch_bounds__(64 * fwd_nw<D>(), 2) void gdn_fwd_out_kernel(FwdArg
     block_u<T, NDV>(Tpp, LDC, Vs, LDD, dv0, U);
     lds_barrier();
     // ST and Out: Vn = U - W S^T; O^T += Vn^T P^T; S' = gamma_C S + Vn^T D K
-    block_x_st<T, D, NDV, true>(Wn, LDD, St, U);
-    if constexpr (OUT) block_vnT_pT<T, NDV, true>(U, Pl, LDC, O);
+    block_x_st<T, D, NDV, PFQ>(Wn, LDD, St, U);
+    if constexpr (OUT) block_vnT_pT<T, NDV, PFQ>(U, Pl, LDC, O);
     f32x4 dsc[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -266,7 +281,7 @@ __global__ __launch_bounds__(64 * fwd_nw<D>(), 2) void gdn_fwd_out_kernel(FwdArg
     for (int bb = 0; bb < NDV; ++bb)
 #pragma unroll
       for (int aa = 0; aa < DKT; ++aa) St[bb][aa] *= gc;
-    block_state_write<T, D, NDV, true>(Ks, LDD, U, dsc, St);
+    block_state_write<T, D, NDV, PFQ>(Ks, LDD, U, dsc, St);
     prev_t0 = t0;
     prev_nv = nv;
     // The next block's inputs: issued here so that they add no register
@@ -278,6 +293,155 @@ __global__ __launch_bounds__(64 * fwd_nw<D>(), 2) void gdn_fwd_out_kernel(FwdArg
   }
   if constexpr (OUT) {
     if (prev_t0 >= 0) store_o();
+  }
+
+  if (OUT && seg == a.P - 1 && a.S_out) {
+    float* So = a.S_out + (size_t)bh * D * D;
+#pragma unroll
+    for (int bb = 0; bb < NDV; ++bb)
+#pragma unroll
+      for (int aa = 0; aa < DKT; ++aa)
+        *reinterpret_cast<f32x4*>(So + (size_t)(16 * (dv0 + bb) + li) * D + 16 * aa + g4) =
+            St[bb][aa];
+  }
+}
+
+// The same computation with two blocks in flight (OutLds): used where its
+// LDS layout fits (bf16).
+template <typename T, int D, int MODE>
+__global__ __launch_bounds__(64 * fwd_nw<D>(), 2) void gdn_fwd_out2_kernel(FwdArgs a, T* hst) {
+  typedef OutLds<T, D> Lz;
+  constexpr int NW = fwd_nw<D>(), NDV = D / 16 / NW, DKT = D / 16;
+  constexpr int LDD = Lz::LDD, LDC = Lz::LDC;
+  constexpr bool STATES = MODE != OUT_ONLY, OUT = MODE != STATES_ONLY;
+  extern __shared__ __align__(16) unsigned char smem[];
+  T* Qs = reinterpret_cast<T*>(smem + Lz::oQ);
+  T* Vs = reinterpret_cast<T*>(smem + Lz::oV);
+  T* Tp = reinterpret_cast<T*>(smem + Lz::oT);
+  T* Tpp = Tp + BLK * LDC;
+  // double buffers, by parity n
+  auto Kb = [&](int n) { return reinterpret_cast<T*>(smem + Lz::oK + n * Lz::rowD); };
+  auto Wb = [&](int n) { return reinterpret_cast<T*>(smem + Lz::oW + n * Lz::rowD); };
+  auto Pb = [&](int n) { return reinterpret_cast<T*>(smem + Lz::oP + n * Lz::sq); };
+  auto Gb = [&](int n) { return gate_lds(smem + Lz::oG + n * kGateBytes); };
+
+  const int w = wave_id(), lane = lane_id(), g4 = 4 * (lane >> 4), li = lane & 15;
+  const int dv0 = NDV * w;
+  const int seg = blockIdx.x % a.P, bh = blockIdx.x / a.P;
+  const int b = bh / a.H, h = bh % a.H;
+  const int blk0 = seg * a.L, blk1 = min(a.nblk, blk0 + a.L);
+  const size_t rs = (size_t)a.H * D;
+  const T* q = seq_base<T, D>(a.q, a, b, h);
+  const T* k = seq_base<T, D>(a.k, a, b, h);
+  const T* v = seq_base<T, D>(a.v, a, b, h);
+  T* o = const_cast<T*>(seq_base<T, D>(a.o, a, b, h));
+  const float* al = a.alpha + (size_t)b * a.T * a.H + h;
+  const float* bt = a.beta + (size_t)b * a.T * a.H + h;
+
+  // State S^T tiles: St[bb][aa] covers dk-tile aa, dv-tile dv0 + bb.
+  f32x4 St[NDV][DKT];
+  {
+    const float* S0 = a.Sst ? a.Sst + ((size_t)bh * a.sst_P + seg) * D * D : nullptr;
+#pragma unroll
+    for (int bb = 0; bb < NDV; ++bb)
+#pragma unroll
+      for (int aa = 0; aa < DKT; ++aa) {
+        const int dv = 16 * (dv0 + bb) + li, dk = 16 * aa + g4;
+        St[bb][aa] = S0 ? *reinterpret_cast<const f32x4*>(S0 + (size_t)dv * D + dk)
+                        : f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+  }
+  if (blk0 >= blk1) return;
+
+  auto fetch = [&](Prefetch<T, D, OUT>& pf, int blk) {
+    pf.fetch(q, k, v, al, bt, tw_block<T>(a.tw, a.nblk, bh, blk), rs, a.H, blk * BLK,
+             min(BLK, a.T - blk * BLK));
+  };
+  // State-free work of a block whose inputs sit in Q, K[n], V, Tp, Tpp and
+  // gates G[n]: P -> P[n], Wn -> W[n], U (registers).
+  auto pre = [&](int n, f32x4 (&U)[NDV][4]) {
+    if constexpr (OUT) block_scores<T, D, NW, true, false>(Qs, Kb(n), LDD, Gb(n), nullptr, 0, Pb(n), LDC);
+    block_w<T, D, NW>(Kb(n), LDD, Tp, LDC, Wb(n));
+    block_u<T, NDV>(Tpp, LDC, Vs, LDD, dv0, U);
+  };
+  // O^T = diag(gamma) S Q^T of the block in Q with gates G[n].
+  f32x4 O[NDV][4];
+  auto out_state_part = [&](int n) {
+    if constexpr (OUT) {
+      zero_acc(O);
+      block_s_yT<T, D, NDV>(St, Qs, LDD, O);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float gr = Gb(n).gam[16 * j + li];
+#pragma unroll
+        for (int bb = 0; bb < NDV; ++bb) O[bb][j] *= gr;
+      }
+    }
+  };
+
+  Prefetch<T, D, OUT> pf;
+  fetch(pf, blk0);
+  pf.stage(Qs, Kb(0), Vs, Tp, Tpp, LDD, LDC, min(BLK, a.T - blk0 * BLK), Gb(0));
+  if (blk0 + 1 < blk1) fetch(pf, blk0 + 1);
+  lds_barrier();
+  f32x4 U[NDV][4];
+  pre(0, U);
+  out_state_part(0);
+  lds_barrier();
+
+  for (int blk = blk0; blk < blk1; ++blk) {
+    const int c = (blk - blk0) & 1, n = c ^ 1;
+    const int t0 = blk * BLK, nv = min(BLK, a.T - t0);
+    const bool next = blk + 1 < blk1;
+    if constexpr (STATES) {
+      T* hb = hst + ((size_t)bh * a.nblk + blk) * D * D;
+#pragma unroll
+      for (int bb = 0; bb < NDV; ++bb)
+#pragma unroll
+        for (int aa = 0; aa < DKT; ++aa) {
+          const f32x4 x = St[bb][aa];
+          st4(hb + (size_t)(16 * (dv0 + bb) + li) * D + 16 * aa + g4, x[0], x[1], x[2], x[3]);
+        }
+    }
+    if (next) {
+      pf.stage(Qs, Kb(n), Vs, Tp, Tpp, LDD, LDC, min(BLK, a.T - t0 - BLK), Gb(n));
+      if (blk + 2 < blk1) fetch(pf, blk + 2);
+    }
+    lds_barrier();
+    // block blk, state part: Vn = U - W S^T; O^T += Vn^T P^T; S' = gamma_C S + Vn^T D K
+    block_x_st<T, D, NDV, true>(Wb(c), LDD, St, U);
+    if constexpr (OUT) block_vnT_pT<T, NDV, true>(U, Pb(c), LDC, O);
+    {
+      f32x4 dsc[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) dsc[i][e] = Gb(c).dec[16 * i + g4 + e];
+      const float gc = Gb(c).gC[0];
+#pragma unroll
+      for (int bb = 0; bb < NDV; ++bb)
+#pragma unroll
+        for (int aa = 0; aa < DKT; ++aa) St[bb][aa] *= gc;
+      block_state_write<T, D, NDV, true>(Kb(c), LDD, U, dsc, St);
+    }
+    if constexpr (OUT) {
+#pragma unroll
+      for (int bb = 0; bb < NDV; ++bb)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int r = 16 * j + li;
+          if (r < nv) {
+            const f32x4 x = O[bb][j];
+            st4(o + (size_t)(t0 + r) * rs + 16 * (dv0 + bb) + g4, x[0], x[1], x[2], x[3]);
+          }
+        }
+    }
+    // block blk+1, state-free part and its S Q^T (S is now its entry state)
+    if (next) {
+      pre(n, U);
+      out_state_part(n);
+    }
+    lds_barrier();
   }
 
   if (OUT && seg == a.P - 1 && a.S_out) {
@@ -507,16 +671,31 @@ hipError_t launch_chain_fwd(const ChainArgs& c, int BH, hipStream_t st, Profiler
   return hipGetLastError();
 }
 
-template <typename T, int D>
-hipError_t launch_states(const FwdArgs& a, void* hst, hipStream_t st, Profiler* prof) {
-  typedef FwdLds<T, D> Lz;
-  hipError_t e = set_lds((const void*)gdn_fwd_out_kernel<T, D, STATES_ONLY>, Lz::out_bytes);
-  if (e != hipSuccess) return e;
-  prof_begin(prof, "gdn_fwd_states", st);
-  hipLaunchKernelGGL((gdn_fwd_out_kernel<T, D, STATES_ONLY>), dim3(a.B * a.H * a.P), dim3(64 * fwd_nw<D>()),
-                     Lz::out_bytes, st, a, reinterpret_cast<T*>(hst));
+// The fused out kernel in MODE: the two-blocks-in-flight form where its LDS
+// layout fits, else the one-block form.
+template <typename T, int D, int MODE>
+static hipError_t launch_out(const FwdArgs& a, T* hst, hipStream_t st, Profiler* prof,
+                             const char* name) {
+  const dim3 grid(a.B * a.H * a.P), block(64 * fwd_nw<D>());
+  hipError_t e;
+  if constexpr (OutLds<T, D>::fits) {
+    constexpr size_t ob = OutLds<T, D>::bytes;
+    if ((e = set_lds((const void*)gdn_fwd_out2_kernel<T, D, MODE>, ob)) != hipSuccess) return e;
+    prof_begin(prof, name, st);
+    hipLaunchKernelGGL((gdn_fwd_out2_kernel<T, D, MODE>), grid, block, ob, st, a, hst);
+  } else {
+    constexpr size_t ob = FwdLds<T, D>::out_bytes;
+    if ((e = set_lds((const void*)gdn_fwd_out_kernel<T, D, MODE>, ob)) != hipSuccess) return e;
+    prof_begin(prof, name, st);
+    hipLaunchKernelGGL((gdn_fwd_out_kernel<T, D, MODE>), grid, block, ob, st, a, hst);
+  }
   prof_end(prof, st);
   return hipGetLastError();
+}
+
+template <typename T, int D>
+hipError_t launch_states(const FwdArgs& a, void* hst, hipStream_t st, Profiler* prof) {
+  return launch_out<T, D, STATES_ONLY>(a, reinterpret_cast<T*>(hst), st, prof, "gdn_fwd_states");
 }
 
 // hsave: when not null, every block's entry state is stored there and the
@@ -524,7 +703,6 @@ hipError_t launch_states(const FwdArgs& a, void* hst, hipStream_t st, Profiler* 
 // caller's saved buffer), so that the backward can skip its recompute.
 template <typename T, int D>
 hipError_t launch_fwd(const FwdArgs& a, void* hsave, hipStream_t st, Profiler* prof) {
-  typedef FwdLds<T, D> Lz;
   hipError_t e;
   const int BH = a.B * a.H;
   if ((e = launch_prep<T, D>(a, st, prof)) != hipSuccess) return e;
@@ -534,23 +712,10 @@ hipError_t launch_fwd(const FwdArgs& a, void* hsave, hipStream_t st, Profiler* p
     ChainArgs c{a.S_in, a.Mseg, a.Nseg, const_cast<float*>(a.Sst), a.P};
     if ((e = launch_chain_fwd<D>(c, BH, st, prof)) != hipSuccess) return e;
   }
-  if (hsave) {
-    if ((e = set_lds((const void*)gdn_fwd_out_kernel<T, D, OUT_AND_STATES>, Lz::out_bytes)) !=
-        hipSuccess)
-      return e;
-    prof_begin(prof, "gdn_fwd_out_save", st);
-    hipLaunchKernelGGL((gdn_fwd_out_kernel<T, D, OUT_AND_STATES>), dim3(BH * a.P),
-                       dim3(64 * fwd_nw<D>()), Lz::out_bytes, st, a, reinterpret_cast<T*>(hsave));
-    prof_end(prof, st);
-    return hipGetLastError();
-  }
-  if ((e = set_lds((const void*)gdn_fwd_out_kernel<T, D, OUT_ONLY>, Lz::out_bytes)) != hipSuccess)
-    return e;
-  prof_begin(prof, "gdn_fwd_out", st);
-  hipLaunchKernelGGL((gdn_fwd_out_kernel<T, D, OUT_ONLY>), dim3(BH * a.P), dim3(64 * fwd_nw<D>()),
-                     Lz::out_bytes, st, a, (T*)nullptr);
-  prof_end(prof, st);
-  return hipGetLastError();
+  if (hsave)
+    return launch_out<T, D, OUT_AND_STATES>(a, reinterpret_cast<T*>(hsave), st, prof,
+                                            "gdn_fwd_out_save");
+  return launch_out<T, D, OUT_ONLY>(a, nullptr, st, prof, "gdn_fwd_out");
 }
 
 #define SF_INST(T, D)                                                                      \

@@ -225,11 +225,14 @@ __global__ __launch_bounds__(4 * D, 2) void gdn_bwd_dscan_kernel(BwdArgs a, int 
 template <int D>
 __global__ __launch_bounds__(256) void gdn_chain_bwd_kernel(const float* dS_out, const float* MTseg,
                                                             const float* NBseg, float* dSend,
-                                                            int P) {
+                                                            int P, int BH) {
   constexpr int RT = D / 16, NT = D / 64, KS = D / 4, LDS_ = D + 4;
   __shared__ __align__(16) float Sl[16 * LDS_];
   const int w = wave_id(), lane = lane_id();
-  const int bh = blockIdx.x / RT, r0 = 16 * (blockIdx.x % RT);
+  int bh, rt;
+  xcd_seq_tile(blockIdx.x, RT, bh, rt);
+  if (bh >= BH) return;
+  const int r0 = 16 * rt;
   const size_t DD = (size_t)D * D;
   const float* G0 = dS_out ? dS_out + bh * DD : nullptr;
   float* out = dSend + (size_t)bh * P * DD;
@@ -842,12 +845,12 @@ hipError_t launch_bwd(const BwdArgs& a0, bool saved, hipStream_t st, Profiler* p
     prof_end(prof, st);
     // 3. chains
     if (!saved) {
-      ChainArgs c{f.S_in, f.Mseg, f.Nseg, const_cast<float*>(f.Sst), P};
+      ChainArgs c{f.S_in, f.Mseg, f.Nseg, const_cast<float*>(f.Sst), P, BH};
       if ((e = launch_chain_fwd<D>(c, BH, st, prof)) != hipSuccess) return e;
     }
     prof_begin(prof, "gdn_chain_bwd", st);
-    hipLaunchKernelGGL((gdn_chain_bwd_kernel<D>), dim3(BH * (D / 16)), dim3(256), 0, st, a.dS_out,
-                       f.MTseg, a.NBseg, a.dSend, P);
+    hipLaunchKernelGGL((gdn_chain_bwd_kernel<D>), dim3(xcd_grid(BH, D / 16)), dim3(256), 0, st,
+                       a.dS_out, f.MTseg, a.NBseg, a.dSend, P, BH);
     prof_end(prof, st);
     dSend = a.dSend;
     dsend_P = P;

@@ -555,7 +555,8 @@ __global__ __launch_bounds__(64 * fwd_nw<D>(), 2) void gdn_fwd_summary_kernel(Fw
 
 // ------------------------------------------------------------ chain ---------
 // Entry states of all segments: Sst[0] = S_in (or 0), Sst[j+1] = Sst[j] M_j + N_j.
-// One workgroup of 4 waves per (b, h, 16 rows of S); fp32 MFMA.  The next
+// One workgroup of 4 waves per (b, h, 16 rows of S), the workgroups of one
+// (b, h) on one XCD; fp32 MFMA.  The next
 // segment's map is loaded into registers while the current product runs, so
 // each step costs one dependent chain of MFMAs, not a round trip to memory.
 template <int D>
@@ -566,7 +567,10 @@ __global__ __launch_bounds__(256) void gdn_chain_fwd_kernel(ChainArgs c) {
   constexpr int LDS_ = D + 4;
   __shared__ __align__(16) float Sl[16 * LDS_];
   const int w = wave_id(), lane = lane_id();
-  const int bh = blockIdx.x / RT, r0 = 16 * (blockIdx.x % RT);
+  int bh, rt;
+  xcd_seq_tile(blockIdx.x, RT, bh, rt);
+  if (bh >= c.BH) return;
+  const int r0 = 16 * rt;
   const size_t DD = (size_t)D * D;
   const float* Sin = c.S_in ? c.S_in + bh * DD : nullptr;
   float* Sst = c.Sst + (size_t)bh * c.P * DD;
@@ -666,7 +670,7 @@ hipError_t launch_prep(const FwdArgs& a, hipStream_t st, Profiler* prof) {
 template <int D>
 hipError_t launch_chain_fwd(const ChainArgs& c, int BH, hipStream_t st, Profiler* prof) {
   prof_begin(prof, "gdn_chain_fwd", st);
-  hipLaunchKernelGGL((gdn_chain_fwd_kernel<D>), dim3(BH * (D / 16)), dim3(256), 0, st, c);
+  hipLaunchKernelGGL((gdn_chain_fwd_kernel<D>), dim3(xcd_grid(BH, D / 16)), dim3(256), 0, st, c);
   prof_end(prof, st);
   return hipGetLastError();
 }
@@ -709,7 +713,7 @@ hipError_t launch_fwd(const FwdArgs& a, void* hsave, hipStream_t st, Profiler* p
   if (a.P > 1) {
     const int nseg = hsave ? a.P : a.P - 1;
     if ((e = launch_fwd_summary<T, D>(a, nseg, st, prof, "gdn_fwd_summary")) != hipSuccess) return e;
-    ChainArgs c{a.S_in, a.Mseg, a.Nseg, const_cast<float*>(a.Sst), a.P};
+    ChainArgs c{a.S_in, a.Mseg, a.Nseg, const_cast<float*>(a.Sst), a.P, BH};
     if ((e = launch_chain_fwd<D>(c, BH, st, prof)) != hipSuccess) return e;
   }
   if (hsave)

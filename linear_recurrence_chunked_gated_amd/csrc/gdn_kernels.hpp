@@ -37,7 +37,21 @@ struct ChainArgs {
   const float* Nseg;
   float* Sst;
   int P;
+  int BH;
 };
+
+// Workgroups are handed to the 8 XCDs round-robin (workgroup i runs on XCD
+// i % 8), and each XCD has its own L2.  The chain kernels run RT workgroups
+// per sequence, all reading the same segment maps, so they are placed on one
+// XCD: workgroup i takes sequence bh (>= BH for padding workgroups, which
+// exit) and row tile r.
+constexpr int kXcds = 8;
+__host__ __device__ inline void xcd_seq_tile(int i, int RT, int& bh, int& r) {
+  const int x = i % kXcds, s = i / kXcds;
+  bh = x + kXcds * (s / RT);
+  r = s % RT;
+}
+inline int xcd_grid(int BH, int RT) { return (BH + kXcds - 1) / kXcds * kXcds * RT; }
 
 struct BwdArgs {
   FwdArgs f;            // inputs, plan and forward workspace (o, S_out unused)

@@ -420,7 +420,10 @@ __global__ __launch_bounds__(4 * D, 2) void gdn_bwd_grads_kernel(BwdArgs a) {
   float* dbp = part + NW * BLK + w * BLK;     // dbeta per token
   float* ddp = part + 2 * NW * BLK + w * BLK; // dD per token
   float* dgc = part + 3 * NW * BLK;           // per-wave <dS', S>
-  const int blk = blockIdx.x % f.nblk, bh = blockIdx.x / f.nblk;
+  // Consecutive workgroups take the heads of one token block, so the rows
+  // of [B, T, H, D] that run concurrently are read whole (H * D elements).
+  const int BH = f.B * f.H;
+  const int blk = blockIdx.x / BH, bh = blockIdx.x % BH;
   const int b = bh / f.H, h = bh % f.H;
   const int t0 = blk * BLK, nv = min(BLK, f.T - t0);
   const size_t rs = (size_t)f.H * D;
@@ -440,26 +443,30 @@ __global__ __launch_bounds__(4 * D, 2) void gdn_bwd_grads_kernel(BwdArgs a) {
   // registers until then.
   typedef Tile<T, D, 4 * D> Tl;
   uint4 r2[Tl::NCH], r3[Tl::NCH];
+  f32x4 Sx[DKT], dSx[DKT];  // by dv-tile: m = dk-tile, n = dv-tile w
   {
-    // issue order = wait order (vmcnt counts in order): gates, q, k, then v, dO
+    // issue order = wait order (vmcnt counts in order): gates, q, k, the
+    // states (first used in phase C), then v, dO; the scheduling barriers
+    // keep the compiler from hoisting the state loads in front of q and k
     const size_t gidx = gofs + (size_t)min(lane, nv - 1) * f.H;
     const float ra = f.alpha[gidx], rb = f.beta[gidx];
     uint4 r0[Tl::NCH], r1[Tl::NCH];
     Tl::load(r0, q, rs, nv);
     Tl::load(r1, k, rs, nv);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int aa = 0; aa < DKT; ++aa) {
+      const size_t off = (size_t)(16 * w + li) * D + 16 * aa + g4;
+      Sx[aa] = ld4f(hS + off);
+      dSx[aa] = ld4f(hG + off);
+    }
+    __builtin_amdgcn_sched_barrier(0);
     Tl::load(r2, v, rs, nv);
     Tl::load(r3, dO, rs, nv);
     for (int i = threadIdx.x; i < 3 * NW * BLK + NW + 4; i += 64 * NW) part[i] = 0.f;
     Tl::to_lds(r0, Qs, LDD, nv);
     Tl::to_lds(r1, Ks, LDD, nv);
     if (w == 0) block_gates(lane < nv ? __logf(ra) : 0.f, lane < nv ? rb : 0.f, G);
-  }
-  f32x4 Sx[DKT], dSx[DKT];  // by dv-tile: m = dk-tile, n = dv-tile w
-#pragma unroll
-  for (int aa = 0; aa < DKT; ++aa) {
-    const size_t off = (size_t)(16 * w + li) * D + 16 * aa + g4;
-    Sx[aa] = ld4f(hS + off);
-    dSx[aa] = ld4f(hG + off);
   }
   lds_barrier();
   // ---- B: scores

@@ -137,7 +137,9 @@ __global__ __launch_bounds__(256) void gdn_prep_kernel(FwdArgs a) {
   float* Tm = reinterpret_cast<float*>(smem + Lz::oT);
   const GateLds G = gate_lds(smem + Lz::oG);
 
-  const int blk = blockIdx.x % a.nblk, bh = blockIdx.x / a.nblk;
+  // consecutive workgroups: the heads of one token block (whole rows of k)
+  const int BH = a.B * a.H;
+  const int blk = blockIdx.x / BH, bh = blockIdx.x % BH;
   const int b = bh / a.H, h = bh % a.H;
   const int t0 = blk * BLK, nv = min(BLK, a.T - t0);
   const size_t rs = (size_t)a.H * D;

@@ -107,7 +107,7 @@ sf_status sf_gdn_chunk_bwd(const sf_gdn_shape* shape, const void* q, const void*
  * chunk's block states until its backward, sf_gdn_chunk_fwd_save also writes
  *   - the entry state of every 64-token block, [B, H, ceil(T/64), Dv, Dk] in
  *     the q/k/v dtype (each state enters the backward's products in it)
- *   - the segment transition maps of the in-chunk scan, transposed, fp32
+ *   - the segment transition maps of the in-chunk scan, row-major, fp32
  *     [B, H, P, Dk, Dk]
  *   - per block, T diag(beta o gamma) and T diag(beta) for T = (I + A)^{-1} of
  *     the block-local (WY/UT) form, [B, H, ceil(T/64), 2, 64, 64] in the

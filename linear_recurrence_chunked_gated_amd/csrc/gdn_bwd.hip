@@ -219,87 +219,6 @@ __global__ __launch_bounds__(4 * D, 2) void gdn_bwd_dscan_kernel(BwdArgs a, int 
   }
 }
 
-// ------------------------------------------------------------ chain ---------
-// Exit gradients of all segments: dSend[P-1] = dS_out (or 0),
-// dSend[j-1] = dSend[j] M_j^T + NB_j.  Same layout as the forward chain.
-template <int D>
-__global__ __launch_bounds__(256) void gdn_chain_bwd_kernel(const float* dS_out, const float* MTseg,
-                                                            const float* NBseg, float* dSend,
-                                                            int P, int BH) {
-  constexpr int RT = D / 16, NT = D / 64, KS = D / 4, LDS_ = D + 4;
-  __shared__ __align__(16) float Sl[16 * LDS_];
-  const int w = wave_id(), lane = lane_id();
-  int bh, rt;
-  xcd_seq_tile(blockIdx.x, RT, bh, rt);
-  if (bh >= BH) return;
-  const int r0 = 16 * rt;
-  const size_t DD = (size_t)D * D;
-  const float* G0 = dS_out ? dS_out + bh * DD : nullptr;
-  float* out = dSend + (size_t)bh * P * DD;
-  for (int i = threadIdx.x; i < 16 * D; i += 256) {
-    const int rr = i / D, cc = i % D;
-    const float x = G0 ? G0[(size_t)(r0 + rr) * D + cc] : 0.f;
-    Sl[rr * LDS_ + cc] = x;
-    out[(size_t)(P - 1) * DD + (size_t)(r0 + rr) * D + cc] = x;
-  }
-  float bm[NT][KS], nn[NT][4];
-  auto load_map = [&](int j, float (&m)[NT][KS], float (&n)[NT][4]) {
-    const float* MT = MTseg + ((size_t)bh * P + j) * DD;  // MT[k][n] = M[n][k]
-    const float* N = NBseg + ((size_t)bh * P + j) * DD;
-#pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      const int col = 16 * (w * NT + t) + (lane & 15);
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) m[t][ks] = MT[(size_t)(4 * ks + (lane >> 4)) * D + col];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) n[t][e] = N[(size_t)(r0 + 4 * (lane >> 4) + e) * D + col];
-    }
-  };
-  if (P > 1) load_map(P - 1, bm, nn);
-  lds_barrier();
-  for (int j = P - 1; j >= 1; --j) {
-    float bm2[NT][KS], nn2[NT][4];
-    const bool more = j >= 2;
-    if (more) load_map(j - 1, bm2, nn2);
-    f32x4 acc[NT][2];
-#pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      acc[t][0] = f32x4{nn[t][0], nn[t][1], nn[t][2], nn[t][3]};
-      acc[t][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      const float av = Sl[(lane & 15) * LDS_ + 4 * ks + (lane >> 4)];
-#pragma unroll
-      for (int t = 0; t < NT; ++t)
-        acc[t][ks & 1] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bm[t][ks], acc[t][ks & 1], 0, 0, 0);
-    }
-    lds_barrier();
-    float* Snext = out + (size_t)(j - 1) * DD;
-#pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      const int n = 16 * (w * NT + t) + (lane & 15);
-      const f32x4 x = acc[t][0] + acc[t][1];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int m = 4 * (lane >> 4) + e;
-        Sl[m * LDS_ + n] = x[e];
-        Snext[(size_t)(r0 + m) * D + n] = x[e];
-      }
-    }
-    if (more) {
-#pragma unroll
-      for (int t = 0; t < NT; ++t) {
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) bm[t][ks] = bm2[t][ks];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) nn[t][e] = nn2[t][e];
-      }
-    }
-    lds_barrier();
-  }
-}
-
 // -------------------------------------------------------- block gradients ---
 // Sums of a 16x16 accumulator tile C[m][n] (lane: m = 4 g + e, n = i):
 // over n for each m (result valid in lanes with i == 0, element e), and over
@@ -853,12 +772,10 @@ hipError_t launch_bwd(const BwdArgs& a0, bool saved, hipStream_t st, Profiler* p
     // 3. chains
     if (!saved) {
       ChainArgs c{f.S_in, f.Mseg, f.Nseg, const_cast<float*>(f.Sst), P, BH};
-      if ((e = launch_chain_fwd<D>(c, BH, st, prof)) != hipSuccess) return e;
+      if ((e = launch_chain<D, false>(c, st, prof)) != hipSuccess) return e;
     }
-    prof_begin(prof, "gdn_chain_bwd", st);
-    hipLaunchKernelGGL((gdn_chain_bwd_kernel<D>), dim3(xcd_grid(BH, D / 16)), dim3(256), 0, st,
-                       a.dS_out, f.MTseg, a.NBseg, a.dSend, P, BH);
-    prof_end(prof, st);
+    ChainArgs cb{a.dS_out, f.MBseg, a.NBseg, a.dSend, P, BH};
+    if ((e = launch_chain<D, true>(cb, st, prof)) != hipSuccess) return e;
     dSend = a.dSend;
     dsend_P = P;
   } else {

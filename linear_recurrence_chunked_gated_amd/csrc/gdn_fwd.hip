@@ -537,106 +537,147 @@ __global__ __launch_bounds__(64 * fwd_nw<D>(), 2) void gdn_fwd_summary_kernel(Fw
   }
 
   // Nt holds N^T (m = dk, n = dv) -> N[dv][dk..]; Mt holds M^T (m = j, n = i) -> M[i][j..].
-  float* Mo = a.Mseg + ((size_t)bh * a.P + seg) * D * D;
+  // The forward chain takes M transposed, the backward chain M row-major.
+  float* MTo = a.Mseg + ((size_t)bh * a.P + seg) * D * D;
   float* No = a.Nseg + ((size_t)bh * a.P + seg) * D * D;
-  float* MTo = a.MTseg ? a.MTseg + ((size_t)bh * a.P + seg) * D * D : nullptr;
+  float* Mo = a.MBseg ? a.MBseg + ((size_t)bh * a.P + seg) * D * D : nullptr;
 #pragma unroll
   for (int bb = 0; bb < NDV; ++bb)
 #pragma unroll
     for (int aa = 0; aa < DKT; ++aa) {
       const size_t off = (size_t)(16 * (dv0 + bb) + li) * D + 16 * aa + g4;
       *reinterpret_cast<f32x4*>(No + off) = Nt[bb][aa];
-      *reinterpret_cast<f32x4*>(Mo + off) = Mt[bb][aa];
-      if (MTo) {
+      if (Mo) *reinterpret_cast<f32x4*>(Mo + off) = Mt[bb][aa];
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          MTo[(size_t)(16 * aa + g4 + e) * D + 16 * (dv0 + bb) + li] = Mt[bb][aa][e];
-      }
+      for (int e = 0; e < 4; ++e)
+        MTo[(size_t)(16 * aa + g4 + e) * D + 16 * (dv0 + bb) + li] = Mt[bb][aa][e];
     }
 }
 
 // ------------------------------------------------------------ chain ---------
-// Entry states of all segments: Sst[0] = S_in (or 0), Sst[j+1] = Sst[j] M_j + N_j.
-// One workgroup of 4 waves per (b, h, 16 rows of S), the workgroups of one
-// (b, h) on one XCD; fp32 MFMA.  The next
-// segment's map is loaded into registers while the current product runs, so
-// each step costs one dependent chain of MFMAs, not a round trip to memory.
-template <int D>
-__global__ __launch_bounds__(256) void gdn_chain_fwd_kernel(ChainArgs c) {
-  constexpr int RT = D / 16;        // row tiles per state
-  constexpr int NT = D / 64;        // column tiles per wave
-  constexpr int KS = D / 4;         // MFMA steps along the contraction
-  constexpr int LDS_ = D + 4;
-  __shared__ __align__(16) float Sl[16 * LDS_];
-  const int w = wave_id(), lane = lane_id();
+// The boundary-state chain between segments, X' = X B_j + C_j for one
+// sequence (Eq. 5 inside the chunk; its backward mirror, Eq. 7, for REV):
+//   forward:  X_0 = S_in (or 0),   X_{j+1} = X_j M_j + N_j,      j = 0 .. P-2
+//   backward: X_{P-1} = dS_out (or 0), X_{j-1} = X_j M_j^T + NB_j, j = P-1 .. 1
+// All X are written to out[P][D][D].  Bt[j] holds B_j^T row-major (the
+// transposed maps forward, the row-major maps backward) so that a lane's
+// 8 contraction elements are contiguous.
+//
+// One workgroup per (sequence, 16 rows of X), D/16 waves, wave w owning
+// output columns 16 w ..; the workgroups of one sequence on one XCD.  Each
+// product runs on bf16 MFMA with the operands split into bf16 pairs, x = hi +
+// lo, and the three terms hi*hi + hi*lo + lo*hi accumulated in fp32: about
+// 2^-16 relative error per term, against fp32 MFMA at a quarter of the rate.
+// The maps of the next two steps are in flight in registers while a step
+// runs, so a step costs its MFMA chain and one LDS hand-off of X.
+__device__ __forceinline__ void split_bf16(const f32x4& a, const f32x4& b, bf16x8& hi, bf16x8& lo) {
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const bf16 ha = (bf16)a[e], hb = (bf16)b[e];
+    hi[e] = ha;
+    hi[4 + e] = hb;
+    lo[e] = (bf16)(a[e] - (float)ha);
+    lo[4 + e] = (bf16)(b[e] - (float)hb);
+  }
+}
+
+template <int D> struct ChainIn {
+  static constexpr int KS = D / 32;
+  f32x4 b[KS][2];  // B^T row (16 w + i), contraction 32 s + 8 g .. + 7
+  float c[4];      // C rows r0 + 4 g + e, column 16 w + i
+};
+
+template <int D, bool REV>
+__global__ __launch_bounds__(64 * (D / 16)) void gdn_chain_kernel(ChainArgs c) {
+  constexpr int RT = D / 16, KS = D / 32, LDX = D + 8;
+  __shared__ __align__(16) bf16 Xs[2][2][16 * LDX];  // [ping-pong][hi, lo] rows of X
+  const int w = wave_id(), lane = lane_id(), g = lane >> 4;
   int bh, rt;
   xcd_seq_tile(blockIdx.x, RT, bh, rt);
   if (bh >= c.BH) return;
-  const int r0 = 16 * rt;
+  const int P = c.P, r0 = 16 * rt, col = 16 * w + (lane & 15);
   const size_t DD = (size_t)D * D;
-  const float* Sin = c.S_in ? c.S_in + bh * DD : nullptr;
-  float* Sst = c.Sst + (size_t)bh * c.P * DD;
-  for (int i = threadIdx.x; i < 16 * D; i += 256) {
-    const int rr = i / D, cc = i % D;
-    const float x = Sin ? Sin[(size_t)(r0 + rr) * D + cc] : 0.f;
-    Sl[rr * LDS_ + cc] = x;
-    Sst[(size_t)(r0 + rr) * D + cc] = x;
-  }
-  float bm[NT][KS], nn[NT][4];
-  auto load_map = [&](int j, float (&m)[NT][KS], float (&n)[NT][4]) {
-    const float* M = c.Mseg + ((size_t)bh * c.P + j) * DD;
-    const float* N = c.Nseg + ((size_t)bh * c.P + j) * DD;
+  const float* Bt = c.Bt + (size_t)bh * P * DD;
+  const float* Cm = c.C + (size_t)bh * P * DD;
+  float* out = c.out + (size_t)bh * P * DD;
+  // this lane's 4 entries of the wave's 16x16 tile: rows r0 + 4 g + e, column col
+  auto put = [&](int buf, int idx, const f32x4& x) {
 #pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      const int col = 16 * (w * NT + t) + (lane & 15);
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) m[t][ks] = M[(size_t)(4 * ks + (lane >> 4)) * D + col];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) n[t][e] = N[(size_t)(r0 + 4 * (lane >> 4) + e) * D + col];
+    for (int e = 0; e < 4; ++e) {
+      const int m = 4 * g + e;
+      out[(size_t)idx * DD + (size_t)(r0 + m) * D + col] = x[e];
+      const bf16 h = (bf16)x[e];
+      Xs[buf][0][m * LDX + col] = h;
+      Xs[buf][1][m * LDX + col] = (bf16)(x[e] - (float)h);
     }
   };
-  if (c.P > 1) load_map(0, bm, nn);
+  const int nst = P - 1;
+  // The map fetches are arranged so that a step waits only for its own
+  // fetch (vmcnt counts in order):
+  //  - a fetch is never conditional (a step past the end is clamped to the
+  //    last one and unused), so the three ring buffers stay in place instead
+  //    of being copied, which would wait for the loads in flight;
+  //  - scheduling barriers keep each fetch's loads together, in order;
+  //  - buffer loads with fixed per-lane byte offsets and a scalar step
+  //    offset need no fresh vector address registers (reusing those would
+  //    wait for the loads that last wrote them).  Offsets past the resource
+  //    read zero instead of faulting.
+  const __amdgpu_buffer_rsrc_t rB = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<float*>(Bt), 0, (int)(P * DD * sizeof(float)), 0x00020000);
+  const __amdgpu_buffer_rsrc_t rC = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<float*>(Cm), 0, (int)(P * DD * sizeof(float)), 0x00020000);
+  const int boff = 4 * (col * D + 8 * g), coff = 4 * ((r0 + 4 * g) * D + col);
+  auto fetch = [&](int i, ChainIn<D>& in) {
+    __builtin_amdgcn_sched_barrier(0);
+    i = min(i, nst - 1);
+    const int so = (REV ? P - 1 - i : i) * (int)(DD * sizeof(float));
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      in.b[s][0] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rB, boff + 128 * s, so, 0));
+      in.b[s][1] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rB, boff + 128 * s + 16, so, 0));
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      in.c[e] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rC, coff + 4 * D * e, so, 0));
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  auto step = [&](int i, const ChainIn<D>& in) {
+    const bf16* Xh = Xs[i & 1][0];
+    const bf16* Xl = Xs[i & 1][1];
+    f32x4 a0 = {in.c[0], in.c[1], in.c[2], in.c[3]}, a1 = {0.f, 0.f, 0.f, 0.f}, a2 = a1;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      const bf16x8 xh = frag_row<bf16, STD>(Xh, LDX, s), xl = frag_row<bf16, STD>(Xl, LDX, s);
+      bf16x8 bh8, bl8;
+      split_bf16(in.b[s][0], in.b[s][1], bh8, bl8);
+      a0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xh, bh8, a0, 0, 0, 0);
+      a1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xh, bl8, a1, 0, 0, 0);
+      a2 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xl, bh8, a2, 0, 0, 0);
+    }
+    put((i + 1) & 1, REV ? P - 2 - i : i + 1, a0 + (a1 + a2));
+    lds_barrier();
+  };
+  {
+    const float* X0 = c.X0 ? c.X0 + (size_t)bh * DD : nullptr;
+    f32x4 x;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) x[e] = X0 ? X0[(size_t)(r0 + 4 * g + e) * D + col] : 0.f;
+    put(0, REV ? P - 1 : 0, x);
+  }
+  if (nst <= 0) return;
+  ChainIn<D> p0, p1, p2;
+  fetch(0, p0);
+  fetch(1, p1);
   lds_barrier();
-  for (int j = 0; j + 1 < c.P; ++j) {
-    float bm2[NT][KS], nn2[NT][4];
-    const bool more = j + 2 < c.P;
-    if (more) load_map(j + 1, bm2, nn2);
-    f32x4 acc[NT][2];
-#pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      acc[t][0] = f32x4{nn[t][0], nn[t][1], nn[t][2], nn[t][3]};
-      acc[t][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      const float av = Sl[(lane & 15) * LDS_ + 4 * ks + (lane >> 4)];
-#pragma unroll
-      for (int t = 0; t < NT; ++t)
-        acc[t][ks & 1] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bm[t][ks], acc[t][ks & 1], 0, 0, 0);
-    }
-    lds_barrier();
-    float* Snext = Sst + (size_t)(j + 1) * DD;
-#pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      const int n = 16 * (w * NT + t) + (lane & 15);
-      const f32x4 x = acc[t][0] + acc[t][1];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int m = 4 * (lane >> 4) + e;
-        Sl[m * LDS_ + n] = x[e];
-        Snext[(size_t)(r0 + m) * D + n] = x[e];
-      }
-    }
-    if (more) {
-#pragma unroll
-      for (int t = 0; t < NT; ++t) {
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) bm[t][ks] = bm2[t][ks];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) nn[t][e] = nn2[t][e];
-      }
-    }
-    lds_barrier();
+  for (int i = 0; i < nst; i += 3) {
+    fetch(i + 2, p2);
+    step(i, p0);
+    if (i + 1 >= nst) break;
+    fetch(i + 3, p0);
+    step(i + 1, p1);
+    if (i + 2 >= nst) break;
+    fetch(i + 4, p1);
+    step(i + 2, p2);
   }
 }
 
@@ -669,10 +710,11 @@ hipError_t launch_prep(const FwdArgs& a, hipStream_t st, Profiler* prof) {
   return hipGetLastError();
 }
 
-template <int D>
-hipError_t launch_chain_fwd(const ChainArgs& c, int BH, hipStream_t st, Profiler* prof) {
-  prof_begin(prof, "gdn_chain_fwd", st);
-  hipLaunchKernelGGL((gdn_chain_fwd_kernel<D>), dim3(xcd_grid(BH, D / 16)), dim3(256), 0, st, c);
+template <int D, bool REV>
+hipError_t launch_chain(const ChainArgs& c, hipStream_t st, Profiler* prof) {
+  prof_begin(prof, REV ? "gdn_chain_bwd" : "gdn_chain_fwd", st);
+  hipLaunchKernelGGL((gdn_chain_kernel<D, REV>), dim3(xcd_grid(c.BH, D / 16)), dim3(4 * D), 0, st,
+                     c);
   prof_end(prof, st);
   return hipGetLastError();
 }
@@ -705,7 +747,7 @@ hipError_t launch_states(const FwdArgs& a, void* hst, hipStream_t st, Profiler* 
 }
 
 // hsave: when not null, every block's entry state is stored there and the
-// segment maps M are computed for all P segments (a.Mseg then points into the
+// segment maps M are computed for all P segments (a.MBseg then points into the
 // caller's saved buffer), so that the backward can skip its recompute.
 template <typename T, int D>
 hipError_t launch_fwd(const FwdArgs& a, void* hsave, hipStream_t st, Profiler* prof) {
@@ -716,7 +758,7 @@ hipError_t launch_fwd(const FwdArgs& a, void* hsave, hipStream_t st, Profiler* p
     const int nseg = hsave ? a.P : a.P - 1;
     if ((e = launch_fwd_summary<T, D>(a, nseg, st, prof, "gdn_fwd_summary")) != hipSuccess) return e;
     ChainArgs c{a.S_in, a.Mseg, a.Nseg, const_cast<float*>(a.Sst), a.P, BH};
-    if ((e = launch_chain_fwd<D>(c, BH, st, prof)) != hipSuccess) return e;
+    if ((e = launch_chain<D, false>(c, st, prof)) != hipSuccess) return e;
   }
   if (hsave)
     return launch_out<T, D, OUT_AND_STATES>(a, reinterpret_cast<T*>(hsave), st, prof,
@@ -733,8 +775,10 @@ SF_INST(bf16, 128)
 SF_INST(bf16, 64)
 SF_INST(float, 64)
 #undef SF_INST
-template hipError_t launch_chain_fwd<128>(const ChainArgs&, int, hipStream_t, Profiler*);
-template hipError_t launch_chain_fwd<64>(const ChainArgs&, int, hipStream_t, Profiler*);
+template hipError_t launch_chain<128, false>(const ChainArgs&, hipStream_t, Profiler*);
+template hipError_t launch_chain<64, false>(const ChainArgs&, hipStream_t, Profiler*);
+template hipError_t launch_chain<128, true>(const ChainArgs&, hipStream_t, Profiler*);
+template hipError_t launch_chain<64, true>(const ChainArgs&, hipStream_t, Profiler*);
 
 }  // namespace sfgdn
 

@@ -23,19 +23,23 @@ struct FwdArgs {
   int B, T, H;
   int nblk, L, P;
   // workspace
-  float* Mseg;         // [B*H][P][D][D]  segment transition maps
-  float* MTseg;        // [B*H][P][D][D]  the same maps transposed (for the backward), or null
+  float* Mseg;         // [B*H][P][D][D]  segment transition maps M (S' = S M + N), transposed:
+                       //                  MT[n][k] = M[k][n], the forward chain's operand
+  float* MBseg;        // [B*H][P][D][D]  the same maps row-major (the backward chain's), or null
   float* Nseg;         // [B*H][P][D][D]  segment zero-entry exit states
   const float* Sst;    // [B*H][sst_P][D][D] segment entry states (S_in when P == 1)
   int sst_P;
   void* tw;            // [B*H][nblk][2][64][64] per-block Tp, Tpp (operand type), by the Pre kernel
 };
 
+// One boundary-state chain over the P segments of each sequence (see
+// gdn_chain_kernel): entry X0 (null = zeros), per-segment B_j^T and C_j,
+// all P states out.
 struct ChainArgs {
-  const float* S_in;
-  const float* Mseg;
-  const float* Nseg;
-  float* Sst;
+  const float* X0;
+  const float* Bt;
+  const float* C;
+  float* out;
   int P;
   int BH;
 };
@@ -101,13 +105,13 @@ hipError_t launch_fwd_summary(const FwdArgs& a, int nseg, hipStream_t st, Profil
                               const char* name);
 template <typename T, int D>
 hipError_t launch_prep(const FwdArgs& a, hipStream_t st, Profiler* prof);
-template <int D>
-hipError_t launch_chain_fwd(const ChainArgs& c, int BH, hipStream_t st, Profiler* prof);
+template <int D, bool REV>
+hipError_t launch_chain(const ChainArgs& c, hipStream_t st, Profiler* prof);
 template <typename T, int D>
 hipError_t launch_states(const FwdArgs& a, void* hst, hipStream_t st, Profiler* prof);
-// saved: a.hst already holds every block's entry state, a.f.MTseg every
-// segment's transposed map and a.f.tw every block's Tp, Tpp (from a saving
-// forward), so the forward recompute is skipped.
+// saved: a.hst already holds every block's entry state, a.f.MBseg every
+// segment's map and a.f.tw every block's Tp, Tpp (from a saving forward), so
+// the forward recompute is skipped.
 template <typename T, int D>
 hipError_t launch_bwd(const BwdArgs& a, bool saved, hipStream_t st, Profiler* prof);
 // Short convolution: GR tokens per backward run; dwp holds the B * ceil(T/GR)

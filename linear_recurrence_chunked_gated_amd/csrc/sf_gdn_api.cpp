@@ -206,8 +206,8 @@ sf_status sf_gdn_chunk_bwd_workspace_size(const sf_gdn_shape* shape, size_t* byt
 
 namespace {
 
-// Layout: per-block entry states [B*H*nblk][D][D], the transposed segment
-// maps [B*H*P][D][D] (P > 1), then the Pre kernel's per-block Tp, Tpp.
+// Layout: per-block entry states [B*H*nblk][D][D], the segment maps
+// [B*H*P][D][D] row-major (P > 1), then the Pre kernel's per-block Tp, Tpp.
 size_t saved_maps_off(const Plan& p) { return blk_buf(p); }
 size_t saved_tw_off(const Plan& p) { return blk_buf(p) + (p.P > 1 ? seg_buf(p) : 0); }
 size_t saved_bytes(const Plan& p) {
@@ -266,7 +266,7 @@ sf_status fwd_impl(const sf_gdn_shape* shape, const void* q, const void* k, cons
     a.tw = save ? (char*)saved + saved_tw_off(p) : ws + fwd_seg(p);
     if (p.P > 1) {
       a.Mseg = (float*)ws;
-      a.MTseg = save ? (float*)((char*)saved + saved_maps_off(p)) : nullptr;
+      a.MBseg = save ? (float*)((char*)saved + saved_maps_off(p)) : nullptr;
       a.Nseg = (float*)(ws + seg_buf(p));
       a.Sst = (float*)(ws + 2 * seg_buf(p));
       a.sst_P = p.P;
@@ -346,11 +346,11 @@ sf_status bwd_impl(const sf_gdn_shape* shape, const void* q, const void* k, cons
     a.hst = ws + 5 * sb;
     a.dhst = ws + 5 * sb + bb;
     f.tw = ws + 5 * sb + 2 * bb;
-    f.MTseg = (float*)(ws + 5 * sb + 2 * bb + tw_buf(p));
+    f.MBseg = (float*)(ws + 5 * sb + 2 * bb + tw_buf(p));
     if (use_saved) {
       char* sv = (char*)const_cast<void*>(saved);
       a.hst = sv;
-      if (p.P > 1) f.MTseg = (float*)(sv + saved_maps_off(p));
+      if (p.P > 1) f.MBseg = (float*)(sv + saved_maps_off(p));
       f.tw = sv + saved_tw_off(p);
     }
     a.dO = dO; a.dS_out = dS_out;

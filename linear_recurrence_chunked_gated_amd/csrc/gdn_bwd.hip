@@ -504,6 +504,7 @@ __global__ __launch_bounds__(4 * D, 2) void gdn_bwd_grads_kernel(BwdArgs a) {
       for (int j = 0; j < NJ; ++j)
         acc[j] = Mma<T>::mma(av, frag_row<T, STD>(Os + 16 * (r0 + j) * LDD, LDD, s), acc[j]);
     }
+    f32x4 pgs = {0.f, 0.f, 0.f, 0.f};  // pg summed over this wave's r-tiles
     const int s0 = 16 * st + g4;
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
@@ -520,8 +521,9 @@ __global__ __launch_bounds__(4 * D, 2) void gdn_bwd_grads_kernel(BwdArgs a) {
       }
       st4(pp, dm[0], dm[1], dm[2], dm[3]);
       add_cols(dgp, 16 * (r0 + j), pg, 1.f);   // dg_r += sum_s
-      add_rows(dgp, 16 * st, pg, -1.f);        // dg_s -= sum_r
+      pgs += pg;
     }
+    add_rows(dgp, 16 * st, pgs, -1.f);         // dg_s -= sum_r
   }
   lds_barrier();
   // ---- H: dQ^T = diag-scaled (S^T dO^T) + K^T dPm^T  (wave: dk-tile w); dK^T starts
@@ -666,6 +668,9 @@ __global__ __launch_bounds__(4 * D, 2) void gdn_bwd_grads_kernel(BwdArgs a) {
       for (int j = 0; j < NJ; ++j)
         kk[j] = Mma<T>::mma(ak, frag_row<T, STD>(Ks + 16 * (s0t + j) * LDD, LDD, s), kk[j]);
     }
+    // db's row sums, over this wave's s-tiles, give both the dbeta_r term and
+    // (times beta_r) the row term of dg
+    f32x4 dbr = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
       const int s = 16 * (s0t + j) + li;
@@ -683,9 +688,17 @@ __global__ __launch_bounds__(4 * D, 2) void gdn_bwd_grads_kernel(BwdArgs a) {
         dkk[e] = da * br * gam;
       }
       store_tile_N(dkk, dKKs, LDC, 16 * rt, 16 * (s0t + j));
-      add_rows(dbp, 16 * rt, db, 1.f);
-      add_rows(dgp, 16 * rt, dag, 1.f);
+      dbr += db;
       add_cols(dgp, 16 * (s0t + j), dag, -1.f);
+    }
+    dbr = tile_sum_over_n(dbr);
+    if (li == 0) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = 16 * rt + g4 + e;
+        lds_add(dbp + r, dbr[e]);
+        lds_add(dgp + r, G.beta[r] * dbr[e]);
+      }
     }
   }
   lds_barrier();

@@ -233,8 +233,26 @@ def bench_conv(args):
     wsb = _lib.alloc_workspace(max(_lib.shortconv_bwd_workspace_bytes(
         _lib.conv_shape(1, n, C, W, x.dtype, 1)) for n in chunks), dev)
     stream = torch.cuda.current_stream()
+    overlap = args.overlap and (save or not wl["bwd"])
+    if overlap:
+        from linear_recurrence_chunked_gated_amd import chain as gchain
+        side = torch.cuda.Stream(device=dev)
+        wsf2 = [wsf, _lib.alloc_workspace(ws_f, dev)]
+        wsb2 = [wsb, _lib.alloc_workspace(ws_b, dev)] if wl["bwd"] else None
+
+    def step_overlap():
+        gchain.chain_fwd(q, k, v, al, be, states[0], chunks, o=o, seg_blocks=args.seg_blocks,
+                         stream=stream, save=save, overlap=True, side_stream=side,
+                         workspaces=wsf2, saved=saved if save else None, states=states)
+        if wl["bwd"]:
+            gchain.chain_bwd(q, k, v, al, be, dO, dS_out, chunks, None,
+                             grads=(dq, dk, dv, dal, dbe), seg_blocks=args.seg_blocks,
+                             stream=stream, saved=saved, overlap=True, side_stream=side,
+                             workspaces=wsb2, state_grads=gst[:len(chunks)])
 
     def step():
+        if overlap:
+            return step_overlap()
         for i in range(len(chunks)):
             sl = slice(bounds[i], bounds[i + 1])
             _lib.shortconv_fwd(x[:, sl], w, states[i], 1, y=y[:, sl], conv_out=states[i + 1],
@@ -350,6 +368,9 @@ def main():
     ap.add_argument("--recompute", action="store_true",
                     help="backward recomputes the forward's block states instead of reading the "
                          "saving forward's buffer")
+    ap.add_argument("--overlap", action="store_true",
+                    help="split-and-overlap: each chunk's state-independent launches run on a "
+                         "second stream beside the previous chunk's chain (saved backward)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run a plain 1 GiB device copy (for rocprofv3 counter scaling) and exit")
     ap.add_argument("--write-traffic", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "CALIB_FETCH_CSV",
@@ -409,8 +430,26 @@ def main():
                                                                        args.seg_blocks)), dev)
                  for n in chunks]
     stream = torch.cuda.current_stream()
+    overlap = args.overlap and (save or not wl["bwd"])
+    if overlap:
+        from linear_recurrence_chunked_gated_amd import chain as gchain
+        side = torch.cuda.Stream(device=dev)
+        wsf2 = [wsf, _lib.alloc_workspace(ws_f, dev)]
+        wsb2 = [wsb, _lib.alloc_workspace(ws_b, dev)] if wl["bwd"] else None
+
+    def step_overlap():
+        gchain.chain_fwd(q, k, v, al, be, states[0], chunks, o=o, seg_blocks=args.seg_blocks,
+                         stream=stream, save=save, overlap=True, side_stream=side,
+                         workspaces=wsf2, saved=saved if save else None, states=states)
+        if wl["bwd"]:
+            gchain.chain_bwd(q, k, v, al, be, dO, dS_out, chunks, None,
+                             grads=(dq, dk, dv, dal, dbe), seg_blocks=args.seg_blocks,
+                             stream=stream, saved=saved, overlap=True, side_stream=side,
+                             workspaces=wsb2, state_grads=gst[:len(chunks)])
 
     def step():
+        if overlap:
+            return step_overlap()
         for i in range(len(chunks)):
             sl = slice(bounds[i], bounds[i + 1])
             _lib.chunk_fwd(q[:, sl], k[:, sl], v[:, sl], al[:, sl], be[:, sl], states[i],
@@ -512,7 +551,9 @@ def main():
                    "d_k": D, "d_v": D, "block": C, "chunks": chunks,
                    "seg_blocks": args.seg_blocks or "auto", "parallelism": "single GPU",
                    "backward_states": "saved by the forward" if save else
-                   ("recomputed" if wl["bwd"] else None)},
+                   ("recomputed" if wl["bwd"] else None),
+                   "overlap": "state-independent launches of the next chunk on a second stream"
+                              if overlap else None},
         "roofline": roofline,
         "path_roofline": path,
         "kernels": {n: {"avg_us": round(x["avg_us"], 2), "launches_per_step": x["launches"] // args.steps,

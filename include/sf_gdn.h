@@ -131,6 +131,40 @@ sf_status sf_gdn_chunk_bwd_saved(const sf_gdn_shape* shape, const void* q, const
                                  float* dbeta, float* dS_in, void* workspace, size_t ws_bytes,
                                  void* stream);
 
+/* Split-and-overlap of consecutive chunks on one GPU (the page's remedy for
+ * the exposed state transition: kernels of other work fill the compute units
+ * the state-transition kernels leave idle; Pith review of StateFlow, Figure 2
+ * caption, and "Assumptions & free parameters", split fraction for overlap).
+ * A chunk's call is cut into two launch groups:
+ *   SF_PHASE_BEGIN  the launches that do not read S_in (forward: Pre and the
+ *                   segment maps) or dS_out (backward: the segment
+ *                   gradient maps from a zero exit gradient);
+ *   SF_PHASE_END    the rest: the boundary-state chain and everything after
+ *                   it; o, S_out (dq .. dS_in) are written here;
+ *   SF_PHASE_ALL    both, which is the plain call.
+ * BEGIN then END with the same arguments computes exactly what one ALL call
+ * computes, bit for bit.  The caller keeps the workspace (and `saved`)
+ * untouched between the two and orders END after BEGIN (same stream, or an
+ * event).  With that, chunk i+1's BEGIN may run on another stream while chunk
+ * i's END runs, each with its own workspace.  BEGIN does not read S_in,
+ * dS_out, o, S_out or the gradient outputs, so they may still be in flight.
+ * sf_gdn_chunk_fwd_split is sf_gdn_chunk_fwd (saved == NULL) or
+ * sf_gdn_chunk_fwd_save; sf_gdn_chunk_bwd_saved_split is
+ * sf_gdn_chunk_bwd_saved.  Arguments, layouts, ownership and errors are those
+ * of the whole calls; an unknown phase is SF_ERR_INVALID_ARG. */
+enum { SF_PHASE_ALL = 0, SF_PHASE_BEGIN = 1, SF_PHASE_END = 2 };
+sf_status sf_gdn_chunk_fwd_split(const sf_gdn_shape* shape, const void* q, const void* k,
+                                 const void* v, const float* alpha, const float* beta,
+                                 const float* S_in, void* o, float* S_out, void* saved,
+                                 size_t saved_bytes, void* workspace, size_t ws_bytes, int phase,
+                                 void* stream);
+sf_status sf_gdn_chunk_bwd_saved_split(const sf_gdn_shape* shape, const void* q, const void* k,
+                                       const void* v, const float* alpha, const float* beta,
+                                       const void* saved, size_t saved_bytes, const void* dO,
+                                       const float* dS_out, void* dq, void* dk, void* dv,
+                                       float* dalpha, float* dbeta, float* dS_in, void* workspace,
+                                       size_t ws_bytes, int phase, void* stream);
+
 /* Short causal depthwise convolution of one chunk, with its boundary state
  * ("auxiliary local-convolution states" of a chunk: Pith review of StateFlow,
  * "What carries the argument"; their reconstruction in the chunked backward:

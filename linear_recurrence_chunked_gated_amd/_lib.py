@@ -42,6 +42,10 @@ SIGNATURES = {
     "sf_gdn_chunk_fwd_save": (ctypes.c_int, [ctypes.POINTER(Shape)] + [_vp] * 9 + [_sz, _vp, _sz, _vp]),
     "sf_gdn_chunk_bwd_saved": (ctypes.c_int, [ctypes.POINTER(Shape)] + [_vp] * 6 + [_sz] + [_vp] * 8
                                + [_vp, _sz, _vp]),
+    "sf_gdn_chunk_fwd_split": (ctypes.c_int, [ctypes.POINTER(Shape)] + [_vp] * 9
+                               + [_sz, _vp, _sz, ctypes.c_int, _vp]),
+    "sf_gdn_chunk_bwd_saved_split": (ctypes.c_int, [ctypes.POINTER(Shape)] + [_vp] * 6 + [_sz]
+                                     + [_vp] * 8 + [_vp, _sz, ctypes.c_int, _vp]),
     "sf_gdn_shortconv_fwd": (ctypes.c_int, [ctypes.POINTER(ConvShape)] + [_vp] * 6),
     "sf_gdn_shortconv_bwd_workspace_size": (ctypes.c_int, [ctypes.POINTER(ConvShape),
                                                            ctypes.POINTER(_sz)]),
@@ -58,6 +62,10 @@ SIGNATURES = {
 }
 
 _lib = None
+
+
+# Launch groups of a chunk call (sf_gdn_chunk_fwd_split, sf_gdn_chunk_bwd_saved_split).
+PHASE_ALL, PHASE_BEGIN, PHASE_END = 0, 1, 2
 
 
 class GDNError(RuntimeError):
@@ -146,12 +154,14 @@ def saved_bytes(shape):
 
 
 def chunk_fwd(q, k, v, alpha, beta, S_in=None, o=None, S_out=None, seg_blocks=0,
-              workspace=None, stream=None, saved=None):
+              workspace=None, stream=None, saved=None, phase=PHASE_ALL):
     """sf_gdn_chunk_fwd on torch tensors.  Returns (o, S_out).
 
     With ``saved`` (a uint8 tensor of at least ``saved_bytes`` bytes, 256-byte
     aligned, or True to allocate one) the saving forward runs and the return
-    value is (o, S_out, saved)."""
+    value is (o, S_out, saved).  ``phase`` selects one launch group
+    (sf_gdn_chunk_fwd_split): PHASE_BEGIN then PHASE_END with the same
+    arguments and workspace equals one PHASE_ALL call."""
     B, T, H, Dk = q.shape
     Dv = v.shape[3]
     dev = q.device
@@ -175,16 +185,24 @@ def chunk_fwd(q, k, v, alpha, beta, S_in=None, o=None, S_out=None, seg_blocks=0,
     if workspace is None or workspace.numel() < need:
         workspace = alloc_workspace(need, dev)
     wsn = ctypes.c_size_t(0 if workspace is None else workspace.numel())
+    if saved is True:
+        n = saved_bytes(shape)
+        saved = (alloc_workspace(n, dev) if n else
+                 torch.empty(0, dtype=torch.uint8, device=dev))
+    if phase != PHASE_ALL:
+        st = load().sf_gdn_chunk_fwd_split(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v),
+                                           _ptr(alpha), _ptr(beta), _ptr(S_in), _ptr(o),
+                                           _ptr(S_out), _ptr(saved),
+                                           ctypes.c_size_t(0 if saved is None else saved.numel()),
+                                           _ptr(workspace), wsn, int(phase), _stream(stream))
+        _check(st, "sf_gdn_chunk_fwd_split")
+        return (o, S_out) if saved is None else (o, S_out, saved)
     if saved is None:
         st = load().sf_gdn_chunk_fwd(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha),
                                      _ptr(beta), _ptr(S_in), _ptr(o), _ptr(S_out),
                                      _ptr(workspace), wsn, _stream(stream))
         _check(st, "sf_gdn_chunk_fwd")
         return o, S_out
-    if saved is True:
-        n = saved_bytes(shape)
-        saved = (alloc_workspace(n, dev) if n else
-                 torch.empty(0, dtype=torch.uint8, device=dev))
     st = load().sf_gdn_chunk_fwd_save(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha),
                                       _ptr(beta), _ptr(S_in), _ptr(o), _ptr(S_out), _ptr(saved),
                                       ctypes.c_size_t(0 if saved is None else saved.numel()),
@@ -194,9 +212,11 @@ def chunk_fwd(q, k, v, alpha, beta, S_in=None, o=None, S_out=None, seg_blocks=0,
 
 
 def chunk_bwd(q, k, v, alpha, beta, S_in, dO, dS_out=None, grads=None, seg_blocks=0,
-              workspace=None, stream=None, saved=None):
+              workspace=None, stream=None, saved=None, phase=PHASE_ALL):
     """sf_gdn_chunk_bwd on torch tensors (sf_gdn_chunk_bwd_saved when
     ``saved`` holds the buffer of a saving forward; S_in is then unused).
+    ``phase`` selects one launch group of the saved backward
+    (sf_gdn_chunk_bwd_saved_split).
 
     Returns (dq, dk, dv, dalpha, dbeta, dS_in).  ``grads`` may supply
     preallocated outputs in that order (dS_in may be None there)."""
@@ -224,7 +244,15 @@ def chunk_bwd(q, k, v, alpha, beta, S_in, dO, dS_out=None, grads=None, seg_block
     if workspace is None or workspace.numel() < need:
         workspace = alloc_workspace(need, dev)
     wsn = ctypes.c_size_t(0 if workspace is None else workspace.numel())
-    if saved is None:
+    if phase != PHASE_ALL:
+        if saved is None:
+            raise ValueError("the split backward needs the saved buffer of a saving forward")
+        st = load().sf_gdn_chunk_bwd_saved_split(
+            ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(saved),
+            ctypes.c_size_t(saved.numel()), _ptr(dO), _ptr(dS_out), _ptr(dq), _ptr(dk), _ptr(dv),
+            _ptr(da), _ptr(db), _ptr(dS_in), _ptr(workspace), wsn, int(phase), _stream(stream))
+        _check(st, "sf_gdn_chunk_bwd_saved_split")
+    elif saved is None:
         st = load().sf_gdn_chunk_bwd(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha),
                                      _ptr(beta), _ptr(S_in), _ptr(dO), _ptr(dS_out), _ptr(dq),
                                      _ptr(dk), _ptr(dv), _ptr(da), _ptr(db), _ptr(dS_in),

@@ -22,13 +22,50 @@ def _bounds(lengths, T):
     return b
 
 
+def _overlapped(n, begin, end, stream, side, order):
+    """Split-and-overlap over chunks in ``order``: chunk i's BEGIN launches
+    (independent of the boundary state) run on ``side`` while the previous
+    chunk's END launches run on ``stream``.  Chunks alternate between two
+    workspaces, so a BEGIN waits only for the END two chunks back, and every
+    END waits for its own BEGIN (Pith review of StateFlow, Figure 2 caption).
+    begin(i, slot) / end(i, slot) enqueue the launches on the given stream."""
+    side.wait_stream(stream)
+    ev_end = {}
+    begin(order[0], 0)
+    ev_begin = side.record_event()
+    for n_i, i in enumerate(order):
+        stream.wait_event(ev_begin)
+        end(i, n_i % 2)
+        ev_end[n_i] = stream.record_event()
+        if n_i + 1 < n:
+            if n_i >= 1:
+                side.wait_event(ev_end[n_i - 1])  # the END that last used this workspace
+            begin(order[n_i + 1], (n_i + 1) % 2)
+            ev_begin = side.record_event()
+
+
+def _ws_pair(workspaces, shapes, backward, dev):
+    if workspaces is not None:
+        return workspaces
+    need = max(_lib.workspace_bytes(s, backward=backward) for s in shapes)
+    return [_lib.alloc_workspace(need, dev), _lib.alloc_workspace(need, dev)]
+
+
 def chain_fwd(q, k, v, alpha, beta, S_in, lengths, o=None, seg_blocks=0, stream=None,
-              save=False):
+              save=False, overlap=False, side_stream=None, workspaces=None, saved=None,
+              states=None):
     """Forward over consecutive chunks.  Returns (o, states) where states[i]
     is chunk i's entry state ([B,H,Dv,Dk] fp32; states[0] is S_in or zeros)
     and states[-1] the final state.  With ``save`` every chunk runs the saving
     forward and the return value is (o, states, saved), saved[i] being chunk
-    i's buffer for the saved backward."""
+    i's buffer for the saved backward.
+
+    ``overlap`` runs each chunk as its two launch groups, the next chunk's
+    state-independent group on ``side_stream`` (a new default-priority stream
+    when None) while the current chunk's chain and output run on ``stream``;
+    results are bitwise those of the plain loop.  ``workspaces`` (two
+    tensors), ``saved`` and ``states`` (len(lengths) + 1 tensors, states[0]
+    the entry state) may be preallocated."""
     B, T, H, Dk = q.shape
     Dv = v.shape[3]
     if B != 1:
@@ -36,6 +73,31 @@ def chain_fwd(q, k, v, alpha, beta, S_in, lengths, o=None, seg_blocks=0, stream=
     bnd = _bounds(lengths, T)
     if o is None:
         o = torch.empty((B, T, H, Dv), dtype=q.dtype, device=q.device)
+    if overlap:
+        dev = q.device
+        main = stream if stream is not None else torch.cuda.current_stream(dev)
+        side = side_stream if side_stream is not None else torch.cuda.Stream(device=dev)
+        shapes = [_lib.make_shape(B, n, H, Dk, Dv, q.dtype, seg_blocks) for n in lengths]
+        ws = _ws_pair(workspaces, shapes, False, dev)
+        if save and saved is None:
+            saved = [_lib.alloc_workspace(_lib.saved_bytes(s), dev) for s in shapes]
+        if states is None:
+            states = [S_in if S_in is not None else
+                      torch.zeros((B, H, Dv, Dk), dtype=torch.float32, device=dev)]
+            states += [torch.empty((B, H, Dv, Dk), dtype=torch.float32, device=dev)
+                       for _ in lengths]
+        sv = saved if save else [None] * len(lengths)
+
+        def call(i, slot, st, phase):
+            sl = slice(bnd[i], bnd[i + 1])
+            _lib.chunk_fwd(q[:, sl], k[:, sl], v[:, sl], alpha[:, sl], beta[:, sl], states[i],
+                           o=o[:, sl], S_out=states[i + 1], seg_blocks=seg_blocks,
+                           workspace=ws[slot], stream=st, saved=sv[i], phase=phase)
+
+        _overlapped(len(lengths), lambda i, slot: call(i, slot, side, _lib.PHASE_BEGIN),
+                    lambda i, slot: call(i, slot, main, _lib.PHASE_END), main, side,
+                    list(range(len(lengths))))
+        return (o, states, saved) if save else (o, states)
     states = [S_in if S_in is not None else
               torch.zeros((B, H, Dv, Dk), dtype=torch.float32, device=q.device)]
     saved = []
@@ -52,12 +114,18 @@ def chain_fwd(q, k, v, alpha, beta, S_in, lengths, o=None, seg_blocks=0, stream=
 
 
 def chain_bwd(q, k, v, alpha, beta, dO, dS_out, lengths, states, grads=None, seg_blocks=0,
-              stream=None, saved=None):
+              stream=None, saved=None, overlap=False, side_stream=None, workspaces=None,
+              state_grads=None):
     """Backward over consecutive chunks, last chunk first, each chunk's
     entry-state gradient feeding the previous chunk's exit gradient.
     ``states`` are the entry states from chain_fwd; ``saved`` the per-chunk
     buffers of a saving chain_fwd (the recompute backward runs without them;
-    ``states`` may then be None).  Returns (dq, dk, dv, dalpha, dbeta, dS_in)."""
+    ``states`` may then be None).  Returns (dq, dk, dv, dalpha, dbeta, dS_in).
+
+    ``overlap`` (saved backward only) runs each chunk's state-independent
+    launch group on ``side_stream`` while the later chunk's chain and
+    gradients run on ``stream``, bitwise equal to the plain loop.
+    ``state_grads`` may preallocate the len(lengths) entry-state gradients."""
     B, T, H, Dk = q.shape
     Dv = v.shape[3]
     if B != 1:
@@ -67,6 +135,32 @@ def chain_bwd(q, k, v, alpha, beta, dO, dS_out, lengths, states, grads=None, seg
         grads = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v),
                  torch.empty_like(alpha), torch.empty_like(beta))
     dq, dk, dv, da, db = grads
+    if overlap:
+        if saved is None:
+            raise ValueError("the overlapped backward needs the saved buffers")
+        dev = q.device
+        main = stream if stream is not None else torch.cuda.current_stream(dev)
+        side = side_stream if side_stream is not None else torch.cuda.Stream(device=dev)
+        shapes = [_lib.make_shape(B, n, H, Dk, Dv, q.dtype, seg_blocks) for n in lengths]
+        ws = _ws_pair(workspaces, shapes, True, dev)
+        if state_grads is None:
+            state_grads = [torch.empty((B, H, Dv, Dk), dtype=torch.float32, device=dev)
+                           for _ in lengths]
+        n = len(lengths)
+
+        def call(i, slot, st, phase):
+            sl = slice(bnd[i], bnd[i + 1])
+            G = dS_out if i == n - 1 else state_grads[i + 1]
+            _lib.chunk_bwd(q[:, sl], k[:, sl], v[:, sl], alpha[:, sl], beta[:, sl], None,
+                           dO[:, sl], G, grads=(dq[:, sl], dk[:, sl], dv[:, sl], da[:, sl],
+                                                db[:, sl], state_grads[i]),
+                           seg_blocks=seg_blocks, workspace=ws[slot], stream=st, saved=saved[i],
+                           phase=phase)
+
+        _overlapped(n, lambda i, slot: call(i, slot, side, _lib.PHASE_BEGIN),
+                    lambda i, slot: call(i, slot, main, _lib.PHASE_END), main, side,
+                    list(range(n - 1, -1, -1)))
+        return dq, dk, dv, da, db, state_grads[0]
     G = dS_out
     for i in range(len(lengths) - 1, -1, -1):
         sl = slice(bnd[i], bnd[i + 1])

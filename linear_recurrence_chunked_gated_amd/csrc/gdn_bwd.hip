@@ -761,12 +761,14 @@ static hipError_t set_lds(const void* fn, size_t bytes) {
 }
 
 template <typename T, int D>
-hipError_t launch_bwd(const BwdArgs& a0, bool saved, hipStream_t st, Profiler* prof) {
+hipError_t launch_bwd(const BwdArgs& a0, bool saved, int phase, hipStream_t st, Profiler* prof) {
   BwdArgs a = a0;
   FwdArgs& f = a.f;
   const int BH = f.B * f.H, P = f.P;
   constexpr size_t scan_bytes = ScanLds<T, D>::bytes, grad_bytes = GradLds<T, D>::bytes;
   hipError_t e;
+  if (phase != PHASE_ALL && !saved) return hipErrorInvalidValue;
+  const bool begin = phase != PHASE_END, end = phase != PHASE_BEGIN;
   // 0. per-block Tp, Tpp (Pre)
   if (!saved && (e = launch_prep<T, D>(f, st, prof)) != hipSuccess) return e;
   const float* dSend = a.dS_out;
@@ -775,13 +777,17 @@ hipError_t launch_bwd(const BwdArgs& a0, bool saved, hipStream_t st, Profiler* p
     // 1. segment maps of the forward (all segments)
     if (!saved && (e = launch_fwd_summary<T, D>(f, P, st, prof, "gdn_bwd_summary")) != hipSuccess)
       return e;
-    // 2. NB maps of segments 1..P-1
-    if ((e = set_lds((const void*)gdn_bwd_dscan_kernel<T, D, false>, ScanLds<T, D>::bytes)) != hipSuccess)
-      return e;
-    prof_begin(prof, "gdn_bwd_dscan_summary", st);
-    hipLaunchKernelGGL((gdn_bwd_dscan_kernel<T, D, false>), dim3(BH * (P - 1)), dim3(4 * D),
-                       scan_bytes, st, a, 1, P - 1, nullptr, 1);
-    prof_end(prof, st);
+    // 2. NB maps of segments 1..P-1 (independent of dS_out)
+    if (begin) {
+      if ((e = set_lds((const void*)gdn_bwd_dscan_kernel<T, D, false>, ScanLds<T, D>::bytes)) !=
+          hipSuccess)
+        return e;
+      prof_begin(prof, "gdn_bwd_dscan_summary", st);
+      hipLaunchKernelGGL((gdn_bwd_dscan_kernel<T, D, false>), dim3(BH * (P - 1)), dim3(4 * D),
+                         scan_bytes, st, a, 1, P - 1, nullptr, 1);
+      prof_end(prof, st);
+    }
+    if (!end) return hipGetLastError();
     // 3. chains
     if (!saved) {
       ChainArgs c{f.S_in, f.Mseg, f.Nseg, const_cast<float*>(f.Sst), P, BH};
@@ -792,6 +798,7 @@ hipError_t launch_bwd(const BwdArgs& a0, bool saved, hipStream_t st, Profiler* p
     dSend = a.dSend;
     dsend_P = P;
   } else {
+    if (!end) return hipSuccess;
     f.Sst = f.S_in;
     f.sst_P = 1;
   }
@@ -814,8 +821,8 @@ hipError_t launch_bwd(const BwdArgs& a0, bool saved, hipStream_t st, Profiler* p
   return hipGetLastError();
 }
 
-template hipError_t launch_bwd<bf16, 128>(const BwdArgs&, bool, hipStream_t, Profiler*);
-template hipError_t launch_bwd<bf16, 64>(const BwdArgs&, bool, hipStream_t, Profiler*);
-template hipError_t launch_bwd<float, 64>(const BwdArgs&, bool, hipStream_t, Profiler*);
+template hipError_t launch_bwd<bf16, 128>(const BwdArgs&, bool, int, hipStream_t, Profiler*);
+template hipError_t launch_bwd<bf16, 64>(const BwdArgs&, bool, int, hipStream_t, Profiler*);
+template hipError_t launch_bwd<float, 64>(const BwdArgs&, bool, int, hipStream_t, Profiler*);
 
 }  // namespace sfgdn

@@ -750,13 +750,19 @@ hipError_t launch_states(const FwdArgs& a, void* hst, hipStream_t st, Profiler* 
 // segment maps M are computed for all P segments (a.MBseg then points into the
 // caller's saved buffer), so that the backward can skip its recompute.
 template <typename T, int D>
-hipError_t launch_fwd(const FwdArgs& a, void* hsave, hipStream_t st, Profiler* prof) {
+hipError_t launch_fwd(const FwdArgs& a, void* hsave, int phase, hipStream_t st, Profiler* prof) {
   hipError_t e;
   const int BH = a.B * a.H;
-  if ((e = launch_prep<T, D>(a, st, prof)) != hipSuccess) return e;
+  if (phase != PHASE_END) {  // Pre and the segment maps: independent of S_in
+    if ((e = launch_prep<T, D>(a, st, prof)) != hipSuccess) return e;
+    if (a.P > 1) {
+      const int nseg = hsave ? a.P : a.P - 1;
+      if ((e = launch_fwd_summary<T, D>(a, nseg, st, prof, "gdn_fwd_summary")) != hipSuccess)
+        return e;
+    }
+    if (phase == PHASE_BEGIN) return hipSuccess;
+  }
   if (a.P > 1) {
-    const int nseg = hsave ? a.P : a.P - 1;
-    if ((e = launch_fwd_summary<T, D>(a, nseg, st, prof, "gdn_fwd_summary")) != hipSuccess) return e;
     ChainArgs c{a.S_in, a.Mseg, a.Nseg, const_cast<float*>(a.Sst), a.P, BH};
     if ((e = launch_chain<D, false>(c, st, prof)) != hipSuccess) return e;
   }
@@ -767,7 +773,7 @@ hipError_t launch_fwd(const FwdArgs& a, void* hsave, hipStream_t st, Profiler* p
 }
 
 #define SF_INST(T, D)                                                                      \
-  template hipError_t launch_fwd<T, D>(const FwdArgs&, void*, hipStream_t, Profiler*);  \
+  template hipError_t launch_fwd<T, D>(const FwdArgs&, void*, int, hipStream_t, Profiler*);  \
   template hipError_t launch_fwd_summary<T, D>(const FwdArgs&, int, hipStream_t, Profiler*, const char*); \
   template hipError_t launch_states<T, D>(const FwdArgs&, void*, hipStream_t, Profiler*);  \
   template hipError_t launch_prep<T, D>(const FwdArgs&, hipStream_t, Profiler*);

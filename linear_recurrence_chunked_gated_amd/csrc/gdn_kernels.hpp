@@ -96,9 +96,15 @@ struct Profiler;
 void prof_begin(Profiler* p, const char* name, hipStream_t st);
 void prof_end(Profiler* p, hipStream_t st);
 
+// A chunk's work in two parts, so that a caller can overlap the part that
+// does not read the boundary state of one chunk with the rest of another:
+// PHASE_BEGIN runs the launches that do not read S_in (dS_out), PHASE_END the
+// others; PHASE_ALL both, in order.
+enum { PHASE_ALL = 0, PHASE_BEGIN = 1, PHASE_END = 2 };
+
 // hsave: optional per-block entry-state output (see launch_fwd).
 template <typename T, int D>
-hipError_t launch_fwd(const FwdArgs& a, void* hsave, hipStream_t st, Profiler* prof);
+hipError_t launch_fwd(const FwdArgs& a, void* hsave, int phase, hipStream_t st, Profiler* prof);
 // Pieces of the forward reused by the backward.
 template <typename T, int D>
 hipError_t launch_fwd_summary(const FwdArgs& a, int nseg, hipStream_t st, Profiler* prof,
@@ -112,8 +118,9 @@ hipError_t launch_states(const FwdArgs& a, void* hst, hipStream_t st, Profiler* 
 // saved: a.hst already holds every block's entry state, a.f.MBseg every
 // segment's map and a.f.tw every block's Tp, Tpp (from a saving forward), so
 // the forward recompute is skipped.
+// phase: PHASE_BEGIN and PHASE_END only with saved.
 template <typename T, int D>
-hipError_t launch_bwd(const BwdArgs& a, bool saved, hipStream_t st, Profiler* prof);
+hipError_t launch_bwd(const BwdArgs& a, bool saved, int phase, hipStream_t st, Profiler* prof);
 // Short convolution: GR tokens per backward run; dwp holds the B * ceil(T/GR)
 // partial weight gradients [C][W] fp32 and room for their group sums.
 template <typename T>

@@ -220,7 +220,7 @@ size_t saved_bytes(const Plan& p) {
 sf_status fwd_impl(const sf_gdn_shape* shape, const void* q, const void* k, const void* v,
                    const float* alpha, const float* beta, const float* S_in, void* o,
                    float* S_out, void* saved, size_t sv_bytes, void* workspace, size_t ws_bytes,
-                   void* stream, bool save) {
+                   void* stream, bool save, int phase = PHASE_ALL) {
   Plan p;
   sf_status s = make_plan(shape, p);
   if (s != SF_OK) return s;
@@ -251,7 +251,7 @@ sf_status fwd_impl(const sf_gdn_shape* shape, const void* q, const void* k, cons
 
   return run_locked([&](Profiler* prof) -> sf_status {
     if (p.T == 0) {
-      if (S_out) {
+      if (S_out && phase != PHASE_BEGIN) {
         hipError_t e = launch_copy_state(S_out, S_in, nst, st);
         if (e != hipSuccess) return hip_fail(e, "state copy");
       }
@@ -276,10 +276,10 @@ sf_status fwd_impl(const sf_gdn_shape* shape, const void* q, const void* k, cons
     }
     hipError_t e;
     if (p.dtype == SF_DTYPE_BF16)
-      e = (p.D == 128) ? launch_fwd<bf16, 128>(a, hsave, st, prof)
-                       : launch_fwd<bf16, 64>(a, hsave, st, prof);
+      e = (p.D == 128) ? launch_fwd<bf16, 128>(a, hsave, phase, st, prof)
+                       : launch_fwd<bf16, 64>(a, hsave, phase, st, prof);
     else
-      e = launch_fwd<float, 64>(a, hsave, st, prof);
+      e = launch_fwd<float, 64>(a, hsave, phase, st, prof);
     if (e != hipSuccess) return hip_fail(e, "forward launch");
     return SF_OK;
   });
@@ -291,7 +291,7 @@ sf_status bwd_impl(const sf_gdn_shape* shape, const void* q, const void* k, cons
                    const float* alpha, const float* beta, const float* S_in, const void* saved,
                    size_t sv_bytes, const void* dO, const float* dS_out, void* dq, void* dk,
                    void* dv, float* dalpha, float* dbeta, float* dS_in, void* workspace,
-                   size_t ws_bytes, void* stream, bool use_saved) {
+                   size_t ws_bytes, void* stream, bool use_saved, int phase = PHASE_ALL) {
   Plan p;
   sf_status s = make_plan(shape, p);
   if (s != SF_OK) return s;
@@ -324,7 +324,7 @@ sf_status bwd_impl(const sf_gdn_shape* shape, const void* q, const void* k, cons
 
   return run_locked([&](Profiler* prof) -> sf_status {
     if (p.T == 0) {
-      if (dS_in) {
+      if (dS_in && phase != PHASE_BEGIN) {
         hipError_t e = launch_copy_state(dS_in, dS_out, nst, st);
         if (e != hipSuccess) return hip_fail(e, "state copy");
       }
@@ -357,10 +357,10 @@ sf_status bwd_impl(const sf_gdn_shape* shape, const void* q, const void* k, cons
     a.dq = dq; a.dk = dk; a.dv = dv; a.dalpha = dalpha; a.dbeta = dbeta; a.dS_in = dS_in;
     hipError_t e;
     if (p.dtype == SF_DTYPE_BF16)
-      e = (p.D == 128) ? launch_bwd<bf16, 128>(a, use_saved, st, prof)
-                       : launch_bwd<bf16, 64>(a, use_saved, st, prof);
+      e = (p.D == 128) ? launch_bwd<bf16, 128>(a, use_saved, phase, st, prof)
+                       : launch_bwd<bf16, 64>(a, use_saved, phase, st, prof);
     else
-      e = launch_bwd<float, 64>(a, use_saved, st, prof);
+      e = launch_bwd<float, 64>(a, use_saved, phase, st, prof);
     if (e == hipErrorNotSupported) return fail(SF_ERR_UNSUPPORTED, "backward not available");
     if (e != hipSuccess) return hip_fail(e, "backward launch");
     return SF_OK;
@@ -453,6 +453,33 @@ sf_status sf_gdn_chunk_bwd_saved(const sf_gdn_shape* shape, const void* q, const
                                  void* stream) {
   return bwd_impl(shape, q, k, v, alpha, beta, nullptr, saved, saved_bytes_, dO, dS_out, dq, dk,
                   dv, dalpha, dbeta, dS_in, workspace, ws_bytes, stream, true);
+}
+
+static bool bad_phase(int phase) {
+  if (phase == SF_PHASE_ALL || phase == SF_PHASE_BEGIN || phase == SF_PHASE_END) return false;
+  fail(SF_ERR_INVALID_ARG, "phase must be SF_PHASE_ALL, SF_PHASE_BEGIN or SF_PHASE_END");
+  return true;
+}
+
+sf_status sf_gdn_chunk_fwd_split(const sf_gdn_shape* shape, const void* q, const void* k,
+                                 const void* v, const float* alpha, const float* beta,
+                                 const float* S_in, void* o, float* S_out, void* saved,
+                                 size_t saved_bytes_, void* workspace, size_t ws_bytes, int phase,
+                                 void* stream) {
+  if (bad_phase(phase)) return SF_ERR_INVALID_ARG;
+  return fwd_impl(shape, q, k, v, alpha, beta, S_in, o, S_out, saved, saved_bytes_, workspace,
+                  ws_bytes, stream, saved != nullptr, phase);
+}
+
+sf_status sf_gdn_chunk_bwd_saved_split(const sf_gdn_shape* shape, const void* q, const void* k,
+                                       const void* v, const float* alpha, const float* beta,
+                                       const void* saved, size_t saved_bytes_, const void* dO,
+                                       const float* dS_out, void* dq, void* dk, void* dv,
+                                       float* dalpha, float* dbeta, float* dS_in, void* workspace,
+                                       size_t ws_bytes, int phase, void* stream) {
+  if (bad_phase(phase)) return SF_ERR_INVALID_ARG;
+  return bwd_impl(shape, q, k, v, alpha, beta, nullptr, saved, saved_bytes_, dO, dS_out, dq, dk,
+                  dv, dalpha, dbeta, dS_in, workspace, ws_bytes, stream, true, phase);
 }
 
 const char* sf_status_string(int status) {

@@ -191,3 +191,22 @@ def test_conv_rejects_missing_overlapping_and_small_workspace():
                                   None) == _lib.SF_ERR_WORKSPACE
     assert L.sf_gdn_shortconv_bwd(ctypes.byref(shape), *args, None, ctypes.c_size_t(0),
                                   None) == _lib.SF_ERR_WORKSPACE
+
+
+def test_split_calls_reject_unknown_phase():
+    L = _lib.load()
+    vp = lambda x: None if x is None else ctypes.c_void_p(x)
+    shape = _shape(T=8192, H=2)
+    st = L.sf_gdn_chunk_fwd_split(ctypes.byref(shape), vp(1 * G), vp(2 * G), vp(3 * G), vp(4 * G),
+                                  vp(5 * G), None, vp(6 * G), vp(7 * G), None, ctypes.c_size_t(0),
+                                  vp(24 * G), ctypes.c_size_t(_lib.workspace_bytes(shape)), 7, None)
+    assert st == _lib.SF_ERR_INVALID_ARG
+    assert "phase" in L.sf_last_error_message().decode()
+    st = L.sf_gdn_chunk_bwd_saved_split(ctypes.byref(shape), vp(1 * G), vp(2 * G), vp(3 * G),
+                                        vp(4 * G), vp(5 * G), vp(20 * G),
+                                        ctypes.c_size_t(_lib.saved_bytes(shape)), vp(6 * G), None,
+                                        vp(8 * G), vp(9 * G), vp(10 * G), vp(11 * G), vp(12 * G),
+                                        None, vp(24 * G),
+                                        ctypes.c_size_t(_lib.workspace_bytes(shape, backward=True)),
+                                        -1, None)
+    assert st == _lib.SF_ERR_INVALID_ARG

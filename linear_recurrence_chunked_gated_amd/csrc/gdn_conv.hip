@@ -180,8 +180,10 @@ __global__ __launch_bounds__(CONV_THREADS) void conv_bwd_kernel(ConvArgs a, int 
 #pragma unroll
     for (int j = 0; j < W; ++j) ld_xe<T, V, W>(x, cin, r1 - 1 + W - 1 - j, a.C, c, xw[j]);
   }
-#pragma unroll 4
-  for (int t = r1 - 1; t >= r0; --t) {
+  // One token t (walking down): g_t, dx_t, this token's dw terms, then the
+  // windows move down and take x_{t-W} (xe row t-1).  TAIL: t + W-1 >= T, so
+  // dx_t also takes dconv_out[t+W-1-T]; HEAD: xe row t-1 may lie in conv_in.
+  auto token = [&](int t, bool tail, bool head) {
     float g0[V];
     conv_g<T, W, V>(a, dy, wt, xw, t, c, g0);
 #pragma unroll
@@ -196,15 +198,13 @@ __global__ __launch_bounds__(CONV_THREADS) void conv_bwd_kernel(ConvArgs a, int 
 #pragma unroll
       for (int j = 0; j < W; ++j) dw[j][i] += gw[0][i] * xw[j][i];
     }
-    const int m = t + W - 1 - a.T;
-    if (m >= 0 && dco) {
+    if (tail && dco) {
       float e[V];
-      ld_vec<T, V>(dco + (size_t)m * a.C + c, e);
+      ld_vec<T, V>(dco + (size_t)(t + W - 1 - a.T) * a.C + c, e);
 #pragma unroll
       for (int i = 0; i < V; ++i) o[i] += e[i];
     }
     st_vec<T, V>(dx + (size_t)t * a.C + c, o);
-    // next t = t - 1: g window moves down, x window moves down
 #pragma unroll
     for (int j = W - 1; j >= 1; --j)
 #pragma unroll
@@ -213,9 +213,20 @@ __global__ __launch_bounds__(CONV_THREADS) void conv_bwd_kernel(ConvArgs a, int 
     for (int j = 0; j + 1 < W; ++j)
 #pragma unroll
       for (int i = 0; i < V; ++i) xw[j][i] = xw[j + 1][i];
-    // the window of t - 1 adds x_{t-W} = xe row t - 1
-    if (t - 1 >= r0) ld_xe<T, V, W>(x, cin, t - 1, a.C, c, xw[W - 1]);
-  }
+    if (head) {
+      if (t - 1 >= r0) ld_xe<T, V, W>(x, cin, t - 1, a.C, c, xw[W - 1]);
+    } else {
+      ld_vec<T, V>(x + (size_t)(t - W) * a.C + c, xw[W - 1]);  // t >= W: a plain x row
+    }
+  };
+  // The last W-1 tokens of the sequence (dconv_out term), then the bulk with
+  // plain x rows and no branches, then the first W tokens (conv_in rows).
+  int t = r1 - 1;
+  for (; t >= r0 && t > a.T - W; --t) token(t, true, t < W);
+  const int tlo = max(r0, W);
+#pragma unroll 8
+  for (; t >= tlo; --t) token(t, false, false);
+  for (; t >= r0; --t) token(t, false, true);
   // this run's dw partial: dwp[(b * nrun + run)][c][j]
   const int nrun = gridDim.y;
   float* p = dwp + ((size_t)b * nrun + blockIdx.y) * a.C * W;

@@ -388,11 +388,13 @@ sf_status make_conv_plan(const sf_conv_shape* s, ConvPlan& p) {
   if (s->C % 8) return fail(SF_ERR_UNSUPPORTED, "C must be a multiple of 8");
   if ((long long)s->B * s->T * s->C > (1LL << 40)) return fail(SF_ERR_UNSUPPORTED, "too large");
   p.B = s->B; p.T = s->T; p.C = s->C; p.W = s->W; p.dtype = s->dtype; p.act = s->act;
-  // Backward runs: enough (channel group, run, b) workgroups to fill the GPU
-  // several times over, at least 32 tokens each (the weight-gradient
-  // partials are per run).
+  // Backward runs: about 1024 (channel group, run, b) workgroups, four per
+  // compute unit, at least 32 tokens each.  Fewer, longer runs cut the
+  // weight-gradient partials (one per run, reduced afterwards) and the per-run
+  // halo; twice as many runs cost more in that reduction, half as many left
+  // compute units idle.
   const long long gx = (s->C / (s->dtype == SF_DTYPE_BF16 ? 4 : 2) + 255) / 256;
-  long long want = (2048 + gx * s->B - 1) / (gx * s->B);
+  long long want = (1024 + gx * s->B - 1) / (gx * s->B);
   if (want < 1) want = 1;
   long long GR = s->T > 0 ? (s->T + want - 1) / want : 16;
   GR = (GR + 15) / 16 * 16;

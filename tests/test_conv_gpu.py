@@ -45,6 +45,7 @@ def oracle(oracle_mod, d, act):
     (1, 1, 64, 4, "f32", 1),         # single token
     (1, 77, 72, 1, "bf16", 0),       # W = 1: no state
     (1, 300, 96, 8, "bf16", 1),      # widest supported window
+    (1, 290, 96, 8, "bf16", 1),      # the last W-1 tokens span two token runs
     (2, 4096, 2048, 4, "bf16", 1),   # several runs per sequence
 ])
 def test_matches_oracle(oracle_mod, B, T, C, W, dtype, act):

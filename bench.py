@@ -60,6 +60,20 @@ def kernel_flops_per_block(name, d):
     return None
 
 
+def kernel_bytes_per_token_head(name, d, elem=2):
+    """Algorithmic HBM bytes per token and head of the kernels that move the
+    method's own inputs and outputs (bf16 activations, fp32 gates): the
+    gradient kernel reads q, k, v, dO, alpha, beta and writes dq, dk, dv,
+    dalpha, dbeta; the output kernel reads q, k, v, alpha, beta and writes o.
+    Intermediate buffers of this design (Tp, Tpp, maps, per-block states) are
+    not counted.  None for kernels that only move intermediates."""
+    if name == "gdn_bwd_grads":
+        return 7 * d * elem + 16
+    if name in ("gdn_fwd_out", "gdn_fwd_out_save"):
+        return 4 * d * elem + 8
+    return None
+
+
 def kernel_flops_per_launch(name, d, H, T, L, P, save=False):
     """Algorithmic flops of one launch for one chunk of T tokens (``save``:
     the saving forward, whose summary covers every segment)."""
@@ -509,13 +523,27 @@ def main():
         fl.append(f)
     roofline = None
     if fl:
+        # The dominant kernel against whichever of its two rooflines binds:
+        # algorithmic flops at the bf16 MFMA peak, or algorithmic bytes at
+        # the HBM peak; the other one is reported beside it.
+        dur = kern[dom]["avg_us"] * 1e-6
         per_launch = sum(fl) / len(fl)
-        achieved = per_launch / (kern[dom]["avg_us"] * 1e-6) / 1e12
-        traffic = load_traffic(dom)
-        roofline = {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 2),
-                    "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                    "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
-                    "flops_per_launch": per_launch}
+        mfma = {"bound": "mfma", "achieved": round(per_launch / dur / 1e12, 2),
+                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(per_launch / dur / 1e12 / PEAK_BF16_TFLOPS, 4)}
+        bth = kernel_bytes_per_token_head(dom, D)
+        hbm = None
+        if bth is not None:
+            by = bth * H * sum(chunks) / len(chunks)
+            hbm = {"bound": "hbm", "achieved": round(by / dur / 1e9, 1), "peak": PEAK_HBM_GBS,
+                   "unit": "GB/s", "frac": round(by / dur / 1e9 / PEAK_HBM_GBS, 4)}
+        if hbm is not None and hbm["frac"] >= mfma["frac"]:
+            main, other = hbm, mfma
+        else:
+            main, other = mfma, hbm
+        roofline = dict(kernel=dom, **main, traffic=load_traffic(dom),
+                        flops_per_launch=per_launch,
+                        bytes_per_launch=None if hbm is None else by, other=other)
     # Whole-path roofline: algorithmic flops and bytes per token-head of the
     # method (fwd 182,955 flop and 1,032 B; fwd+bwd 726,358 flop and 2,840 B at
     # d = 128, block 64) plus the boundary states each chunk call moves.

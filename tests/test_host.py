@@ -210,3 +210,17 @@ def test_split_calls_reject_unknown_phase():
                                         ctypes.c_size_t(_lib.workspace_bytes(shape, backward=True)),
                                         -1, None)
     assert st == _lib.SF_ERR_INVALID_ARG
+
+
+def test_bench_algorithmic_figures():
+    """The benchmark's per-kernel models against the method's per-token-head
+    figures at d = 128, block C = 64: bytes fwd 4 d * 2 + 8 = 1,032 and bwd
+    7 d * 2 + 16 = 1,808 (bf16 activations, fp32 gates); the forward output
+    kernel's matrix products 2 C (3 d + 2 d) + 6 d^2 = 180,224 flop (the
+    forward's 182,955 without the triangular solve's (2/3) C^2, which is not
+    an MFMA product)."""
+    import bench
+    assert bench.kernel_bytes_per_token_head("gdn_bwd_grads", 128) == 1808
+    assert bench.kernel_bytes_per_token_head("gdn_fwd_out", 128) == 1032
+    assert bench.kernel_bytes_per_token_head("gdn_fwd_summary", 128) is None
+    assert bench.kernel_flops_per_block("gdn_fwd_out", 128) / 64 == 180224

@@ -211,6 +211,11 @@ def workload(name):
     if name == "fwdbwd_h16_t16384_d128":
         return dict(T=16384, H=16, D=128, chunks=[16384], bwd=True, s_in_std=None, seed=20260003,
                     desc="T=16384, H=16, d=128, bf16, one chunk fwd+bwd")
+    if name == "fwd_h16_t8192_d128_8x1024":
+        return dict(T=8192, H=16, D=128, chunks=[1024] * 8, bwd=False, s_in_std=None,
+                    seed=20260001,
+                    desc="T=8192, H=16, d=128, bf16, 8 chunks of 1024 chained, fwd only "
+                         "(launch-bound)")
     if name == "fwd_h16_t65536_d128":
         return dict(T=65536, H=16, D=128, chunks=[65536], bwd=False, s_in_std=0.1, seed=20260102,
                     desc="T=65536, H=16, d=128, bf16, one chunk fwd, S_in ~ N(0, 0.1)")
@@ -218,6 +223,42 @@ def workload(name):
         return dict(T=65536, H=32, D=128, chunks=[65536], bwd=False, s_in_std=0.1, seed=20260002,
                     desc="T=65536, H=32, d=128, bf16, one chunk fwd, S_in ~ N(0, 0.1)")
     raise SystemExit("unknown workload %r" % name)
+
+
+def measured_peaks(dev):
+    """What this GPU delivers in practice, for the fractions beside the
+    datasheet ones: a plain 1 GiB device-to-device copy (bytes read plus
+    bytes written over its duration) and a dense 8192^3 bf16 matrix product
+    through torch (2 m n k flop over its duration)."""
+    import torch
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+
+    def timed(fn, reps):
+        for _ in range(2):
+            fn()
+        torch.cuda.synchronize()
+        a, b = ev(), ev()
+        a.record()
+        for _ in range(reps):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) * 1e-3 / reps
+
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    t_copy = timed(lambda: dst.copy_(src), 10)
+    del src, dst
+    m = 8192
+    x = torch.randn(m, m, device=dev, dtype=torch.bfloat16)
+    y = torch.randn(m, m, device=dev, dtype=torch.bfloat16)
+    t_mm = timed(lambda: torch.matmul(x, y), 10)
+    del x, y
+    torch.cuda.empty_cache()
+    return {"hbm_copy_GBs": round(2 * n / t_copy / 1e9, 1),
+            "bf16_gemm_TFLOPs": round(2.0 * m * m * m / t_mm / 1e12, 1),
+            "how": "1 GiB device copy (read + write bytes); 8192^3 bf16 torch.matmul"}
 
 
 def bench_conv(args):
@@ -375,9 +416,14 @@ def main():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default="fwdbwd_h16_t262144_d128_8skew",
                     help="fwdbwd_h16_t262144_d128_8skew (default), fwdbwd_h16_t16384_d128, "
-                         "fwd_h16_t65536_d128, fwd_h32_t65536_d128, or "
+                         "fwd_h16_t65536_d128, fwd_h32_t65536_d128, fwd_h16_t8192_d128_8x1024, or "
                          "conv_qkv_h16_t262144_d128_8skew (the short convolution)")
     ap.add_argument("--seg-blocks", type=int, default=0)
+    ap.add_argument("--cold", action="store_true",
+                    help="write a 512 MiB scratch buffer before every timed step (outside the "
+                         "timed events) so that no input is served from the last-level cache")
+    ap.add_argument("--no-measured-peaks", action="store_true",
+                    help="skip the copy and GEMM measurements of the achievable peaks")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--recompute", action="store_true",
                     help="backward recomputes the forward's block states instead of reading the "
@@ -485,16 +531,30 @@ def main():
         step()
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    if args.cold:
+        scratch = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(args.steps)]
     with _lib.profile(capacity=256 * args.steps * len(chunks) + 64) as prof:
         torch.cuda.synchronize()
-        e0.record(stream)
         wall0 = time.perf_counter()
-        for _ in range(args.steps):
-            step()
-        e1.record(stream)
+        if args.cold:
+            for i in range(args.steps):
+                scratch.fill_(i & 255)
+                ev[i][0].record(stream)
+                step()
+                ev[i][1].record(stream)
+        else:
+            e0.record(stream)
+            for _ in range(args.steps):
+                step()
+            e1.record(stream)
         torch.cuda.synchronize()
         wall = time.perf_counter() - wall0
-    ms = e0.elapsed_time(e1) / args.steps
+    if args.cold:
+        ms = sum(a.elapsed_time(b) for a, b in ev) / args.steps
+    else:
+        ms = e0.elapsed_time(e1) / args.steps
     tok_s = T / (ms * 1e-3)
 
     # Per-kernel times over the timed region.
@@ -503,16 +563,8 @@ def main():
     dom = max(kern, key=lambda n: kern[n]["total_ms_per_step"])
     # Algorithmic flops of the dominant kernel per launch (averaged over the
     # chunk sizes of one step).
-    L_of = {}
-    for n in chunks:
-        nblk = (n + C - 1) // C
-        if args.seg_blocks:
-            L = args.seg_blocks
-        else:
-            P0 = min(nblk, max(1, -(-256 // H)))
-            L = -(-nblk // P0)
-        L = min(L, nblk)
-        L_of[n] = (L, -(-nblk // L))
+    L_of = {n: _lib.segment_plan(_lib.make_shape(1, n, H, D, D, q.dtype, args.seg_blocks))
+            for n in chunks}
     fl = []
     for n in chunks:
         L, P = L_of[n]
@@ -558,6 +610,14 @@ def main():
             "frac": round(t_roof / (ms * 1e-3), 4),
             "algorithmic_flops": F, "algorithmic_bytes": Bytes}
 
+    peaks = None if args.no_measured_peaks else measured_peaks(dev)
+    if peaks and roofline:
+        key = "hbm_copy_GBs" if roofline["bound"] == "hbm" else "bf16_gemm_TFLOPs"
+        roofline["frac_of_measured_peak"] = round(roofline["achieved"] / peaks[key], 4)
+    if peaks:
+        t_meas = max(F / (peaks["bf16_gemm_TFLOPs"] * 1e12), Bytes / (peaks["hbm_copy_GBs"] * 1e9))
+        path["frac_of_measured_peaks"] = round(t_meas / (ms * 1e-3), 4)
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(wl)
@@ -587,6 +647,8 @@ def main():
         "kernels": {n: {"avg_us": round(x["avg_us"], 2), "launches_per_step": x["launches"] // args.steps,
                         "ms_per_step": round(x["total_ms_per_step"], 4)} for n, x in kern.items()},
         "wall_s_timed": round(wall, 3),
+        "cold_cache": bool(args.cold),
+        "measured_peaks": peaks,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

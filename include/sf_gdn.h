@@ -73,6 +73,14 @@ typedef struct {
   int seg_blocks;  /* 0 = automatic */
 } sf_gdn_shape;
 
+/* The in-chunk parallel scan's plan for a shape: *seg_blocks kernel blocks
+ * per segment and *segments segments (P = ceil(nblk / seg_blocks); 0 for an
+ * empty chunk).  The segment-parallel form is the chunk chain of Eq. 5
+ * applied inside the chunk.  With shape->seg_blocks = 0 the library picks
+ * enough segments to occupy the GPU, but no fewer blocks per segment than
+ * about sqrt(0.3 nblk).  Host only, no GPU call. */
+sf_status sf_gdn_segment_plan(const sf_gdn_shape* shape, int* seg_blocks, int* segments);
+
 /* Workspace bytes (256-byte aligned start required) for the calls below.
  * Returns SF_OK and writes *bytes, or an error for an unsupported shape. */
 sf_status sf_gdn_chunk_fwd_workspace_size(const sf_gdn_shape* shape, size_t* bytes);

@@ -39,6 +39,8 @@ SIGNATURES = {
     "sf_gdn_chunk_fwd": (ctypes.c_int, [ctypes.POINTER(Shape)] + [_vp] * 8 + [_vp, _sz, _vp]),
     "sf_gdn_chunk_bwd": (ctypes.c_int, [ctypes.POINTER(Shape)] + [_vp] * 14 + [_vp, _sz, _vp]),
     "sf_gdn_chunk_saved_size": (ctypes.c_int, [ctypes.POINTER(Shape), ctypes.POINTER(_sz)]),
+    "sf_gdn_segment_plan": (ctypes.c_int, [ctypes.POINTER(Shape), ctypes.POINTER(ctypes.c_int),
+                                           ctypes.POINTER(ctypes.c_int)]),
     "sf_gdn_chunk_fwd_save": (ctypes.c_int, [ctypes.POINTER(Shape)] + [_vp] * 9 + [_sz, _vp, _sz, _vp]),
     "sf_gdn_chunk_bwd_saved": (ctypes.c_int, [ctypes.POINTER(Shape)] + [_vp] * 6 + [_sz] + [_vp] * 8
                                + [_vp, _sz, _vp]),
@@ -123,6 +125,14 @@ def workspace_bytes(shape, backward=False):
     fn = load().sf_gdn_chunk_bwd_workspace_size if backward else load().sf_gdn_chunk_fwd_workspace_size
     _check(fn(ctypes.byref(shape), ctypes.byref(n)), "workspace_size")
     return n.value
+
+
+def segment_plan(shape):
+    """(blocks per segment, segments) of the in-chunk scan for `shape`."""
+    L, P = ctypes.c_int(0), ctypes.c_int(0)
+    _check(load().sf_gdn_segment_plan(ctypes.byref(shape), ctypes.byref(L), ctypes.byref(P)),
+           "segment_plan")
+    return L.value, P.value
 
 
 def alloc_workspace(nbytes, device):

@@ -1,5 +1,6 @@
 // C ABI of the chunked gated delta-rule library: argument checks, the
 // segment plan, workspace carving and kernel launches on the caller's stream.
+#include <cmath>
 #include <hip/hip_runtime.h>
 
 #include <mutex>
@@ -60,12 +61,19 @@ sf_status make_plan(const sf_gdn_shape* s, Plan& p) {
   } else {
     int L = s->seg_blocks;
     if (L == 0) {
-      // Enough segments that B*H*P workgroups cover the 256 compute units.
+      // Enough segments that B*H*P workgroups cover the 256 compute units,
+      // but no shorter than about sqrt(0.3 nblk) blocks: each segment adds
+      // one dependent step to the chain (about 2 us), each block of
+      // segment length about 7 us to the summary and output passes, so on
+      // short chunks, where 256 workgroups cannot be filled with whole
+      // work anyway, the sum of the two is smallest there.
       const long long bh = (long long)s->B * s->H;
       long long P0 = (256 + bh - 1) / bh;
       if (P0 > p.nblk) P0 = p.nblk;
       if (P0 < 1) P0 = 1;
       L = (int)((p.nblk + P0 - 1) / P0);
+      const int Lmin = (int)std::lround(std::sqrt(0.3 * (double)p.nblk));
+      if (L < Lmin) L = Lmin;
     }
     if (L > p.nblk) L = p.nblk;
     p.L = L;
@@ -183,6 +191,16 @@ sf_status hip_fail(hipError_t e, const char* what) {
 
 // ---------------------------------------------------------------- ABI ------
 extern "C" {
+
+sf_status sf_gdn_segment_plan(const sf_gdn_shape* shape, int* seg_blocks, int* segments) {
+  Plan p;
+  sf_status s = make_plan(shape, p);
+  if (s != SF_OK) return s;
+  if (!seg_blocks || !segments) return fail(SF_ERR_INVALID_ARG, "output pointer is NULL");
+  *seg_blocks = p.L;
+  *segments = p.P;
+  return SF_OK;
+}
 
 sf_status sf_gdn_chunk_fwd_workspace_size(const sf_gdn_shape* shape, size_t* bytes) {
   Plan p;

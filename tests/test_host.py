@@ -119,8 +119,9 @@ def _bwd_saved(shape, saved=20 * G, svn=None, ws=24 * G, wsn=None, dq=8 * G):
 def test_saved_buffer_validation():
     shape = _shape(T=8192, H=2)
     need = _lib.saved_bytes(shape)
-    # per-block fp32 entry states at least
-    assert need >= 2 * (8192 // 64) * 128 * 128 * 4
+    # at least the per-block entry states and Tp, Tpp, in bf16, of 2 heads
+    nblk = 8192 // 64
+    assert need >= 2 * nblk * (128 * 128 + 2 * 64 * 64) * 2
     for call in (_fwd_save, _bwd_saved):
         assert call(shape, svn=need - 1) == _lib.SF_ERR_INVALID_ARG
         assert "saved" in _lib.load().sf_last_error_message().decode()
@@ -224,3 +225,20 @@ def test_bench_algorithmic_figures():
     assert bench.kernel_bytes_per_token_head("gdn_fwd_out", 128) == 1032
     assert bench.kernel_bytes_per_token_head("gdn_fwd_summary", 128) is None
     assert bench.kernel_flops_per_block("gdn_fwd_out", 128) / 64 == 180224
+
+
+def test_segment_plan():
+    """The in-chunk scan's segments: enough to occupy 256 compute units, no
+    shorter than about sqrt(0.3 nblk) blocks, an explicit length honoured,
+    none for an empty chunk."""
+    plan = lambda T, H, seg=0: _lib.segment_plan(_shape(T=T, H=H, seg=seg))
+    assert plan(65536, 16) == (64, 16)      # 16 heads x 16 segments
+    assert plan(62720, 16) == (62, 16)      # ragged last segment
+    assert plan(16384, 16) == (16, 16)
+    assert plan(65536, 32) == (128, 8)
+    assert plan(1024, 16) == (2, 8)         # short chunk: floor sqrt(0.3 * 16) ~ 2
+    assert plan(256, 2) == (1, 4)
+    assert plan(64, 16) == (1, 1)
+    assert plan(1024, 16, seg=1) == (1, 16)
+    assert plan(1024, 16, seg=64) == (16, 1)  # clamped to the chunk
+    assert plan(0, 16) == (1, 0)

@@ -30,9 +30,18 @@ def rel_err(x, ref, head_axis=None):
     return worst
 
 
+def frob_err(x, ref):
+    """||x - ref||_F / ||ref||_F (reported beside the max-relative bar)."""
+    x = np.asarray(x, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    den = np.linalg.norm(ref)
+    return float(np.linalg.norm(x - ref) / den) if den > 0 else float(np.linalg.norm(x))
+
+
 def assert_close(name, x, ref, tol, head_axis=None):
     e = rel_err(x, ref, head_axis)
-    assert e <= tol, "%s: max relative error %.3e > %.1e" % (name, e, tol)
+    assert e <= tol, "%s: max relative error %.3e > %.1e (relative Frobenius error %.3e)" % (
+        name, e, tol, frob_err(x, ref))
     return e
 
 

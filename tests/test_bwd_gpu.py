@@ -200,6 +200,32 @@ def test_saved_chain_nonuniform_fwd_bwd(oracle_mod):
     check_all([f64(x) for x in g], oracle_bwd(oracle_mod, d), TOL["bf16"])
 
 
+def test_full_size_benchmark_chain_sampled_head(oracle_mod):
+    """The benchmark workload at its full size and in the launch
+    configuration the benchmark times: T = 262,144, H = 16, d = 128, bf16,
+    eight chunks by the c_i(0.5) plan, the saving forward then the saved
+    backward, chained.  Inputs are drawn on the device by the seeded
+    generator, as the benchmark draws them; one head is copied out and
+    checked whole against the unchunked oracle (chunking is exact in real
+    arithmetic), forward and backward."""
+    T, H = 262144, 16
+    lengths = chunk_lengths(T, 8, 0.5)
+    dd = inputs(1, T, H, 128, "bf16", seed=20260004, grads=True, device="cuda")
+    o, states, saved = gdn.chain_fwd(dd["q"], dd["k"], dd["v"], dd["alpha"], dd["beta"], None,
+                                     lengths, save=True)
+    g = gdn.chain_bwd(dd["q"], dd["k"], dd["v"], dd["alpha"], dd["beta"], dd["dO"],
+                      dd["dS_out"], lengths, None, saved=saved)
+    torch.cuda.synchronize()
+    hs = [9]
+    sub = head_slice(dd, hs)
+    o_ref, s_ref = oracle_mod.gdn_fwd(*oracle_args(sub))
+    assert_close("o", f64(o[:, :, hs]), o_ref, TOL["bf16"], head_axis=2)
+    assert_close("S_out", f64(states[-1][:, hs]), s_ref, TOL["bf16"], head_axis=1)
+    ref = oracle_bwd(oracle_mod, sub)
+    sel = [f64(x[:, :, hs]) if ax == 2 else f64(x[:, hs]) for x, ax in zip(g, HEAD_AXIS)]
+    check_all(sel, ref, TOL["bf16"])
+
+
 def test_saved_bwd_empty_chunk():
     d = to_dev(inputs(1, 0, 2, 64, "bf16", seed=10, s_in_std=0.1, grads=True))
     fa = (d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["S_in"])

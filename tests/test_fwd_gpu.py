@@ -123,6 +123,21 @@ def test_full_size_h32_t65536_sampled_heads(oracle_mod):
     assert_close("S_out", S[:, hs], S_ref, TOL["bf16"], head_axis=1)
 
 
+def test_full_size_h16_t65536_sampled_heads(oracle_mod):
+    """The forward-only target shape (T=65536, H=16, d=128, bf16, S_in ~
+    N(0, 0.1)), drawn on the device by the seeded generator as the benchmark
+    draws it, in the launch configuration the benchmark times (16 segments
+    of 64 blocks); the oracle checks two whole heads."""
+    dd = inputs(1, 65536, 16, 128, "bf16", seed=20260102, s_in_std=0.1, device="cuda")
+    o, S = gdn.chunk_fwd(dd["q"], dd["k"], dd["v"], dd["alpha"], dd["beta"], dd["S_in"])
+    torch.cuda.synchronize()
+    hs = [2, 13]
+    sub = head_slice(dd, hs)
+    o_ref, S_ref = oracle_mod.gdn_fwd(*oracle_args(sub))
+    assert_close("o", f64(o[:, :, hs]), o_ref, TOL["bf16"], head_axis=2)
+    assert_close("S_out", f64(S[:, hs]), S_ref, TOL["bf16"], head_axis=1)
+
+
 def test_nonuniform_chunk_lengths_are_block_multiples():
     lengths = chunk_lengths(262144, 8, 0.5)
     assert sum(lengths) == 262144 and all(n % 64 == 0 for n in lengths)

@@ -113,8 +113,10 @@ sf_status sf_gdn_chunk_bwd(const sf_gdn_shape* shape, const void* q, const void*
  * as the page's per-chunk activation release implies ("What carries the
  * argument"; Referee Report, major comment 1).  When memory allows keeping a
  * chunk's block states until its backward, sf_gdn_chunk_fwd_save also writes
- *   - the entry state of every 64-token block, [B, H, ceil(T/64), Dv, Dk] in
- *     the q/k/v dtype (each state enters the backward's products in it)
+ *   - the entry state of every 64-token block, B*H*ceil(T/64) states of
+ *     Dv x Dk values in the q/k/v dtype (each state enters the backward's
+ *     products in it), each in the library's internal tile order (the order
+ *     in which its matrix-core accumulators hold it), not row-major
  *   - the segment transition maps of the in-chunk scan, row-major, fp32
  *     [B, H, P, Dk, Dk]
  *   - per block, T diag(beta o gamma) and T diag(beta) for T = (I + A)^{-1} of

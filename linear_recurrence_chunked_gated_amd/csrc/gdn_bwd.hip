@@ -151,14 +151,9 @@ __global__ __launch_bounds__(4 * D, 2) void gdn_bwd_dscan_kernel(BwdArgs a, int 
   for (int blk = blk1 - 1; blk >= blk0; --blk) {
     const int t0 = blk * BLK, nv = min(BLK, f.T - t0);
     pf.stage(Qs, Ks, Os, Tp, LDD, LDC, nv, G);
-    if constexpr (MAIN) {
-      T* gb = reinterpret_cast<T*>(a.dhst) + ((size_t)bh * f.nblk + blk) * D * D;
-#pragma unroll
-      for (int aa = 0; aa < DKT; ++aa) {
-        const f32x4 x = dSv[aa];
-        st4(gb + (size_t)(16 * w + li) * D + 16 * aa + g4, x[0], x[1], x[2], x[3]);
-      }
-    }
+    if constexpr (MAIN)
+      StateTiles<T, D>::store(reinterpret_cast<T*>(a.dhst) + ((size_t)bh * f.nblk + blk) * D * D,
+                              w, lane, dSv);
     if (blk > blk0)
       pf.fetch(q, k, dO, al, bt, tp_block<T>(f.tw, f.nblk, bh, blk - 1), rs, f.H, t0 - BLK, BLK);
     lds_barrier();
@@ -373,12 +368,8 @@ __global__ __launch_bounds__(4 * D, 2) void gdn_bwd_grads_kernel(BwdArgs a) {
     Tl::load(r0, q, rs, nv);
     Tl::load(r1, k, rs, nv);
     __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int aa = 0; aa < DKT; ++aa) {
-      const size_t off = (size_t)(16 * w + li) * D + 16 * aa + g4;
-      Sx[aa] = ld4f(hS + off);
-      dSx[aa] = ld4f(hG + off);
-    }
+    StateTiles<T, D>::load(hS, w, lane, Sx);
+    StateTiles<T, D>::load(hG, w, lane, dSx);
     __builtin_amdgcn_sched_barrier(0);
     Tl::load(r2, v, rs, nv);
     Tl::load(r3, dO, rs, nv);

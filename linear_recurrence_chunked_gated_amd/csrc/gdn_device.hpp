@@ -206,6 +206,48 @@ __device__ __forceinline__ f32x4 ld4f(const bf16* p) {
 }
 __device__ __forceinline__ f32x4 ld4f(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
 
+// Per-block states (and state gradients) in HBM, D x D values per block, in
+// the order the MFMA accumulators hold them: the 16 x D tile of wave w
+// (rows 16 w ..), then, per lane, 16-byte vectors of the lane's
+// accumulator entries.  Lane l = i + 16 g holds, for each 16 x 16 tile a,
+// rows 16 w + i and columns 16 a + 4 g .. + 3; vector v packs tiles
+// v * TPV .. + TPV - 1.  Every store and load of a state is then one
+// contiguous 1 KiB per wave instruction.
+template <typename T, int D> struct StateTiles {
+  static constexpr int E = 16 / (int)sizeof(T);  // elements per 16-byte vector
+  static constexpr int TPV = E / 4;              // 16 x 16 tiles per vector
+  static constexpr int NV = D / 16 / TPV;        // vectors per lane
+  static_assert(TPV >= 1 && NV * TPV == D / 16, "tile packing");
+  __device__ static __forceinline__ size_t off(int w, int lane, int v) {
+    return (size_t)w * 16 * D + (size_t)v * 64 * E + (size_t)lane * E;
+  }
+  __device__ static __forceinline__ void store(T* blockbase, int w, int lane, const f32x4* x) {
+#pragma unroll
+    for (int v = 0; v < NV; ++v) {
+      if constexpr (TPV == 2) {
+        const f32x4 a = x[2 * v], b = x[2 * v + 1];
+        const bf16x8 h = {(bf16)a[0], (bf16)a[1], (bf16)a[2], (bf16)a[3],
+                          (bf16)b[0], (bf16)b[1], (bf16)b[2], (bf16)b[3]};
+        *reinterpret_cast<bf16x8*>(blockbase + off(w, lane, v)) = h;
+      } else {
+        *reinterpret_cast<f32x4*>(blockbase + off(w, lane, v)) = x[v];
+      }
+    }
+  }
+  __device__ static __forceinline__ void load(const T* blockbase, int w, int lane, f32x4* x) {
+#pragma unroll
+    for (int v = 0; v < NV; ++v) {
+      if constexpr (TPV == 2) {
+        const bf16x8 h = *reinterpret_cast<const bf16x8*>(blockbase + off(w, lane, v));
+        x[2 * v] = f32x4{(float)h[0], (float)h[1], (float)h[2], (float)h[3]};
+        x[2 * v + 1] = f32x4{(float)h[4], (float)h[5], (float)h[6], (float)h[7]};
+      } else {
+        x[v] = *reinterpret_cast<const f32x4*>(blockbase + off(w, lane, v));
+      }
+    }
+  }
+};
+
 // dst[n][m..m+3] = scale * acc for the tile at (m0, n0).
 template <typename T>
 __device__ __forceinline__ void store_tile_T(const f32x4& acc, T* dst, int ld, int m0, int n0,

@@ -241,14 +241,8 @@ __global__ __launch_bounds__(64 * fwd_nw<D>(), 2) void gdn_fwd_out_kernel(FwdArg
     const int t0 = blk * BLK, nv = min(BLK, a.T - t0);
     pf.stage(Qs, Ks, Vs, Tp, Tpp, LDD, LDC, nv, G);
     if constexpr (STATES) {
-      T* hb = hst + ((size_t)bh * a.nblk + blk) * D * D;
-#pragma unroll
-      for (int bb = 0; bb < NDV; ++bb)
-#pragma unroll
-        for (int aa = 0; aa < DKT; ++aa) {
-          const f32x4 x = St[bb][aa];
-          st4(hb + (size_t)(16 * (dv0 + bb) + li) * D + 16 * aa + g4, x[0], x[1], x[2], x[3]);
-        }
+      static_assert(NDV == 1, "one state tile row per wave");
+      StateTiles<T, D>::store(hst + ((size_t)bh * a.nblk + blk) * D * D, dv0, lane, St[0]);
     }
     if constexpr (OUT) {
       if (prev_t0 >= 0) store_o();
@@ -396,14 +390,8 @@ __global__ __launch_bounds__(64 * fwd_nw<D>(), 2) void gdn_fwd_out2_kernel(FwdAr
     const int t0 = blk * BLK, nv = min(BLK, a.T - t0);
     const bool next = blk + 1 < blk1;
     if constexpr (STATES) {
-      T* hb = hst + ((size_t)bh * a.nblk + blk) * D * D;
-#pragma unroll
-      for (int bb = 0; bb < NDV; ++bb)
-#pragma unroll
-        for (int aa = 0; aa < DKT; ++aa) {
-          const f32x4 x = St[bb][aa];
-          st4(hb + (size_t)(16 * (dv0 + bb) + li) * D + 16 * aa + g4, x[0], x[1], x[2], x[3]);
-        }
+      static_assert(NDV == 1, "one state tile row per wave");
+      StateTiles<T, D>::store(hst + ((size_t)bh * a.nblk + blk) * D * D, dv0, lane, St[0]);
     }
     if (next) {
       pf.stage(Qs, Kb(n), Vs, Tp, Tpp, LDD, LDC, min(BLK, a.T - t0 - BLK), Gb(n));

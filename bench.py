@@ -11,10 +11,13 @@ d_k = d_v = 128, bf16, split into 8 chunks by the hybrid-cost plan
 c_i(alpha = 0.5) of Eq. 9 (a = 1, b = 0.25, literal token units).  Inputs are
 synthetic and resident in HBM before timing starts.
 
-Prints one JSON line with the metric, a roofline for the dominant kernel
-(per-launch times from HIP events recorded around every launch on the
-launching stream during the timed region) and for the whole path, and the
-fp64 CPU oracle timed on a bounded sample.
+The timed region replays one captured step as a HIP graph K times (every
+launch of the step; the host's launch gaps removed); --eager times the
+launches themselves.  Per-kernel times come from HIP events recorded around
+every launch on its stream during K eager steps with the same inputs.
+
+Prints one JSON line with the metric, a roofline for the dominant kernel and
+for the whole path, and the fp64 CPU oracle timed on a bounded sample.
 """
 import argparse
 import hashlib
@@ -308,6 +311,7 @@ def bench_conv(args):
     def step():
         if overlap:
             return step_overlap()
+        stream = torch.cuda.current_stream()  # the capture stream under --graph
         for i in range(len(chunks)):
             sl = slice(bounds[i], bounds[i + 1])
             _lib.shortconv_fwd(x[:, sl], w, states[i], 1, y=y[:, sl], conv_out=states[i + 1],
@@ -422,6 +426,9 @@ def main():
     ap.add_argument("--cold", action="store_true",
                     help="write a 512 MiB scratch buffer before every timed step (outside the "
                          "timed events) so that no input is served from the last-level cache")
+    ap.add_argument("--eager", action="store_true",
+                    help="time eager launches instead of replays of one step captured as a HIP "
+                         "graph (the default; per-kernel times always come from an eager pass)")
     ap.add_argument("--no-measured-peaks", action="store_true",
                     help="skip the copy and GEMM measurements of the achievable peaks")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -510,6 +517,7 @@ def main():
     def step():
         if overlap:
             return step_overlap()
+        stream = torch.cuda.current_stream()  # the capture stream under --graph
         for i in range(len(chunks)):
             sl = slice(bounds[i], bounds[i + 1])
             _lib.chunk_fwd(q[:, sl], k[:, sl], v[:, sl], al[:, sl], be[:, sl], states[i],
@@ -527,10 +535,30 @@ def main():
                                saved=saved[i])
                 G = gst[i]
 
+    # The timed region replays one captured step (every launch of the step,
+    # none skipped) unless launches are to be timed one by one, the step spans
+    # two streams (--overlap) or a cache flush sits between steps (--cold).
+    use_graph = not (args.eager or overlap or args.cold)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    graph = None
+    if use_graph:
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        wall0 = time.perf_counter()
+        e0.record(stream)
+        for _ in range(args.steps):
+            graph.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        wall_graph = time.perf_counter() - wall0
+        ms_graph = e0.elapsed_time(e1) / args.steps
     if args.cold:
         scratch = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
         ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
@@ -553,11 +581,13 @@ def main():
         wall = time.perf_counter() - wall0
     if args.cold:
         ms = sum(a.elapsed_time(b) for a, b in ev) / args.steps
+    elif graph is not None:
+        ms, wall = ms_graph, wall_graph  # the eager pass above only supplies per-kernel times
     else:
         ms = e0.elapsed_time(e1) / args.steps
     tok_s = T / (ms * 1e-3)
 
-    # Per-kernel times over the timed region.
+    # Per-kernel times over the eager steps (the timed region itself with --eager).
     kern = {name: {"launches": n, "avg_us": tot / n * 1e3, "total_ms_per_step": tot / args.steps}
             for name, (n, tot) in prof.results.items()}
     dom = max(kern, key=lambda n: kern[n]["total_ms_per_step"])
@@ -641,7 +671,9 @@ def main():
                    "backward_states": "saved by the forward" if save else
                    ("recomputed" if wl["bwd"] else None),
                    "overlap": "state-independent launches of the next chunk on a second stream"
-                              if overlap else None},
+                              if overlap else None,
+                   "launch": ("one captured step replayed as a HIP graph (per-kernel times from "
+                              "an eager pass)") if graph is not None else "eager"},
         "roofline": roofline,
         "path_roofline": path,
         "kernels": {n: {"avg_us": round(x["avg_us"], 2), "launches_per_step": x["launches"] // args.steps,

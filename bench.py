@@ -299,6 +299,7 @@ def bench_conv(args):
         wsb2 = [wsb, _lib.alloc_workspace(ws_b, dev)] if wl["bwd"] else None
 
     def step_overlap():
+        stream = torch.cuda.current_stream()  # the capture stream when graph-replayed
         gchain.chain_fwd(q, k, v, al, be, states[0], chunks, o=o, seg_blocks=args.seg_blocks,
                          stream=stream, save=save, overlap=True, side_stream=side,
                          workspaces=wsf2, saved=saved if save else None, states=states)
@@ -505,6 +506,7 @@ def main():
         wsb2 = [wsb, _lib.alloc_workspace(ws_b, dev)] if wl["bwd"] else None
 
     def step_overlap():
+        stream = torch.cuda.current_stream()  # the capture stream when graph-replayed
         gchain.chain_fwd(q, k, v, al, be, states[0], chunks, o=o, seg_blocks=args.seg_blocks,
                          stream=stream, save=save, overlap=True, side_stream=side,
                          workspaces=wsf2, saved=saved if save else None, states=states)
@@ -537,7 +539,8 @@ def main():
 
     # The timed region replays one captured step (every launch of the step,
     # none skipped) unless launches are to be timed one by one, the step spans
-    # two streams (--overlap) or a cache flush sits between steps (--cold).
+    # two streams (--overlap; captured, it measured slower than the plain
+    # captured step) or a cache flush sits between steps (--cold).
     use_graph = not (args.eager or overlap or args.cold)
     for _ in range(args.warmup):
         step()

@@ -510,6 +510,13 @@ __global__ __launch_bounds__(64 * fwd_nw<D>(), 2) void gdn_fwd_summary_kernel(Fw
 #pragma unroll
       for (int aa = 0; aa < DKT; ++aa) Nt[bb][aa] *= gc;
     block_state_write<T, D, NDV>(Ks, LDD, X, dsc, Nt);
+    // The next block's inputs go out here, so that their latency is covered
+    // by the M update (registers do not allow them over the N update too; for
+    // fp32 operands not even over the M update).
+    constexpr bool EARLY = sizeof(T) == 2;
+    if (EARLY && blk + 1 < blk1)
+      pf.fetch(nullptr, k, v, al, bt, tw_block<T>(a.tw, a.nblk, bh, blk + 1), rs, a.H, t0 + BLK,
+               min(BLK, a.T - t0 - BLK));
     // M: Z = -(W M^T) ; M' = gamma_C M + (D Z)^T-term through K
     zero_acc(X);
     block_x_st<T, D, NDV>(Wn, LDD, Mt, X);
@@ -518,7 +525,7 @@ __global__ __launch_bounds__(64 * fwd_nw<D>(), 2) void gdn_fwd_summary_kernel(Fw
 #pragma unroll
       for (int aa = 0; aa < DKT; ++aa) Mt[bb][aa] *= gc;
     block_state_write<T, D, NDV>(Ks, LDD, X, dsc, Mt);
-    if (blk + 1 < blk1)
+    if (!EARLY && blk + 1 < blk1)
       pf.fetch(nullptr, k, v, al, bt, tw_block<T>(a.tw, a.nblk, bh, blk + 1), rs, a.H, t0 + BLK,
                min(BLK, a.T - t0 - BLK));
     lds_barrier();

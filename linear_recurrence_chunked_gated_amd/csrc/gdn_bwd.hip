@@ -48,18 +48,25 @@ template <typename T, int D> struct ScanPrefetch {
   typedef Tile<T, BLK, 4 * D> Tt;
   uint4 rq[Tl::NCH], rk[Tl::NCH], ro[Tl::NCH], rp[Tt::NCH];
   float ra = 1.f, rb = 0.f;  // raw gates of the next block (wave 0)
+  // PART: 1 the gates and Tp, 2 q and k, 4 dO (bit mask); spread over a
+  // block so that the address unit works beside the matrix work.
+  template <int PART = 7>
   __device__ __forceinline__ void fetch(const T* q, const T* k, const T* dO, const float* al,
                                         const float* bt, const T* tp, size_t rs, int H, int t0,
                                         int nv) {
-    if (wave_id() == 0) {
-      const size_t idx = (size_t)(t0 + min(lane_id(), nv - 1)) * H;
-      ra = al[idx];
-      rb = bt[idx];
+    if constexpr (PART & 1) {
+      if (wave_id() == 0) {
+        const size_t idx = (size_t)(t0 + min(lane_id(), nv - 1)) * H;
+        ra = al[idx];
+        rb = bt[idx];
+      }
+      Tt::load(rp, tp, BLK, BLK);
     }
-    Tt::load(rp, tp, BLK, BLK);
-    Tl::load(rq, q + (size_t)t0 * rs, rs, nv);
-    Tl::load(rk, k + (size_t)t0 * rs, rs, nv);
-    Tl::load(ro, dO + (size_t)t0 * rs, rs, nv);
+    if constexpr (PART & 2) {
+      Tl::load(rq, q + (size_t)t0 * rs, rs, nv);
+      Tl::load(rk, k + (size_t)t0 * rs, rs, nv);
+    }
+    if constexpr (PART & 4) Tl::load(ro, dO + (size_t)t0 * rs, rs, nv);
   }
   __device__ __forceinline__ void stage(T* Qs, T* Ks, T* Os, T* Tp, int ld, int ldc, int nv,
                                         const GateLds& G) {
@@ -154,11 +161,18 @@ __global__ __launch_bounds__(4 * D, 2) void gdn_bwd_dscan_kernel(BwdArgs a, int 
     if constexpr (MAIN)
       StateTiles<T, D>::store(reinterpret_cast<T*>(a.dhst) + ((size_t)bh * f.nblk + blk) * D * D,
                               w, lane, dSv);
-    if (blk > blk0)
-      pf.fetch(q, k, dO, al, bt, tp_block<T>(f.tw, f.nblk, bh, blk - 1), rs, f.H, t0 - BLK, BLK);
+    // the previous block's inputs, in three parts over the first half of this one
+    const bool more = blk > blk0;
+    auto fetch_part = [&](auto part) {
+      pf.template fetch<decltype(part)::value>(q, k, dO, al, bt,
+                                               tp_block<T>(f.tw, f.nblk, bh, blk - 1), rs, f.H,
+                                               t0 - BLK, BLK);
+    };
+    if (more) fetch_part(std::integral_constant<int, 1>{});
     lds_barrier();
     // P scores, the dO^T diag(gamma) Q term and Wn = -Tp K
     block_scores<T, D, NW, true, false>(Qs, Ks, LDD, G, nullptr, 0, Pl, LDC);
+    if (more) fetch_part(std::integral_constant<int, 2>{});
     f32x4 X2[DKT];
 #pragma unroll
     for (int aa = 0; aa < DKT; ++aa) X2[aa] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -171,6 +185,7 @@ __global__ __launch_bounds__(4 * D, 2) void gdn_bwd_dscan_kernel(BwdArgs a, int 
     }
     block_w<T, D, NW>(Ks, LDD, Tp, LDC, Wn);
     lds_barrier();
+    if (more) fetch_part(std::integral_constant<int, 4>{});
     // dVn = P^T dO + D (K dS'^T)
     f32x4 dvn[4], kd[4];
 #pragma unroll

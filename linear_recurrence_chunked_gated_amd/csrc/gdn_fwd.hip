@@ -94,19 +94,27 @@ template <typename T, int D, bool WITH_Q> struct Prefetch {
   typedef Tile<T, BLK, 64 * fwd_nw<D>()> Tt;
   uint4 rq[WITH_Q ? Tl::NCH : 1], rk[Tl::NCH], rv[Tl::NCH], rp[Tt::NCH], rpp[Tt::NCH];
   float ra = 1.f, rb = 0.f;  // raw gates of the next block (wave 0)
+  // PART: 1 the gates and Tp, Tpp, 2 q and k, 4 v (bit mask).  Spreading the
+  // parts over a block keeps the address unit's time for them beside the
+  // matrix work instead of stalling every wave at once.
+  template <int PART = 7>
   __device__ __forceinline__ void fetch(const T* q, const T* k, const T* v, const float* al,
                                         const float* bt, const T* tw, size_t rs, int H, int t0,
                                         int nv) {
-    if (wave_id() == 0) {
-      const size_t idx = (size_t)(t0 + min(lane_id(), nv - 1)) * H;
-      ra = al[idx];
-      rb = bt[idx];
+    if constexpr (PART & 1) {
+      if (wave_id() == 0) {
+        const size_t idx = (size_t)(t0 + min(lane_id(), nv - 1)) * H;
+        ra = al[idx];
+        rb = bt[idx];
+      }
+      Tt::load(rp, tw, BLK, BLK);
+      Tt::load(rpp, tw + BLK * BLK, BLK, BLK);
     }
-    Tt::load(rp, tw, BLK, BLK);
-    Tt::load(rpp, tw + BLK * BLK, BLK, BLK);
-    if constexpr (WITH_Q) Tl::load(rq, q + (size_t)t0 * rs, rs, nv);
-    Tl::load(rk, k + (size_t)t0 * rs, rs, nv);
-    Tl::load(rv, v + (size_t)t0 * rs, rs, nv);
+    if constexpr (PART & 2) {
+      if constexpr (WITH_Q) Tl::load(rq, q + (size_t)t0 * rs, rs, nv);
+      Tl::load(rk, k + (size_t)t0 * rs, rs, nv);
+    }
+    if constexpr (PART & 4) Tl::load(rv, v + (size_t)t0 * rs, rs, nv);
   }
   __device__ __forceinline__ void stage(T* Qs, T* Ks, T* Vs, T* Tp, T* Tpp, int ld, int ldc,
                                         int nv, const GateLds& G) {
@@ -353,6 +361,10 @@ __global__ __launch_bounds__(64 * fwd_nw<D>(), 2) void gdn_fwd_out2_kernel(FwdAr
     pf.fetch(q, k, v, al, bt, tw_block<T>(a.tw, a.nblk, bh, blk), rs, a.H, blk * BLK,
              min(BLK, a.T - blk * BLK));
   };
+  auto fetch_part = [&](auto part, Prefetch<T, D, OUT>& pf, int blk) {
+    pf.template fetch<decltype(part)::value>(q, k, v, al, bt, tw_block<T>(a.tw, a.nblk, bh, blk),
+                                             rs, a.H, blk * BLK, min(BLK, a.T - blk * BLK));
+  };
   // State-free work of a block whose inputs sit in Q, K[n], V, Tp, Tpp and
   // gates G[n]: P -> P[n], Wn -> W[n], U (registers).
   auto pre = [&](int n, f32x4 (&U)[NDV][4]) {
@@ -393,13 +405,15 @@ __global__ __launch_bounds__(64 * fwd_nw<D>(), 2) void gdn_fwd_out2_kernel(FwdAr
       static_assert(NDV == 1, "one state tile row per wave");
       StateTiles<T, D>::store(hst + ((size_t)bh * a.nblk + blk) * D * D, dv0, lane, St[0]);
     }
+    const bool next2 = blk + 2 < blk1;
     if (next) {
       pf.stage(Qs, Kb(n), Vs, Tp, Tpp, LDD, LDC, min(BLK, a.T - t0 - BLK), Gb(n));
-      if (blk + 2 < blk1) fetch(pf, blk + 2);
+      if (next2) fetch_part(std::integral_constant<int, 1>{}, pf, blk + 2);
     }
     lds_barrier();
     // block blk, state part: Vn = U - W S^T; O^T += Vn^T P^T; S' = gamma_C S + Vn^T D K
     block_x_st<T, D, NDV, true>(Wb(c), LDD, St, U);
+    if (next2) fetch_part(std::integral_constant<int, 2>{}, pf, blk + 2);
     if constexpr (OUT) block_vnT_pT<T, NDV, true>(U, Pb(c), LDC, O);
     {
       f32x4 dsc[4];
@@ -414,6 +428,7 @@ __global__ __launch_bounds__(64 * fwd_nw<D>(), 2) void gdn_fwd_out2_kernel(FwdAr
         for (int aa = 0; aa < DKT; ++aa) St[bb][aa] *= gc;
       block_state_write<T, D, NDV, true>(Kb(c), LDD, U, dsc, St);
     }
+    if (next2) fetch_part(std::integral_constant<int, 4>{}, pf, blk + 2);
     if constexpr (OUT) {
 #pragma unroll
       for (int bb = 0; bb < NDV; ++bb)

@@ -367,35 +367,38 @@ __global__ __launch_bounds__(4 * D, 2) void gdn_bwd_grads_kernel(BwdArgs a) {
   const T* hS = reinterpret_cast<const T*>(a.hst) + ((size_t)bh * f.nblk + blk) * D * D;
   const T* hG = reinterpret_cast<const T*>(a.dhst) + ((size_t)bh * f.nblk + blk) * D * D;
 
-  // ---- A: inputs, states (by dv-tile), partial sums.  Q, K and the gates
-  // are staged now; V and dO (first used after the solve) stay in flight in
-  // registers until then.
+  // ---- A: Q, K and the gates, then the states (by dv-tile, first used in
+  // phase C); V and dO (first used after the solve) go out during the scores
+  // and stay in flight in registers until then.  Each group of loads is
+  // issued once the previous one's data is needed or staged, so that no wave
+  // stalls issuing loads it will not use for a while ahead of those it needs
+  // first (the address unit takes a workgroup's 128 KB at about 64 bytes per
+  // cycle); issue order is wait order (vmcnt counts in order).
   typedef Tile<T, D, 4 * D> Tl;
   uint4 r2[Tl::NCH], r3[Tl::NCH];
   f32x4 Sx[DKT], dSx[DKT];  // by dv-tile: m = dk-tile, n = dv-tile w
   {
-    // issue order = wait order (vmcnt counts in order): gates, q, k, the
-    // states (first used in phase C), then v, dO; the scheduling barriers
-    // keep the compiler from hoisting the state loads in front of q and k
     const size_t gidx = gofs + (size_t)min(lane, nv - 1) * f.H;
     const float ra = f.alpha[gidx], rb = f.beta[gidx];
     uint4 r0[Tl::NCH], r1[Tl::NCH];
     Tl::load(r0, q, rs, nv);
     Tl::load(r1, k, rs, nv);
-    __builtin_amdgcn_sched_barrier(0);
-    StateTiles<T, D>::load(hS, w, lane, Sx);
-    StateTiles<T, D>::load(hG, w, lane, dSx);
-    __builtin_amdgcn_sched_barrier(0);
-    Tl::load(r2, v, rs, nv);
-    Tl::load(r3, dO, rs, nv);
     for (int i = threadIdx.x; i < 3 * NW * BLK + NW + 4; i += 64 * NW) part[i] = 0.f;
     Tl::to_lds(r0, Qs, LDD, nv);
     Tl::to_lds(r1, Ks, LDD, nv);
     if (w == 0) block_gates(lane < nv ? __logf(ra) : 0.f, lane < nv ? rb : 0.f, G);
+    __builtin_amdgcn_sched_barrier(0);
+    StateTiles<T, D>::load(hS, w, lane, Sx);
+    StateTiles<T, D>::load(hG, w, lane, dSx);
+    __builtin_amdgcn_sched_barrier(0);
   }
   lds_barrier();
   // ---- B: scores
   block_scores<T, D, NW, true>(Qs, Ks, LDD, G, Af, LDF, Pl, LDC);
+  __builtin_amdgcn_sched_barrier(0);
+  Tl::load(r2, v, rs, nv);
+  Tl::load(r3, dO, rs, nv);
+  __builtin_amdgcn_sched_barrier(0);
   lds_barrier();
   // ---- C: T = (I + A)^{-1}, Tp, Tpp; zero Tm's upper blocks (solve scratch).
   // Meanwhile S and dS' go through LDS once, so that every wave also holds

@@ -368,8 +368,8 @@ __global__ __launch_bounds__(4 * D, 2) void gdn_bwd_grads_kernel(BwdArgs a) {
   const T* hG = reinterpret_cast<const T*>(a.dhst) + ((size_t)bh * f.nblk + blk) * D * D;
 
   // ---- A: Q, K and the gates, then the states (by dv-tile, first used in
-  // phase C); V and dO (first used after the solve) go out during the scores
-  // and stay in flight in registers until then.  Each group of loads is
+  // phase C); V and dO (first used after the solve) go out at the start of
+  // the solve and stay in flight in registers until then.  Each group of loads is
   // issued once the previous one's data is needed or staged, so that no wave
   // stalls issuing loads it will not use for a while ahead of those it needs
   // first (the address unit takes a workgroup's 128 KB at about 64 bytes per
@@ -395,10 +395,6 @@ __global__ __launch_bounds__(4 * D, 2) void gdn_bwd_grads_kernel(BwdArgs a) {
   lds_barrier();
   // ---- B: scores
   block_scores<T, D, NW, true>(Qs, Ks, LDD, G, Af, LDF, Pl, LDC);
-  __builtin_amdgcn_sched_barrier(0);
-  Tl::load(r2, v, rs, nv);
-  Tl::load(r3, dO, rs, nv);
-  __builtin_amdgcn_sched_barrier(0);
   lds_barrier();
   // ---- C: T = (I + A)^{-1}, Tp, Tpp; zero Tm's upper blocks (solve scratch).
   // Meanwhile S and dS' go through LDS once, so that every wave also holds
@@ -413,6 +409,10 @@ __global__ __launch_bounds__(4 * D, 2) void gdn_bwd_grads_kernel(BwdArgs a) {
     st4(Sc + off, Sx[aa][0], Sx[aa][1], Sx[aa][2], Sx[aa][3]);
     st4(Gc + off, dSx[aa][0], dSx[aa][1], dSx[aa][2], dSx[aa][3]);
   }
+  __builtin_amdgcn_sched_barrier(0);
+  Tl::load(r2, v, rs, nv);
+  Tl::load(r3, dO, rs, nv);
+  __builtin_amdgcn_sched_barrier(0);
   block_solve(Af, Tm, LDF);  // its first barrier publishes the copies
   constexpr int KST = D / Mma<T>::KSTEP;
   typename Mma<T>::frag skf[KST], gkf[KST];

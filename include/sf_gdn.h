@@ -119,9 +119,8 @@ sf_status sf_gdn_chunk_bwd(const sf_gdn_shape* shape, const void* q, const void*
  *     in which its matrix-core accumulators hold it), not row-major
  *   - the segment transition maps of the in-chunk scan, row-major, fp32
  *     [B, H, P, Dk, Dk]
- *   - per block, T diag(beta o gamma) and T diag(beta) for T = (I + A)^{-1} of
- *     the block-local (WY/UT) form, [B, H, ceil(T/64), 2, 64, 64] in the
- *     q/k/v dtype
+ *   - per block, T diag(beta) for T = (I + A)^{-1} of the block-local (WY/UT)
+ *     form, [B, H, ceil(T/64), 64, 64] in the q/k/v dtype
  * into the caller's `saved` buffer (size from sf_gdn_chunk_saved_size for
  * the same shape, 256-byte aligned; opaque otherwise), and
  * sf_gdn_chunk_bwd_saved computes the same gradients as sf_gdn_chunk_bwd from

@@ -169,8 +169,9 @@ __device__ __forceinline__ void block_solve(const float* Af, float* Tm, int ldf)
   lds_barrier();
 }
 
-// Tp = T diag(beta o gamma), Tpp = T diag(beta), in the operand type, by a
-// workgroup of NT threads.  Upper 16x16 blocks are written as zero.
+// Tp = T diag(beta o gamma) (unless Tp is null) and Tpp = T diag(beta), in the
+// operand type, by a workgroup of NT threads.  Upper 16x16 blocks are written
+// as zero.
 template <typename T, int NT>
 __device__ __forceinline__ void block_tprime(const float* Tm, int ldf, const GateLds& G, T* Tp,
                                              T* Tpp, int ldc) {
@@ -185,18 +186,42 @@ __device__ __forceinline__ void block_tprime(const float* Tm, int ldf, const Gat
     float t[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) t[e] = upper ? 0.f : Tm[r * ldf + s + e];
-    st4(Tp + r * ldc + s, t[0] * G.bg[s], t[1] * G.bg[s + 1], t[2] * G.bg[s + 2],
-        t[3] * G.bg[s + 3]);
+    if (Tp)
+      st4(Tp + r * ldc + s, t[0] * G.bg[s], t[1] * G.bg[s + 1], t[2] * G.bg[s + 2],
+          t[3] * G.bg[s + 3]);
     st4(Tpp + r * ldc + s, t[0] * G.beta[s], t[1] * G.beta[s + 1], t[2] * G.beta[s + 2],
         t[3] * G.beta[s + 3]);
   }
 }
 
+// The transpose read of rows k of a row-major tile (B operand over k, STD
+// order) with element k scaled by gam[k].
+template <typename T>
+__device__ __forceinline__ typename Mma<T>::frag frag_tr_gamma(const T* p, int ld, int s,
+                                                               const float* gam);
+template <>
+__device__ __forceinline__ bf16x8 frag_tr_gamma<bf16>(const bf16* p, int ld, int s,
+                                                      const float* gam) {
+  bf16x8 f = frag_tr<bf16, STD>(p, ld, s);
+  const int r0 = 32 * s + 8 * (lane_id() >> 4);
+#pragma unroll
+  for (int j = 0; j < 8; ++j) f[j] = (bf16)((float)f[j] * gam[r0 + j]);
+  return f;
+}
+template <>
+__device__ __forceinline__ float frag_tr_gamma<float>(const float* p, int ld, int s,
+                                                      const float* gam) {
+  return frag_tr<float, STD>(p, ld, s) * gam[4 * s + (lane_id() >> 4)];
+}
+
 // Wn = -W, row-major [r][dk], by a workgroup of NW waves (wave w: dk-tiles
 // NDK*w ..): computed as W^T = K^T Tp^T with K^T read through the transpose
-// read from the row-major K tile.
+// read from the row-major K tile.  With gam, the tile given is Tpp = T
+// diag(beta) and Tp = Tpp diag(gamma) is applied through K instead:
+// W = Tpp (diag(gamma) K), each K^T operand element k scaled by gamma_k.
 template <typename T, int D, int NW>
-__device__ __forceinline__ void block_w(const T* Ks, int ldd, const T* Tp, int ldc, T* Wn) {
+__device__ __forceinline__ void block_w(const T* Ks, int ldd, const T* Tp, int ldc, T* Wn,
+                                        const float* gam = nullptr) {
   constexpr int NDK = D / 16 / NW;
   const int w = wave_id();
   f32x4 acc[NDK][4];
@@ -208,7 +233,8 @@ __device__ __forceinline__ void block_w(const T* Ks, int ldd, const T* Tp, int l
     for (int j = 0; j < 4; ++j) bt[j] = frag_row<T, STD>(Tp + 16 * j * ldc, ldc, s);
 #pragma unroll
     for (int i = 0; i < NDK; ++i) {
-      const auto a = frag_tr<T, STD>(Ks + 16 * (NDK * w + i), ldd, s);
+      const auto a = gam ? frag_tr_gamma<T>(Ks + 16 * (NDK * w + i), ldd, s, gam)
+                         : frag_tr<T, STD>(Ks + 16 * (NDK * w + i), ldd, s);
 #pragma unroll
       for (int j = 0; j < 4; ++j) acc[i][j] = Mma<T>::mma(a, bt[j], acc[i][j]);
     }

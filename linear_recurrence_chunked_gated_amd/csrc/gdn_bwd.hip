@@ -29,7 +29,7 @@ __device__ __forceinline__ const T* tok_base(const void* p, int T_, int H, int b
 }
 
 // ------------------------------------------------------------------ LDS ----
-// dscan: RQ Q | RK K | RO dO | RW Wn | RT Tp | RP P | RG gates
+// dscan: RQ Q | RK K | RO dO | RW Wn | RT Tpp | RP P | RG gates
 template <typename T, int D> struct ScanLds {
   static constexpr int LDD = D + Lay<T>::PAD;
   static constexpr int LDC = BLK + Lay<T>::PAD;
@@ -41,14 +41,14 @@ template <typename T, int D> struct ScanLds {
   static_assert(bytes <= 160 * 1024, "LDS budget");
 };
 
-// Per-block inputs of the reverse scan in flight (q, k, dO rows, Tp from the
+// Per-block inputs of the reverse scan in flight (q, k, dO rows, Tpp from the
 // Pre kernel and gates).
 template <typename T, int D> struct ScanPrefetch {
   typedef Tile<T, D, 4 * D> Tl;
   typedef Tile<T, BLK, 4 * D> Tt;
   uint4 rq[Tl::NCH], rk[Tl::NCH], ro[Tl::NCH], rp[Tt::NCH];
   float ra = 1.f, rb = 0.f;  // raw gates of the next block (wave 0)
-  // PART: 1 the gates and Tp, 2 q and k, 4 dO (bit mask); spread over a
+  // PART: 1 the gates and Tpp, 2 q and k, 4 dO (bit mask); spread over a
   // block so that the address unit works beside the matrix work.
   template <int PART = 7>
   __device__ __forceinline__ void fetch(const T* q, const T* k, const T* dO, const float* al,
@@ -81,30 +81,11 @@ template <typename T, int D> struct ScanPrefetch {
   }
 };
 
-// Tp of block blk of sequence bh (the first of its [2][64][64] pair).
+// Tpp = T diag(beta) of block blk of sequence bh ([64][64]; the Pre kernel
+// stores only Tpp, Tp = Tpp diag(gamma) is applied through K).
 template <typename T>
 __device__ __forceinline__ const T* tp_block(const void* tw, int nblk, int bh, int blk) {
-  return reinterpret_cast<const T*>(tw) + ((size_t)bh * nblk + blk) * 2 * BLK * BLK;
-}
-
-// B operand rows dv of gamma_r dO[r][dv] (k = r, STD order): the transpose read
-// of dO scaled per contraction element.
-template <typename T>
-__device__ __forceinline__ typename Mma<T>::frag frag_tr_gamma(const T* p, int ld, int s,
-                                                               const float* gam);
-template <>
-__device__ __forceinline__ bf16x8 frag_tr_gamma<bf16>(const bf16* p, int ld, int s,
-                                                      const float* gam) {
-  bf16x8 f = frag_tr<bf16, STD>(p, ld, s);
-  const int r0 = 32 * s + 8 * (lane_id() >> 4);
-#pragma unroll
-  for (int j = 0; j < 8; ++j) f[j] = (bf16)((float)f[j] * gam[r0 + j]);
-  return f;
-}
-template <>
-__device__ __forceinline__ float frag_tr_gamma<float>(const float* p, int ld, int s,
-                                                      const float* gam) {
-  return frag_tr<float, STD>(p, ld, s) * gam[4 * s + (lane_id() >> 4)];
+  return reinterpret_cast<const T*>(tw) + ((size_t)bh * nblk + blk) * BLK * BLK;
 }
 
 // ------------------------------------------------------- reverse dS scan ---
@@ -124,7 +105,7 @@ __global__ __launch_bounds__(4 * D, 2) void gdn_bwd_dscan_kernel(BwdArgs a, int 
   T* Wn = reinterpret_cast<T*>(smem + Lz::oW);
   T* Ks = reinterpret_cast<T*>(smem + Lz::oK);
   T* Os = reinterpret_cast<T*>(smem + Lz::oO);
-  T* Tp = reinterpret_cast<T*>(smem + Lz::oT);
+  T* Tpp = reinterpret_cast<T*>(smem + Lz::oT);
   T* Pl = reinterpret_cast<T*>(smem + Lz::oP);
   const GateLds G = gate_lds(smem + Lz::oG);
 
@@ -157,7 +138,7 @@ __global__ __launch_bounds__(4 * D, 2) void gdn_bwd_dscan_kernel(BwdArgs a, int 
   }
   for (int blk = blk1 - 1; blk >= blk0; --blk) {
     const int t0 = blk * BLK, nv = min(BLK, f.T - t0);
-    pf.stage(Qs, Ks, Os, Tp, LDD, LDC, nv, G);
+    pf.stage(Qs, Ks, Os, Tpp, LDD, LDC, nv, G);
     if constexpr (MAIN)
       StateTiles<T, D>::store(reinterpret_cast<T*>(a.dhst) + ((size_t)bh * f.nblk + blk) * D * D,
                               w, lane, dSv);
@@ -170,7 +151,7 @@ __global__ __launch_bounds__(4 * D, 2) void gdn_bwd_dscan_kernel(BwdArgs a, int 
     };
     if (more) fetch_part(std::integral_constant<int, 1>{});
     lds_barrier();
-    // P scores, the dO^T diag(gamma) Q term and Wn = -Tp K
+    // P scores, the dO^T diag(gamma) Q term and Wn = -Tpp diag(gamma) K
     block_scores<T, D, NW, true, false>(Qs, Ks, LDD, G, nullptr, 0, Pl, LDC);
     if (more) fetch_part(std::integral_constant<int, 2>{});
     f32x4 X2[DKT];
@@ -183,7 +164,7 @@ __global__ __launch_bounds__(4 * D, 2) void gdn_bwd_dscan_kernel(BwdArgs a, int 
       for (int aa = 0; aa < DKT; ++aa)
         X2[aa] = Mma<T>::mma(frag_tr<T, STD>(Qs + 16 * aa, LDD, s), bo, X2[aa]);
     }
-    block_w<T, D, NW>(Ks, LDD, Tp, LDC, Wn);
+    block_w<T, D, NW>(Ks, LDD, Tpp, LDC, Wn, G.gam);
     lds_barrier();
     if (more) fetch_part(std::integral_constant<int, 4>{});
     // dVn = P^T dO + D (K dS'^T)

@@ -5,8 +5,9 @@
 // state affinely, S' = S M_b + N_b with M_b = gamma_C I - W^T D K and
 // N_b = U^T D K, so a segment is an affine map too.  The forward runs
 //   0. gdn_prep:        per block, fully parallel, the state-free part of
-//      Pre: T = (I + A)^{-1} and its scaled copies Tp, Tpp (the only serial
-//      step inside a block, so it is kept out of the scan kernels);
+//      Pre: T = (I + A)^{-1} and its scaled copy Tpp = T diag(beta) (the
+//      only serial step inside a block, so it is kept out of the scan
+//      kernels; Tp = Tpp diag(gamma) is applied through K where W is formed);
 //   1. gdn_fwd_summary: per segment (except the last), its map (M, N) from
 //      the identity and a zero state, fully parallel;
 //   2. gdn_chain_fwd:   segment entry states S_{j+1} = S_j M_j + N_j, a short
@@ -29,7 +30,7 @@ namespace sfgdn {
 //   RK : K (row-major; K^T operands come from transpose reads)
 //   RV : V (row-major; V^T operands come from transpose reads)
 //   RW : Wn = -W (for Vn)
-//   RT : Tp, Tpp (from the Pre kernel)
+//   RT : Tpp (from the Pre kernel; the first half of the region is unused)
 //   RP : P (masked decayed scores, for the output)
 //   RG : gate vectors
 template <typename T, int D> struct FwdLds {
@@ -76,25 +77,26 @@ __device__ __forceinline__ const T* seq_base(const void* p, const FwdArgs& a, in
 }
 
 
-// Per-block inputs in flight: the next block's rows (q, k, v), its Tp and
-// Tpp from the Pre kernel and its gates are loaded into registers while the
+// Per-block inputs in flight: the next block's rows (q, k, v), its Tpp
+// from the Pre kernel and its gates are loaded into registers while the
 // current block computes.
 // Waves per workgroup of the forward kernels: one per 16-column tile of the
 // state.
 template <int D> constexpr int fwd_nw() { return D / 16; }
 
-// Tp, Tpp of block blk of sequence bh: [2][64][64] row-major.
+// Tpp = T diag(beta) of block blk of sequence bh: [64][64] row-major (Tp =
+// Tpp diag(gamma) is applied through K when W is formed).
 template <typename T>
 __device__ __forceinline__ const T* tw_block(const void* tw, int nblk, int bh, int blk) {
-  return reinterpret_cast<const T*>(tw) + ((size_t)bh * nblk + blk) * 2 * BLK * BLK;
+  return reinterpret_cast<const T*>(tw) + ((size_t)bh * nblk + blk) * BLK * BLK;
 }
 
 template <typename T, int D, bool WITH_Q> struct Prefetch {
   typedef Tile<T, D, 64 * fwd_nw<D>()> Tl;
   typedef Tile<T, BLK, 64 * fwd_nw<D>()> Tt;
-  uint4 rq[WITH_Q ? Tl::NCH : 1], rk[Tl::NCH], rv[Tl::NCH], rp[Tt::NCH], rpp[Tt::NCH];
+  uint4 rq[WITH_Q ? Tl::NCH : 1], rk[Tl::NCH], rv[Tl::NCH], rpp[Tt::NCH];
   float ra = 1.f, rb = 0.f;  // raw gates of the next block (wave 0)
-  // PART: 1 the gates and Tp, Tpp, 2 q and k, 4 v (bit mask).  Spreading the
+  // PART: 1 the gates and Tpp, 2 q and k, 4 v (bit mask).  Spreading the
   // parts over a block keeps the address unit's time for them beside the
   // matrix work instead of stalling every wave at once.
   template <int PART = 7>
@@ -107,8 +109,7 @@ template <typename T, int D, bool WITH_Q> struct Prefetch {
         ra = al[idx];
         rb = bt[idx];
       }
-      Tt::load(rp, tw, BLK, BLK);
-      Tt::load(rpp, tw + BLK * BLK, BLK, BLK);
+      Tt::load(rpp, tw, BLK, BLK);
     }
     if constexpr (PART & 2) {
       if constexpr (WITH_Q) Tl::load(rq, q + (size_t)t0 * rs, rs, nv);
@@ -116,9 +117,8 @@ template <typename T, int D, bool WITH_Q> struct Prefetch {
     }
     if constexpr (PART & 4) Tl::load(rv, v + (size_t)t0 * rs, rs, nv);
   }
-  __device__ __forceinline__ void stage(T* Qs, T* Ks, T* Vs, T* Tp, T* Tpp, int ld, int ldc,
-                                        int nv, const GateLds& G) {
-    Tt::to_lds(rp, Tp, ldc, BLK);
+  __device__ __forceinline__ void stage(T* Qs, T* Ks, T* Vs, T* Tpp, int ld, int ldc, int nv,
+                                        const GateLds& G) {
     Tt::to_lds(rpp, Tpp, ldc, BLK);
     if constexpr (WITH_Q) Tl::to_lds(rq, Qs, ld, nv);
     Tl::to_lds(rk, Ks, ld, nv);
@@ -170,7 +170,7 @@ __global__ __launch_bounds__(256) void gdn_prep_kernel(FwdArgs a) {
   lds_barrier();
   block_solve(Af, Tm, LDF);
   T* out = const_cast<T*>(tw_block<T>(a.tw, a.nblk, bh, blk));
-  block_tprime<T, 256>(Tm, LDF, G, out, out + BLK * BLK, BLK);
+  block_tprime<T, 256>(Tm, LDF, G, nullptr, out, BLK);
 }
 
 // --------------------------------------------------------- fused out -------
@@ -247,7 +247,7 @@ __global__ __launch_bounds__(64 * fwd_nw<D>(), 2) void gdn_fwd_out_kernel(FwdArg
 
   for (int blk = blk0; blk < blk1; ++blk) {
     const int t0 = blk * BLK, nv = min(BLK, a.T - t0);
-    pf.stage(Qs, Ks, Vs, Tp, Tpp, LDD, LDC, nv, G);
+    pf.stage(Qs, Ks, Vs, Tpp, LDD, LDC, nv, G);
     if constexpr (STATES) {
       static_assert(NDV == 1, "one state tile row per wave");
       StateTiles<T, D>::store(hst + ((size_t)bh * a.nblk + blk) * D * D, dv0, lane, St[0]);
@@ -256,7 +256,7 @@ __global__ __launch_bounds__(64 * fwd_nw<D>(), 2) void gdn_fwd_out_kernel(FwdArg
       if (prev_t0 >= 0) store_o();
     }
     lds_barrier();
-    // P = masked Q K^T o Gamma; O^T = diag(gamma) S Q^T; Wn = -Tp K; U = Tpp V
+    // P = masked Q K^T o Gamma; O^T = diag(gamma) S Q^T; Wn = -Tpp diag(gamma) K; U = Tpp V
     if constexpr (OUT) {
       block_scores<T, D, NW, true, false>(Qs, Ks, LDD, G, nullptr, 0, Pl, LDC);
       zero_acc(O);
@@ -268,7 +268,7 @@ __global__ __launch_bounds__(64 * fwd_nw<D>(), 2) void gdn_fwd_out_kernel(FwdArg
         for (int bb = 0; bb < NDV; ++bb) O[bb][j] *= gr;
       }
     }
-    block_w<T, D, NW>(Ks, LDD, Tp, LDC, Wn);
+    block_w<T, D, NW>(Ks, LDD, Tpp, LDC, Wn, G.gam);
     f32x4 U[NDV][4];
     block_u<T, NDV>(Tpp, LDC, Vs, LDD, dv0, U);
     lds_barrier();
@@ -369,7 +369,7 @@ __global__ __launch_bounds__(64 * fwd_nw<D>(), 2) void gdn_fwd_out2_kernel(FwdAr
   // gates G[n]: P -> P[n], Wn -> W[n], U (registers).
   auto pre = [&](int n, f32x4 (&U)[NDV][4]) {
     if constexpr (OUT) block_scores<T, D, NW, true, false>(Qs, Kb(n), LDD, Gb(n), nullptr, 0, Pb(n), LDC);
-    block_w<T, D, NW>(Kb(n), LDD, Tp, LDC, Wb(n));
+    block_w<T, D, NW>(Kb(n), LDD, Tpp, LDC, Wb(n), Gb(n).gam);
     block_u<T, NDV>(Tpp, LDC, Vs, LDD, dv0, U);
   };
   // O^T = diag(gamma) S Q^T of the block in Q with gates G[n].
@@ -389,7 +389,7 @@ __global__ __launch_bounds__(64 * fwd_nw<D>(), 2) void gdn_fwd_out2_kernel(FwdAr
 
   Prefetch<T, D, OUT> pf;
   fetch(pf, blk0);
-  pf.stage(Qs, Kb(0), Vs, Tp, Tpp, LDD, LDC, min(BLK, a.T - blk0 * BLK), Gb(0));
+  pf.stage(Qs, Kb(0), Vs, Tpp, LDD, LDC, min(BLK, a.T - blk0 * BLK), Gb(0));
   if (blk0 + 1 < blk1) fetch(pf, blk0 + 1);
   lds_barrier();
   f32x4 U[NDV][4];
@@ -407,7 +407,7 @@ __global__ __launch_bounds__(64 * fwd_nw<D>(), 2) void gdn_fwd_out2_kernel(FwdAr
     }
     const bool next2 = blk + 2 < blk1;
     if (next) {
-      pf.stage(Qs, Kb(n), Vs, Tp, Tpp, LDD, LDC, min(BLK, a.T - t0 - BLK), Gb(n));
+      pf.stage(Qs, Kb(n), Vs, Tpp, LDD, LDC, min(BLK, a.T - t0 - BLK), Gb(n));
       if (next2) fetch_part(std::integral_constant<int, 1>{}, pf, blk + 2);
     }
     lds_barrier();
@@ -506,9 +506,9 @@ __global__ __launch_bounds__(64 * fwd_nw<D>(), 2) void gdn_fwd_summary_kernel(Fw
              min(BLK, a.T - blk0 * BLK));
   for (int blk = blk0; blk < blk1; ++blk) {
     const int t0 = blk * BLK, nv = min(BLK, a.T - t0);
-    pf.stage(nullptr, Ks, Vs, Tp, Tpp, LDD, LDC, nv, G);
+    pf.stage(nullptr, Ks, Vs, Tpp, LDD, LDC, nv, G);
     lds_barrier();
-    block_w<T, D, NW>(Ks, LDD, Tp, LDC, Wn);
+    block_w<T, D, NW>(Ks, LDD, Tpp, LDC, Wn, G.gam);
     f32x4 X[NDV][4];
     block_u<T, NDV>(Tpp, LDC, Vs, LDD, dv0, X);
     lds_barrier();

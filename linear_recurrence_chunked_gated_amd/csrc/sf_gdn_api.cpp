@@ -90,9 +90,9 @@ sf_status make_plan(const sf_gdn_shape* s, Plan& p) {
 size_t dd(const Plan& p) { return (size_t)p.D * p.D; }
 size_t seg_buf(const Plan& p) { return align_up((size_t)p.B * p.H * p.P * dd(p) * sizeof(float)); }
 size_t elem(const Plan& p) { return p.dtype == SF_DTYPE_BF16 ? 2 : 4; }
-// per-block Tp, Tpp of the Pre kernel: [B*H][nblk][2][64][64] in the operand type
+// per-block Tpp = T diag(beta) of the Pre kernel: [B*H][nblk][64][64] in the operand type
 size_t tw_buf(const Plan& p) {
-  return align_up((size_t)p.B * p.H * p.nblk * 2 * BLK * BLK * elem(p));
+  return align_up((size_t)p.B * p.H * p.nblk * BLK * BLK * elem(p));  // Tpp per block
 }
 size_t fwd_seg(const Plan& p) { return p.P > 1 ? 3 * seg_buf(p) : 0; }
 size_t fwd_ws(const Plan& p) { return fwd_seg(p) + tw_buf(p); }
@@ -225,7 +225,7 @@ sf_status sf_gdn_chunk_bwd_workspace_size(const sf_gdn_shape* shape, size_t* byt
 namespace {
 
 // Layout: per-block entry states [B*H*nblk][D][D], the segment maps
-// [B*H*P][D][D] row-major (P > 1), then the Pre kernel's per-block Tp, Tpp.
+// [B*H*P][D][D] row-major (P > 1), then the Pre kernel's per-block Tpp.
 size_t saved_maps_off(const Plan& p) { return blk_buf(p); }
 size_t saved_tw_off(const Plan& p) { return blk_buf(p) + (p.P > 1 ? seg_buf(p) : 0); }
 size_t saved_bytes(const Plan& p) {
@@ -234,7 +234,7 @@ size_t saved_bytes(const Plan& p) {
 }
 
 // Forward; with `saved` it also stores the per-block entry states, all
-// segment maps and the per-block Tp, Tpp there.
+// segment maps and the per-block Tpp there.
 sf_status fwd_impl(const sf_gdn_shape* shape, const void* q, const void* k, const void* v,
                    const float* alpha, const float* beta, const float* S_in, void* o,
                    float* S_out, void* saved, size_t sv_bytes, void* workspace, size_t ws_bytes,

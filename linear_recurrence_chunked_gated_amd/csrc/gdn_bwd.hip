@@ -245,6 +245,24 @@ __device__ __forceinline__ f32x4 tile_sum_over_n(f32x4 v) {
 __device__ __forceinline__ float tile_sum_over_m(f32x4 v) {
   return sum_rows4((v[0] + v[1]) + (v[2] + v[3]));
 }
+
+// fp32 operands of the gate-chain products (dT T^T and T^T Y, 64 x 64 x 64)
+// go through the bf16 matrix cores as split tiles: x ~ hi + lo with
+// hi = bf16(x) and lo = bf16(x - hi), about 16 significant bits.  A split
+// tile row holds hi[64] | lo[64] | pad, SPLIT_LD bf16 = the bytes of an fp32
+// row of BLK + 4, so a split tile takes an fp32 tile's region.
+constexpr int SPLIT_LD = 2 * (BLK + 4);
+__device__ __forceinline__ void split_store(bf16* row, int c, float x) {
+  const bf16 h = (bf16)x;
+  row[c] = h;
+  row[BLK + c] = (bf16)(x - (float)h);
+}
+// C += A B^T with both operands split, dropping only the lo*lo term.
+__device__ __forceinline__ f32x4 mma_split(bf16x8 ah, bf16x8 al, bf16x8 bh, bf16x8 bl, f32x4 c) {
+  c = Mma<bf16>::mma(al, bh, c);
+  c = Mma<bf16>::mma(ah, bl, c);
+  return Mma<bf16>::mma(ah, bh, c);
+}
 // *p += x in LDS without waiting for the old value (ds_add_f32).  The partial
 // arrays are per wave, so the order of the additions is this wave's program
 // order and the sums stay deterministic.
@@ -582,6 +600,19 @@ __global__ __launch_bounds__(4 * D, 2) void gdn_bwd_grads_kernel(BwdArgs a) {
   }
   lds_barrier();
   // ---- J: dTp = dW K^T, dTpp = dVn V^T (m = r, n = s); dT; column terms
+  // (bf16: T also goes to a split tile in the Q region, free after phase H)
+  constexpr bool SPLIT = sizeof(T) == 2;
+  bf16* Tx = reinterpret_cast<bf16*>(smem + Lz::oQ);   // T, split
+  bf16* dTx = reinterpret_cast<bf16*>(smem + Lz::oW);  // dT, split (in place of dTf)
+  bf16* YTx = reinterpret_cast<bf16*>(smem + Lz::oV);  // Y^T, split (in place of Yf)
+  static_assert(Lz::zR >= BLK * SPLIT_LD * 2 && Lz::zW >= BLK * SPLIT_LD * 2, "split tiles");
+  if constexpr (SPLIT) {
+    for (int i = threadIdx.x; i < BLK * BLK / 8; i += 64 * NW) {
+      const int r = i >> 3, c0 = 8 * (i & 7);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) split_store(Tx + r * SPLIT_LD, c0 + e, Tm[r * LDF + c0 + e]);
+    }
+  }
   {
     const int rt = w & 3, s0t = (w >> 2) * NJ;
     f32x4 a1[NJ], a2[NJ];
@@ -612,7 +643,12 @@ __global__ __launch_bounds__(4 * D, 2) void gdn_bwd_grads_kernel(BwdArgs a) {
         c1[e] = a1[j][e] * tv;  // d(beta gamma)_s
         c2[e] = a2[j][e] * tv;  // dbeta_s through Tpp
       }
-      store_tile_N(dt, dTf, LDF, 16 * rt, 16 * (s0t + j));
+      if constexpr (SPLIT) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) split_store(dTx + (16 * rt + g4 + e) * SPLIT_LD, s, dt[e]);
+      } else {
+        store_tile_N(dt, dTf, LDF, 16 * rt, 16 * (s0t + j));
+      }
       const float sbg = tile_sum_over_m(c1), sb2 = tile_sum_over_m(c2);
       if (lane < 16) {
         lds_add(dbp + s, sb2 + gs * sbg);
@@ -621,21 +657,49 @@ __global__ __launch_bounds__(4 * D, 2) void gdn_bwd_grads_kernel(BwdArgs a) {
     }
   }
   lds_barrier();
-  // ---- K: Y = dT T^T (fp32)
+  // ---- K: Y = dT T^T (fp32 products; split tiles for bf16)
   {
     const int rt = w & 3, s0t = (w >> 2) * NJ;
     f32x4 acc[NJ];
 #pragma unroll
     for (int j = 0; j < NJ; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if constexpr (SPLIT) {
+      const bf16* pa = dTx + 16 * rt * SPLIT_LD;
 #pragma unroll
-    for (int s = 0; s < BLK / 4; ++s) {
-      const float av = frag_row<float, STD>(dTf + 16 * rt * LDF, LDF, s);
+      for (int s = 0; s < BLK / Mma<bf16>::KSTEP; ++s) {
+        const bf16x8 ah = frag_row<bf16, STD>(pa, SPLIT_LD, s);
+        const bf16x8 al = frag_row<bf16, STD>(pa + BLK, SPLIT_LD, s);
 #pragma unroll
-      for (int j = 0; j < NJ; ++j)
-        acc[j] = Mma<float>::mma(av, frag_row<float, STD>(Tm + 16 * (s0t + j) * LDF, LDF, s), acc[j]);
+        for (int j = 0; j < NJ; ++j) {
+          const bf16* pb = Tx + 16 * (s0t + j) * SPLIT_LD;
+          acc[j] = mma_split(ah, al, frag_row<bf16, STD>(pb, SPLIT_LD, s),
+                             frag_row<bf16, STD>(pb + BLK, SPLIT_LD, s), acc[j]);
+        }
+      }
+      // Y^T[s'][r .. r+3], split
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        bf16* row = YTx + (16 * (s0t + j) + li) * SPLIT_LD + 16 * rt + g4;
+        bf16x4 h, l;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          h[e] = (bf16)acc[j][e];
+          l[e] = (bf16)(acc[j][e] - (float)h[e]);
+        }
+        *reinterpret_cast<bf16x4*>(row) = h;
+        *reinterpret_cast<bf16x4*>(row + BLK) = l;
+      }
+    } else {
+#pragma unroll
+      for (int s = 0; s < BLK / 4; ++s) {
+        const float av = frag_row<float, STD>(dTf + 16 * rt * LDF, LDF, s);
+#pragma unroll
+        for (int j = 0; j < NJ; ++j)
+          acc[j] = Mma<float>::mma(av, frag_row<float, STD>(Tm + 16 * (s0t + j) * LDF, LDF, s), acc[j]);
+      }
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) store_tile_N(acc[j], Yf, LDF, 16 * rt, 16 * (s0t + j));
     }
-#pragma unroll
-    for (int j = 0; j < NJ; ++j) store_tile_N(acc[j], Yf, LDF, 16 * rt, 16 * (s0t + j));
   }
   lds_barrier();
   // ---- L: dA = -T^T Y (strictly lower); A-terms of dbeta, dg; dKK
@@ -644,12 +708,26 @@ __global__ __launch_bounds__(4 * D, 2) void gdn_bwd_grads_kernel(BwdArgs a) {
     f32x4 acc[NJ], kk[NJ];
 #pragma unroll
     for (int j = 0; j < NJ; ++j) acc[j] = kk[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if constexpr (SPLIT) {
 #pragma unroll
-    for (int s = 0; s < BLK / 4; ++s) {
-      const float at = frag_tr<float, STD>(Tm + 16 * rt, LDF, s);
+      for (int s = 0; s < BLK / Mma<bf16>::KSTEP; ++s) {
+        const bf16x8 ah = frag_tr<bf16, STD>(Tx + 16 * rt, SPLIT_LD, s);
+        const bf16x8 al = frag_tr<bf16, STD>(Tx + BLK + 16 * rt, SPLIT_LD, s);
 #pragma unroll
-      for (int j = 0; j < NJ; ++j)
-        acc[j] = Mma<float>::mma(at, frag_tr<float, STD>(Yf + 16 * (s0t + j), LDF, s), acc[j]);
+        for (int j = 0; j < NJ; ++j) {
+          const bf16* pb = YTx + 16 * (s0t + j) * SPLIT_LD;
+          acc[j] = mma_split(ah, al, frag_row<bf16, STD>(pb, SPLIT_LD, s),
+                             frag_row<bf16, STD>(pb + BLK, SPLIT_LD, s), acc[j]);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int s = 0; s < BLK / 4; ++s) {
+        const float at = frag_tr<float, STD>(Tm + 16 * rt, LDF, s);
+#pragma unroll
+        for (int j = 0; j < NJ; ++j)
+          acc[j] = Mma<float>::mma(at, frag_tr<float, STD>(Yf + 16 * (s0t + j), LDF, s), acc[j]);
+      }
     }
 #pragma unroll
     for (int s = 0; s < D / Mma<T>::KSTEP; ++s) {

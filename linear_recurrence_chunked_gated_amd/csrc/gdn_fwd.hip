@@ -490,14 +490,18 @@ __global__ __launch_bounds__(64 * fwd_nw<D>(), 2) void gdn_fwd_summary_kernel(Fw
   const float* al = a.alpha + (size_t)b * a.T * a.H + h;
   const float* bt = a.beta + (size_t)b * a.T * a.H + h;
 
-  f32x4 Nt[NDV][DKT], Mt[NDV][DKT];
+  // NM[bb] holds N^T, NM[NDV + bb] holds M^T (tiles m = dk, n = dv): the two
+  // maps go through every product together as 2 NDV state tiles, so each W
+  // and K operand read from LDS serves both.
+  f32x4 NM[2 * NDV][DKT];
 #pragma unroll
   for (int bb = 0; bb < NDV; ++bb)
 #pragma unroll
     for (int aa = 0; aa < DKT; ++aa) {
-      Nt[bb][aa] = f32x4{0.f, 0.f, 0.f, 0.f};
+      NM[bb][aa] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int e = 0; e < 4; ++e) Mt[bb][aa][e] = (16 * aa + g4 + e == 16 * (dv0 + bb) + li) ? 1.f : 0.f;
+      for (int e = 0; e < 4; ++e)
+        NM[NDV + bb][aa][e] = (16 * aa + g4 + e == 16 * (dv0 + bb) + li) ? 1.f : 0.f;
     }
 
   Prefetch<T, D, false> pf;
@@ -519,34 +523,34 @@ __global__ __launch_bounds__(64 * fwd_nw<D>(), 2) void gdn_fwd_summary_kernel(Fw
       for (int e = 0; e < 4; ++e) dsc[i][e] = G.dec[16 * i + g4 + e];
     const float gc = G.gC[0];
     // N: Vn0 = U - W N^T ; N' = gamma_C N + Vn0^T D K
-    block_x_st<T, D, NDV>(Wn, LDD, Nt, X);
+    // M: Z = -(W M^T)    ; M' = gamma_C M + Z^T D K
+    constexpr bool EARLY = sizeof(T) == 2;
+    f32x4 X2[2 * NDV][4];
 #pragma unroll
     for (int bb = 0; bb < NDV; ++bb)
 #pragma unroll
-      for (int aa = 0; aa < DKT; ++aa) Nt[bb][aa] *= gc;
-    block_state_write<T, D, NDV>(Ks, LDD, X, dsc, Nt);
+      for (int i = 0; i < 4; ++i) {
+        X2[bb][i] = X[bb][i];
+        X2[NDV + bb][i] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+    block_x_st<T, D, 2 * NDV>(Wn, LDD, NM, X2);
+#pragma unroll
+    for (int bb = 0; bb < 2 * NDV; ++bb)
+#pragma unroll
+      for (int aa = 0; aa < DKT; ++aa) NM[bb][aa] *= gc;
     // The next block's inputs go out here, so that their latency is covered
-    // by the M update (registers do not allow them over the N update too; for
-    // fp32 operands not even over the M update).
-    constexpr bool EARLY = sizeof(T) == 2;
+    // by the state writes (for fp32 operands registers do not allow it).
     if (EARLY && blk + 1 < blk1)
       pf.fetch(nullptr, k, v, al, bt, tw_block<T>(a.tw, a.nblk, bh, blk + 1), rs, a.H, t0 + BLK,
                min(BLK, a.T - t0 - BLK));
-    // M: Z = -(W M^T) ; M' = gamma_C M + (D Z)^T-term through K
-    zero_acc(X);
-    block_x_st<T, D, NDV>(Wn, LDD, Mt, X);
-#pragma unroll
-    for (int bb = 0; bb < NDV; ++bb)
-#pragma unroll
-      for (int aa = 0; aa < DKT; ++aa) Mt[bb][aa] *= gc;
-    block_state_write<T, D, NDV>(Ks, LDD, X, dsc, Mt);
+    block_state_write<T, D, 2 * NDV>(Ks, LDD, X2, dsc, NM);
     if (!EARLY && blk + 1 < blk1)
       pf.fetch(nullptr, k, v, al, bt, tw_block<T>(a.tw, a.nblk, bh, blk + 1), rs, a.H, t0 + BLK,
                min(BLK, a.T - t0 - BLK));
     lds_barrier();
   }
 
-  // Nt holds N^T (m = dk, n = dv) -> N[dv][dk..]; Mt holds M^T (m = j, n = i) -> M[i][j..].
+  // NM holds N^T (m = dk, n = dv) -> N[dv][dk..] and M^T (m = j, n = i) -> M[i][j..].
   // The forward chain takes M transposed, the backward chain M row-major.
   float* MTo = a.Mseg + ((size_t)bh * a.P + seg) * D * D;
   float* No = a.Nseg + ((size_t)bh * a.P + seg) * D * D;
@@ -556,11 +560,11 @@ __global__ __launch_bounds__(64 * fwd_nw<D>(), 2) void gdn_fwd_summary_kernel(Fw
 #pragma unroll
     for (int aa = 0; aa < DKT; ++aa) {
       const size_t off = (size_t)(16 * (dv0 + bb) + li) * D + 16 * aa + g4;
-      *reinterpret_cast<f32x4*>(No + off) = Nt[bb][aa];
-      if (Mo) *reinterpret_cast<f32x4*>(Mo + off) = Mt[bb][aa];
+      *reinterpret_cast<f32x4*>(No + off) = NM[bb][aa];
+      if (Mo) *reinterpret_cast<f32x4*>(Mo + off) = NM[NDV + bb][aa];
 #pragma unroll
       for (int e = 0; e < 4; ++e)
-        MTo[(size_t)(16 * aa + g4 + e) * D + 16 * (dv0 + bb) + li] = Mt[bb][aa][e];
+        MTo[(size_t)(16 * aa + g4 + e) * D + 16 * (dv0 + bb) + li] = NM[NDV + bb][aa][e];
     }
 }
 

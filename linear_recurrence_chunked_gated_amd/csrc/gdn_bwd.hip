@@ -293,7 +293,7 @@ __device__ __forceinline__ void add_cols(float* part, int n0, f32x4 v, float sig
 template <typename T, int D> struct GradLds {
   static constexpr int NW = D / 16;
   static constexpr int LDD = D + Lay<T>::PAD;
-  static constexpr int LDC = BLK + Lay<T>::PAD;
+  static constexpr int LDC = BLK + Lay<T>::PADC;
   static constexpr int LDF = BLK + 4;
   static constexpr size_t cmax(size_t a, size_t b) { return a > b ? a : b; }
   static constexpr size_t rowD = (size_t)BLK * LDD * sizeof(T);
@@ -376,9 +376,11 @@ __global__ __launch_bounds__(4 * D, 2) void gdn_bwd_grads_kernel(BwdArgs a) {
   typedef Tile<T, D, 4 * D> Tl;
   uint4 r2[Tl::NCH], r3[Tl::NCH];
   f32x4 Sx[DKT], dSx[DKT];  // by dv-tile: m = dk-tile, n = dv-tile w
+  // alpha of this lane's token, kept for dalpha at the end (no global load
+  // there: it would wait for every store of the block, vmcnt being in order)
+  const float ra = f.alpha[gofs + (size_t)min(lane, nv - 1) * f.H];
   {
-    const size_t gidx = gofs + (size_t)min(lane, nv - 1) * f.H;
-    const float ra = f.alpha[gidx], rb = f.beta[gidx];
+    const float rb = f.beta[gofs + (size_t)min(lane, nv - 1) * f.H];
     uint4 r0[Tl::NCH], r1[Tl::NCH];
     Tl::load(r0, q, rs, nv);
     Tl::load(r1, k, rs, nv);
@@ -817,7 +819,7 @@ __global__ __launch_bounds__(4 * D, 2) void gdn_bwd_grads_kernel(BwdArgs a) {
     }
     if (j < nv) {
       const size_t idx = gofs + (size_t)j * f.H;
-      a.dalpha[idx] = x / f.alpha[idx];
+      a.dalpha[idx] = x / ra;
       a.dbeta[idx] = dbv;
     }
   }

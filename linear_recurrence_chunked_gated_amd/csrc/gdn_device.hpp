@@ -71,6 +71,11 @@ template <> struct Mma<float> {
 template <typename T> struct Lay {
   static constexpr int VEC = 16 / sizeof(T);  // elements per 16-byte chunk
   static constexpr int PAD = VEC;             // row padding (elements)
+  // Row padding of 64-wide tiles (scores, Tp, Tpp) in kernels that mostly
+  // read them: 32 bytes for bf16, so that 16-byte row reads of eight
+  // consecutive rows hit distinct banks (8-byte writes of such rows conflict
+  // more, so kernels that write them often keep PAD).
+  static constexpr int PADC = sizeof(T) == 2 ? 2 * VEC : VEC;
   typedef T pack4 __attribute__((ext_vector_type(4)));
 };
 

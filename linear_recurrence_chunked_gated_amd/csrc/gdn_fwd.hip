@@ -35,7 +35,7 @@ namespace sfgdn {
 //   RG : gate vectors
 template <typename T, int D> struct FwdLds {
   static constexpr int LDD = D + Lay<T>::PAD;
-  static constexpr int LDC = BLK + Lay<T>::PAD;
+  static constexpr int LDC = BLK + Lay<T>::PADC;
   static constexpr size_t rowD = (size_t)BLK * LDD * sizeof(T);
   static constexpr size_t sq = (size_t)BLK * LDC * sizeof(T);
   static constexpr size_t oQ = 0, oK = oQ + rowD, oV = oK + rowD, oW = oV + rowD,

@@ -133,15 +133,13 @@ __device__ __forceinline__ void block_solve(const float* Af, float* Tm, int ldf)
   lds_barrier();
   float* X = Tm + 16;  // blocks (0,1) and (0,2) as scratch: X_w at column 16 (w + 1)
   if (w < 2) {
+    // X_w is written and read back by this wave alone: LDS operations of one
+    // wave take effect in order, so no workgroup barrier sits between.
     const int ib = 2 * w + 1, jb = 2 * w;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     gemm_nn_f32<16>(acc, Af + 16 * ib * ldf + 16 * jb, ldf, Tm + 16 * jb * ldf + 16 * jb, ldf);
     store_tile_N(acc, X + 16 * w, ldf, 0, 0);
-  }
-  lds_barrier();
-  if (w < 2) {
-    const int ib = 2 * w + 1, jb = 2 * w;
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    acc = f32x4{0.f, 0.f, 0.f, 0.f};
     gemm_nn_f32<16>(acc, Tm + 16 * ib * ldf + 16 * ib, ldf, X + 16 * w, ldf);
     store_tile_N(acc, Tm + 16 * ib * ldf + 16 * jb, ldf, 0, 0, -1.f);
   }

@@ -115,9 +115,19 @@ __device__ __forceinline__ void block_scores(const T* Qs, const T* Ks, int ldd, 
 // first for the pairs (1,0) and (3,2), then for rows 32..63 x cols 0..31.
 // The upper blocks of Tm are never part of T; they serve as scratch here and
 // must be treated as zero by readers.  Ends with a workgroup barrier.
-__device__ __forceinline__ void block_solve(const float* Af, float* Tm, int ldf) {
+// Wave SUBW does the substitution while the other waves run side(), work of
+// their own that needs neither A nor T; wave SUBW runs its side() during the
+// first block step, which occupies waves 0 and 1 only (SUBW >= 2 then).
+struct NoSide {
+  __device__ void operator()() const {}
+};
+template <int SUBW = 0, class Side = NoSide>
+__device__ __forceinline__ void block_solve(const float* Af, float* Tm, int ldf,
+                                            Side&& side = Side()) {
+  static_assert(SUBW == 0 || SUBW >= 2, "the substituting wave runs its side work in step 1");
   const int w = wave_id(), lane = lane_id();
-  if (w == 0) {
+  if (w != SUBW) side();
+  if (w == SUBW) {
     const int base = 16 * (lane >> 4), c = lane & 15;
     float x[16];
 #pragma unroll
@@ -143,6 +153,7 @@ __device__ __forceinline__ void block_solve(const float* Af, float* Tm, int ldf)
     gemm_nn_f32<16>(acc, Tm + 16 * ib * ldf + 16 * ib, ldf, X + 16 * w, ldf);
     store_tile_N(acc, Tm + 16 * ib * ldf + 16 * jb, ldf, 0, 0, -1.f);
   }
+  if (SUBW != 0 && w == SUBW) side();
   lds_barrier();
   float* R = Tm + 32;  // rows 0..31 x cols 32..63 (upper blocks) as scratch
   if (w < 4) {

@@ -414,7 +414,22 @@ __global__ __launch_bounds__(4 * D, 2) void gdn_bwd_grads_kernel(BwdArgs a) {
   Tl::load(r2, v, rs, nv);
   Tl::load(r3, dO, rs, nv);
   __builtin_amdgcn_sched_barrier(0);
-  block_solve(Af, Tm, LDF);  // its first barrier publishes the copies
+  // K dS'^T (this wave's dv-tile), for dVn in phase E: it needs only K and
+  // dS', so it runs while the last wave does the substitution (and that wave
+  // runs it during the first block step)
+  f32x4 kd[4];
+  auto kd_side = [&]() {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) kd[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < D / Mma<T>::KSTEP; ++s) {
+      const auto bs = AccFrag<T>::get(dSx, s);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        kd[i] = Mma<T>::mma(frag_row<T, PERM>(Ks + 16 * i * LDD, LDD, s), bs, kd[i]);
+    }
+  };
+  block_solve<NW - 1>(Af, Tm, LDF, kd_side);  // its first barrier publishes the copies
   constexpr int KST = D / Mma<T>::KSTEP;
   typename Mma<T>::frag skf[KST], gkf[KST];
 #pragma unroll
@@ -459,20 +474,13 @@ __global__ __launch_bounds__(4 * D, 2) void gdn_bwd_grads_kernel(BwdArgs a) {
   // dVn = P^T dO + D (K dS'^T)
   f32x4 dvn[4];
   {
-    f32x4 kd[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) dvn[i] = kd[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int i = 0; i < 4; ++i) dvn[i] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int s = 0; s < BLK / Mma<T>::KSTEP; ++s) {
       const auto bo = frag_tr<T, STD>(Os + 16 * w, LDD, s);
 #pragma unroll
       for (int i = 0; i < 4; ++i) dvn[i] = Mma<T>::mma(frag_tr<T, STD>(Pl + 16 * i, LDC, s), bo, dvn[i]);
-    }
-#pragma unroll
-    for (int s = 0; s < D / Mma<T>::KSTEP; ++s) {
-      const auto bs = AccFrag<T>::get(dSx, s);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) kd[i] = Mma<T>::mma(frag_row<T, PERM>(Ks + 16 * i * LDD, LDD, s), bs, kd[i]);
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i)

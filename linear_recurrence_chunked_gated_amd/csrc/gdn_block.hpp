@@ -69,7 +69,8 @@ __device__ __forceinline__ void block_gates(float la, float be, const GateLds& G
 // lane stores 4 consecutive s.
 template <typename T, int D, int NW, bool WITH_Q, bool WITH_A = true>
 __device__ __forceinline__ void block_scores(const T* Qs, const T* Ks, int ldd, const GateLds& G,
-                                             float* Af, int ldf, T* Pl, int ldc) {
+                                             float* Af, int ldf, T* Pl, int ldc,
+                                             f32x4* kk = nullptr) {
   constexpr int NJ = 16 / NW;
   const int w = wave_id(), lane = lane_id();
   const int st = w & 3, r0 = (w >> 2) * NJ;
@@ -86,6 +87,10 @@ __device__ __forceinline__ void block_scores(const T* Qs, const T* Ks, int ldd, 
       if constexpr (WITH_Q)
         accP[j] = Mma<T>::mma(a, frag_row<T, STD>(Qs + 16 * (r0 + j) * ldd, ldd, s), accP[j]);
     }
+  }
+  if (kk) {  // the raw K K^T tiles (m = st, n = r0 + j), for callers that need them later
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) kk[j] = accA[j];
   }
   const int s0 = 16 * st + 4 * (lane >> 4);
   float gs[4];

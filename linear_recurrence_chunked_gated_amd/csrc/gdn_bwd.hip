@@ -395,7 +395,8 @@ __global__ __launch_bounds__(4 * D, 2) void gdn_bwd_grads_kernel(BwdArgs a) {
   }
   lds_barrier();
   // ---- B: scores
-  block_scores<T, D, NW, true>(Qs, Ks, LDD, G, Af, LDF, Pl, LDC);
+  f32x4 kk[NJ];  // K K^T tiles (m = 16 (w & 3), n = 16 ((w >> 2) NJ + j)), for phase L
+  block_scores<T, D, NW, true>(Qs, Ks, LDD, G, Af, LDF, Pl, LDC, kk);
   lds_barrier();
   // ---- C: T = (I + A)^{-1}, Tp, Tpp; zero Tm's upper blocks (solve scratch).
   // Meanwhile S and dS' go through LDS once, so that every wave also holds
@@ -715,9 +716,9 @@ __global__ __launch_bounds__(4 * D, 2) void gdn_bwd_grads_kernel(BwdArgs a) {
   // ---- L: dA = -T^T Y (strictly lower); A-terms of dbeta, dg; dKK
   {
     const int rt = w & 3, s0t = (w >> 2) * NJ;
-    f32x4 acc[NJ], kk[NJ];
+    f32x4 acc[NJ];
 #pragma unroll
-    for (int j = 0; j < NJ; ++j) acc[j] = kk[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < NJ; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
     if constexpr (SPLIT) {
 #pragma unroll
       for (int s = 0; s < BLK / Mma<bf16>::KSTEP; ++s) {
@@ -738,13 +739,6 @@ __global__ __launch_bounds__(4 * D, 2) void gdn_bwd_grads_kernel(BwdArgs a) {
         for (int j = 0; j < NJ; ++j)
           acc[j] = Mma<float>::mma(at, frag_tr<float, STD>(Yf + 16 * (s0t + j), LDF, s), acc[j]);
       }
-    }
-#pragma unroll
-    for (int s = 0; s < D / Mma<T>::KSTEP; ++s) {
-      const auto ak = frag_row<T, STD>(Ks + 16 * rt * LDD, LDD, s);
-#pragma unroll
-      for (int j = 0; j < NJ; ++j)
-        kk[j] = Mma<T>::mma(ak, frag_row<T, STD>(Ks + 16 * (s0t + j) * LDD, LDD, s), kk[j]);
     }
     // db's row sums, over this wave's s-tiles, give both the dbeta_r term and
     // (times beta_r) the row term of dg

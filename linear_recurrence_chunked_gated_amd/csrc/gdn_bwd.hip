@@ -210,6 +210,181 @@ __global__ __launch_bounds__(4 * D, 2) void gdn_bwd_dscan_kernel(BwdArgs a, int 
   }
 }
 
+// The reverse scan with two blocks in flight (where its LDS plan fits, bf16):
+// the state-free work of the next block in the walk (P, dO^T diag(gamma) Q
+// and Wn) runs in the same barrier phase as the state work of the current
+// one, on double-buffered K, dO, P, Wn and gates, so a block takes two
+// barrier phases instead of three.  Each product is formed as in
+// gdn_bwd_dscan_kernel, which remains for layouts that do not fit (fp32).
+template <typename T, int D> struct Scan2Lds {
+  static constexpr int LDD = D + Lay<T>::PAD;
+  static constexpr int LDC = BLK + Lay<T>::PAD;
+  static constexpr size_t rowD = (size_t)BLK * LDD * sizeof(T);
+  static constexpr size_t sq = (size_t)BLK * LDC * sizeof(T);
+  static constexpr size_t oQ = 0, oT = oQ + rowD, oK = oT + sq, oO = oK + 2 * rowD,
+                          oW = oO + 2 * rowD, oP = oW + 2 * rowD, oG = oP + 2 * sq;
+  static constexpr size_t bytes = oG + 2 * kGateBytes;
+  static constexpr bool fits = bytes <= 160 * 1024;
+};
+
+template <typename T, int D, bool MAIN>
+__global__ __launch_bounds__(4 * D, 2) void gdn_bwd_dscan2_kernel(BwdArgs a, int seg0, int nseg,
+                                                                  const float* dSend,
+                                                                  int dsend_P) {
+  typedef Scan2Lds<T, D> Lz;
+  constexpr int DKT = D / 16, NW = D / 16;
+  constexpr int LDD = Lz::LDD, LDC = Lz::LDC;
+  extern __shared__ __align__(16) unsigned char smem[];
+  T* Qs = reinterpret_cast<T*>(smem + Lz::oQ);
+  T* Tpp = reinterpret_cast<T*>(smem + Lz::oT);
+  auto Kb = [&](int n) { return reinterpret_cast<T*>(smem + Lz::oK + n * Lz::rowD); };
+  auto Ob = [&](int n) { return reinterpret_cast<T*>(smem + Lz::oO + n * Lz::rowD); };
+  auto Wb = [&](int n) { return reinterpret_cast<T*>(smem + Lz::oW + n * Lz::rowD); };
+  auto Pb = [&](int n) { return reinterpret_cast<T*>(smem + Lz::oP + n * Lz::sq); };
+  auto Gb = [&](int n) { return gate_lds(smem + Lz::oG + n * kGateBytes); };
+
+  const FwdArgs& f = a.f;
+  const int w = wave_id(), lane = lane_id(), g4 = 4 * (lane >> 4), li = lane & 15;
+  const int seg = seg0 + blockIdx.x % nseg, bh = blockIdx.x / nseg;
+  const int b = bh / f.H, h = bh % f.H;
+  const int blk0 = seg * f.L, blk1 = min(f.nblk, blk0 + f.L);
+  const size_t rs = (size_t)f.H * D;
+  const T* q = tok_base<T, D>(f.q, f.T, f.H, b, h);
+  const T* k = tok_base<T, D>(f.k, f.T, f.H, b, h);
+  const T* dO = tok_base<T, D>(a.dO, f.T, f.H, b, h);
+  const float* al = f.alpha + (size_t)b * f.T * f.H + h;
+  const float* bt = f.beta + (size_t)b * f.T * f.H + h;
+
+  f32x4 dSv[DKT];
+  {
+    const float* G0 = (MAIN && dSend) ? dSend + ((size_t)bh * dsend_P + seg) * D * D : nullptr;
+#pragma unroll
+    for (int aa = 0; aa < DKT; ++aa)
+      dSv[aa] = G0 ? *reinterpret_cast<const f32x4*>(G0 + (size_t)(16 * w + li) * D + 16 * aa + g4)
+                   : f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  ScanPrefetch<T, D> pf;
+  auto fetch = [&](int blk) {
+    pf.fetch(q, k, dO, al, bt, tp_block<T>(f.tw, f.nblk, bh, blk), rs, f.H, blk * BLK,
+             min(BLK, f.T - blk * BLK));
+  };
+  auto fetch_part = [&](auto part, int blk) {
+    pf.template fetch<decltype(part)::value>(q, k, dO, al, bt, tp_block<T>(f.tw, f.nblk, bh, blk),
+                                             rs, f.H, blk * BLK, BLK);
+  };
+  // State-free work of the block staged in Q, K[n], dO[n], Tpp and gates G[n]:
+  // P -> P[n], X2 = dO^T diag(gamma) Q (registers), Wn = -Tpp diag(gamma) K -> W[n].
+  f32x4 X2[DKT];
+  auto pre = [&](int n) {
+    const GateLds Gn = Gb(n);
+    block_scores<T, D, NW, true, false>(Qs, Kb(n), LDD, Gn, nullptr, 0, Pb(n), LDC);
+#pragma unroll
+    for (int aa = 0; aa < DKT; ++aa) X2[aa] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < BLK / Mma<T>::KSTEP; ++s) {
+      const auto bo = frag_tr_gamma<T>(Ob(n) + 16 * w, LDD, s, Gn.gam);
+#pragma unroll
+      for (int aa = 0; aa < DKT; ++aa)
+        X2[aa] = Mma<T>::mma(frag_tr<T, STD>(Qs + 16 * aa, LDD, s), bo, X2[aa]);
+    }
+    block_w<T, D, NW>(Kb(n), LDD, Tpp, LDC, Wb(n), Gn.gam);
+  };
+
+  if (blk0 < blk1) {
+    fetch(blk1 - 1);
+    pf.stage(Qs, Kb(0), Ob(0), Tpp, LDD, LDC, min(BLK, f.T - (blk1 - 1) * BLK), Gb(0));
+    if (blk1 - 2 >= blk0) fetch(blk1 - 2);
+    lds_barrier();
+    pre(0);
+    lds_barrier();
+  }
+  for (int blk = blk1 - 1; blk >= blk0; --blk) {
+    const int c = (blk1 - 1 - blk) & 1, n = c ^ 1;
+    const bool next = blk > blk0, next2 = blk - 1 > blk0;
+    if constexpr (MAIN)
+      StateTiles<T, D>::store(reinterpret_cast<T*>(a.dhst) + ((size_t)bh * f.nblk + blk) * D * D,
+                              w, lane, dSv);
+    // the next block (blk - 1) into the other buffers; the one after it goes
+    // out in three parts over this block
+    if (next) {
+      pf.stage(Qs, Kb(n), Ob(n), Tpp, LDD, LDC, BLK, Gb(n));
+      if (next2) fetch_part(std::integral_constant<int, 1>{}, blk - 2);
+    }
+    lds_barrier();
+    // block blk: dVn = P^T dO + D (K dS'^T); dS = gamma_C dS' + X2 - dVn^T W
+    {
+      const GateLds Gc = Gb(c);
+      f32x4 dvn[4], kd[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) dvn[i] = kd[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < BLK / Mma<T>::KSTEP; ++s) {
+        const auto bo = frag_tr<T, STD>(Ob(c) + 16 * w, LDD, s);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          dvn[i] = Mma<T>::mma(frag_tr<T, STD>(Pb(c) + 16 * i, LDC, s), bo, dvn[i]);
+      }
+#pragma unroll
+      for (int s = 0; s < D / Mma<T>::KSTEP; ++s) {
+        const auto bs = AccFrag<T>::get(dSv, s);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          kd[i] = Mma<T>::mma(frag_row<T, PERM>(Kb(c) + 16 * i * LDD, LDD, s), bs, kd[i]);
+      }
+      if (next2) fetch_part(std::integral_constant<int, 2>{}, blk - 2);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) dvn[i][e] += Gc.dec[16 * i + g4 + e] * kd[i][e];
+      const float gc = Gc.gC[0];
+#pragma unroll
+      for (int aa = 0; aa < DKT; ++aa) dSv[aa] = gc * dSv[aa] + X2[aa];
+#pragma unroll
+      for (int s = 0; s < BLK / Mma<T>::KSTEP; ++s) {
+        const auto bv = AccFrag<T>::get(dvn, s);
+#pragma unroll
+        for (int aa = 0; aa < DKT; ++aa)
+          dSv[aa] = Mma<T>::mma(frag_tr<T, PERM>(Wb(c) + 16 * aa, LDD, s), bv, dSv[aa]);
+      }
+    }
+    // block blk - 1, state-free part
+    if (next) pre(n);
+    if (next2) fetch_part(std::integral_constant<int, 4>{}, blk - 2);
+    lds_barrier();
+  }
+
+  float* out = MAIN ? ((seg == 0 && a.dS_in) ? a.dS_in + (size_t)bh * D * D : nullptr)
+                    : a.NBseg + ((size_t)bh * f.P + seg) * D * D;
+  if (out) {
+#pragma unroll
+    for (int aa = 0; aa < DKT; ++aa)
+      *reinterpret_cast<f32x4*>(out + (size_t)(16 * w + li) * D + 16 * aa + g4) = dSv[aa];
+  }
+}
+
+static hipError_t set_lds(const void* fn, size_t bytes);
+
+// The reverse scan over nseg segments from seg0, in the two-block form where it fits.
+template <typename T, int D, bool MAIN>
+static hipError_t launch_dscan(const BwdArgs& a, int seg0, int nseg, const float* dSend,
+                               int dsend_P, hipStream_t st) {
+  const int grid = a.f.B * a.f.H * nseg;
+  constexpr size_t lds2 = Scan2Lds<T, D>::bytes, lds1 = ScanLds<T, D>::bytes;
+  if constexpr (Scan2Lds<T, D>::fits) {
+    hipError_t e = set_lds((const void*)gdn_bwd_dscan2_kernel<T, D, MAIN>, Scan2Lds<T, D>::bytes);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((gdn_bwd_dscan2_kernel<T, D, MAIN>), dim3(grid), dim3(4 * D),
+                       lds2, st, a, seg0, nseg, dSend, dsend_P);
+  } else {
+    hipError_t e = set_lds((const void*)gdn_bwd_dscan_kernel<T, D, MAIN>, ScanLds<T, D>::bytes);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((gdn_bwd_dscan_kernel<T, D, MAIN>), dim3(grid), dim3(4 * D),
+                       lds1, st, a, seg0, nseg, dSend, dsend_P);
+  }
+  return hipGetLastError();
+}
+
 // -------------------------------------------------------- block gradients ---
 // Sums of a 16x16 accumulator tile C[m][n] (lane: m = 4 g + e, n = i):
 // over n for each m (result valid in lanes with i == 0, element e), and over
@@ -837,7 +1012,7 @@ hipError_t launch_bwd(const BwdArgs& a0, bool saved, int phase, hipStream_t st, 
   BwdArgs a = a0;
   FwdArgs& f = a.f;
   const int BH = f.B * f.H, P = f.P;
-  constexpr size_t scan_bytes = ScanLds<T, D>::bytes, grad_bytes = GradLds<T, D>::bytes;
+  constexpr size_t grad_bytes = GradLds<T, D>::bytes;
   hipError_t e;
   if (phase != PHASE_ALL && !saved) return hipErrorInvalidValue;
   const bool begin = phase != PHASE_END, end = phase != PHASE_BEGIN;
@@ -851,13 +1026,10 @@ hipError_t launch_bwd(const BwdArgs& a0, bool saved, int phase, hipStream_t st, 
       return e;
     // 2. NB maps of segments 1..P-1 (independent of dS_out)
     if (begin) {
-      if ((e = set_lds((const void*)gdn_bwd_dscan_kernel<T, D, false>, ScanLds<T, D>::bytes)) !=
-          hipSuccess)
-        return e;
       prof_begin(prof, "gdn_bwd_dscan_summary", st);
-      hipLaunchKernelGGL((gdn_bwd_dscan_kernel<T, D, false>), dim3(BH * (P - 1)), dim3(4 * D),
-                         scan_bytes, st, a, 1, P - 1, nullptr, 1);
+      e = launch_dscan<T, D, false>(a, 1, P - 1, nullptr, 1, st);
       prof_end(prof, st);
+      if (e != hipSuccess) return e;
     }
     if (!end) return hipGetLastError();
     // 3. chains
@@ -877,12 +1049,10 @@ hipError_t launch_bwd(const BwdArgs& a0, bool saved, int phase, hipStream_t st, 
   // 4. block entry states
   if (!saved && (e = launch_states<T, D>(f, a.hst, st, prof)) != hipSuccess) return e;
   // 5. block exit gradients and dS_in
-  if ((e = set_lds((const void*)gdn_bwd_dscan_kernel<T, D, true>, ScanLds<T, D>::bytes)) != hipSuccess)
-    return e;
   prof_begin(prof, "gdn_bwd_dscan", st);
-  hipLaunchKernelGGL((gdn_bwd_dscan_kernel<T, D, true>), dim3(BH * P), dim3(4 * D),
-                     scan_bytes, st, a, 0, P, dSend, dsend_P);
+  e = launch_dscan<T, D, true>(a, 0, P, dSend, dsend_P, st);
   prof_end(prof, st);
+  if (e != hipSuccess) return e;
   // 6. per-block gradients
   if ((e = set_lds((const void*)gdn_bwd_grads_kernel<T, D>, GradLds<T, D>::bytes)) != hipSuccess)
     return e;

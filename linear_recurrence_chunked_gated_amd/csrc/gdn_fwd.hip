@@ -568,6 +568,137 @@ __global__ __launch_bounds__(64 * fwd_nw<D>(), 2) void gdn_fwd_summary_kernel(Fw
     }
 }
 
+// The segment summary with two blocks in flight (where its LDS plan fits,
+// bf16): the next block's W and U are formed in the same barrier phase as
+// the current block's map updates, on double-buffered K, W and gates, so a
+// block takes two barrier phases instead of three.
+template <typename T, int D> struct Sum2Lds {
+  static constexpr int LDD = D + Lay<T>::PAD;
+  static constexpr int LDC = BLK + Lay<T>::PADC;
+  static constexpr size_t rowD = (size_t)BLK * LDD * sizeof(T);
+  static constexpr size_t sq = (size_t)BLK * LDC * sizeof(T);
+  static constexpr size_t oV = 0, oT = oV + rowD, oK = oT + sq, oW = oK + 2 * rowD,
+                          oG = oW + 2 * rowD;
+  static constexpr size_t bytes = oG + 2 * kGateBytes;
+  static constexpr bool fits = bytes <= 160 * 1024 && sizeof(T) == 2;
+};
+
+template <typename T, int D>
+__global__ __launch_bounds__(64 * fwd_nw<D>(), 2) void gdn_fwd_summary2_kernel(FwdArgs a, int nseg) {
+  typedef Sum2Lds<T, D> Lz;
+  constexpr int NW = fwd_nw<D>(), NDV = D / 16 / NW, DKT = D / 16;
+  constexpr int LDD = Lz::LDD, LDC = Lz::LDC;
+  extern __shared__ __align__(16) unsigned char smem[];
+  T* Vs = reinterpret_cast<T*>(smem + Lz::oV);
+  T* Tpp = reinterpret_cast<T*>(smem + Lz::oT);
+  auto Kb = [&](int n) { return reinterpret_cast<T*>(smem + Lz::oK + n * Lz::rowD); };
+  auto Wb = [&](int n) { return reinterpret_cast<T*>(smem + Lz::oW + n * Lz::rowD); };
+  auto Gb = [&](int n) { return gate_lds(smem + Lz::oG + n * kGateBytes); };
+
+  const int w = wave_id(), lane = lane_id(), g4 = 4 * (lane >> 4), li = lane & 15;
+  const int dv0 = NDV * w;
+  const int seg = blockIdx.x % nseg, bh = blockIdx.x / nseg;
+  const int b = bh / a.H, h = bh % a.H;
+  const int blk0 = seg * a.L, blk1 = min(a.nblk, blk0 + a.L);
+  const size_t rs = (size_t)a.H * D;
+  const T* k = seq_base<T, D>(a.k, a, b, h);
+  const T* v = seq_base<T, D>(a.v, a, b, h);
+  const float* al = a.alpha + (size_t)b * a.T * a.H + h;
+  const float* bt = a.beta + (size_t)b * a.T * a.H + h;
+
+  // NM[bb] holds N^T, NM[NDV + bb] holds M^T (tiles m = dk, n = dv), as in
+  // gdn_fwd_summary_kernel.
+  f32x4 NM[2 * NDV][DKT];
+#pragma unroll
+  for (int bb = 0; bb < NDV; ++bb)
+#pragma unroll
+    for (int aa = 0; aa < DKT; ++aa) {
+      NM[bb][aa] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        NM[NDV + bb][aa][e] = (16 * aa + g4 + e == 16 * (dv0 + bb) + li) ? 1.f : 0.f;
+    }
+
+  Prefetch<T, D, false> pf;
+  auto fetch = [&](int blk) {
+    pf.fetch(nullptr, k, v, al, bt, tw_block<T>(a.tw, a.nblk, bh, blk), rs, a.H, blk * BLK,
+             min(BLK, a.T - blk * BLK));
+  };
+  auto fetch_part = [&](auto part, int blk) {
+    pf.template fetch<decltype(part)::value>(nullptr, k, v, al, bt, tw_block<T>(a.tw, a.nblk, bh, blk),
+                                             rs, a.H, blk * BLK, min(BLK, a.T - blk * BLK));
+  };
+  // state-free work of the block staged in K[n], V, Tpp and gates G[n]
+  f32x4 U[NDV][4];
+  auto pre = [&](int n) {
+    block_w<T, D, NW>(Kb(n), LDD, Tpp, LDC, Wb(n), Gb(n).gam);
+    block_u<T, NDV>(Tpp, LDC, Vs, LDD, dv0, U);
+  };
+
+  if (blk0 < blk1) {
+    fetch(blk0);
+    pf.stage(nullptr, Kb(0), Vs, Tpp, LDD, LDC, min(BLK, a.T - blk0 * BLK), Gb(0));
+    if (blk0 + 1 < blk1) fetch(blk0 + 1);
+    lds_barrier();
+    pre(0);
+    lds_barrier();
+  }
+  for (int blk = blk0; blk < blk1; ++blk) {
+    const int c = (blk - blk0) & 1, n = c ^ 1;
+    const bool next = blk + 1 < blk1, next2 = blk + 2 < blk1;
+    if (next) {
+      pf.stage(nullptr, Kb(n), Vs, Tpp, LDD, LDC, min(BLK, a.T - (blk + 1) * BLK), Gb(n));
+      if (next2) fetch_part(std::integral_constant<int, 1>{}, blk + 2);
+    }
+    lds_barrier();
+    // block blk:  N: Vn0 = U - W N^T ; N' = gamma_C N + Vn0^T D K
+    //             M: Z = -(W M^T)    ; M' = gamma_C M + Z^T D K
+    {
+      const GateLds Gc = Gb(c);
+      f32x4 dsc[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) dsc[i][e] = Gc.dec[16 * i + g4 + e];
+      const float gc = Gc.gC[0];
+      f32x4 X2[2 * NDV][4];
+#pragma unroll
+      for (int bb = 0; bb < NDV; ++bb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          X2[bb][i] = U[bb][i];
+          X2[NDV + bb][i] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+      block_x_st<T, D, 2 * NDV>(Wb(c), LDD, NM, X2);
+#pragma unroll
+      for (int bb = 0; bb < 2 * NDV; ++bb)
+#pragma unroll
+        for (int aa = 0; aa < DKT; ++aa) NM[bb][aa] *= gc;
+      if (next2) fetch_part(std::integral_constant<int, 2>{}, blk + 2);
+      block_state_write<T, D, 2 * NDV>(Kb(c), LDD, X2, dsc, NM);
+    }
+    // block blk + 1, state-free part
+    if (next) pre(n);
+    if (next2) fetch_part(std::integral_constant<int, 4>{}, blk + 2);
+    lds_barrier();
+  }
+
+  float* MTo = a.Mseg + ((size_t)bh * a.P + seg) * D * D;
+  float* No = a.Nseg + ((size_t)bh * a.P + seg) * D * D;
+  float* Mo = a.MBseg ? a.MBseg + ((size_t)bh * a.P + seg) * D * D : nullptr;
+#pragma unroll
+  for (int bb = 0; bb < NDV; ++bb)
+#pragma unroll
+    for (int aa = 0; aa < DKT; ++aa) {
+      const size_t off = (size_t)(16 * (dv0 + bb) + li) * D + 16 * aa + g4;
+      *reinterpret_cast<f32x4*>(No + off) = NM[bb][aa];
+      if (Mo) *reinterpret_cast<f32x4*>(Mo + off) = NM[NDV + bb][aa];
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        MTo[(size_t)(16 * aa + g4 + e) * D + 16 * (dv0 + bb) + li] = NM[NDV + bb][aa][e];
+    }
+}
+
 // ------------------------------------------------------------ chain ---------
 // The boundary-state chain between segments, X' = X B_j + C_j for one
 // sequence (Eq. 5 inside the chunk; its backward mirror, Eq. 7, for REV):
@@ -704,12 +835,22 @@ template <typename T, int D>
 hipError_t launch_fwd_summary(const FwdArgs& a, int nseg, hipStream_t st, Profiler* prof,
                               const char* name) {
   typedef FwdLds<T, D> Lz;
-  hipError_t e = set_lds((const void*)gdn_fwd_summary_kernel<T, D>, Lz::out_bytes);
-  if (e != hipSuccess) return e;
-  prof_begin(prof, name, st);
-  hipLaunchKernelGGL((gdn_fwd_summary_kernel<T, D>), dim3(a.B * a.H * nseg), dim3(64 * fwd_nw<D>()),
-                     Lz::out_bytes, st, a, nseg);
-  prof_end(prof, st);
+  constexpr size_t lds1 = Lz::out_bytes, lds2 = Sum2Lds<T, D>::bytes;
+  if constexpr (Sum2Lds<T, D>::fits) {
+    hipError_t e = set_lds((const void*)gdn_fwd_summary2_kernel<T, D>, lds2);
+    if (e != hipSuccess) return e;
+    prof_begin(prof, name, st);
+    hipLaunchKernelGGL((gdn_fwd_summary2_kernel<T, D>), dim3(a.B * a.H * nseg),
+                       dim3(64 * fwd_nw<D>()), lds2, st, a, nseg);
+    prof_end(prof, st);
+  } else {
+    hipError_t e = set_lds((const void*)gdn_fwd_summary_kernel<T, D>, lds1);
+    if (e != hipSuccess) return e;
+    prof_begin(prof, name, st);
+    hipLaunchKernelGGL((gdn_fwd_summary_kernel<T, D>), dim3(a.B * a.H * nseg),
+                       dim3(64 * fwd_nw<D>()), lds1, st, a, nseg);
+    prof_end(prof, st);
+  }
   return hipGetLastError();
 }
 

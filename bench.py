@@ -150,10 +150,12 @@ def kernel_label(name):
     else:
         mm = re.search(r"L[ib](\d+)EEE", name)
         last = mm.group(1) if mm else ""
+    if base == "gdn_fwd_summary2":  # two-blocks-in-flight form
+        return "gdn_fwd_summary"
     if base in ("gdn_fwd_out", "gdn_fwd_out2"):  # one- and two-blocks-in-flight forms
         return {"0": "gdn_fwd_out", "1": "gdn_fwd_states", "2": "gdn_fwd_out_save"}.get(
             last, "gdn_fwd_out")
-    if base == "gdn_bwd_dscan":
+    if base in ("gdn_bwd_dscan", "gdn_bwd_dscan2"):
         return "gdn_bwd_dscan" if last in ("1", "true") else "gdn_bwd_dscan_summary"
     if base == "gdn_chain":
         return "gdn_chain_bwd" if last in ("1", "true") else "gdn_chain_fwd"

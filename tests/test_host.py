@@ -227,6 +227,23 @@ def test_bench_algorithmic_figures():
     assert bench.kernel_flops_per_block("gdn_fwd_out", 128) / 64 == 180224
 
 
+def test_kernel_labels():
+    """Profiler kernel names (mangled and demangled) map to the launch labels
+    the profiles and traffic figures use, for every form of a kernel."""
+    import bench
+    lab = bench.kernel_label
+    assert lab("_ZN5sfgdn21gdn_bwd_dscan2_kernelIDF16bLi128ELb1EEEvNS_7BwdArgsEiiPKfi") == "gdn_bwd_dscan"
+    assert lab("_ZN5sfgdn21gdn_bwd_dscan2_kernelIDF16bLi128ELb0EEEvNS_7BwdArgsEiiPKfi") == "gdn_bwd_dscan_summary"
+    assert lab("_ZN5sfgdn20gdn_bwd_dscan_kernelIfLi64ELb1EEEvNS_7BwdArgsEiiPKfi") == "gdn_bwd_dscan"
+    assert lab("void sfgdn::gdn_bwd_dscan2_kernel<__bf16, 128, false>(sfgdn::BwdArgs, int, int, float const*, int)") == "gdn_bwd_dscan_summary"
+    assert lab("_ZN5sfgdn23gdn_fwd_summary2_kernelIDF16bLi128EEEvNS_7FwdArgsEi") == "gdn_fwd_summary"
+    assert lab("_ZN5sfgdn22gdn_fwd_summary_kernelIfLi64EEEvNS_7FwdArgsEi") == "gdn_fwd_summary"
+    assert lab("_ZN5sfgdn19gdn_fwd_out2_kernelIDF16bLi128ELi2EEEvNS_7FwdArgsEPT_") == "gdn_fwd_out_save"
+    assert lab("_ZN5sfgdn20gdn_bwd_grads_kernelIDF16bLi128EEEvNS_7BwdArgsE") == "gdn_bwd_grads"
+    assert lab("_ZN5sfgdn16gdn_chain_kernelILi128ELb1EEEvNS_9ChainArgsE") == "gdn_chain_bwd"
+    assert lab("elementwise_kernel") is None
+
+
 def test_segment_plan():
     """The in-chunk scan's segments: enough to occupy 256 compute units, no
     shorter than about sqrt(0.3 nblk) blocks, an explicit length honoured,

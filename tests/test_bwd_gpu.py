@@ -47,6 +47,7 @@ def check_all(got, ref, tol):
     (1, 1, 2, 128, "bf16", 0.1, 0.1, 1.0, 0),      # single token
     (1, 65, 2, 64, "bf16", 0.1, None, 0.01, 1),    # no exit gradient
     (2, 2048, 2, 128, "bf16", 0.1, 0.1, 0.01, 5),
+    (1, 1000, 2, 64, "bf16", 0.1, 0.1, 0.01, 5),   # d = 64: segments of 5, 5, 5, 1 blocks
 ])
 def test_bwd_matches_oracle(oracle_mod, B, T, H, D, dtype, s_in, ds, decay, seg):
     d = inputs(B, T, H, D, dtype, seed=2000 + T + H, s_in_std=s_in, grads=True, decay=decay,

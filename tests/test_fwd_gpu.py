@@ -33,6 +33,7 @@ def run_fwd(d, seg_blocks=0):
     (1, 63, 2, 64, "bf16", 0.1, 0.01, 0),      # one partial block
     (1, 65, 1, 128, "bf16", 0.1, 0.01, 1),     # one full block and one token
     (1, 2048, 4, 128, "bf16", 0.1, 0.01, 5),   # ragged segments (32 blocks / 5)
+    (1, 1000, 2, 64, "bf16", 0.1, 0.01, 5),    # d = 64: segments of 5, 5, 5, 1 blocks
 ])
 def test_fwd_matches_oracle(oracle_mod, B, T, H, D, dtype, s_in, decay, seg):
     d = inputs(B, T, H, D, dtype, seed=1000 + T + H, s_in_std=s_in, decay=decay)

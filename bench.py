@@ -193,6 +193,91 @@ def write_traffic(fetch_csv, write_csv, calib_fetch_csv, calib_write_csv, calib_
     print(json.dumps(out, indent=1))
 
 
+def _read_stats_csv(path):
+    """{launch label: average duration in us} from a rocprofv3 --stats kernel
+    table (one row per kernel name)."""
+    import csv
+    out = {}
+    with open(path) as f:
+        for row in csv.DictReader(f):
+            name = row.get("Name") or row.get("KernelName") or row.get("Kernel_Name")
+            avg = row.get("AverageNs") or row.get("Average_Ns") or row.get("AverageNS")
+            lab = kernel_label(name or "")
+            if lab is None or avg is None:
+                continue
+            calls = float(row.get("Calls", 1))
+            tot, n = out.get(lab, (0.0, 0.0))
+            out[lab] = (tot + float(avg) * calls, n + calls)
+    return {k: t / n / 1e3 for k, (t, n) in out.items()}
+
+
+def write_counters(out_md, stats_csv, pmc_csvs, title, commands, cus=256, simds=1024,
+                   xcds=8):
+    """Per-kernel hardware-counter table from rocprofv3 --pmc runs (counter
+    values summed over a dispatch's instances, averaged over the dispatches
+    of a kernel) and the average durations of a --kernel-trace --stats run:
+      bf16 TFLOP/s     SQ_INSTS_VALU_MFMA_MOPS_BF16 * 512 / duration
+      MFMA busy        SQ_VALU_MFMA_BUSY_CYCLES / (active cycles * SIMDs)
+      LDS active       SQ_LDS_IDX_ACTIVE / (active cycles * CUs)
+      bank conflict    SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE
+    with active cycles = GRBM_GUI_ACTIVE / XCDs (the counter is per XCD)."""
+    dur = _read_stats_csv(stats_csv)
+    vals = {}
+    import csv
+    for path in pmc_csvs:
+        sums = {}
+        with open(path) as f:
+            for row in csv.DictReader(f):
+                name = row.get("Kernel_Name") or row.get("Kernel-Name") or row.get("KernelName")
+                ctr = row.get("Counter_Name") or row.get("Counter-Name")
+                val = row.get("Counter_Value") or row.get("Counter-Value")
+                disp = row.get("Dispatch_Id") or row.get("Dispatch-Id")
+                lab = kernel_label(name or "")
+                if lab is None or ctr is None or val is None:
+                    continue
+                key = (lab, disp, ctr)
+                sums[key] = sums.get(key, 0.0) + float(val)
+        per = {}
+        for (lab, _, ctr), v in sums.items():
+            per.setdefault((lab, ctr), []).append(v)
+        for (lab, ctr), v in per.items():
+            vals.setdefault(lab, {})[ctr] = sum(v) / len(v)
+    rows = []
+    for lab in sorted(vals, key=lambda k: -dur.get(k, 0.0)):
+        c = vals[lab]
+        d_us = dur.get(lab)
+        act = c.get("GRBM_GUI_ACTIVE", 0.0) / xcds
+        mops = c.get("SQ_INSTS_VALU_MFMA_MOPS_BF16")
+        tf = mops * 512 / (d_us * 1e-6) / 1e12 if (mops is not None and d_us) else None
+        mb = c.get("SQ_VALU_MFMA_BUSY_CYCLES")
+        lds = c.get("SQ_LDS_IDX_ACTIVE")
+        bc = c.get("SQ_LDS_BANK_CONFLICT")
+        fmt = lambda x, f: "" if x is None else f % x
+        rows.append("| %s | %s | %s | %s | %s | %s | %s | %s | %s |" % (
+            lab, fmt(d_us, "%.1f"), fmt(mops and mops * 512 / 1e9, "%.1f"), fmt(tf, "%.0f"),
+            fmt(tf and tf / PEAK_BF16_TFLOPS * 100, "%.1f%%"),
+            fmt(mb and act and mb / (act * simds) * 100, "%.1f%%"),
+            fmt(lds and act and lds / (act * cus) * 100, "%.1f%%"),
+            fmt(bc is not None and lds and bc / lds * 100, "%.1f%%"),
+            fmt(c.get("SQ_INSTS_LDS"), "%.3g")))
+    text = ["# " + title, "",
+            "Commands (run from the repository root on one MI355X, after "
+            "`cd /tmp && export TMPDIR=/tmp`):", "", "```"] + commands + ["```", "",
+            "Counter values are summed over a dispatch's instances and averaged over the dispatches "
+            "of a kernel; durations are the averages of the kernel-trace run. bf16 GFLOP = "
+            "SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512 (executed matrix-core work, padding included); "
+            "MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / %d x %d SIMDs); LDS active = "
+            "SQ_LDS_IDX_ACTIVE / (GRBM_GUI_ACTIVE / %d x %d CUs); bank conflict = "
+            "SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE (share of LDS-active cycles stalled on bank "
+            "conflicts)." % (xcds, simds, xcds, cus), "",
+            "| kernel | avg (us) | bf16 GFLOP / launch | bf16 TFLOP/s | of 2.5 PF | MFMA busy | "
+            "LDS active | bank conflict | LDS instr / launch |",
+            "|---|---:|---:|---:|---:|---:|---:|---:|---:|"] + rows
+    with open(out_md, "w") as f:
+        f.write("\n".join(text) + "\n")
+    print("\n".join(text))
+
+
 def copy_calibration(nbytes=1 << 30, reps=4):
     """A plain device copy of known size, for scaling HBM byte counters."""
     import torch
@@ -293,28 +378,9 @@ def bench_conv(args):
     wsb = _lib.alloc_workspace(max(_lib.shortconv_bwd_workspace_bytes(
         _lib.conv_shape(1, n, C, W, x.dtype, 1)) for n in chunks), dev)
     stream = torch.cuda.current_stream()
-    overlap = args.overlap and (save or not wl["bwd"])
-    if overlap:
-        from linear_recurrence_chunked_gated_amd import chain as gchain
-        side = torch.cuda.Stream(device=dev)
-        wsf2 = [wsf, _lib.alloc_workspace(ws_f, dev)]
-        wsb2 = [wsb, _lib.alloc_workspace(ws_b, dev)] if wl["bwd"] else None
-
-    def step_overlap():
-        stream = torch.cuda.current_stream()  # the capture stream when graph-replayed
-        gchain.chain_fwd(q, k, v, al, be, states[0], chunks, o=o, seg_blocks=args.seg_blocks,
-                         stream=stream, save=save, overlap=True, side_stream=side,
-                         workspaces=wsf2, saved=saved if save else None, states=states)
-        if wl["bwd"]:
-            gchain.chain_bwd(q, k, v, al, be, dO, dS_out, chunks, None,
-                             grads=(dq, dk, dv, dal, dbe), seg_blocks=args.seg_blocks,
-                             stream=stream, saved=saved, overlap=True, side_stream=side,
-                             workspaces=wsb2, state_grads=gst[:len(chunks)])
 
     def step():
-        if overlap:
-            return step_overlap()
-        stream = torch.cuda.current_stream()  # the capture stream under --graph
+        stream = torch.cuda.current_stream()
         for i in range(len(chunks)):
             sl = slice(bounds[i], bounds[i + 1])
             _lib.shortconv_fwd(x[:, sl], w, states[i], 1, y=y[:, sl], conv_out=states[i + 1],
@@ -363,7 +429,8 @@ def bench_conv(args):
             if el >= 5.0 or 2 * n > T:
                 break
             n *= 2
-        cpu = {"value": round(n / el, 1), "unit": "tokens/s", "cores": 1, "kind": "oracle",
+        cpu = {"value": round(n / el, 1), "unit": "tokens/s", "cores": 1,
+               "nproc": os.cpu_count(), "kind": "oracle",
                "sample": "first %d tokens x %d channels of the workload, one chunk, fwd+bwd, "
                          "fp64 loop (%.1f s)" % (n, C, el)}
     line = {
@@ -411,7 +478,8 @@ def cpu_baseline(wl, seconds_target=7.0):
         if dt >= seconds_target or 2 * n > wl["T"]:
             break
         n *= 2
-    return {"value": n / dt, "unit": "tokens/s", "cores": int(nt), "kind": "oracle",
+    return {"value": n / dt, "unit": "tokens/s", "cores": int(nt), "nproc": os.cpu_count(),
+            "kind": "oracle",
             "sample": "first %d tokens x %d heads of the workload's sequence, one chunk, %s, "
                       "fp64 token loop (%.1f s)" % (n, H, "fwd+bwd" if wl["bwd"] else "fwd", dt)}
 
@@ -441,14 +509,28 @@ def main():
     ap.add_argument("--overlap", action="store_true",
                     help="split-and-overlap: each chunk's state-independent launches run on a "
                          "second stream beside the previous chunk's chain (saved backward)")
+    ap.add_argument("--split-fraction", type=float, default=None, metavar="F",
+                    help="cut every chunk at fraction F into two parts run as chunks (with "
+                         "--overlap: part b's state-independent launches beside part a's chain)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run a plain 1 GiB device copy (for rocprofv3 counter scaling) and exit")
+    ap.add_argument("--write-counters", nargs="+", metavar="ARG",
+                    help="OUT_MD TITLE STATS_CSV PMC_CSV... [CMD COMMAND...]: per-kernel counter "
+                         "table from rocprofv3 runs")
     ap.add_argument("--write-traffic", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "CALIB_FETCH_CSV",
                                                          "CALIB_WRITE_CSV"),
                     help="turn rocprofv3 FETCH_SIZE/WRITE_SIZE runs into profiles/traffic.json")
     args = ap.parse_args()
     if args.write_traffic:
         write_traffic(*args.write_traffic, calib_bytes=1 << 30)
+        return
+    if args.write_counters:
+        a = args.write_counters
+        cmds = []
+        if "CMD" in a:
+            i = a.index("CMD")
+            a, cmds = a[:i], a[i + 1:]
+        write_counters(a[0], a[2], a[3:], a[1], cmds)
         return
     if args.copy_calibration:
         copy_calibration()
@@ -470,6 +552,11 @@ def main():
 
     wl = workload(args.workload)
     T, H, D, chunks = wl["T"], wl["H"], wl["D"], wl["chunks"]
+    plan_chunks = chunks
+    if args.split_fraction:
+        # the page's split at fraction f: every chunk runs as two parts
+        from linear_recurrence_chunked_gated_amd.chain import split_lengths
+        chunks = split_lengths(chunks, args.split_fraction)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     d = gdn_inputs(1, T, H, D, D, dtype="bf16", seed=wl["seed"], s_in_std=wl["s_in_std"],
@@ -671,7 +758,9 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": args.workload, "description": wl["desc"], "B": 1, "T": T, "H": H,
-                   "d_k": D, "d_v": D, "block": C, "chunks": chunks,
+                   "d_k": D, "d_v": D, "block": C, "chunks": plan_chunks,
+                   "split_fraction": args.split_fraction,
+                   "parts": chunks if args.split_fraction else None,
                    "seg_blocks": args.seg_blocks or "auto", "parallelism": "single GPU",
                    "backward_states": "saved by the forward" if save else
                    ("recomputed" if wl["bwd"] else None),

@@ -112,6 +112,18 @@ def _stream(stream):
     return ctypes.c_void_p(stream.cuda_stream)
 
 
+def used_on(stream, *tensors):
+    """Mark tensors that this module allocated on the current stream as in
+    use by ``stream`` when the kernels run there, so that the caching
+    allocator does not hand their memory to current-stream work before the
+    kernels are done (tensor.record_stream).  No-op for the current stream."""
+    if stream is None or stream == torch.cuda.current_stream(stream.device):
+        return
+    for t in tensors:
+        if t is not None and t.numel() > 0:
+            t.record_stream(stream)
+
+
 def make_shape(B, T, H, Dk, Dv, dtype, seg_blocks=0):
     if isinstance(dtype, torch.dtype):
         if dtype not in _DTYPES:
@@ -186,19 +198,23 @@ def chunk_fwd(q, k, v, alpha, beta, S_in=None, o=None, S_out=None, seg_blocks=0,
         _need(S_in, "S_in", torch.float32, (B, H, Dv, Dk), dev)
     if o is None:
         o = torch.empty((B, T, H, Dv), dtype=q.dtype, device=dev)
+        used_on(stream, o)
     _need(o, "o", q.dtype, (B, T, H, Dv), dev)
     if S_out is None:
         S_out = torch.empty((B, H, Dv, Dk), dtype=torch.float32, device=dev)
+        used_on(stream, S_out)
     _need(S_out, "S_out", torch.float32, (B, H, Dv, Dk), dev)
     shape = make_shape(B, T, H, Dk, Dv, q.dtype, seg_blocks)
     need = workspace_bytes(shape)
     if workspace is None or workspace.numel() < need:
         workspace = alloc_workspace(need, dev)
+        used_on(stream, workspace)
     wsn = ctypes.c_size_t(0 if workspace is None else workspace.numel())
     if saved is True:
         n = saved_bytes(shape)
         saved = (alloc_workspace(n, dev) if n else
                  torch.empty(0, dtype=torch.uint8, device=dev))
+        used_on(stream, saved)
     if phase != PHASE_ALL:
         st = load().sf_gdn_chunk_fwd_split(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v),
                                            _ptr(alpha), _ptr(beta), _ptr(S_in), _ptr(o),
@@ -248,11 +264,13 @@ def chunk_bwd(q, k, v, alpha, beta, S_in, dO, dS_out=None, grads=None, seg_block
         grads = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v),
                  torch.empty_like(alpha), torch.empty_like(beta),
                  torch.empty((B, H, Dv, Dk), dtype=torch.float32, device=dev))
+        used_on(stream, *grads)
     dq, dk, dv, da, db, dS_in = grads
     shape = make_shape(B, T, H, Dk, Dv, q.dtype, seg_blocks)
     need = workspace_bytes(shape, backward=True)
     if workspace is None or workspace.numel() < need:
         workspace = alloc_workspace(need, dev)
+        used_on(stream, workspace)
     wsn = ctypes.c_size_t(0 if workspace is None else workspace.numel())
     if phase != PHASE_ALL:
         if saved is None:
@@ -309,9 +327,11 @@ def shortconv_fwd(x, w, conv_in=None, act=0, y=None, conv_out=None, want_state=T
         _need(conv_in, "conv_in", x.dtype, (B, W - 1, C), dev)
     if y is None:
         y = torch.empty_like(x)
+        used_on(stream, y)
     _need(y, "y", x.dtype, (B, T, C), dev)
     if want_state and conv_out is None and W > 1:
         conv_out = torch.empty((B, W - 1, C), dtype=x.dtype, device=dev)
+        used_on(stream, conv_out)
     shape = conv_shape(B, T, C, W, x.dtype, act)
     _check(load().sf_gdn_shortconv_fwd(ctypes.byref(shape), _ptr(x), _ptr(w), _ptr(conv_in),
                                        _ptr(y), _ptr(conv_out) if W > 1 else None,
@@ -335,14 +355,18 @@ def shortconv_bwd(x, w, conv_in, dy, dconv_out=None, act=0, dx=None, dw=None, wa
             _need(t, n, x.dtype, (B, W - 1, C), dev)
     if dx is None:
         dx = torch.empty_like(x)
+        used_on(stream, dx)
     if dw is None:
         dw = torch.empty_like(w)
+        used_on(stream, dw)
     dci = (torch.empty((B, W - 1, C), dtype=x.dtype, device=dev)
            if want_state and W > 1 else None)
+    used_on(stream, dci)
     shape = conv_shape(B, T, C, W, x.dtype, act)
     need = shortconv_bwd_workspace_bytes(shape)
     if workspace is None or workspace.numel() < need:
         workspace = alloc_workspace(need, dev)
+        used_on(stream, workspace)
     _check(load().sf_gdn_shortconv_bwd(ctypes.byref(shape), _ptr(x), _ptr(w), _ptr(conv_in),
                                        _ptr(dy), _ptr(dconv_out), _ptr(dx), _ptr(dw), _ptr(dci),
                                        _ptr(workspace),

@@ -3,6 +3,7 @@
 #include <cmath>
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <mutex>
 #include <stdint.h>
 #include <stdio.h>
@@ -80,6 +81,11 @@ sf_status make_plan(const sf_gdn_shape* s, Plan& p) {
     p.P = (p.nblk + L - 1) / L;
     if ((long long)p.B * p.H * p.P > (1LL << 30))
       return fail(SF_ERR_UNSUPPORTED, "too many segments");
+    // The chain kernels address one sequence's P segment maps through a
+    // buffer resource with a 32-bit byte range.
+    if ((unsigned long long)p.P * p.D * p.D * sizeof(float) > 0x7fffffffULL)
+      return fail(SF_ERR_UNSUPPORTED,
+                  "too many segments per sequence for the chain kernels (raise seg_blocks)");
   }
   // per-block states and state gradients are stored in the operand type (the
   // precision in which they enter every product that reads them)
@@ -143,7 +149,7 @@ struct ProfRec {
 namespace sfgdn {
 struct Profiler {
   std::mutex mu;
-  bool on = false;
+  std::atomic<bool> on{false};
   std::vector<hipEvent_t> ev;
   std::vector<ProfRec> recs;
   int open = -1;
@@ -172,11 +178,13 @@ void prof_end(Profiler* p, hipStream_t st) {
 namespace {
 Profiler g_prof;
 
-Profiler* prof_if_on() { return g_prof.on ? &g_prof : nullptr; }
+Profiler* prof_if_on() { return g_prof.on.load(std::memory_order_acquire) ? &g_prof : nullptr; }
 
+// A call records its launches only while profiling is on, under the
+// profiler's lock (begin/end take it too); otherwise it runs unlocked.
 template <typename F>
 sf_status run_locked(F f) {
-  if (g_prof.on) {
+  if (g_prof.on.load(std::memory_order_acquire)) {
     std::lock_guard<std::mutex> lk(g_prof.mu);
     return f(prof_if_on());
   }
@@ -534,13 +542,13 @@ sf_status sf_gdn_profile_begin(int capacity) {
       return hip_fail(r, "hipEventCreate");
     }
   }
-  g_prof.on = true;
+  g_prof.on.store(true, std::memory_order_release);
   return SF_OK;
 }
 
 sf_status sf_gdn_profile_end(void) {
   std::lock_guard<std::mutex> lk(g_prof.mu);
-  g_prof.on = false;
+  g_prof.on.store(false, std::memory_order_release);
   for (const ProfRec& r : g_prof.recs) {
     hipError_t e = hipEventSynchronize(g_prof.ev[r.ev + 1]);
     if (e != hipSuccess) return hip_fail(e, "hipEventSynchronize");

@@ -259,3 +259,71 @@ def test_segment_plan():
     assert plan(1024, 16, seg=1) == (1, 16)
     assert plan(1024, 16, seg=64) == (16, 1)  # clamped to the chunk
     assert plan(0, 16) == (1, 0)
+
+
+def test_rejects_plans_beyond_the_chain_kernels_range():
+    """The chain kernels address one sequence's segment maps through a
+    32-bit byte range: P * D * D * 4 bytes must fit, so an explicit one-block
+    segment on a chunk of 2,097,152 tokens at D = 128 (32,768 segments) is
+    refused on the host, and the default plan for the same chunk is not."""
+    big = 32768 * 64
+    L, P = ctypes.c_int(0), ctypes.c_int(0)
+    lib = _lib.load()
+    s = _shape(T=big, H=1, seg=1)
+    assert lib.sf_gdn_segment_plan(ctypes.byref(s), ctypes.byref(L), ctypes.byref(P)) == \
+        _lib.SF_ERR_UNSUPPORTED
+    assert "segments" in lib.sf_last_error_message().decode()
+    assert _lib.segment_plan(_shape(T=big - 64, H=1, seg=1)) == (1, 32767)
+    assert _lib.segment_plan(_shape(T=big, H=1))[1] < 32768
+
+
+_NO_GPU_CALL = r"""
+import ctypes, sys
+sys.path.insert(0, sys.argv[1])
+from linear_recurrence_chunked_gated_amd import _lib
+G = 1 << 30
+L = _lib.load()
+vp = lambda x: None if x is None else ctypes.c_void_p(x)
+shape = _lib.Shape(1, 128, 2, 128, 128, 1, 0)
+ws = _lib.workspace_bytes(shape)
+st = L.sf_gdn_chunk_fwd(ctypes.byref(shape), vp(G), vp(2 * G), vp(3 * G), vp(4 * G), vp(5 * G),
+                        None, vp(6 * G), vp(7 * G), vp(16 * G), ctypes.c_size_t(ws), None)
+print(st, L.sf_last_error_message().decode())
+"""
+
+
+def test_hip_failure_is_a_status():
+    """A call whose arguments pass the host checks but whose HIP calls fail
+    returns SF_ERR_HIP with the HIP error text; nothing aborts.  Run in a
+    child process that can see no GPU (ROCR_VISIBLE_DEVICES and
+    HIP_VISIBLE_DEVICES empty), so the failure is the runtime's own and no
+    kernel can ever run on the placeholder pointers."""
+    import subprocess
+    import sys
+    env = dict(os.environ, ROCR_VISIBLE_DEVICES="", HIP_VISIBLE_DEVICES="",
+               CUDA_VISIBLE_DEVICES="")
+    r = subprocess.run([sys.executable, "-c", _NO_GPU_CALL, ROOT], capture_output=True, text=True,
+                       env=env, timeout=120)
+    assert r.returncode == 0, r.stderr
+    line = r.stdout.strip().splitlines()[-1]
+    code, msg = line.split(" ", 1)
+    assert int(code) == _lib.SF_ERR_HIP, line
+    assert msg, line
+
+
+def test_split_lengths():
+    """The split at fraction f: each chunk into two parts of whole 64-token
+    blocks, the first about f of it; order and total preserved; chunks of
+    one block stay whole; f outside (0, 1) is refused."""
+    from linear_recurrence_chunked_gated_amd.chain import split_lengths
+    L = chunk_lengths(262144, 8, 0.5)
+    for f in (0.3, 0.5, 0.7, 0.9):
+        parts = split_lengths(L, f)
+        assert len(parts) == 2 * len(L) and sum(parts) == sum(L)
+        assert all(p > 0 and p % 64 == 0 for p in parts)
+        for i, n in enumerate(L):
+            assert parts[2 * i] + parts[2 * i + 1] == n
+            assert abs(parts[2 * i] - f * n) <= 32
+    assert split_lengths([64, 128], 0.5) == [64, 64, 64]
+    with pytest.raises(ValueError):
+        split_lengths(L, 1.0)

@@ -2,14 +2,15 @@
 call, sf_gdn_chunk_fwd_split and sf_gdn_chunk_bwd_saved_split): BEGIN then
 END equals one whole call bit for bit, and the overlapped chunk chains (the
 next chunk's state-independent launches on a second stream) equal the plain
-chains bit for bit."""
+chains bit for bit and the unchunked fp64 oracle within the bf16 bar, per
+head."""
 import pytest
 import torch
 
 import linear_recurrence_chunked_gated_amd as gdn
 from linear_recurrence_chunked_gated_amd import _lib
 from linear_recurrence_chunked_gated_amd.plan import chunk_lengths
-from gdn_testutil import inputs, to_dev
+from gdn_testutil import TOL, assert_close, inputs, to_dev, oracle_args, f64, as_f64
 
 pytestmark = pytest.mark.gpu
 
@@ -67,7 +68,7 @@ def test_split_saved_backward_equals_whole(B, T, H, D, dtype, seg):
 @pytest.mark.parametrize("lengths,H", [(chunk_lengths(16384, 8, 0.5), 4),
                                        ([1000, 64, 1936], 2),   # ragged, odd count
                                        ([1000], 2)])
-def test_overlapped_chains_equal_plain(lengths, H):
+def test_overlapped_chains_equal_plain(oracle_mod, lengths, H):
     T, n = sum(lengths), len(lengths)
     d = to_dev(inputs(1, T, H, 128, "bf16", seed=4200 + n, s_in_std=0.1, grads=True,
                       decay=0.01))
@@ -83,3 +84,42 @@ def test_overlapped_chains_equal_plain(lengths, H):
         assert torch.equal(a, b) and torch.equal(a, c)
     for name, x, y in zip(("dq", "dk", "dv", "dalpha", "dbeta", "dS_in"), g1, g2):
         assert torch.equal(x, y), name
+    # the overlapped chains against the unchunked oracle (chunking is exact in
+    # real arithmetic: Eqs. 5 and 7)
+    o_ref, S_ref = oracle_mod.gdn_fwd(*oracle_args(d))
+    for o in (o2, o3):
+        assert_close("o", f64(o), o_ref, TOL["bf16"], head_axis=2)
+    for st in (st2, st3):
+        assert_close("S_out", f64(st[-1]), S_ref, TOL["bf16"], head_axis=1)
+    g_ref = oracle_mod.gdn_bwd(*oracle_args(d), as_f64(d["dO"]), as_f64(d["dS_out"]))
+    for name, x, r, ax in zip(("dq", "dk", "dv", "dalpha", "dbeta", "dS_in"), g2, g_ref,
+                              (2, 2, 2, 2, 2, 1)):
+        assert_close(name, f64(x), r, TOL["bf16"], head_axis=ax)
+
+
+@pytest.mark.parametrize("f", [0.5, 0.7])
+def test_split_fraction_chains(oracle_mod, f):
+    """Every chunk cut at fraction f into two parts (the page's split for
+    overlap), overlapped on two streams: bit for bit the same split run on
+    one stream, and the unchunked oracle within the bf16 bar, per head."""
+    lengths = chunk_lengths(16384, 8, 0.5)
+    d = to_dev(inputs(1, sum(lengths), 4, 128, "bf16", seed=4300, s_in_std=0.1, grads=True,
+                      decay=0.01))
+    fa = (d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["S_in"])
+    o1, st1, sv1 = gdn.chain_fwd(*fa, lengths, save=True, split=f)
+    g1 = gdn.chain_bwd(*fa[:5], d["dO"], d["dS_out"], lengths, None, saved=sv1, split=f)
+    o2, st2, sv2 = gdn.chain_fwd(*fa, lengths, save=True, overlap=True, split=f)
+    g2 = gdn.chain_bwd(*fa[:5], d["dO"], d["dS_out"], lengths, None, saved=sv2, overlap=True,
+                       split=f)
+    torch.cuda.synchronize()
+    assert len(sv1) == 2 * len(lengths)
+    assert torch.equal(o1, o2) and torch.equal(st1[-1], st2[-1])
+    for name, x, y in zip(("dq", "dk", "dv", "dalpha", "dbeta", "dS_in"), g1, g2):
+        assert torch.equal(x, y), name
+    o_ref, S_ref = oracle_mod.gdn_fwd(*oracle_args(d))
+    assert_close("o", f64(o2), o_ref, TOL["bf16"], head_axis=2)
+    assert_close("S_out", f64(st2[-1]), S_ref, TOL["bf16"], head_axis=1)
+    g_ref = oracle_mod.gdn_bwd(*oracle_args(d), as_f64(d["dO"]), as_f64(d["dS_out"]))
+    for name, x, r, ax in zip(("dq", "dk", "dv", "dalpha", "dbeta", "dS_in"), g2, g_ref,
+                              (2, 2, 2, 2, 2, 1)):
+        assert_close(name, f64(x), r, TOL["bf16"], head_axis=ax)

@@ -109,7 +109,7 @@ __device__ __forceinline__ void block_scores(const T* Qs, const T* Ks, int ldd, 
       p[e] = gam * accP[j][e];
     }
     if constexpr (WITH_A) st4(Af + r * ldf + s0, a[0], a[1], a[2], a[3]);
-    if constexpr (WITH_Q) st4(Pl + r * ldc + s0, p[0], p[1], p[2], p[3]);
+    if constexpr (WITH_Q) st4(lds_sw(Pl + r * ldc + s0, ldc), p[0], p[1], p[2], p[3]);
   }
 }
 
@@ -184,9 +184,10 @@ __device__ __forceinline__ void block_solve(const float* Af, float* Tm, int ldf,
 }
 
 // Tp = T diag(beta o gamma) (unless Tp is null) and Tpp = T diag(beta), in the
-// operand type, by a workgroup of NT threads.  Upper 16x16 blocks are written
-// as zero.
-template <typename T, int NT>
+// operand type, by a workgroup of NT threads, into LDS tiles (LDS_DST) or a
+// plain row-major array in global memory.  Upper 16x16 blocks are written as
+// zero.
+template <typename T, int NT, bool LDS_DST>
 __device__ __forceinline__ void block_tprime(const float* Tm, int ldf, const GateLds& G, T* Tp,
                                              T* Tpp, int ldc) {
   constexpr int EPT = BLK * BLK / NT;   // elements per thread
@@ -200,10 +201,15 @@ __device__ __forceinline__ void block_tprime(const float* Tm, int ldf, const Gat
     float t[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) t[e] = upper ? 0.f : Tm[r * ldf + s + e];
+    T* dp = Tp + r * ldc + s;
+    T* dpp = Tpp + r * ldc + s;
+    if constexpr (LDS_DST) {
+      dp = lds_sw(dp, ldc);
+      dpp = lds_sw(dpp, ldc);
+    }
     if (Tp)
-      st4(Tp + r * ldc + s, t[0] * G.bg[s], t[1] * G.bg[s + 1], t[2] * G.bg[s + 2],
-          t[3] * G.bg[s + 3]);
-    st4(Tpp + r * ldc + s, t[0] * G.beta[s], t[1] * G.beta[s + 1], t[2] * G.beta[s + 2],
+      st4(dp, t[0] * G.bg[s], t[1] * G.bg[s + 1], t[2] * G.bg[s + 2], t[3] * G.bg[s + 3]);
+    st4(dpp, t[0] * G.beta[s], t[1] * G.beta[s + 1], t[2] * G.beta[s + 2],
         t[3] * G.beta[s + 3]);
   }
 }

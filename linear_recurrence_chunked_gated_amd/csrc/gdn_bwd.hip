@@ -39,6 +39,8 @@ template <typename T, int D> struct ScanLds {
                           oP = oT + sq, oG = oP + sq;
   static constexpr size_t bytes = oG + kGateBytes;
   static_assert(bytes <= 160 * 1024, "LDS budget");
+  static_assert(sizeof(T) != 2 || (oK % 4096 == 0 && oO % 4096 == 0 && oW % 4096 == 0 &&
+                                   oT % 4096 == 0 && oP % 4096 == 0), "swizzled tiles 4 KiB aligned");
 };
 
 // Per-block inputs of the reverse scan in flight (q, k, dO rows, Tpp from the
@@ -216,9 +218,11 @@ __global__ __launch_bounds__(4 * D, 2) void gdn_bwd_dscan_kernel(BwdArgs a, int 
 // one, on double-buffered K, dO, P, Wn and gates, so a block takes two
 // barrier phases instead of three.  Each product is formed as in
 // gdn_bwd_dscan_kernel, which remains for layouts that do not fit (fp32).
+// Padded rows (no swizzle), as in the segment summary: 8-byte row pairs
+// and transpose reads dominate here.
 template <typename T, int D> struct Scan2Lds {
-  static constexpr int LDD = D + Lay<T>::PAD;
-  static constexpr int LDC = BLK + Lay<T>::PAD;
+  static constexpr int LDD = D + Lay<T>::PADX;
+  static constexpr int LDC = BLK + Lay<T>::PADX;
   static constexpr size_t rowD = (size_t)BLK * LDD * sizeof(T);
   static constexpr size_t sq = (size_t)BLK * LDC * sizeof(T);
   static constexpr size_t oQ = 0, oT = oQ + rowD, oK = oT + sq, oO = oK + 2 * rowD,
@@ -424,13 +428,13 @@ __device__ __forceinline__ float tile_sum_over_m(f32x4 v) {
 // fp32 operands of the gate-chain products (dT T^T and T^T Y, 64 x 64 x 64)
 // go through the bf16 matrix cores as split tiles: x ~ hi + lo with
 // hi = bf16(x) and lo = bf16(x - hi), about 16 significant bits.  A split
-// tile row holds hi[64] | lo[64] | pad, SPLIT_LD bf16 = the bytes of an fp32
-// row of BLK + 4, so a split tile takes an fp32 tile's region.
-constexpr int SPLIT_LD = 2 * (BLK + 4);
+// tile row holds hi[64] | lo[64], SPLIT_LD bf16 = 256 bytes, swizzled like
+// any 256-byte bf16 row.
+constexpr int SPLIT_LD = 2 * BLK;
 __device__ __forceinline__ void split_store(bf16* row, int c, float x) {
   const bf16 h = (bf16)x;
-  row[c] = h;
-  row[BLK + c] = (bf16)(x - (float)h);
+  *lds_sw(row + c, SPLIT_LD) = h;
+  *lds_sw(row + BLK + c, SPLIT_LD) = (bf16)(x - (float)h);
 }
 // C += A B^T with both operands split, dropping only the lo*lo term.
 __device__ __forceinline__ f32x4 mma_split(bf16x8 ah, bf16x8 al, bf16x8 bh, bf16x8 bl, f32x4 c) {
@@ -475,16 +479,23 @@ template <typename T, int D> struct GradLds {
   static constexpr size_t f64x64 = (size_t)BLK * LDF * sizeof(float);
   static constexpr size_t sq64 = (size_t)BLK * LDC * sizeof(T);
   static constexpr bool DVN_IN_A = sizeof(T) == 4;  // dVn fits the Tpp half only for fp32
-  static constexpr size_t zR = cmax(rowD, f64x64);
+  static constexpr bool BF = sizeof(T) == 2;  // swizzled bf16 tiles: regions 4 KiB aligned,
+                                              // split tiles in place of the fp32 Y and dT
+  static constexpr size_t al(size_t x) { return BF ? lds_align(x) : x; }
+  static constexpr size_t zSplit = (size_t)BLK * 2 * BLK * 2;  // a split tile (64 rows x 256 B)
+  static constexpr size_t zR = BF ? cmax(rowD, zSplit) : cmax(rowD, f64x64);
   static constexpr size_t zA = cmax(f64x64, 2 * sq64);
-  static constexpr size_t zW = cmax(rowD, f64x64);
+  static constexpr size_t zW = BF ? cmax(rowD, zSplit) : cmax(rowD, f64x64);
   static constexpr size_t zD = DVN_IN_A ? 0 : cmax(rowD, sq64);
   static constexpr size_t zPart = (3 * NW * BLK + NW + 4) * sizeof(float);
   static constexpr size_t oQ = 0, oK = oQ + zR, oV = oK + zR, oO = oV + zR, oT = oO + zR,
-                          oA = oT + f64x64, oP = oA + zA, oW = oP + sq64, oD = oW + zW,
-                          oG = oD + zD, oPart = oG + kGateBytes;
+                          oA = al(oT + f64x64), oP = al(oA + zA), oW = al(oP + sq64),
+                          oD = al(oW + zW), oG = oD + zD, oPart = oG + kGateBytes;
   static constexpr size_t bytes = oPart + zPart;
   static_assert(bytes <= 160 * 1024, "LDS budget");
+  static_assert(!BF || (oK % 4096 == 0 && oV % 4096 == 0 && oO % 4096 == 0 && oA % 4096 == 0 &&
+                        oP % 4096 == 0 && oW % 4096 == 0 && oD % 4096 == 0),
+                "swizzled tiles 4 KiB aligned");
   static_assert(!DVN_IN_A || sq64 >= rowD, "dVn must fit the Tpp half");
   // a [D][LDD] copy of the state fits V+dO and W+dVn (adjacent regions)
   static constexpr size_t zS = (size_t)D * LDD * sizeof(T);
@@ -583,8 +594,8 @@ __global__ __launch_bounds__(4 * D, 2) void gdn_bwd_grads_kernel(BwdArgs a) {
 #pragma unroll
   for (int aa = 0; aa < DKT; ++aa) {
     const int off = (16 * w + li) * LDD + 16 * aa + g4;
-    st4(Sc + off, Sx[aa][0], Sx[aa][1], Sx[aa][2], Sx[aa][3]);
-    st4(Gc + off, dSx[aa][0], dSx[aa][1], dSx[aa][2], dSx[aa][3]);
+    st4(lds_sw(Sc + off, LDD), Sx[aa][0], Sx[aa][1], Sx[aa][2], Sx[aa][3]);
+    st4(lds_sw(Gc + off, LDD), dSx[aa][0], dSx[aa][1], dSx[aa][2], dSx[aa][3]);
   }
   __builtin_amdgcn_sched_barrier(0);
   Tl::load(r2, v, rs, nv);
@@ -613,7 +624,7 @@ __global__ __launch_bounds__(4 * D, 2) void gdn_bwd_grads_kernel(BwdArgs a) {
     skf[s] = frag_tr<T, PERM>(Sc + 16 * w, LDD, s);
     gkf[s] = frag_tr<T, PERM>(Gc + 16 * w, LDD, s);
   }
-  block_tprime<T, 64 * NW>(Tm, LDF, G, Tp, Tpp, LDC);
+  block_tprime<T, 64 * NW, true>(Tm, LDF, G, Tp, Tpp, LDC);
   lds_barrier();  // copies read before V and dO replace them
   Tl::to_lds(r2, Vs, LDD, nv);
   Tl::to_lds(r3, Os, LDD, nv);
@@ -703,7 +714,7 @@ __global__ __launch_bounds__(4 * D, 2) void gdn_bwd_grads_kernel(BwdArgs a) {
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
       const int r = 16 * (r0 + j) + li;
-      T* pp = Pl + r * LDC + s0;
+      T* pp = lds_sw(Pl + r * LDC + s0, LDC);  // 4 elements of one 16-byte chunk
       f32x4 pg, dm;
       const float gr = G.g[r];
 #pragma unroll
@@ -738,8 +749,9 @@ __global__ __launch_bounds__(4 * D, 2) void gdn_bwd_grads_kernel(BwdArgs a) {
       acc[j] *= G.gam[r];
       // O-term of dg: dg_r += sum_dk Q[r][dk] dQ1[r][dk]
       f32x4 qv;
+      const T* qr = lds_sw(Qs + r * LDD + 16 * w + g4, LDD);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) qv[e] = (float)Qs[r * LDD + 16 * w + g4 + e] * acc[j][e];
+      for (int e = 0; e < 4; ++e) qv[e] = (float)qr[e] * acc[j][e];
       add_cols(dgp, 16 * j, qv, 1.f);
     }
 #pragma unroll
@@ -778,8 +790,9 @@ __global__ __launch_bounds__(4 * D, 2) void gdn_bwd_grads_kernel(BwdArgs a) {
       store_tile_T(acc[j], dWs, LDD, 16 * w, 16 * j, -1.f);
       const int s = 16 * j + li;
       f32x4 kv;
+      const T* kr = lds_sw(Ks + s * LDD + 16 * w + g4, LDD);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) kv[e] = (float)Ks[s * LDD + 16 * w + g4 + e] * x2[j][e];
+      for (int e = 0; e < 4; ++e) kv[e] = (float)kr[e] * x2[j][e];
       add_cols(ddp, 16 * j, kv, 1.f);
       dKt[j] += G.dec[s] * x2[j];
     }
@@ -872,8 +885,8 @@ __global__ __launch_bounds__(4 * D, 2) void gdn_bwd_grads_kernel(BwdArgs a) {
           h[e] = (bf16)acc[j][e];
           l[e] = (bf16)(acc[j][e] - (float)h[e]);
         }
-        *reinterpret_cast<bf16x4*>(row) = h;
-        *reinterpret_cast<bf16x4*>(row + BLK) = l;
+        *reinterpret_cast<bf16x4*>(lds_sw(row, SPLIT_LD)) = h;
+        *reinterpret_cast<bf16x4*>(lds_sw(row + BLK, SPLIT_LD)) = l;
       }
     } else {
 #pragma unroll

@@ -19,11 +19,13 @@
 //    (lane l owns C[m = 4 g + e][n = i]), so an accumulator can be fed back as
 //    an operand whose rows are its n index and whose contraction index is its
 //    m index, without leaving registers.
-//  * Operands in LDS are row-major tiles padded by 16 bytes per row.  A tile
-//    stored as X[k][n] (contraction index on rows) is read as an operand with
-//    rows n through the gfx950 transpose read ds_read_b64_tr_b16: within each
-//    16-lane group, input lane m addresses row m / 4, columns 4 (m % 4) .. +3,
-//    and output lane i receives column i of those 4 rows.
+//  * Operands in LDS are row-major tiles.  bf16 tiles have unpadded rows of
+//    128 or 256 bytes, stored swizzled (see lds_sw); fp32 tiles are padded by
+//    16 bytes per row.  A tile stored as X[k][n] (contraction index on rows)
+//    is read as an operand with rows n through the gfx950 transpose read
+//    ds_read_b64_tr_b16: within each 16-lane group, input lane m addresses
+//    row m / 4, columns 4 (m % 4) .. +3, and output lane i receives column i
+//    of those 4 rows.
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -70,14 +72,46 @@ template <> struct Mma<float> {
 
 template <typename T> struct Lay {
   static constexpr int VEC = 16 / sizeof(T);  // elements per 16-byte chunk
-  static constexpr int PAD = VEC;             // row padding (elements)
-  // Row padding of 64-wide tiles (scores, Tp, Tpp) in kernels that mostly
-  // read them: 32 bytes for bf16, so that 16-byte row reads of eight
-  // consecutive rows hit distinct banks (8-byte writes of such rows conflict
-  // more, so kernels that write them often keep PAD).
-  static constexpr int PADC = sizeof(T) == 2 ? 2 * VEC : VEC;
+  // Row padding (elements): none for the swizzled bf16 tiles, 16 bytes for
+  // fp32 tiles (so that 16 rows of a 4-byte fragment read hit distinct banks).
+  static constexpr int PAD = sizeof(T) == 2 ? 0 : VEC;
+  static constexpr int PADC = PAD;
+  // Padded bf16 rows, for kernels that keep them instead of the swizzle:
+  // 16 bytes per row (32 for 64-wide tiles that are mostly read by rows).
+  static constexpr int PADX = VEC;
+  static constexpr int PADXC = sizeof(T) == 2 ? 2 * VEC : VEC;
   typedef T pack4 __attribute__((ext_vector_type(4)));
 };
+
+// LDS region offsets: swizzled tiles start on 4 KiB boundaries (16 rows of
+// 256 bytes), so that a tile's row index is in the address bits lds_sw reads.
+constexpr size_t lds_align(size_t x) { return (x + 4095) / 4096 * 4096; }
+
+// The LDS position of element address p of a row-major bf16 tile with ld
+// elements per row.  Rows of 256 bytes (16 chunks of 16 bytes) store chunk c
+// of row r at c ^ (r & 15), rows of 128 bytes at c ^ ((r >> 1) & 7); any other
+// row length, and fp32 tiles, are stored as addressed (padded rows).
+// Measured on gfx950 with 8 waves (cycles per wave instruction), these masks
+// put every access form of the kernels at its conflict-free cost: 16-byte row
+// reads of 16 rows x 4 chunks 4.4 (8.1 with 272-byte padded rows, 8.0 with
+// 144-byte ones), 8-byte row-pair reads 5.5, transpose reads 4.2, 8-byte
+// transposed stores 8 and 2-byte stores 4, none worse than padded rows.
+// The mask is a function of the address alone (tiles are 4 KiB aligned), so
+// it is applied to final element addresses, on the 32-bit LDS address.  A
+// kernel that keeps padded rows (ld of any other length) gets p unchanged.
+template <typename T>
+__device__ __forceinline__ T* lds_sw(T* p, int ld) {
+  const int rowb = ld * (int)sizeof(T);
+  if (sizeof(T) != 2 || (rowb != 256 && rowb != 128)) return p;
+  typedef __attribute__((address_space(3))) T lds_t;
+  const unsigned a = (unsigned)(size_t)(lds_t*)p;  // the 32-bit LDS address
+  const unsigned b = a ^ ((a >> 4) & (rowb == 256 ? 0xF0u : 0x70u));
+  return (T*)(lds_t*)(size_t)b;
+}
+template <typename T>
+__device__ __forceinline__ const T* lds_sw(const T* p, int ld) {
+  return lds_sw(const_cast<T*>(p), ld);
+}
 
 // ---------------------------------------------------------------- frags ----
 // Operand rows from a row-major LDS tile: p points at the fragment's row 0
@@ -87,13 +121,13 @@ frag_row(const T* p, int ld, int s);
 
 template <> __device__ __forceinline__ bf16x8 frag_row<bf16, STD>(const bf16* p, int ld, int s) {
   const int l = lane_id();
-  return *reinterpret_cast<const bf16x8*>(p + (l & 15) * ld + 32 * s + 8 * (l >> 4));
+  return *reinterpret_cast<const bf16x8*>(lds_sw(p + (l & 15) * ld + 32 * s + 8 * (l >> 4), ld));
 }
 template <> __device__ __forceinline__ bf16x8 frag_row<bf16, PERM>(const bf16* p, int ld, int s) {
   const int l = lane_id();
   const bf16* q = p + (l & 15) * ld + 32 * s + 4 * (l >> 4);
-  const bf16x4 lo = *reinterpret_cast<const bf16x4*>(q);
-  const bf16x4 hi = *reinterpret_cast<const bf16x4*>(q + 16);
+  const bf16x4 lo = *reinterpret_cast<const bf16x4*>(lds_sw(q, ld));
+  const bf16x4 hi = *reinterpret_cast<const bf16x4*>(lds_sw(q + 16, ld));
   return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 }
 template <> __device__ __forceinline__ float frag_row<float, STD>(const float* p, int ld, int s) {
@@ -119,7 +153,7 @@ __device__ __forceinline__ bf16x4 ds_tr4(const bf16* p) {
 // rows k0 .. k0+3 of X, columns n0 .. n0+15, delivered transposed.
 __device__ __forceinline__ bf16x4 tr_rows4(const bf16* p, int ld, int k0) {
   const int i = lane_id() & 15;
-  return ds_tr4(p + (k0 + (i >> 2)) * ld + 4 * (i & 3));
+  return ds_tr4(lds_sw(p + (k0 + (i >> 2)) * ld + 4 * (i & 3), ld));
 }
 template <> __device__ __forceinline__ bf16x8 frag_tr<bf16, STD>(const bf16* p, int ld, int s) {
   const int g = lane_id() >> 4;
@@ -253,23 +287,24 @@ template <typename T, int D> struct StateTiles {
   }
 };
 
-// dst[n][m..m+3] = scale * acc for the tile at (m0, n0).
+// LDS tile dst[n][m..m+3] = scale * acc for the tile at (m0, n0).
 template <typename T>
 __device__ __forceinline__ void store_tile_T(const f32x4& acc, T* dst, int ld, int m0, int n0,
                                              float scale = 1.f) {
   const int lane = lane_id();
   const int m = m0 + 4 * (lane >> 4), n = n0 + (lane & 15);
-  st4(dst + n * ld + m, scale * acc[0], scale * acc[1], scale * acc[2], scale * acc[3]);
+  st4(lds_sw(dst + n * ld + m, ld), scale * acc[0], scale * acc[1], scale * acc[2],
+      scale * acc[3]);
 }
 
-// dst[m + e][n] = scale * acc[e].
+// LDS tile dst[m + e][n] = scale * acc[e].
 template <typename T>
 __device__ __forceinline__ void store_tile_N(const f32x4& acc, T* dst, int ld, int m0, int n0,
                                              float scale = 1.f) {
   const int lane = lane_id();
   const int m = m0 + 4 * (lane >> 4), n = n0 + (lane & 15);
 #pragma unroll
-  for (int e = 0; e < 4; ++e) dst[(m + e) * ld + n] = from_f<T>(scale * acc[e]);
+  for (int e = 0; e < 4; ++e) *lds_sw(dst + (m + e) * ld + n, ld) = from_f<T>(scale * acc[e]);
 }
 
 // ---------------------------------------------------------------------------
@@ -307,7 +342,7 @@ template <typename T, int D, int NT> struct Tile {
       v.y = ok ? v.y : 0u;
       v.z = ok ? v.z : 0u;
       v.w = ok ? v.w : 0u;
-      *reinterpret_cast<uint4*>(s + row * ld + ch * VEC) = v;
+      *reinterpret_cast<uint4*>(lds_sw(s + row * ld + ch * VEC, ld)) = v;
     }
   }
 };

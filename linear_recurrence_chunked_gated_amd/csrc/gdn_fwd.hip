@@ -42,6 +42,8 @@ template <typename T, int D> struct FwdLds {
                           oT = oW + rowD, oP = oT + 2 * sq, oG = oP + sq;
   static constexpr size_t out_bytes = oG + kGateBytes;
   static_assert(out_bytes <= 160 * 1024, "LDS budget");
+  static_assert(sizeof(T) != 2 || (oK % 4096 == 0 && oV % 4096 == 0 && oW % 4096 == 0 &&
+                                   oT % 4096 == 0 && oP % 4096 == 0), "swizzled tiles 4 KiB aligned");
 };
 
 // Fused out kernel, two blocks in flight: block b's state work reads K, W, P
@@ -56,6 +58,8 @@ template <typename T, int D> struct OutLds {
                           oW = oK + 2 * rowD, oP = oW + 2 * rowD, oG = oP + 2 * sq;
   static constexpr size_t bytes = oG + 2 * kGateBytes;
   static constexpr bool fits = bytes <= 160 * 1024;
+  static_assert(sizeof(T) != 2 || (oV % 4096 == 0 && oT % 4096 == 0 && oK % 4096 == 0 &&
+                                   oW % 4096 == 0 && oP % 4096 == 0), "swizzled tiles 4 KiB aligned");
 };
 
 // Pre kernel: RK K -> Tm (fp32 T, solve scratch; K is dead once A is formed)
@@ -170,7 +174,7 @@ __global__ __launch_bounds__(256) void gdn_prep_kernel(FwdArgs a) {
   lds_barrier();
   block_solve(Af, Tm, LDF);
   T* out = const_cast<T*>(tw_block<T>(a.tw, a.nblk, bh, blk));
-  block_tprime<T, 256>(Tm, LDF, G, nullptr, out, BLK);
+  block_tprime<T, 256, false>(Tm, LDF, G, nullptr, out, BLK);
 }
 
 // --------------------------------------------------------- fused out -------
@@ -572,9 +576,11 @@ __global__ __launch_bounds__(64 * fwd_nw<D>(), 2) void gdn_fwd_summary_kernel(Fw
 // bf16): the next block's W and U are formed in the same barrier phase as
 // the current block's map updates, on double-buffered K, W and gates, so a
 // block takes two barrier phases instead of three.
+// Padded rows (no swizzle): this kernel reads its W tile through 8-byte row
+// pairs, which the padded layout lets the compiler fetch in one instruction.
 template <typename T, int D> struct Sum2Lds {
-  static constexpr int LDD = D + Lay<T>::PAD;
-  static constexpr int LDC = BLK + Lay<T>::PADC;
+  static constexpr int LDD = D + Lay<T>::PADX;
+  static constexpr int LDC = BLK + Lay<T>::PADXC;
   static constexpr size_t rowD = (size_t)BLK * LDD * sizeof(T);
   static constexpr size_t sq = (size_t)BLK * LDC * sizeof(T);
   static constexpr size_t oV = 0, oT = oV + rowD, oK = oT + sq, oW = oK + 2 * rowD,

@@ -107,6 +107,22 @@ sf_status sf_gdn_chunk_bwd(const sf_gdn_shape* shape, const void* q, const void*
                            float* dalpha, float* dbeta, float* dS_in, void* workspace,
                            size_t ws_bytes, void* stream);
 
+/* The forward without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  It computes exactly what
+ * sf_gdn_chunk_fwd computes, bit for bit, with the workspace taken from a
+ * static device array of the library (64 MiB per GPU, held until the process
+ * ends; its address is looked up once per device on the first call with that
+ * device current).  It allocates and frees nothing.  A shape whose forward
+ * workspace (sf_gdn_chunk_fwd_workspace_size) exceeds 64 MiB returns
+ * SF_ERR_WORKSPACE before anything is enqueued.  Every call on one GPU uses
+ * the same array, and nothing in it needs to start at any value: calls that
+ * overlap in time on one GPU (two streams, two threads) race on it, so the
+ * caller orders them (one stream, or events). */
+sf_status sf_gdn_chunk_fwd_noalloc(const sf_gdn_shape* shape, const void* q, const void* k,
+                                   const void* v, const float* alpha, const float* beta,
+                                   const float* S_in, void* o, float* S_out, void* stream);
+
 /* Saving forward and saved backward (no recompute of the forward scan).
  *
  * The backward above rebuilds the chunk's state trajectory from the inputs,

@@ -38,6 +38,7 @@ SIGNATURES = {
     "sf_gdn_chunk_bwd_workspace_size": (ctypes.c_int, [ctypes.POINTER(Shape), ctypes.POINTER(_sz)]),
     "sf_gdn_chunk_fwd": (ctypes.c_int, [ctypes.POINTER(Shape)] + [_vp] * 8 + [_vp, _sz, _vp]),
     "sf_gdn_chunk_bwd": (ctypes.c_int, [ctypes.POINTER(Shape)] + [_vp] * 14 + [_vp, _sz, _vp]),
+    "sf_gdn_chunk_fwd_noalloc": (ctypes.c_int, [ctypes.POINTER(Shape)] + [_vp] * 8 + [_vp]),
     "sf_gdn_chunk_saved_size": (ctypes.c_int, [ctypes.POINTER(Shape), ctypes.POINTER(_sz)]),
     "sf_gdn_segment_plan": (ctypes.c_int, [ctypes.POINTER(Shape), ctypes.POINTER(ctypes.c_int),
                                            ctypes.POINTER(ctypes.c_int)]),
@@ -235,6 +236,39 @@ def chunk_fwd(q, k, v, alpha, beta, S_in=None, o=None, S_out=None, seg_blocks=0,
                                       _ptr(workspace), wsn, _stream(stream))
     _check(st, "sf_gdn_chunk_fwd_save")
     return o, S_out, saved
+
+
+def chunk_fwd_noalloc(q, k, v, alpha, beta, S_in=None, o=None, S_out=None, seg_blocks=0,
+                      stream=None):
+    """sf_gdn_chunk_fwd_noalloc on torch tensors: the forward with the
+    library's static workspace.  o and S_out must be preallocated by the
+    caller when nothing may be allocated here.  Returns (o, S_out)."""
+    B, T, H, Dk = q.shape
+    Dv = v.shape[3]
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("tensors must be on a GPU device")
+    _need(q, "q", q.dtype, (B, T, H, Dk), dev)
+    _need(k, "k", q.dtype, (B, T, H, Dk), dev)
+    _need(v, "v", q.dtype, (B, T, H, Dv), dev)
+    _need(alpha, "alpha", torch.float32, (B, T, H), dev)
+    _need(beta, "beta", torch.float32, (B, T, H), dev)
+    if S_in is not None:
+        _need(S_in, "S_in", torch.float32, (B, H, Dv, Dk), dev)
+    if o is None:
+        o = torch.empty((B, T, H, Dv), dtype=q.dtype, device=dev)
+        used_on(stream, o)
+    _need(o, "o", q.dtype, (B, T, H, Dv), dev)
+    if S_out is None:
+        S_out = torch.empty((B, H, Dv, Dk), dtype=torch.float32, device=dev)
+        used_on(stream, S_out)
+    _need(S_out, "S_out", torch.float32, (B, H, Dv, Dk), dev)
+    shape = make_shape(B, T, H, Dk, Dv, q.dtype, seg_blocks)
+    st = load().sf_gdn_chunk_fwd_noalloc(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v),
+                                         _ptr(alpha), _ptr(beta), _ptr(S_in), _ptr(o),
+                                         _ptr(S_out), _stream(stream))
+    _check(st, "sf_gdn_chunk_fwd_noalloc")
+    return o, S_out
 
 
 def chunk_bwd(q, k, v, alpha, beta, S_in, dO, dS_out=None, grads=None, seg_blocks=0,

@@ -483,6 +483,53 @@ sf_status sf_gdn_chunk_bwd_saved(const sf_gdn_shape* shape, const void* q, const
                   dv, dalpha, dbeta, dS_in, workspace, ws_bytes, stream, true);
 }
 
+// ------------------------------------------------ no-allocation forward ----
+// Workspace of sf_gdn_chunk_fwd_noalloc: one static device array per GPU,
+// held until the process ends.  Host code never uses the array's name as an
+// address: each device's copy is looked up once (hipGetSymbolAddress, with
+// that device current) and that pointer is what the kernels get.
+constexpr size_t kScratchBytes = (size_t)64 << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+namespace {
+std::mutex g_scratch_mu;
+std::vector<void*> g_scratch_ptr;  // by device ordinal; null until looked up
+
+sf_status scratch_for_current_device(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if ((size_t)dev >= g_scratch_ptr.size()) g_scratch_ptr.resize((size_t)dev + 1, nullptr);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    if (!ptr) return fail(SF_ERR_HIP, "hipGetSymbolAddress(scratch) returned NULL");
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return SF_OK;
+}
+}  // namespace
+
+sf_status sf_gdn_chunk_fwd_noalloc(const sf_gdn_shape* shape, const void* q, const void* k,
+                                   const void* v, const float* alpha, const float* beta,
+                                   const float* S_in, void* o, float* S_out, void* stream) {
+  Plan p;
+  sf_status s = make_plan(shape, p);
+  if (s != SF_OK) return s;
+  const size_t need = fwd_ws(p);
+  if (need > kScratchBytes)
+    return fail(SF_ERR_WORKSPACE, "the no-allocation forward needs " + std::to_string(need) +
+                                      " bytes of workspace; its static scratch holds " +
+                                      std::to_string(kScratchBytes));
+  void* ws = nullptr;
+  if ((s = scratch_for_current_device(&ws)) != SF_OK) return s;
+  return fwd_impl(shape, q, k, v, alpha, beta, S_in, o, S_out, nullptr, 0, ws, kScratchBytes,
+                  stream, false);
+}
+
 static bool bad_phase(int phase) {
   if (phase == SF_PHASE_ALL || phase == SF_PHASE_BEGIN || phase == SF_PHASE_END) return false;
   fail(SF_ERR_INVALID_ARG, "phase must be SF_PHASE_ALL, SF_PHASE_BEGIN or SF_PHASE_END");

@@ -19,6 +19,8 @@
 //   5. gdn_bwd_dscan<main>: per segment from its true exit gradient, the exit
 //      gradient dS'_b of every block, and dS_in
 //   6. gdn_bwd_grads: per block, fully parallel, dq dk dv dalpha dbeta.
+#include <algorithm>
+
 #include "gdn_kernels.hpp"
 
 namespace sfgdn {
@@ -29,14 +31,17 @@ __device__ __forceinline__ const T* tok_base(const void* p, int T_, int H, int b
 }
 
 // ------------------------------------------------------------------ LDS ----
-// dscan: RQ Q | RK K | RO dO | RW Wn | RT Tpp | RP P | RG gates
+// dscan: RQ Q | RK K | RO dO | RW Wn | RT Tpp | RP P | RG gates.  Where that
+// would not fit (fp32 operands at d = 128), Wn shares Q's region: the
+// products that read Q then finish before W is formed, with a barrier between.
 template <typename T, int D> struct ScanLds {
   static constexpr int LDD = D + Lay<T>::PAD;
   static constexpr int LDC = BLK + Lay<T>::PAD;
   static constexpr size_t rowD = (size_t)BLK * LDD * sizeof(T);
   static constexpr size_t sq = (size_t)BLK * LDC * sizeof(T);
-  static constexpr size_t oQ = 0, oK = oQ + rowD, oO = oK + rowD, oW = oO + rowD, oT = oW + rowD,
-                          oP = oT + sq, oG = oP + sq;
+  static constexpr bool W_IN_Q = 4 * rowD + 2 * sq + kGateBytes > 160 * 1024;
+  static constexpr size_t oQ = 0, oK = oQ + rowD, oO = oK + rowD, oW = W_IN_Q ? oQ : oO + rowD,
+                          oT = (W_IN_Q ? oO : oW) + rowD, oP = oT + sq, oG = oP + sq;
   static constexpr size_t bytes = oG + kGateBytes;
   static_assert(bytes <= 160 * 1024, "LDS budget");
   static_assert(sizeof(T) != 2 || (oK % 4096 == 0 && oO % 4096 == 0 && oW % 4096 == 0 &&
@@ -166,6 +171,7 @@ __global__ __launch_bounds__(4 * D, 2) void gdn_bwd_dscan_kernel(BwdArgs a, int 
       for (int aa = 0; aa < DKT; ++aa)
         X2[aa] = Mma<T>::mma(frag_tr<T, STD>(Qs + 16 * aa, LDD, s), bo, X2[aa]);
     }
+    if constexpr (Lz::W_IN_Q) lds_barrier();  // Q read before W replaces it
     block_w<T, D, NW>(Ks, LDD, Tpp, LDC, Wn, G.gam);
     lds_barrier();
     if (more) fetch_part(std::integral_constant<int, 4>{});
@@ -467,8 +473,11 @@ __device__ __forceinline__ void add_cols(float* part, int n0, f32x4 v, float sig
 
 // LDS plan of the gradient kernel (regions reused by phase):
 //   RQ Q | RK K | RV V -> Y | RO dO -> dW | RT Tm | RA Af -> Tp, Tpp (-> dVn, dKK
-//   for fp32) | RP P -> dPm | RW Wn -> Vn -> dT | RD dVn -> dKK (bf16) | gates,
-//   per-wave partial sums.
+//   for fp32 at d = 64) | RP P -> dPm | RW Wn -> Vn -> dT | RD dVn -> dKK |
+//   gates, per-wave partial sums.
+// FAR (fp32 operands at d = 128, where the 64 x 128 tiles are 33 KiB each):
+// RQ, RK, RV and RO lie in a global area of the workgroup instead of LDS,
+// which holds the rest (142 KiB).
 template <typename T, int D> struct GradLds {
   static constexpr int NW = D / 16;
   static constexpr int LDD = D + Lay<T>::PAD;
@@ -478,7 +487,8 @@ template <typename T, int D> struct GradLds {
   static constexpr size_t rowD = (size_t)BLK * LDD * sizeof(T);
   static constexpr size_t f64x64 = (size_t)BLK * LDF * sizeof(float);
   static constexpr size_t sq64 = (size_t)BLK * LDC * sizeof(T);
-  static constexpr bool DVN_IN_A = sizeof(T) == 4;  // dVn fits the Tpp half only for fp32
+  // dVn fits the Tpp half of RA for fp32 at d = 64 only
+  static constexpr bool DVN_IN_A = sizeof(T) == 4 && sq64 >= rowD;
   static constexpr bool BF = sizeof(T) == 2;  // swizzled bf16 tiles: regions 4 KiB aligned,
                                               // split tiles in place of the fp32 Y and dT
   static constexpr size_t al(size_t x) { return BF ? lds_align(x) : x; }
@@ -488,9 +498,16 @@ template <typename T, int D> struct GradLds {
   static constexpr size_t zW = BF ? cmax(rowD, zSplit) : cmax(rowD, f64x64);
   static constexpr size_t zD = DVN_IN_A ? 0 : cmax(rowD, sq64);
   static constexpr size_t zPart = (3 * NW * BLK + NW + 4) * sizeof(float);
-  static constexpr size_t oQ = 0, oK = oQ + zR, oV = oK + zR, oO = oV + zR, oT = oO + zR,
-                          oA = al(oT + f64x64), oP = al(oA + zA), oW = al(oP + sq64),
-                          oD = al(oW + zW), oG = oD + zD, oPart = oG + kGateBytes;
+  // the input regions, from the start of their area (LDS, or the global area)
+  static constexpr size_t oQ = 0, oK = oQ + zR, oV = oK + zR, oO = oV + zR, zIn = oO + zR;
+  static constexpr size_t rest(size_t o0) {
+    return al(al(al(al(o0 + f64x64) + zA) + sq64) + zW) + zD + kGateBytes + zPart;
+  }
+  static constexpr bool FAR = rest(zIn) > 160 * 1024;
+  static constexpr size_t far_bytes = FAR ? zIn : 0;
+  static constexpr size_t oT = FAR ? 0 : zIn, oA = al(oT + f64x64), oP = al(oA + zA),
+                          oW = al(oP + sq64), oD = al(oW + zW), oG = oD + zD,
+                          oPart = oG + kGateBytes;
   static constexpr size_t bytes = oPart + zPart;
   static_assert(bytes <= 160 * 1024, "LDS budget");
   static_assert(!BF || (oK % 4096 == 0 && oV % 4096 == 0 && oO % 4096 == 0 && oA % 4096 == 0 &&
@@ -499,22 +516,31 @@ template <typename T, int D> struct GradLds {
   static_assert(!DVN_IN_A || sq64 >= rowD, "dVn must fit the Tpp half");
   // a [D][LDD] copy of the state fits V+dO and W+dVn (adjacent regions)
   static constexpr size_t zS = (size_t)D * LDD * sizeof(T);
-  static_assert(oO + zR - oV >= zS && (oD + zD) - oW >= zS, "state copies");
+  static_assert(zIn - oV >= zS && (oD + zD) - oW >= zS, "state copies");
 };
 
+// The gradients of block id (of B*H*nblk, the heads of one token block
+// consecutive).  smem: the workgroup's LDS; in: the area of the input regions
+// (smem, or the workgroup's global area when FAR).
 template <typename T, int D>
-__global__ __launch_bounds__(4 * D, 2) void gdn_bwd_grads_kernel(BwdArgs a) {
+__device__ __forceinline__ void grads_block(const BwdArgs& a, int id, unsigned char* smem,
+                                            unsigned char* in) {
   typedef GradLds<T, D> Lz;
   constexpr int NW = Lz::NW, DKT = D / 16;
   constexpr int LDD = Lz::LDD, LDC = Lz::LDC, LDF = Lz::LDF;
   constexpr int NJ = 16 / NW;  // 64x64 tiles per wave
-  extern __shared__ __align__(16) unsigned char smem[];
-  T* Qs = reinterpret_cast<T*>(smem + Lz::oQ);
-  T* Ks = reinterpret_cast<T*>(smem + Lz::oK);
-  T* Vs = reinterpret_cast<T*>(smem + Lz::oV);
-  float* Yf = reinterpret_cast<float*>(smem + Lz::oV);
-  T* Os = reinterpret_cast<T*>(smem + Lz::oO);
-  T* dWs = reinterpret_cast<T*>(smem + Lz::oO);
+  // With the input regions in global memory, a barrier must also publish
+  // the global stores (the regions in LDS need only the LDS one).
+  auto bar = [] {
+    if constexpr (Lz::FAR) full_barrier();
+    else lds_barrier();
+  };
+  T* Qs = reinterpret_cast<T*>(in + Lz::oQ);
+  T* Ks = reinterpret_cast<T*>(in + Lz::oK);
+  T* Vs = reinterpret_cast<T*>(in + Lz::oV);
+  float* Yf = reinterpret_cast<float*>(in + Lz::oV);
+  T* Os = reinterpret_cast<T*>(in + Lz::oO);
+  T* dWs = reinterpret_cast<T*>(in + Lz::oO);
   float* Tm = reinterpret_cast<float*>(smem + Lz::oT);
   float* Af = reinterpret_cast<float*>(smem + Lz::oA);
   T* Tp = reinterpret_cast<T*>(smem + Lz::oA);
@@ -537,7 +563,7 @@ __global__ __launch_bounds__(4 * D, 2) void gdn_bwd_grads_kernel(BwdArgs a) {
   // Consecutive workgroups take the heads of one token block, so the rows
   // of [B, T, H, D] that run concurrently are read whole (H * D elements).
   const int BH = f.B * f.H;
-  const int blk = blockIdx.x / BH, bh = blockIdx.x % BH;
+  const int blk = id / BH, bh = id % BH;
   const int b = bh / f.H, h = bh % f.H;
   const int t0 = blk * BLK, nv = min(BLK, f.T - t0);
   const size_t rs = (size_t)f.H * D;
@@ -579,17 +605,17 @@ __global__ __launch_bounds__(4 * D, 2) void gdn_bwd_grads_kernel(BwdArgs a) {
     StateTiles<T, D>::load(hG, w, lane, dSx);
     __builtin_amdgcn_sched_barrier(0);
   }
-  lds_barrier();
+  bar();
   // ---- B: scores
   f32x4 kk[NJ];  // K K^T tiles (m = 16 (w & 3), n = 16 ((w >> 2) NJ + j)), for phase L
   block_scores<T, D, NW, true>(Qs, Ks, LDD, G, Af, LDF, Pl, LDC, kk);
-  lds_barrier();
+  bar();
   // ---- C: T = (I + A)^{-1}, Tp, Tpp; zero Tm's upper blocks (solve scratch).
   // Meanwhile S and dS' go through LDS once, so that every wave also holds
   // them by dk-tile (S^T, dS'^T rows 16 w .. as operands over dv, for dQ, dW
   // and dK2): copies [dv][dk] in the V/dO and W/dVn regions, which are free
   // until V, dO are staged and W is formed.
-  T* Sc = reinterpret_cast<T*>(smem + Lz::oV);
+  T* Sc = reinterpret_cast<T*>(in + Lz::oV);
   T* Gc = reinterpret_cast<T*>(smem + Lz::oW);
 #pragma unroll
   for (int aa = 0; aa < DKT; ++aa) {
@@ -597,6 +623,7 @@ __global__ __launch_bounds__(4 * D, 2) void gdn_bwd_grads_kernel(BwdArgs a) {
     st4(lds_sw(Sc + off, LDD), Sx[aa][0], Sx[aa][1], Sx[aa][2], Sx[aa][3]);
     st4(lds_sw(Gc + off, LDD), dSx[aa][0], dSx[aa][1], dSx[aa][2], dSx[aa][3]);
   }
+  if constexpr (Lz::FAR) vm_wait();  // the S copy is global: stored before the solve's barrier
   __builtin_amdgcn_sched_barrier(0);
   Tl::load(r2, v, rs, nv);
   Tl::load(r3, dO, rs, nv);
@@ -625,10 +652,10 @@ __global__ __launch_bounds__(4 * D, 2) void gdn_bwd_grads_kernel(BwdArgs a) {
     gkf[s] = frag_tr<T, PERM>(Gc + 16 * w, LDD, s);
   }
   block_tprime<T, 64 * NW, true>(Tm, LDF, G, Tp, Tpp, LDC);
-  lds_barrier();  // copies read before V and dO replace them
+  bar();  // copies read before V and dO replace them
   Tl::to_lds(r2, Vs, LDD, nv);
   Tl::to_lds(r3, Os, LDD, nv);
-  lds_barrier();
+  bar();
   for (int i = threadIdx.x; i < BLK * BLK; i += 64 * NW) {
     const int r = i >> 6, s = i & 63;
     if ((s >> 4) > (r >> 4)) Tm[r * LDF + s] = 0.f;
@@ -637,7 +664,7 @@ __global__ __launch_bounds__(4 * D, 2) void gdn_bwd_grads_kernel(BwdArgs a) {
   block_w<T, D, NW>(Ks, LDD, Tp, LDC, Wn);
   f32x4 U[1][4];
   block_u<T, 1>(Tpp, LDC, Vs, LDD, w, U);
-  lds_barrier();
+  bar();
   // ---- E: <dS', S> of this wave's rows (for the gate of the block end);
   // Vn = U - W S^T (registers), then to LDS
   {
@@ -655,7 +682,7 @@ __global__ __launch_bounds__(4 * D, 2) void gdn_bwd_grads_kernel(BwdArgs a) {
     for (int aa = 0; aa < DKT; ++aa) Sv[0][aa] = Sx[aa];
     block_x_st<T, D, 1, true>(Wn, LDD, Sv, U);
   }
-  lds_barrier();
+  bar();
 #pragma unroll
   for (int i = 0; i < 4; ++i) store_tile_N(U[0][i], Vns, LDD, 16 * i, 16 * w);
   // dVn = P^T dO + D (K dS'^T)
@@ -691,11 +718,11 @@ __global__ __launch_bounds__(4 * D, 2) void gdn_bwd_grads_kernel(BwdArgs a) {
       if (r < nv) st4(dv + (size_t)r * rs + 16 * w + g4, acc[j][0], acc[j][1], acc[j][2], acc[j][3]);
     }
   }
-  lds_barrier();
+  bar();
   // ---- F: dVn to LDS
 #pragma unroll
   for (int i = 0; i < 4; ++i) store_tile_N(dvn[i], dVns, LDD, 16 * i, 16 * w);
-  lds_barrier();
+  bar();
   // ---- G: dP^T (m = s, n = r) = Vn dO^T ; P-term of dg ; dPm = dP o Gamma o mask in place of P
   {
     const int st = w & 3, r0 = (w >> 2) * NJ;
@@ -730,7 +757,7 @@ __global__ __launch_bounds__(4 * D, 2) void gdn_bwd_grads_kernel(BwdArgs a) {
     }
     add_rows(dgp, 16 * st, pgs, -1.f);         // dg_s -= sum_r
   }
-  lds_barrier();
+  bar();
   // ---- H: dQ^T = diag-scaled (S^T dO^T) + K^T dPm^T  (wave: dk-tile w); dK^T starts
   f32x4 dKt[4];
   {
@@ -771,7 +798,7 @@ __global__ __launch_bounds__(4 * D, 2) void gdn_bwd_grads_kernel(BwdArgs a) {
       if (r < nv) st4(dq + (size_t)r * rs + 16 * w + g4, acc[j][0], acc[j][1], acc[j][2], acc[j][3]);
     }
   }
-  lds_barrier();  // dO reads done: its region takes dW
+  bar();  // dO reads done: its region takes dW
   // ---- I: dW^T = -(S^T dVn^T) -> dW row-major ; dK2^T = dS'^T Vn^T scaled by D ; D-term
   {
     f32x4 acc[4], x2[4];
@@ -797,13 +824,13 @@ __global__ __launch_bounds__(4 * D, 2) void gdn_bwd_grads_kernel(BwdArgs a) {
       dKt[j] += G.dec[s] * x2[j];
     }
   }
-  lds_barrier();
+  bar();
   // ---- J: dTp = dW K^T, dTpp = dVn V^T (m = r, n = s); dT; column terms
   // (bf16: T also goes to a split tile in the Q region, free after phase H)
   constexpr bool SPLIT = sizeof(T) == 2;
-  bf16* Tx = reinterpret_cast<bf16*>(smem + Lz::oQ);   // T, split
+  bf16* Tx = reinterpret_cast<bf16*>(in + Lz::oQ);    // T, split
   bf16* dTx = reinterpret_cast<bf16*>(smem + Lz::oW);  // dT, split (in place of dTf)
-  bf16* YTx = reinterpret_cast<bf16*>(smem + Lz::oV);  // Y^T, split (in place of Yf)
+  bf16* YTx = reinterpret_cast<bf16*>(in + Lz::oV);   // Y^T, split (in place of Yf)
   static_assert(Lz::zR >= BLK * SPLIT_LD * 2 && Lz::zW >= BLK * SPLIT_LD * 2, "split tiles");
   if constexpr (SPLIT) {
     for (int i = threadIdx.x; i < BLK * BLK / 8; i += 64 * NW) {
@@ -827,7 +854,7 @@ __global__ __launch_bounds__(4 * D, 2) void gdn_bwd_grads_kernel(BwdArgs a) {
         a2[j] = Mma<T>::mma(au, frag_row<T, STD>(Vs + 16 * (s0t + j) * LDD, LDD, s), a2[j]);
       }
     }
-    lds_barrier();  // Vn (region RW) and V reads done before dT overwrites RW
+    bar();  // Vn (region RW) and V reads done before dT overwrites RW
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
       const int s = 16 * (s0t + j) + li;
@@ -855,7 +882,7 @@ __global__ __launch_bounds__(4 * D, 2) void gdn_bwd_grads_kernel(BwdArgs a) {
       }
     }
   }
-  lds_barrier();
+  bar();
   // ---- K: Y = dT T^T (fp32 products; split tiles for bf16)
   {
     const int rt = w & 3, s0t = (w >> 2) * NJ;
@@ -900,7 +927,7 @@ __global__ __launch_bounds__(4 * D, 2) void gdn_bwd_grads_kernel(BwdArgs a) {
       for (int j = 0; j < NJ; ++j) store_tile_N(acc[j], Yf, LDF, 16 * rt, 16 * (s0t + j));
     }
   }
-  lds_barrier();
+  bar();
   // ---- L: dA = -T^T Y (strictly lower); A-terms of dbeta, dg; dKK
   {
     const int rt = w & 3, s0t = (w >> 2) * NJ;
@@ -961,7 +988,7 @@ __global__ __launch_bounds__(4 * D, 2) void gdn_bwd_grads_kernel(BwdArgs a) {
       }
     }
   }
-  lds_barrier();
+  bar();
   // ---- M: dK^T += K^T (dKK + dKK^T)^T-terms + dW^T Tp ; store dk
   {
 #pragma unroll
@@ -981,7 +1008,7 @@ __global__ __launch_bounds__(4 * D, 2) void gdn_bwd_grads_kernel(BwdArgs a) {
       if (s < nv) st4(dk + (size_t)s * rs + 16 * w + g4, dKt[j][0], dKt[j][1], dKt[j][2], dKt[j][3]);
     }
   }
-  lds_barrier();
+  bar();
   // ---- N: gate gradients
   if (w == 0) {
     const int j = lane;
@@ -1012,6 +1039,23 @@ __global__ __launch_bounds__(4 * D, 2) void gdn_bwd_grads_kernel(BwdArgs a) {
       a.dalpha[idx] = x / ra;
       a.dbeta[idx] = dbv;
     }
+  }
+}
+
+template <typename T, int D>
+__global__ __launch_bounds__(4 * D, 2) void gdn_bwd_grads_kernel(BwdArgs a) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  if constexpr (GradLds<T, D>::FAR) {
+    // a grid of at most kFarGroups workgroups, each with its own global area,
+    // striding over the blocks
+    unsigned char* in = reinterpret_cast<unsigned char*>(a.far) + (size_t)blockIdx.x * GradLds<T, D>::far_bytes;
+    const int n = a.f.B * a.f.H * a.f.nblk;
+    for (int id = blockIdx.x; id < n; id += gridDim.x) {
+      grads_block<T, D>(a, id, smem, in);
+      full_barrier();  // every read of this block done before the next one's stores
+    }
+  } else {
+    grads_block<T, D>(a, blockIdx.x, smem, smem);
   }
 }
 
@@ -1069,15 +1113,23 @@ hipError_t launch_bwd(const BwdArgs& a0, bool saved, int phase, hipStream_t st, 
   // 6. per-block gradients
   if ((e = set_lds((const void*)gdn_bwd_grads_kernel<T, D>, GradLds<T, D>::bytes)) != hipSuccess)
     return e;
+  if (GradLds<T, D>::FAR && !a.far) return hipErrorInvalidValue;
+  const int nblocks = BH * f.nblk;
+  const int grid = GradLds<T, D>::FAR ? std::min(nblocks, kFarGroups) : nblocks;
   prof_begin(prof, "gdn_bwd_grads", st);
-  hipLaunchKernelGGL((gdn_bwd_grads_kernel<T, D>), dim3(BH * f.nblk), dim3(4 * D),
-                     grad_bytes, st, a);
+  hipLaunchKernelGGL((gdn_bwd_grads_kernel<T, D>), dim3(grid), dim3(4 * D), grad_bytes, st, a);
   prof_end(prof, st);
   return hipGetLastError();
 }
 
+size_t bwd_far_bytes(bool f32, int D) {
+  if (!f32) return 0;
+  return (D == 128 ? GradLds<float, 128>::far_bytes : GradLds<float, 64>::far_bytes) * kFarGroups;
+}
+
 template hipError_t launch_bwd<bf16, 128>(const BwdArgs&, bool, int, hipStream_t, Profiler*);
 template hipError_t launch_bwd<bf16, 64>(const BwdArgs&, bool, int, hipStream_t, Profiler*);
+template hipError_t launch_bwd<float, 128>(const BwdArgs&, bool, int, hipStream_t, Profiler*);
 template hipError_t launch_bwd<float, 64>(const BwdArgs&, bool, int, hipStream_t, Profiler*);
 
 }  // namespace sfgdn

@@ -51,6 +51,14 @@ __device__ __forceinline__ int wave_id() {
 __device__ __forceinline__ void lds_barrier() {
   __asm__ __volatile__("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
+// A barrier after which the other waves of the workgroup also see this wave's
+// global stores: the stores are complete (vmcnt) and a workgroup's waves share
+// one compute unit and its vector L1.  For tiles kept in a per-workgroup
+// global area instead of LDS.
+__device__ __forceinline__ void full_barrier() {
+  __asm__ __volatile__("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+__device__ __forceinline__ void vm_wait() { __asm__ __volatile__("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 enum KOrder { STD = 0, PERM = 1 };
 

@@ -24,26 +24,37 @@
 namespace sfgdn {
 
 // ------------------------------------------------------------------ LDS ----
-// Scan kernels: one workgroup = D/16 waves, one per 16-column slice of the
-// state.  Regions:
-//   RQ : Q (P scores, S Q^T)
+// One-block scan kernels (the forms used where the two-block plans below do
+// not fit): one workgroup = D/16 waves, one per 16-column slice of the state.
+// Regions:
 //   RK : K (row-major; K^T operands come from transpose reads)
 //   RV : V (row-major; V^T operands come from transpose reads)
 //   RW : Wn = -W (for Vn)
-//   RT : Tpp (from the Pre kernel; the first half of the region is unused)
-//   RP : P (masked decayed scores, for the output)
+//   RT : Tpp (from the Pre kernel)
 //   RG : gate vectors
+// and, for the out kernel only,
+//   RQ : Q (P scores, S Q^T)
+//   RP : P (masked decayed scores, for the output)
+// The summary stops after RG.  Where the out kernel's plan would not fit
+// otherwise (fp32 operands at d = 128: 64 x 128 fp32 tiles are 33 KiB), W
+// shares V's region and RQ takes RW: U = Tpp V is then formed before W, with
+// a barrier between.
 template <typename T, int D> struct FwdLds {
   static constexpr int LDD = D + Lay<T>::PAD;
   static constexpr int LDC = BLK + Lay<T>::PADC;
   static constexpr size_t rowD = (size_t)BLK * LDD * sizeof(T);
   static constexpr size_t sq = (size_t)BLK * LDC * sizeof(T);
-  static constexpr size_t oQ = 0, oK = oQ + rowD, oV = oK + rowD, oW = oV + rowD,
-                          oT = oW + rowD, oP = oT + 2 * sq, oG = oP + sq;
-  static constexpr size_t out_bytes = oG + kGateBytes;
-  static_assert(out_bytes <= 160 * 1024, "LDS budget");
-  static_assert(sizeof(T) != 2 || (oK % 4096 == 0 && oV % 4096 == 0 && oW % 4096 == 0 &&
-                                   oT % 4096 == 0 && oP % 4096 == 0), "swizzled tiles 4 KiB aligned");
+  static constexpr size_t al(size_t x) { return sizeof(T) == 2 ? lds_align(x) : x; }
+  static constexpr size_t oK = 0, oV = oK + rowD, oW = oV + rowD, oT = oW + rowD, oG = oT + sq;
+  static constexpr size_t sum_bytes = oG + kGateBytes;
+  static constexpr bool W_IN_V = al(sum_bytes) + rowD + sq > 160 * 1024;
+  static constexpr size_t oWo = W_IN_V ? oV : oW;
+  static constexpr size_t oQ = W_IN_V ? oW : al(sum_bytes);
+  static constexpr size_t oP = W_IN_V ? al(sum_bytes) : oQ + rowD;
+  static constexpr size_t out_bytes = oP + sq;
+  static_assert(sum_bytes <= 160 * 1024 && out_bytes <= 160 * 1024, "LDS budget");
+  static_assert(sizeof(T) != 2 || (oV % 4096 == 0 && oW % 4096 == 0 && oT % 4096 == 0 &&
+                                   oQ % 4096 == 0 && oP % 4096 == 0), "swizzled tiles 4 KiB aligned");
 };
 
 // Fused out kernel, two blocks in flight: block b's state work reads K, W, P
@@ -197,9 +208,8 @@ __global__ __launch_bounds__(64 * fwd_nw<D>(), 2) void gdn_fwd_out_kernel(FwdArg
   T* Qs = reinterpret_cast<T*>(smem + Lz::oQ);
   T* Ks = reinterpret_cast<T*>(smem + Lz::oK);
   T* Vs = reinterpret_cast<T*>(smem + Lz::oV);
-  T* Wn = reinterpret_cast<T*>(smem + Lz::oW);
-  T* Tp = reinterpret_cast<T*>(smem + Lz::oT);
-  T* Tpp = Tp + BLK * LDC;
+  T* Wn = reinterpret_cast<T*>(smem + Lz::oWo);
+  T* Tpp = reinterpret_cast<T*>(smem + Lz::oT);
   T* Pl = reinterpret_cast<T*>(smem + Lz::oP);
   const GateLds G = gate_lds(smem + Lz::oG);
 
@@ -272,9 +282,10 @@ __global__ __launch_bounds__(64 * fwd_nw<D>(), 2) void gdn_fwd_out_kernel(FwdArg
         for (int bb = 0; bb < NDV; ++bb) O[bb][j] *= gr;
       }
     }
-    block_w<T, D, NW>(Ks, LDD, Tpp, LDC, Wn, G.gam);
     f32x4 U[NDV][4];
     block_u<T, NDV>(Tpp, LDC, Vs, LDD, dv0, U);
+    if constexpr (Lz::W_IN_V) lds_barrier();  // V read before W replaces it
+    block_w<T, D, NW>(Ks, LDD, Tpp, LDC, Wn, G.gam);
     lds_barrier();
     // ST and Out: Vn = U - W S^T; O^T += Vn^T P^T; S' = gamma_C S + Vn^T D K
     block_x_st<T, D, NDV, PFQ>(Wn, LDD, St, U);
@@ -479,8 +490,7 @@ __global__ __launch_bounds__(64 * fwd_nw<D>(), 2) void gdn_fwd_summary_kernel(Fw
   T* Wn = reinterpret_cast<T*>(smem + Lz::oW);
   T* Ks = reinterpret_cast<T*>(smem + Lz::oK);
   T* Vs = reinterpret_cast<T*>(smem + Lz::oV);
-  T* Tp = reinterpret_cast<T*>(smem + Lz::oT);
-  T* Tpp = Tp + BLK * LDC;
+  T* Tpp = reinterpret_cast<T*>(smem + Lz::oT);
   const GateLds G = gate_lds(smem + Lz::oG);
 
   const int w = wave_id(), lane = lane_id(), g4 = 4 * (lane >> 4), li = lane & 15;
@@ -841,7 +851,7 @@ template <typename T, int D>
 hipError_t launch_fwd_summary(const FwdArgs& a, int nseg, hipStream_t st, Profiler* prof,
                               const char* name) {
   typedef FwdLds<T, D> Lz;
-  constexpr size_t lds1 = Lz::out_bytes, lds2 = Sum2Lds<T, D>::bytes;
+  constexpr size_t lds1 = Lz::sum_bytes, lds2 = Sum2Lds<T, D>::bytes;
   if constexpr (Sum2Lds<T, D>::fits) {
     hipError_t e = set_lds((const void*)gdn_fwd_summary2_kernel<T, D>, lds2);
     if (e != hipSuccess) return e;
@@ -940,6 +950,7 @@ hipError_t launch_fwd(const FwdArgs& a, void* hsave, int phase, hipStream_t st, 
   template hipError_t launch_prep<T, D>(const FwdArgs&, hipStream_t, Profiler*);
 SF_INST(bf16, 128)
 SF_INST(bf16, 64)
+SF_INST(float, 128)
 SF_INST(float, 64)
 #undef SF_INST
 template hipError_t launch_chain<128, false>(const ChainArgs&, hipStream_t, Profiler*);

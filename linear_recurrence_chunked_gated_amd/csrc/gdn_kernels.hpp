@@ -72,7 +72,15 @@ struct BwdArgs {
   float* dSend;         // [B*H][P][D][D] state gradient at each segment's exit
   void* hst;            // [B*H][nblk][D][D] block entry states (state storage type)
   void* dhst;           // [B*H][nblk][D][D] gradient wrt each block's exit state
+  void* far;            // the gradient kernel's global tile areas (see bwd_far_bytes), or null
 };
+
+// Where the gradient kernel's input tiles do not fit its LDS plan (fp32 at
+// d = 128) they live in global areas, one per workgroup, and a grid of at
+// most kFarGroups workgroups (one per compute unit) strides over the blocks.
+constexpr int kFarGroups = 256;
+// Bytes of those areas for the operand type and head size (0: tiles in LDS).
+size_t bwd_far_bytes(bool f32, int D);
 
 // Short causal convolution of one chunk (see gdn_conv.hip).  Token tensors
 // [B, T, C] and boundary states [B, W-1, C] in the operand type; weights and

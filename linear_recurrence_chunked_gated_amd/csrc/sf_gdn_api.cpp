@@ -46,8 +46,6 @@ sf_status make_plan(const sf_gdn_shape* s, Plan& p) {
   if (s->seg_blocks < 0) return fail(SF_ERR_INVALID_ARG, "seg_blocks must be >= 0");
   if (s->Dk != s->Dv) return fail(SF_ERR_UNSUPPORTED, "Dk != Dv is not supported");
   if (s->Dk != 64 && s->Dk != 128) return fail(SF_ERR_UNSUPPORTED, "Dk must be 64 or 128");
-  if (s->dtype == SF_DTYPE_F32 && s->Dk != 64)
-    return fail(SF_ERR_UNSUPPORTED, "fp32 inputs are supported for Dk = Dv = 64 only");
   if ((long long)s->B * s->H > (1LL << 20))
     return fail(SF_ERR_UNSUPPORTED, "B*H too large");
   p.B = s->B;
@@ -103,9 +101,11 @@ size_t tw_buf(const Plan& p) {
 size_t fwd_seg(const Plan& p) { return p.P > 1 ? 3 * seg_buf(p) : 0; }
 size_t fwd_ws(const Plan& p) { return fwd_seg(p) + tw_buf(p); }
 size_t blk_buf(const Plan& p) { return align_up((size_t)p.B * p.H * p.nblk * dd(p) * p.state_elem); }
+// the gradient kernel's global tile areas (fp32 at d = 128)
+size_t far_buf(const Plan& p) { return align_up(bwd_far_bytes(p.dtype == SF_DTYPE_F32, p.D)); }
 size_t bwd_ws(const Plan& p) {
   if (p.P == 0) return 0;
-  return 3 * seg_buf(p) + 3 * seg_buf(p) + 2 * blk_buf(p) + tw_buf(p);
+  return 3 * seg_buf(p) + 3 * seg_buf(p) + 2 * blk_buf(p) + tw_buf(p) + far_buf(p);
 }
 
 struct Range {
@@ -305,7 +305,8 @@ sf_status fwd_impl(const sf_gdn_shape* shape, const void* q, const void* k, cons
       e = (p.D == 128) ? launch_fwd<bf16, 128>(a, hsave, phase, st, prof)
                        : launch_fwd<bf16, 64>(a, hsave, phase, st, prof);
     else
-      e = launch_fwd<float, 64>(a, hsave, phase, st, prof);
+      e = (p.D == 128) ? launch_fwd<float, 128>(a, hsave, phase, st, prof)
+                       : launch_fwd<float, 64>(a, hsave, phase, st, prof);
     if (e != hipSuccess) return hip_fail(e, "forward launch");
     return SF_OK;
   });
@@ -373,6 +374,7 @@ sf_status bwd_impl(const sf_gdn_shape* shape, const void* q, const void* k, cons
     a.dhst = ws + 5 * sb + bb;
     f.tw = ws + 5 * sb + 2 * bb;
     f.MBseg = (float*)(ws + 5 * sb + 2 * bb + tw_buf(p));
+    a.far = far_buf(p) ? ws + 6 * sb + 2 * bb + tw_buf(p) : nullptr;
     if (use_saved) {
       char* sv = (char*)const_cast<void*>(saved);
       a.hst = sv;
@@ -386,7 +388,8 @@ sf_status bwd_impl(const sf_gdn_shape* shape, const void* q, const void* k, cons
       e = (p.D == 128) ? launch_bwd<bf16, 128>(a, use_saved, phase, st, prof)
                        : launch_bwd<bf16, 64>(a, use_saved, phase, st, prof);
     else
-      e = launch_bwd<float, 64>(a, use_saved, phase, st, prof);
+      e = (p.D == 128) ? launch_bwd<float, 128>(a, use_saved, phase, st, prof)
+                       : launch_bwd<float, 64>(a, use_saved, phase, st, prof);
     if (e == hipErrorNotSupported) return fail(SF_ERR_UNSUPPORTED, "backward not available");
     if (e != hipSuccess) return hip_fail(e, "backward launch");
     return SF_OK;

@@ -42,6 +42,9 @@ def check_all(got, ref, tol):
     (1, 256, 2, 64, "f32", None, 0.1, 1.0, 0),
     (1, 256, 2, 64, "f32", 0.1, 0.1, 0.01, 1),
     (2, 333, 2, 64, "f32", 0.1, 0.1, 0.01, 2),     # ragged, B = 2
+    (1, 256, 2, 128, "f32", None, 0.1, 1.0, 0),    # fp32 at d = 128
+    (2, 333, 2, 128, "f32", 0.1, 0.1, 0.01, 2),    # fp32 at d = 128: ragged, B = 2
+    (1, 1000, 2, 128, "f32", 0.1, 0.1, 0.01, 3),   # fp32 at d = 128: ragged segments
     (1, 1000, 3, 128, "bf16", 0.1, 0.1, 0.01, 0),  # ragged, several segments
     (1, 640, 2, 128, "bf16", None, 0.1, 1.0, 3),
     (1, 1, 2, 128, "bf16", 0.1, 0.1, 1.0, 0),      # single token
@@ -168,6 +171,7 @@ def test_bwd_empty_chunk_passes_gradient():
 @pytest.mark.parametrize("B,T,H,D,dtype,seg,decay", [
     (1, 256, 2, 64, "f32", 1, 0.01),
     (2, 333, 2, 64, "f32", 2, 0.01),      # ragged, B = 2
+    (2, 333, 2, 128, "f32", 2, 0.01),     # fp32 at d = 128: ragged, B = 2
     (1, 1000, 3, 128, "bf16", 0, 0.01),   # ragged, several segments
     (1, 640, 2, 128, "bf16", 100, 0.01),  # one segment
     (1, 1, 2, 128, "bf16", 0, 1.0),       # single token (as in the oracle test above)
@@ -205,6 +209,26 @@ def test_saved_buffer_reused_across_shapes():
         torch.cuda.synchronize()
         for name, x, y in zip(NAMES, g1, g2):
             assert torch.equal(x, y), name
+
+
+def test_fp32_d128_chain_fwd_bwd(oracle_mod):
+    """fp32 at d = 128, chained over three uneven chunks (Eqs. 5 and 7), the
+    saving forward and the saved backward, against the unchunked oracle at
+    the fp32 bar.  8 heads x 64 blocks in the largest chunk: more blocks
+    than the gradient kernel's workgroups, so each workgroup takes several."""
+    T = 4096 + 1000
+    lengths = [4096, 640, 360]
+    d = inputs(1, T, 8, 128, "f32", seed=20260020, s_in_std=0.1, grads=True, decay=0.01)
+    dd = to_dev(d)
+    o, states, saved = gdn.chain_fwd(dd["q"], dd["k"], dd["v"], dd["alpha"], dd["beta"],
+                                     dd["S_in"], lengths, save=True)
+    g = gdn.chain_bwd(dd["q"], dd["k"], dd["v"], dd["alpha"], dd["beta"], dd["dO"],
+                      dd["dS_out"], lengths, None, saved=saved)
+    torch.cuda.synchronize()
+    o_ref, S_ref = oracle_mod.gdn_fwd(*oracle_args(d))
+    assert_close("o", f64(o), o_ref, TOL["f32"], head_axis=2)
+    assert_close("S_out", f64(states[-1]), S_ref, TOL["f32"], head_axis=1)
+    check_all([f64(x) for x in g], oracle_bwd(oracle_mod, d), TOL["f32"])
 
 
 def test_saved_chain_nonuniform_fwd_bwd(oracle_mod):
@@ -262,7 +286,7 @@ def test_saved_bwd_empty_chunk():
 # softplus(N(0,1))), S_in ~ N(0, 0.1)): the boundary state enters every
 # output and gradient.  Forward and backward, recompute and saved paths.
 SHORT = [(T, D, dt) for T in (1, 2, 65) for D in (64, 128) for dt in ("bf16",)] + \
-        [(T, 64, "f32") for T in (1, 2, 65)]
+        [(T, D, "f32") for T in (1, 2, 65) for D in (64, 128)]
 
 
 def _short_case(T, D, dtype, saved):

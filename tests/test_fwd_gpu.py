@@ -27,6 +27,9 @@ def run_fwd(d, seg_blocks=0):
     (1, 256, 2, 64, "f32", None, 1.0, 0),      # the fp32 shape, unchained
     (1, 256, 2, 64, "f32", 0.1, 0.01, 1),      # slow decay, one block per segment
     (2, 333, 3, 64, "f32", 0.1, 0.01, 2),      # ragged tail, B = 2
+    (1, 256, 2, 128, "f32", None, 1.0, 0),     # fp32 at d = 128
+    (2, 333, 2, 128, "f32", 0.1, 0.01, 2),     # fp32 at d = 128: ragged tail, B = 2
+    (1, 1000, 2, 128, "f32", 0.1, 0.01, 3),    # fp32 at d = 128: ragged segments
     (1, 1000, 3, 128, "bf16", 0.1, 0.01, 0),   # ragged, several segments
     (2, 640, 2, 128, "bf16", None, 1.0, 3),
     (1, 1, 2, 128, "bf16", 0.1, 1.0, 0),       # single token
@@ -44,11 +47,12 @@ def test_fwd_matches_oracle(oracle_mod, B, T, H, D, dtype, s_in, decay, seg):
     assert_close("S_out", S, S_ref, tol, head_axis=1)
 
 
+@pytest.mark.parametrize("D", [64, 128])
 @pytest.mark.parametrize("decay", [1.0, 0.01])
-def test_fp32_chained_4x64(oracle_mod, decay):
+def test_fp32_chained_4x64(oracle_mod, decay, D):
     """Four chunks of 64 tokens chained through S_in/S_out (Eq. 5) against
     the unchunked oracle, fp32 bar."""
-    d = inputs(1, 256, 2, 64, "f32", seed=20260000, decay=decay)
+    d = inputs(1, 256, 2, D, "f32", seed=20260000, decay=decay)
     dd = to_dev(d)
     o, states = gdn.chain_fwd(dd["q"], dd["k"], dd["v"], dd["alpha"], dd["beta"], None, [64] * 4)
     torch.cuda.synchronize()

@@ -26,7 +26,7 @@ def _heads_equal(x, y, axis, skip):
 
 
 @pytest.mark.parametrize("where", ["v", "k", "alpha", "beta", "S_in"])
-@pytest.mark.parametrize("D,dtype", [(128, "bf16"), (64, "f32")])
+@pytest.mark.parametrize("D,dtype", [(128, "bf16"), (64, "f32"), (128, "f32")])
 def test_forward_nan_stays_in_its_sequence(where, D, dtype):
     d = to_dev(inputs(2, 700, 3, D, dtype, seed=61, s_in_std=0.1, decay=0.05))
     fa = [d[k] for k in ("q", "k", "v", "alpha", "beta", "S_in")]

@@ -42,8 +42,10 @@
  * ABI.  Not checked (documented preconditions, checking would cost a pass over
  * HBM): 0 < alpha <= 1, finite inputs.  NaN inputs propagate.
  *
- * Supported: Dk == Dv in {64, 128} for bf16, Dk == Dv == 64 for fp32; any
- * T >= 0 (a partial last 64-token block is handled in the kernels).
+ * Supported: Dk == Dv in {64, 128} for bf16 and for fp32; any T >= 0 (a
+ * partial last 64-token block is handled in the kernels).  The backward
+ * workspace of fp32 at d = 128 includes 256 global tile areas of 132 KiB for
+ * the gradient kernel (its tiles do not fit LDS at that size).
  */
 #ifndef SF_GDN_H
 #define SF_GDN_H

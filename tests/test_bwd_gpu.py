@@ -62,10 +62,10 @@ def test_bwd_matches_oracle(oracle_mod, B, T, H, D, dtype, s_in, ds, decay, seg)
 
 def test_full_size_t16384_sampled_heads(oracle_mod):
     """H=16, T=16384, d=128, bf16, dO ~ N(0,1), dS_out ~ N(0,0.1), S_in = 0, in
-    the launch configuration the benchmark uses; two heads checked whole."""
+    the launch configuration the benchmark uses; four heads checked whole."""
     d = inputs(1, 16384, 16, 128, "bf16", seed=20260003, grads=True)
     got = run_bwd(d)
-    hs = [0, 15]
+    hs = [0, 5, 10, 15]
     sub = head_slice(d, hs)
     ref = oracle_bwd(oracle_mod, sub)
     sel = [g[:, :, hs] if ax == 2 else g[:, hs] for g, ax in zip(got, HEAD_AXIS)]
@@ -76,7 +76,7 @@ def test_full_size_t16384_nonzero_state_sampled(oracle_mod):
     """Supplementary run with S_in ~ N(0, 0.1) so dalpha sees the entry state."""
     d = inputs(1, 16384, 16, 128, "bf16", seed=20260013, s_in_std=0.1, grads=True, decay=0.01)
     got = run_bwd(d)
-    hs = [3]
+    hs = [3, 8, 12]
     sub = head_slice(d, hs)
     ref = oracle_bwd(oracle_mod, sub)
     sel = [g[:, :, hs] if ax == 2 else g[:, hs] for g, ax in zip(got, HEAD_AXIS)]
@@ -246,12 +246,12 @@ def test_saved_chain_nonuniform_fwd_bwd(oracle_mod):
     check_all([f64(x) for x in g], oracle_bwd(oracle_mod, d), TOL["bf16"])
 
 
-def test_full_size_benchmark_chain_sampled_head(oracle_mod):
+def test_full_size_benchmark_chain_sampled_heads(oracle_mod):
     """The benchmark workload at its full size and in the launch
     configuration the benchmark times: T = 262,144, H = 16, d = 128, bf16,
     eight chunks by the c_i(0.5) plan, the saving forward then the saved
     backward, chained.  Inputs are drawn on the device by the seeded
-    generator, as the benchmark draws them; one head is copied out and
+    generator, as the benchmark draws them; four heads are copied out and
     checked whole against the unchunked oracle (chunking is exact in real
     arithmetic), forward and backward."""
     T, H = 262144, 16
@@ -262,7 +262,7 @@ def test_full_size_benchmark_chain_sampled_head(oracle_mod):
     g = gdn.chain_bwd(dd["q"], dd["k"], dd["v"], dd["alpha"], dd["beta"], dd["dO"],
                       dd["dS_out"], lengths, None, saved=saved)
     torch.cuda.synchronize()
-    hs = [9]
+    hs = [1, 6, 9, 14]
     sub = head_slice(dd, hs)
     o_ref, s_ref = oracle_mod.gdn_fwd(*oracle_args(sub))
     assert_close("o", f64(o[:, :, hs]), o_ref, TOL["bf16"], head_axis=2)

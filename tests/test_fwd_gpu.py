@@ -118,10 +118,10 @@ def test_empty_chunk_passes_state():
 def test_full_size_h32_t65536_sampled_heads(oracle_mod):
     """One GPU's share of a 256K-token sequence (T=65536, H=32, d=128, bf16,
     S_in ~ N(0, 0.1)), in the launch configuration the benchmark uses; the
-    oracle checks two whole heads."""
+    oracle checks four whole heads."""
     d = inputs(1, 65536, 32, 128, "bf16", seed=20260002, s_in_std=0.1)
     o, S = run_fwd(d)
-    hs = [0, 31]
+    hs = [0, 11, 20, 31]
     sub = head_slice(d, hs)
     o_ref, S_ref = oracle_mod.gdn_fwd(*oracle_args(sub))
     assert_close("o", o[:, :, hs], o_ref, TOL["bf16"], head_axis=2)
@@ -132,11 +132,11 @@ def test_full_size_h16_t65536_sampled_heads(oracle_mod):
     """The forward-only target shape (T=65536, H=16, d=128, bf16, S_in ~
     N(0, 0.1)), drawn on the device by the seeded generator as the benchmark
     draws it, in the launch configuration the benchmark times (16 segments
-    of 64 blocks); the oracle checks two whole heads."""
+    of 64 blocks); the oracle checks four whole heads."""
     dd = inputs(1, 65536, 16, 128, "bf16", seed=20260102, s_in_std=0.1, device="cuda")
     o, S = gdn.chunk_fwd(dd["q"], dd["k"], dd["v"], dd["alpha"], dd["beta"], dd["S_in"])
     torch.cuda.synchronize()
-    hs = [2, 13]
+    hs = [2, 6, 9, 13]
     sub = head_slice(dd, hs)
     o_ref, S_ref = oracle_mod.gdn_fwd(*oracle_args(sub))
     assert_close("o", f64(o[:, :, hs]), o_ref, TOL["bf16"], head_axis=2)

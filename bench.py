@@ -52,7 +52,7 @@ def kernel_flops_per_block(name, d):
     if name in ("gdn_bwd_dscan", "gdn_bwd_dscan_summary"):
         return (pre - g(C, d, C)) + g(d, d, C) + g(C, d, C) + g(C, d, d) + g(d, d, C)
     if name == "gdn_bwd_grads":
-        return (pre + g(C, d, d)                       # recompute incl. Vn
+        return (g(C, C, d) + g(C, C, d)                # K K^T, Q K^T (Vn from the forward)
                 + g(C, d, C) + g(C, d, d)              # dVn
                 + g(C, d, C) + g(C, C, d)              # dV, dP
                 + g(C, d, d) + g(C, d, C) + g(C, d, C)  # dQ, dK1

@@ -139,6 +139,10 @@ sf_status sf_gdn_chunk_fwd_noalloc(const sf_gdn_shape* shape, const void* q, con
  *     [B, H, P, Dk, Dk]
  *   - per block, T diag(beta) for T = (I + A)^{-1} of the block-local (WY/UT)
  *     form, [B, H, ceil(T/64), 64, 64] in the q/k/v dtype
+ *   - per block, the auxiliary V^new = U - W S^T of the block-local form
+ *     ("What carries the argument"; Referee Report, major comment 1: the
+ *     backward needs the same V^new as the forward), 64 x Dv values in the
+ *     q/k/v dtype, in the internal tile order
  * into the caller's `saved` buffer (size from sf_gdn_chunk_saved_size for
  * the same shape, 256-byte aligned; opaque otherwise), and
  * sf_gdn_chunk_bwd_saved computes the same gradients as sf_gdn_chunk_bwd from

@@ -15,7 +15,7 @@
 //   2. gdn_bwd_dscan<summary>: per segment, dS at its entry from a zero exit
 //      gradient (NB_seg)
 //   3. forward chain of entry states, reverse chain of exit gradients
-//   4. block entry states h_b of every block                    [forward kernel]
+//   4. block entry states h_b and V^new of every block             [forward kernel]
 //   5. gdn_bwd_dscan<main>: per segment from its true exit gradient, the exit
 //      gradient dS'_b of every block, and dS_in
 //   6. gdn_bwd_grads: per block, fully parallel, dq dk dv dalpha dbeta.
@@ -473,7 +473,7 @@ __device__ __forceinline__ void add_cols(float* part, int n0, f32x4 v, float sig
 
 // LDS plan of the gradient kernel (regions reused by phase):
 //   RQ Q | RK K | RV V -> Y | RO dO -> dW | RT Tm | RA Af -> Tp, Tpp (-> dVn, dKK
-//   for fp32 at d = 64) | RP P -> dPm | RW Wn -> Vn -> dT | RD dVn -> dKK |
+//   for fp32 at d = 64) | RP P -> dPm | RW Vn -> dT | RD dVn -> dKK |
 //   gates, per-wave partial sums.
 // FAR (fp32 operands at d = 128, where the 64 x 128 tiles are 33 KiB each):
 // RQ, RK, RV and RO lie in a global area of the workgroup instead of LDS,
@@ -546,7 +546,6 @@ __device__ __forceinline__ void grads_block(const BwdArgs& a, int id, unsigned c
   T* Tp = reinterpret_cast<T*>(smem + Lz::oA);
   T* Tpp = Tp + BLK * LDC;
   T* Pl = reinterpret_cast<T*>(smem + Lz::oP);
-  T* Wn = reinterpret_cast<T*>(smem + Lz::oW);
   T* Vns = reinterpret_cast<T*>(smem + Lz::oW);
   float* dTf = reinterpret_cast<float*>(smem + Lz::oW);
   T* dVns = Lz::DVN_IN_A ? Tpp : reinterpret_cast<T*>(smem + Lz::oD);
@@ -577,6 +576,8 @@ __device__ __forceinline__ void grads_block(const BwdArgs& a, int id, unsigned c
   const size_t gofs = (size_t)b * f.T * f.H + (size_t)t0 * f.H + h;
   const T* hS = reinterpret_cast<const T*>(a.hst) + ((size_t)bh * f.nblk + blk) * D * D;
   const T* hG = reinterpret_cast<const T*>(a.dhst) + ((size_t)bh * f.nblk + blk) * D * D;
+  // Vn of this block as the forward formed it (this wave's dv-tile)
+  const T* hV = reinterpret_cast<const T*>(f.vst) + ((size_t)bh * f.nblk + blk) * BLK * D;
 
   // ---- A: Q, K and the gates, then the states (by dv-tile, first used in
   // phase C); V and dO (first used after the solve) go out at the start of
@@ -627,6 +628,8 @@ __device__ __forceinline__ void grads_block(const BwdArgs& a, int id, unsigned c
   __builtin_amdgcn_sched_barrier(0);
   Tl::load(r2, v, rs, nv);
   Tl::load(r3, dO, rs, nv);
+  uint4 rvn[StateTiles<T, BLK>::NV];
+  StateTiles<T, BLK>::load_raw(hV, w, lane, rvn);
   __builtin_amdgcn_sched_barrier(0);
   // K dS'^T (this wave's dv-tile), for dVn in phase E: it needs only K and
   // dS', so it runs while the last wave does the substitution (and that wave
@@ -652,21 +655,21 @@ __device__ __forceinline__ void grads_block(const BwdArgs& a, int id, unsigned c
     gkf[s] = frag_tr<T, PERM>(Gc + 16 * w, LDD, s);
   }
   block_tprime<T, 64 * NW, true>(Tm, LDF, G, Tp, Tpp, LDC);
-  bar();  // copies read before V and dO replace them
+  bar();  // copies read before V, dO and Vn replace them
   Tl::to_lds(r2, Vs, LDD, nv);
   Tl::to_lds(r3, Os, LDD, nv);
+  {
+    f32x4 vx[4];
+    StateTiles<T, BLK>::unpack(rvn, vx);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) store_tile_N(vx[i], Vns, LDD, 16 * i, 16 * w);
+  }
   bar();
   for (int i = threadIdx.x; i < BLK * BLK; i += 64 * NW) {
     const int r = i >> 6, s = i & 63;
     if ((s >> 4) > (r >> 4)) Tm[r * LDF + s] = 0.f;
   }
-  // ---- D: W, U
-  block_w<T, D, NW>(Ks, LDD, Tp, LDC, Wn);
-  f32x4 U[1][4];
-  block_u<T, 1>(Tpp, LDC, Vs, LDD, w, U);
-  bar();
-  // ---- E: <dS', S> of this wave's rows (for the gate of the block end);
-  // Vn = U - W S^T (registers), then to LDS
+  // ---- E: <dS', S> of this wave's rows (for the gate of the block end)
   {
     f32x4 p = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -676,15 +679,6 @@ __device__ __forceinline__ void grads_block(const BwdArgs& a, int id, unsigned c
     for (int off = 1; off < 64; off <<= 1) x += __shfl_xor(x, off, 64);
     if (lane == 0) dgc[w] = x;
   }
-  {
-    f32x4 Sv[1][DKT];
-#pragma unroll
-    for (int aa = 0; aa < DKT; ++aa) Sv[0][aa] = Sx[aa];
-    block_x_st<T, D, 1, true>(Wn, LDD, Sv, U);
-  }
-  bar();
-#pragma unroll
-  for (int i = 0; i < 4; ++i) store_tile_N(U[0][i], Vns, LDD, 16 * i, 16 * w);
   // dVn = P^T dO + D (K dS'^T)
   f32x4 dvn[4];
   {
@@ -1103,7 +1097,7 @@ hipError_t launch_bwd(const BwdArgs& a0, bool saved, int phase, hipStream_t st, 
     f.Sst = f.S_in;
     f.sst_P = 1;
   }
-  // 4. block entry states
+  // 4. block entry states and Vn
   if (!saved && (e = launch_states<T, D>(f, a.hst, st, prof)) != hipSuccess) return e;
   // 5. block exit gradients and dS_in
   prof_begin(prof, "gdn_bwd_dscan", st);

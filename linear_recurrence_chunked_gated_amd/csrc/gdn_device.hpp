@@ -293,6 +293,25 @@ template <typename T, int D> struct StateTiles {
       }
     }
   }
+  // The same in two steps: the loads, then (once their data is needed) the
+  // conversion, so that the loads can stay in flight meanwhile.
+  __device__ static __forceinline__ void load_raw(const T* blockbase, int w, int lane,
+                                                  uint4 (&r)[NV]) {
+#pragma unroll
+    for (int v = 0; v < NV; ++v) r[v] = *reinterpret_cast<const uint4*>(blockbase + off(w, lane, v));
+  }
+  __device__ static __forceinline__ void unpack(const uint4 (&r)[NV], f32x4* x) {
+#pragma unroll
+    for (int v = 0; v < NV; ++v) {
+      if constexpr (TPV == 2) {
+        const bf16x8 h = __builtin_bit_cast(bf16x8, r[v]);
+        x[2 * v] = f32x4{(float)h[0], (float)h[1], (float)h[2], (float)h[3]};
+        x[2 * v + 1] = f32x4{(float)h[4], (float)h[5], (float)h[6], (float)h[7]};
+      } else {
+        x[v] = __builtin_bit_cast(f32x4, r[v]);
+      }
+    }
+  }
 };
 
 // LDS tile dst[n][m..m+3] = scale * acc for the tile at (m0, n0).

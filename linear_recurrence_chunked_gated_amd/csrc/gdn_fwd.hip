@@ -95,6 +95,12 @@ __device__ __forceinline__ const T* seq_base(const void* p, const FwdArgs& a, in
 // Per-block inputs in flight: the next block's rows (q, k, v), its Tpp
 // from the Pre kernel and its gates are loaded into registers while the
 // current block computes.
+// Vn of block blk of sequence bh in a.vst: 64 x D values in tile order.
+template <typename T, int D>
+__device__ __forceinline__ T* vn_block(const FwdArgs& a, int bh, int blk) {
+  return reinterpret_cast<T*>(a.vst) + ((size_t)bh * a.nblk + blk) * BLK * D;
+}
+
 // Waves per workgroup of the forward kernels: one per 16-column tile of the
 // state.
 template <int D> constexpr int fwd_nw() { return D / 16; }
@@ -289,6 +295,8 @@ __global__ __launch_bounds__(64 * fwd_nw<D>(), 2) void gdn_fwd_out_kernel(FwdArg
     lds_barrier();
     // ST and Out: Vn = U - W S^T; O^T += Vn^T P^T; S' = gamma_C S + Vn^T D K
     block_x_st<T, D, NDV, PFQ>(Wn, LDD, St, U);
+    if constexpr (STATES)
+      StateTiles<T, BLK>::store(vn_block<T, D>(a, bh, blk), dv0, lane, U[0]);
     if constexpr (OUT) block_vnT_pT<T, NDV, PFQ>(U, Pl, LDC, O);
     f32x4 dsc[4];
 #pragma unroll
@@ -428,6 +436,8 @@ __global__ __launch_bounds__(64 * fwd_nw<D>(), 2) void gdn_fwd_out2_kernel(FwdAr
     lds_barrier();
     // block blk, state part: Vn = U - W S^T; O^T += Vn^T P^T; S' = gamma_C S + Vn^T D K
     block_x_st<T, D, NDV, true>(Wb(c), LDD, St, U);
+    if constexpr (STATES)
+      StateTiles<T, BLK>::store(vn_block<T, D>(a, bh, blk), dv0, lane, U[0]);
     if (next2) fetch_part(std::integral_constant<int, 2>{}, pf, blk + 2);
     if constexpr (OUT) block_vnT_pT<T, NDV, true>(U, Pb(c), LDC, O);
     {
@@ -897,6 +907,7 @@ static hipError_t launch_out(const FwdArgs& a, T* hst, hipStream_t st, Profiler*
                              const char* name) {
   const dim3 grid(a.B * a.H * a.P), block(64 * fwd_nw<D>());
   hipError_t e;
+  if (MODE != OUT_ONLY && (!hst || !a.vst)) return hipErrorInvalidValue;
   if constexpr (OutLds<T, D>::fits) {
     constexpr size_t ob = OutLds<T, D>::bytes;
     if ((e = set_lds((const void*)gdn_fwd_out2_kernel<T, D, MODE>, ob)) != hipSuccess) return e;

@@ -29,7 +29,10 @@ struct FwdArgs {
   float* Nseg;         // [B*H][P][D][D]  segment zero-entry exit states
   const float* Sst;    // [B*H][sst_P][D][D] segment entry states (S_in when P == 1)
   int sst_P;
-  void* tw;            // [B*H][nblk][2][64][64] per-block Tp, Tpp (operand type), by the Pre kernel
+  void* tw;            // [B*H][nblk][64][64] per-block Tpp (operand type), by the Pre kernel
+  void* vst;           // [B*H][nblk][64 x D] per-block Vn (operand type, in the order of
+                       // StateTiles<T, 64>: wave w's 64 x 16 slice, dv-tile w), written by
+                       // the state-storing forward and read by the gradient kernel
 };
 
 // One boundary-state chain over the P segments of each sequence (see

@@ -101,11 +101,13 @@ size_t tw_buf(const Plan& p) {
 size_t fwd_seg(const Plan& p) { return p.P > 1 ? 3 * seg_buf(p) : 0; }
 size_t fwd_ws(const Plan& p) { return fwd_seg(p) + tw_buf(p); }
 size_t blk_buf(const Plan& p) { return align_up((size_t)p.B * p.H * p.nblk * dd(p) * p.state_elem); }
+// per-block Vn of the state-storing forward: [B*H][nblk][64 x D] in the operand type
+size_t vn_buf(const Plan& p) { return align_up((size_t)p.B * p.H * p.nblk * BLK * p.D * elem(p)); }
 // the gradient kernel's global tile areas (fp32 at d = 128)
 size_t far_buf(const Plan& p) { return align_up(bwd_far_bytes(p.dtype == SF_DTYPE_F32, p.D)); }
 size_t bwd_ws(const Plan& p) {
   if (p.P == 0) return 0;
-  return 3 * seg_buf(p) + 3 * seg_buf(p) + 2 * blk_buf(p) + tw_buf(p) + far_buf(p);
+  return 3 * seg_buf(p) + 3 * seg_buf(p) + 2 * blk_buf(p) + tw_buf(p) + vn_buf(p) + far_buf(p);
 }
 
 struct Range {
@@ -236,13 +238,14 @@ namespace {
 // [B*H*P][D][D] row-major (P > 1), then the Pre kernel's per-block Tpp.
 size_t saved_maps_off(const Plan& p) { return blk_buf(p); }
 size_t saved_tw_off(const Plan& p) { return blk_buf(p) + (p.P > 1 ? seg_buf(p) : 0); }
+size_t saved_vn_off(const Plan& p) { return saved_tw_off(p) + tw_buf(p); }
 size_t saved_bytes(const Plan& p) {
   if (p.P == 0) return 0;
-  return saved_tw_off(p) + tw_buf(p);
+  return saved_vn_off(p) + vn_buf(p);
 }
 
 // Forward; with `saved` it also stores the per-block entry states, all
-// segment maps and the per-block Tpp there.
+// segment maps, the per-block Tpp and the per-block Vn there.
 sf_status fwd_impl(const sf_gdn_shape* shape, const void* q, const void* k, const void* v,
                    const float* alpha, const float* beta, const float* S_in, void* o,
                    float* S_out, void* saved, size_t sv_bytes, void* workspace, size_t ws_bytes,
@@ -290,6 +293,7 @@ sf_status fwd_impl(const sf_gdn_shape* shape, const void* q, const void* k, cons
     char* ws = (char*)workspace;
     void* hsave = save ? saved : nullptr;
     a.tw = save ? (char*)saved + saved_tw_off(p) : ws + fwd_seg(p);
+    a.vst = save ? (char*)saved + saved_vn_off(p) : nullptr;
     if (p.P > 1) {
       a.Mseg = (float*)ws;
       a.MBseg = save ? (float*)((char*)saved + saved_maps_off(p)) : nullptr;
@@ -374,12 +378,14 @@ sf_status bwd_impl(const sf_gdn_shape* shape, const void* q, const void* k, cons
     a.dhst = ws + 5 * sb + bb;
     f.tw = ws + 5 * sb + 2 * bb;
     f.MBseg = (float*)(ws + 5 * sb + 2 * bb + tw_buf(p));
-    a.far = far_buf(p) ? ws + 6 * sb + 2 * bb + tw_buf(p) : nullptr;
+    f.vst = ws + 6 * sb + 2 * bb + tw_buf(p);
+    a.far = far_buf(p) ? ws + 6 * sb + 2 * bb + tw_buf(p) + vn_buf(p) : nullptr;
     if (use_saved) {
       char* sv = (char*)const_cast<void*>(saved);
       a.hst = sv;
       if (p.P > 1) f.MBseg = (float*)(sv + saved_maps_off(p));
       f.tw = sv + saved_tw_off(p);
+      f.vst = sv + saved_vn_off(p);
     }
     a.dO = dO; a.dS_out = dS_out;
     a.dq = dq; a.dk = dk; a.dv = dv; a.dalpha = dalpha; a.dbeta = dbeta; a.dS_in = dS_in;

@@ -191,6 +191,91 @@ def write_traffic(fetch_csv, write_csv, calib_fetch_csv, calib_write_csv, calib_
     with open(path, "w") as f:
         json.dump(out, f, indent=1)
     print(json.dumps(out, indent=1))
+    _write_traffic_md(out, os.path.join(HERE, "profiles", "traffic_fwdbwd_h16_t262144_d128.md"))
+
+
+# Bytes per 64-token block that a kernel moves of the method's own tensors
+# (q, k, v, dO in; o, dq, dk, dv out; the gates), bf16 activations at width d,
+# counted every time a kernel moves them.  Everything else a kernel moves is
+# this design's intermediates (Tpp, per-block states, V^new, dS', the
+# segment maps).
+def method_bytes_per_block(name, d, elem=2):
+    tile, gates = C * d * elem, C * 4
+    return {"gdn_prep": tile + 2 * gates,                       # k; alpha, beta
+            "gdn_fwd_summary": 2 * tile + 2 * gates,            # k, v
+            "gdn_fwd_out_save": 4 * tile + 2 * gates,           # q, k, v; o
+            "gdn_fwd_out": 4 * tile + 2 * gates,
+            "gdn_bwd_dscan_summary": 3 * tile + 2 * gates,      # q, k, dO
+            "gdn_bwd_dscan": 3 * tile + 2 * gates,
+            "gdn_bwd_grads": 7 * tile + 4 * gates,              # q, k, v, dO; dq, dk, dv; gates
+            }.get(name, 0)
+
+
+def _write_traffic_md(tr, path):
+    """The traffic table of the benchmark workload (8 skewed chunks, H = 16,
+    d = 128, saving forward and saved backward): per launch, the counters'
+    bytes split into the method's tensors and this design's intermediates,
+    and per step (one launch of each kernel per chunk)."""
+    from linear_recurrence_chunked_gated_amd import _lib
+    import torch
+    wl = workload("fwdbwd_h16_t262144_d128_8skew")
+    H, d, chunks = wl["H"], wl["D"], wl["chunks"]
+    nch = len(chunks)
+    blocks = {}
+    for n in chunks:
+        L, P = _lib.segment_plan(_lib.make_shape(1, n, H, d, d, torch.bfloat16, 0))
+        nb = (n + C - 1) // C
+        for k in ("gdn_prep", "gdn_fwd_summary", "gdn_fwd_out_save", "gdn_bwd_dscan",
+                  "gdn_bwd_grads"):
+            blocks[k] = blocks.get(k, 0) + H * nb / nch
+        blocks["gdn_bwd_dscan_summary"] = (blocks.get("gdn_bwd_dscan_summary", 0)
+                                           + H * max(nb - min(L, nb), 0) / nch)
+    rows, tot_step, meth_step = [], 0.0, 0.0
+    for k, v in sorted(tr["kernels"].items(), key=lambda kv: -kv[1]["bytes_per_launch"]):
+        m = method_bytes_per_block(k, d) * blocks.get(k, 0)
+        t = v["bytes_per_launch"]
+        tot_step += t * nch
+        meth_step += m * nch
+        rows.append("| %s | %.1f | %.1f | %.1f | %.1f | %.1f | %.2f |" % (
+            k, v["fetch_bytes"] / 1e6, v["write_bytes"] / 1e6, t / 1e6, m / 1e6, (t - m) / 1e6,
+            t * nch / 1e9))
+    algo = wl["T"] * H * (2840)  # fwd+bwd algorithmic bytes per token-head (bf16, d = 128)
+    c = tr["calibration"]
+    cmds = ["rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/tr_fetch -o tr_fetch -- "
+            "python -u bench.py --steps 1 --warmup 1 --no-cpu-baseline",
+            "rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/tr_write -o tr_write -- "
+            "python -u bench.py --steps 1 --warmup 1 --no-cpu-baseline",
+            "rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/tr_cfetch -o tr_cfetch -- "
+            "python -u bench.py --copy-calibration",
+            "rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/tr_cwrite -o tr_cwrite -- "
+            "python -u bench.py --copy-calibration",
+            "python bench.py --write-traffic gpurun_out/tr_fetch/tr_fetch_counter_collection.csv "
+            "gpurun_out/tr_write/tr_write_counter_collection.csv "
+            "gpurun_out/tr_cfetch/tr_cfetch_counter_collection.csv "
+            "gpurun_out/tr_cwrite/tr_cwrite_counter_collection.csv"]
+    text = ["# HBM traffic per launch: chained fwd+bwd, T=262144, H=16, d=128, bf16, 8 skewed chunks",
+            "", "Commands (run from the repository root on one MI355X, with `TMPDIR=/tmp`), one "
+            "counter per pass:", "", "```"] + cmds + ["```", "",
+            "Calibration: a plain 1 GiB device copy (torch `copy_`) reads FETCH_SIZE = %.0f KiB and "
+            "WRITE_SIZE = %.0f KiB, so fetch counts are scaled by %.4f and write counts by %.4f."
+            % (c["fetch_kib_per_copy"], c["write_kib_per_copy"], c["fetch_scale"], c["write_scale"]),
+            "", "Bytes are per launch, averaged over every launch of the run (8 chunk sizes; the "
+            "warm-up step, the captured step's replays and the eager step). \"method tensors\" is "
+            "what a kernel moves of q, k, v, dO, o, dq, dk, dv and the gates, counted each time a "
+            "kernel moves them (`method_bytes_per_block` in `bench.py`, times the blocks one launch "
+            "covers); \"intermediates\" is the rest: this design's Tpp, per-block states, V^new, "
+            "state gradients and segment maps (and any re-read). `profiles/traffic.json` holds the "
+            "same figures with the hash of the kernel sources they were taken on; `bench.py` reports "
+            "`roofline.traffic` only while that hash matches.", "",
+            "| kernel | fetch (MB) | write (MB) | total (MB) | method tensors (MB) | "
+            "intermediates (MB) | per step (GB) |",
+            "|---|---:|---:|---:|---:|---:|---:|"] + rows + ["",
+            "Per step: %.1f GB, of which %.1f GB are the method's tensors and %.1f GB intermediates, "
+            "against %.2f GB of algorithmic bytes (each tensor moved once: 2,840 B per token-head); "
+            "%.2fx." % (tot_step / 1e9, meth_step / 1e9, (tot_step - meth_step) / 1e9, algo / 1e9,
+                        tot_step / algo), "", "Source hash: `%s`." % tr["source_hash"]]
+    with open(path, "w") as f:
+        f.write("\n".join(text) + "\n")
 
 
 def _read_stats_csv(path):
@@ -261,8 +346,8 @@ def write_counters(out_md, stats_csv, pmc_csvs, title, commands, cus=256, simds=
             fmt(bc is not None and lds and bc / lds * 100, "%.1f%%"),
             fmt(c.get("SQ_INSTS_LDS"), "%.3g")))
     text = ["# " + title, "",
-            "Commands (run from the repository root on one MI355X, after "
-            "`cd /tmp && export TMPDIR=/tmp`):", "", "```"] + commands + ["```", "",
+            "Commands (run from the repository root on one MI355X, with `TMPDIR=/tmp`):", "",
+            "```"] + commands + ["```", "",
             "Counter values are summed over a dispatch's instances and averaged over the dispatches "
             "of a kernel; durations are the averages of the kernel-trace run. bf16 GFLOP = "
             "SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512 (executed matrix-core work, padding included); "

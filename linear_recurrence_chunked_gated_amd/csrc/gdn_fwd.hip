@@ -988,4 +988,45 @@ hipError_t launch_copy_state(float* dst, const float* src, size_t n, hipStream_t
   hipLaunchKernelGGL(copy_state_kernel, dim3((unsigned)blocks), dim3(256), 0, st, dst, src, n);
   return hipGetLastError();
 }
+
+// ------------------------------------------------------------- casts -------
+// Eight elements per thread; n is a multiple of 8 (a whole number of rows of
+// width 64 or 128).  bf16 from fp32 rounds to nearest even.
+__global__ void cast_to_f32_kernel(float* dst, const bf16* src, size_t n8) {
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n8;
+       i += (size_t)gridDim.x * blockDim.x) {
+    const bf16x8 x = reinterpret_cast<const bf16x8*>(src)[i];
+    f32x4* d = reinterpret_cast<f32x4*>(dst) + 2 * i;
+    d[0] = f32x4{(float)x[0], (float)x[1], (float)x[2], (float)x[3]};
+    d[1] = f32x4{(float)x[4], (float)x[5], (float)x[6], (float)x[7]};
+  }
+}
+__global__ void cast_to_bf16_kernel(bf16* dst, const float* src, size_t n8) {
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n8;
+       i += (size_t)gridDim.x * blockDim.x) {
+    const f32x4 a = reinterpret_cast<const f32x4*>(src)[2 * i];
+    const f32x4 b = reinterpret_cast<const f32x4*>(src)[2 * i + 1];
+    reinterpret_cast<bf16x8*>(dst)[i] =
+        bf16x8{(bf16)a[0], (bf16)a[1], (bf16)a[2], (bf16)a[3],
+               (bf16)b[0], (bf16)b[1], (bf16)b[2], (bf16)b[3]};
+  }
+}
+static unsigned cast_blocks(size_t n8) {
+  size_t blocks = (n8 + 255) / 256;
+  return (unsigned)(blocks > 4096 ? 4096 : blocks);
+}
+hipError_t launch_cast_to_f32(float* dst, const void* src, size_t n, hipStream_t st) {
+  if (n == 0) return hipSuccess;
+  if (n % 8) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(cast_to_f32_kernel, dim3(cast_blocks(n / 8)), dim3(256), 0, st, dst,
+                     reinterpret_cast<const bf16*>(src), n / 8);
+  return hipGetLastError();
+}
+hipError_t launch_cast_to_bf16(void* dst, const float* src, size_t n, hipStream_t st) {
+  if (n == 0) return hipSuccess;
+  if (n % 8) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(cast_to_bf16_kernel, dim3(cast_blocks(n / 8)), dim3(256), 0, st,
+                     reinterpret_cast<bf16*>(dst), src, n / 8);
+  return hipGetLastError();
+}
 }  // namespace sfgdn

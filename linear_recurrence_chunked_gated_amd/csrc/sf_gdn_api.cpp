@@ -15,6 +15,9 @@
 
 namespace sfgdn {
 hipError_t launch_copy_state(float* dst, const float* src, size_t n, hipStream_t st);
+// n elements between bf16 and fp32 (n a multiple of 8)
+hipError_t launch_cast_to_f32(float* dst, const void* src, size_t n, hipStream_t st);
+hipError_t launch_cast_to_bf16(void* dst, const float* src, size_t n, hipStream_t st);
 }
 
 using namespace sfgdn;
@@ -35,6 +38,13 @@ struct Plan {
   int B, T, H, D, dtype;
   int nblk, L, P;
   size_t state_elem;  // bytes per stored per-block state element (bwd)
+  // A bf16 chunk of one block (T <= 64) runs on the fp32 kernels, on fp32
+  // copies of its token tensors in the workspace, and its outputs are rounded
+  // to bf16 at the end.  Such a chunk costs next to nothing either way, and
+  // in fp32 its gradients keep their accuracy where a one- or two-token
+  // chunk's gate gradients, single sums with heavy cancellation, lose it to
+  // the rounding of bf16 operands.
+  bool up;
 };
 
 sf_status make_plan(const sf_gdn_shape* s, Plan& p) {
@@ -88,6 +98,7 @@ sf_status make_plan(const sf_gdn_shape* s, Plan& p) {
   // per-block states and state gradients are stored in the operand type (the
   // precision in which they enter every product that reads them)
   p.state_elem = p.dtype == SF_DTYPE_BF16 ? 2 : 4;
+  p.up = p.dtype == SF_DTYPE_BF16 && p.nblk == 1;
   return SF_OK;
 }
 
@@ -99,16 +110,33 @@ size_t tw_buf(const Plan& p) {
   return align_up((size_t)p.B * p.H * p.nblk * BLK * BLK * elem(p));  // Tpp per block
 }
 size_t fwd_seg(const Plan& p) { return p.P > 1 ? 3 * seg_buf(p) : 0; }
-size_t fwd_ws(const Plan& p) { return fwd_seg(p) + tw_buf(p); }
+// The plan the kernels run (fp32 for an upcast chunk) and the size of one
+// fp32 copy of a token tensor.
+Plan kplan(const Plan& p) {
+  Plan k = p;
+  if (p.up) {
+    k.dtype = SF_DTYPE_F32;
+    k.state_elem = 4;
+    k.up = false;
+  }
+  return k;
+}
+size_t tok_f32(const Plan& p) { return align_up((size_t)p.B * p.T * p.H * p.D * 4); }
+// kernel workspaces of a plan (the kernels' dtype)
+size_t fwd_core(const Plan& p) { return fwd_seg(p) + tw_buf(p); }
 size_t blk_buf(const Plan& p) { return align_up((size_t)p.B * p.H * p.nblk * dd(p) * p.state_elem); }
 // per-block Vn of the state-storing forward: [B*H][nblk][64 x D] in the operand type
 size_t vn_buf(const Plan& p) { return align_up((size_t)p.B * p.H * p.nblk * BLK * p.D * elem(p)); }
 // the gradient kernel's global tile areas (fp32 at d = 128)
 size_t far_buf(const Plan& p) { return align_up(bwd_far_bytes(p.dtype == SF_DTYPE_F32, p.D)); }
-size_t bwd_ws(const Plan& p) {
+size_t bwd_core(const Plan& p) {
   if (p.P == 0) return 0;
   return 3 * seg_buf(p) + 3 * seg_buf(p) + 2 * blk_buf(p) + tw_buf(p) + vn_buf(p) + far_buf(p);
 }
+// caller workspaces: an upcast chunk adds fp32 copies of q, k, v, o (forward)
+// or q, k, v, dO, dq, dk, dv (backward) after the kernels' workspace
+size_t fwd_ws(const Plan& p) { return p.up ? fwd_core(kplan(p)) + 4 * tok_f32(p) : fwd_core(p); }
+size_t bwd_ws(const Plan& p) { return p.up ? bwd_core(kplan(p)) + 7 * tok_f32(p) : bwd_core(p); }
 
 struct Range {
   const void* p;
@@ -239,9 +267,11 @@ namespace {
 size_t saved_maps_off(const Plan& p) { return blk_buf(p); }
 size_t saved_tw_off(const Plan& p) { return blk_buf(p) + (p.P > 1 ? seg_buf(p) : 0); }
 size_t saved_vn_off(const Plan& p) { return saved_tw_off(p) + tw_buf(p); }
+// laid out for the kernels' plan (an upcast chunk saves fp32)
 size_t saved_bytes(const Plan& p) {
   if (p.P == 0) return 0;
-  return saved_vn_off(p) + vn_buf(p);
+  const Plan k = kplan(p);
+  return saved_vn_off(k) + vn_buf(k);
 }
 
 // Forward; with `saved` it also stores the per-block entry states, all
@@ -286,32 +316,52 @@ sf_status fwd_impl(const sf_gdn_shape* shape, const void* q, const void* k, cons
       }
       return SF_OK;
     }
-    FwdArgs a{};
-    a.q = q; a.k = k; a.v = v; a.alpha = alpha; a.beta = beta; a.S_in = S_in;
-    a.o = o; a.S_out = S_out;
-    a.B = p.B; a.T = p.T; a.H = p.H; a.nblk = p.nblk; a.L = p.L; a.P = p.P;
+    const Plan kp = kplan(p);
     char* ws = (char*)workspace;
+    const void *kq = q, *kk = k, *kv = v;
+    void* ko = o;
+    float* up = nullptr;  // fp32 copies of q, k, v, o (upcast chunk)
+    hipError_t e;
+    if (p.up) {
+      char* base = ws + fwd_core(kp);
+      float* c[4];
+      for (int i = 0; i < 4; ++i) c[i] = (float*)(base + i * tok_f32(p));
+      if (phase != PHASE_END) {
+        const void* src[3] = {q, k, v};
+        for (int i = 0; i < 3; ++i)
+          if ((e = launch_cast_to_f32(c[i], src[i], ntok * p.D, st)) != hipSuccess)
+            return hip_fail(e, "input cast");
+      }
+      kq = c[0]; kk = c[1]; kv = c[2]; ko = c[3];
+      up = c[3];
+    }
+    FwdArgs a{};
+    a.q = kq; a.k = kk; a.v = kv; a.alpha = alpha; a.beta = beta; a.S_in = S_in;
+    a.o = ko; a.S_out = S_out;
+    a.B = p.B; a.T = p.T; a.H = p.H; a.nblk = p.nblk; a.L = p.L; a.P = p.P;
     void* hsave = save ? saved : nullptr;
-    a.tw = save ? (char*)saved + saved_tw_off(p) : ws + fwd_seg(p);
-    a.vst = save ? (char*)saved + saved_vn_off(p) : nullptr;
+    a.tw = save ? (char*)saved + saved_tw_off(kp) : ws + fwd_seg(kp);
+    a.vst = save ? (char*)saved + saved_vn_off(kp) : nullptr;
     if (p.P > 1) {
       a.Mseg = (float*)ws;
-      a.MBseg = save ? (float*)((char*)saved + saved_maps_off(p)) : nullptr;
-      a.Nseg = (float*)(ws + seg_buf(p));
-      a.Sst = (float*)(ws + 2 * seg_buf(p));
+      a.MBseg = save ? (float*)((char*)saved + saved_maps_off(kp)) : nullptr;
+      a.Nseg = (float*)(ws + seg_buf(kp));
+      a.Sst = (float*)(ws + 2 * seg_buf(kp));
       a.sst_P = p.P;
     } else {
       a.Sst = S_in;
       a.sst_P = 1;
     }
-    hipError_t e;
-    if (p.dtype == SF_DTYPE_BF16)
+    if (kp.dtype == SF_DTYPE_BF16)
       e = (p.D == 128) ? launch_fwd<bf16, 128>(a, hsave, phase, st, prof)
                        : launch_fwd<bf16, 64>(a, hsave, phase, st, prof);
     else
       e = (p.D == 128) ? launch_fwd<float, 128>(a, hsave, phase, st, prof)
                        : launch_fwd<float, 64>(a, hsave, phase, st, prof);
     if (e != hipSuccess) return hip_fail(e, "forward launch");
+    if (up && phase != PHASE_BEGIN &&
+        (e = launch_cast_to_bf16(o, up, ntok * p.D, st)) != hipSuccess)
+      return hip_fail(e, "output cast");
     return SF_OK;
   });
 }
@@ -361,13 +411,32 @@ sf_status bwd_impl(const sf_gdn_shape* shape, const void* q, const void* k, cons
       }
       return SF_OK;
     }
+    const Plan kp = kplan(p);
+    char* ws = (char*)workspace;
+    const void *kq = q, *kk = k, *kv = v, *kdo = dO;
+    void *kdq = dq, *kdk = dk, *kdv = dv;
+    float* up = nullptr;  // fp32 copies of q, k, v, dO, dq, dk, dv (upcast chunk)
+    hipError_t e;
+    if (p.up) {
+      char* base = ws + bwd_core(kp);
+      float* c[7];
+      for (int i = 0; i < 7; ++i) c[i] = (float*)(base + i * tok_f32(p));
+      if (phase != PHASE_END) {
+        const void* src[4] = {q, k, v, dO};
+        for (int i = 0; i < 4; ++i)
+          if ((e = launch_cast_to_f32(c[i], src[i], ntok * p.D, st)) != hipSuccess)
+            return hip_fail(e, "input cast");
+      }
+      kq = c[0]; kk = c[1]; kv = c[2]; kdo = c[3];
+      kdq = c[4]; kdk = c[5]; kdv = c[6];
+      up = c[4];
+    }
     BwdArgs a{};
     FwdArgs& f = a.f;
-    f.q = q; f.k = k; f.v = v; f.alpha = alpha; f.beta = beta; f.S_in = S_in;
+    f.q = kq; f.k = kk; f.v = kv; f.alpha = alpha; f.beta = beta; f.S_in = S_in;
     f.o = nullptr; f.S_out = nullptr;
     f.B = p.B; f.T = p.T; f.H = p.H; f.nblk = p.nblk; f.L = p.L; f.P = p.P;
-    char* ws = (char*)workspace;
-    const size_t sb = seg_buf(p), bb = blk_buf(p);
+    const size_t sb = seg_buf(kp), bb = blk_buf(kp);
     f.Mseg = (float*)ws;
     f.Nseg = (float*)(ws + sb);
     f.Sst = (float*)(ws + 2 * sb);
@@ -377,20 +446,19 @@ sf_status bwd_impl(const sf_gdn_shape* shape, const void* q, const void* k, cons
     a.hst = ws + 5 * sb;
     a.dhst = ws + 5 * sb + bb;
     f.tw = ws + 5 * sb + 2 * bb;
-    f.MBseg = (float*)(ws + 5 * sb + 2 * bb + tw_buf(p));
-    f.vst = ws + 6 * sb + 2 * bb + tw_buf(p);
-    a.far = far_buf(p) ? ws + 6 * sb + 2 * bb + tw_buf(p) + vn_buf(p) : nullptr;
+    f.MBseg = (float*)(ws + 5 * sb + 2 * bb + tw_buf(kp));
+    f.vst = ws + 6 * sb + 2 * bb + tw_buf(kp);
+    a.far = far_buf(kp) ? ws + 6 * sb + 2 * bb + tw_buf(kp) + vn_buf(kp) : nullptr;
     if (use_saved) {
       char* sv = (char*)const_cast<void*>(saved);
       a.hst = sv;
-      if (p.P > 1) f.MBseg = (float*)(sv + saved_maps_off(p));
-      f.tw = sv + saved_tw_off(p);
-      f.vst = sv + saved_vn_off(p);
+      if (p.P > 1) f.MBseg = (float*)(sv + saved_maps_off(kp));
+      f.tw = sv + saved_tw_off(kp);
+      f.vst = sv + saved_vn_off(kp);
     }
-    a.dO = dO; a.dS_out = dS_out;
-    a.dq = dq; a.dk = dk; a.dv = dv; a.dalpha = dalpha; a.dbeta = dbeta; a.dS_in = dS_in;
-    hipError_t e;
-    if (p.dtype == SF_DTYPE_BF16)
+    a.dO = kdo; a.dS_out = dS_out;
+    a.dq = kdq; a.dk = kdk; a.dv = kdv; a.dalpha = dalpha; a.dbeta = dbeta; a.dS_in = dS_in;
+    if (kp.dtype == SF_DTYPE_BF16)
       e = (p.D == 128) ? launch_bwd<bf16, 128>(a, use_saved, phase, st, prof)
                        : launch_bwd<bf16, 64>(a, use_saved, phase, st, prof);
     else
@@ -398,6 +466,13 @@ sf_status bwd_impl(const sf_gdn_shape* shape, const void* q, const void* k, cons
                        : launch_bwd<float, 64>(a, use_saved, phase, st, prof);
     if (e == hipErrorNotSupported) return fail(SF_ERR_UNSUPPORTED, "backward not available");
     if (e != hipSuccess) return hip_fail(e, "backward launch");
+    if (up && phase != PHASE_BEGIN) {
+      void* dst[3] = {dq, dk, dv};
+      for (int i = 0; i < 3; ++i)
+        if ((e = launch_cast_to_bf16(dst[i], up + i * (tok_f32(p) / 4), ntok * p.D, st)) !=
+            hipSuccess)
+          return hip_fail(e, "output cast");
+    }
     return SF_OK;
   });
 }

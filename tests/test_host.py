@@ -144,6 +144,22 @@ def test_workspace_sizes():
     assert _lib.workspace_bytes(_shape(T=65536, H=16, seg=1)) > f
 
 
+@pytest.mark.parametrize("T,B,H,D", [(1, 1, 4, 128), (64, 2, 3, 64), (37, 1, 16, 128)])
+def test_one_block_bf16_chunk_sizes(T, B, H, D):
+    """A bf16 chunk of one 64-token block runs on the fp32 kernels: its saved
+    buffer is the fp32 chunk's, and its workspaces are the fp32 chunk's plus
+    fp32 copies of its token tensors (q, k, v, o forward; q, k, v, dO, dq,
+    dk, dv backward), each rounded up to 256 bytes.  Two blocks stay bf16."""
+    bf, f32 = _lib.Shape(B, T, H, D, D, 1, 0), _lib.Shape(B, T, H, D, D, 0, 0)
+    copy = -(-(B * T * H * D * 4) // 256) * 256
+    assert _lib.saved_bytes(bf) == _lib.saved_bytes(f32)
+    assert _lib.workspace_bytes(bf) == _lib.workspace_bytes(f32) + 4 * copy
+    assert _lib.workspace_bytes(bf, backward=True) == \
+        _lib.workspace_bytes(f32, backward=True) + 7 * copy
+    two = _lib.Shape(B, 65, H, D, D, 1, 0)
+    assert _lib.saved_bytes(two) < _lib.saved_bytes(_lib.Shape(B, 65, H, D, D, 0, 0))
+
+
 @pytest.mark.parametrize("T,N,alpha", [(262144, 8, 0.5), (262144, 8, 0.0), (262144, 8, 1.0),
                                        (131072, 4, 0.75), (65536, 16, 0.25)])
 def test_planner_matches_oracle_search(T, N, alpha):

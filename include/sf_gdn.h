@@ -45,7 +45,11 @@
  * Supported: Dk == Dv in {64, 128} for bf16 and for fp32; any T >= 0 (a
  * partial last 64-token block is handled in the kernels).  The backward
  * workspace of fp32 at d = 128 includes 256 global tile areas of 132 KiB for
- * the gradient kernel (its tiles do not fit LDS at that size).
+ * the gradient kernel (its tiles do not fit LDS at that size).  A bf16 chunk
+ * of one 64-token block (T <= 64) is computed by the fp32 kernels on fp32
+ * copies of its inputs, with o, dq, dk and dv rounded to bf16 at the end: its
+ * workspaces include those copies and its saved buffer has the fp32 layout
+ * (the workspace and saved-size queries account for both).
  */
 #ifndef SF_GDN_H
 #define SF_GDN_H

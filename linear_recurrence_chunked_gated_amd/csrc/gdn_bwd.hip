@@ -712,8 +712,11 @@ __device__ __forceinline__ void grads_block(const BwdArgs& a, int id, unsigned c
       if (r < nv) st4(dv + (size_t)r * rs + 16 * w + g4, acc[j][0], acc[j][1], acc[j][2], acc[j][3]);
     }
   }
-  bar();
-  // ---- F: dVn to LDS
+  // ---- F: dVn to LDS.  Where dVn takes the Tpp tile (fp32 at d = 64) every
+  // wave's reads of Tpp above come first; elsewhere its region is free, and
+  // the barrier below alone keeps phase G's writes of dPm behind the reads of
+  // P above.
+  if constexpr (Lz::DVN_IN_A) bar();
 #pragma unroll
   for (int i = 0; i < 4; ++i) store_tile_N(dvn[i], dVns, LDD, 16 * i, 16 * w);
   bar();

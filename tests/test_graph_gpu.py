@@ -54,10 +54,13 @@ def _outputs(buf):
     return [buf["o"], buf["states"][-1], buf["gst"][0]] + list(buf["grads"])
 
 
-def test_graph_replays_equal_eager():
+@pytest.mark.parametrize("dtype,lengths", [
+    ("bf16", [1024, 64, 1984, 960]),   # the 64-token chunk runs on the fp32 kernels
+    ("f32", [1024, 64, 4608]),         # fp32 at d = 128: the gradient kernel's global tile areas, reused (288 blocks)
+])
+def test_graph_replays_equal_eager(dtype, lengths):
     H, D = 4, 128
-    lengths = [1024, 64, 1984, 960]
-    d = to_dev(inputs(1, sum(lengths), H, D, "bf16", seed=31, grads=True, decay=0.01))
+    d = to_dev(inputs(1, sum(lengths), H, D, dtype, seed=31, grads=True, decay=0.01))
     buf = _chain_buffers(d, lengths, H, D)
     _step(d, lengths, buf)
     torch.cuda.synchronize()

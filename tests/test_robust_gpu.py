@@ -67,6 +67,27 @@ def test_backward_nan_stays_in_its_sequence(saved):
         _heads_equal(x, y, axis, 1)
 
 
+def test_backward_nan_stays_in_its_sequence_fp32_d128():
+    """fp32 at d = 128, whose gradient kernel keeps its input tiles in a
+    global area per workgroup and strides over the blocks (B * H * nblk =
+    384 blocks against 256 workgroups, so areas are reused): a NaN in one
+    sequence's dO reaches that sequence's gradients only, and the other
+    sequences' gradients are bit for bit those of the clean run."""
+    d = to_dev(inputs(2, 4000, 3, 128, "f32", seed=64, s_in_std=0.1, grads=True, decay=0.05))
+    fa = (d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["S_in"])
+    dO2 = d["dO"].clone()
+    b, t, h = 0, 2500, 1
+    dO2[b, t, h, 9] = float("nan")
+    g1 = gdn.chunk_bwd(*fa, d["dO"], d["dS_out"])
+    g2 = gdn.chunk_bwd(*fa, dO2, d["dS_out"])
+    torch.cuda.synchronize()
+    for name, x, y in zip(NAMES, g1, g2):
+        axis = 0 if name == "dS_in" else 1  # batch-major views: [B, H, ...] or [B, T, H, ...]
+        assert torch.isnan(y[b].select(axis, h)).any(), name
+        assert torch.equal(x[1 - b], y[1 - b]), name  # the other batch row
+        _heads_equal(x[b], y[b], axis, h)
+
+
 def test_chains_on_a_side_stream_equal_current_stream():
     """Chunk chains launched on a non-current stream, with the binding
     allocating workspaces and outputs itself, give the current-stream results

@@ -59,7 +59,8 @@ template <typename T, int D> struct FwdLds {
 
 // Fused out kernel, two blocks in flight: block b's state work reads K, W, P
 // and gates of buffer b % 2 while block b+1's state-free work fills the other
-// buffer.  Q, V, Tp, Tpp are single (consumed within one phase).
+// buffer.  Q, V and Tpp are single (consumed within one phase; the first half
+// of the T region is unused).
 template <typename T, int D> struct OutLds {
   static constexpr int LDD = D + Lay<T>::PAD;
   static constexpr int LDC = BLK + Lay<T>::PAD;
@@ -154,8 +155,9 @@ template <typename T, int D, bool WITH_Q> struct Prefetch {
 // ------------------------------------------------------------ Pre ----------
 // One workgroup of 4 waves per 64-token block, every block of every sequence
 // in parallel: gates, A = strict lower part of diag(beta) (K K^T o Gamma),
-// T = (I + A)^{-1} (fp32), then Tp = T diag(beta o gamma) and
-// Tpp = T diag(beta) in the operand type to tw[b*H + h][block][2][64][64].
+// T = (I + A)^{-1} (fp32), then Tpp = T diag(beta) in the operand type to
+// tw[b*H + h][block][64][64] (the kernels that form W = Tp K apply
+// Tp = Tpp diag(gamma) through K).
 template <typename T, int D>
 __global__ __launch_bounds__(256) void gdn_prep_kernel(FwdArgs a) {
   typedef PrepLds<T, D> Lz;
@@ -388,7 +390,7 @@ __global__ __launch_bounds__(64 * fwd_nw<D>(), 2) void gdn_fwd_out2_kernel(FwdAr
     pf.template fetch<decltype(part)::value>(q, k, v, al, bt, tw_block<T>(a.tw, a.nblk, bh, blk),
                                              rs, a.H, blk * BLK, min(BLK, a.T - blk * BLK));
   };
-  // State-free work of a block whose inputs sit in Q, K[n], V, Tp, Tpp and
+  // State-free work of a block whose inputs sit in Q, K[n], V, Tpp and
   // gates G[n]: P -> P[n], Wn -> W[n], U (registers).
   auto pre = [&](int n, f32x4 (&U)[NDV][4]) {
     if constexpr (OUT) block_scores<T, D, NW, true, false>(Qs, Kb(n), LDD, Gb(n), nullptr, 0, Pb(n), LDC);

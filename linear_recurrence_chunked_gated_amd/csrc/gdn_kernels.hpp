@@ -125,10 +125,12 @@ hipError_t launch_prep(const FwdArgs& a, hipStream_t st, Profiler* prof);
 template <int D, bool REV>
 hipError_t launch_chain(const ChainArgs& c, hipStream_t st, Profiler* prof);
 template <typename T, int D>
+// Every block's entry state into hst and its Vn into a.vst.
 hipError_t launch_states(const FwdArgs& a, void* hst, hipStream_t st, Profiler* prof);
 // saved: a.hst already holds every block's entry state, a.f.MBseg every
-// segment's map and a.f.tw every block's Tp, Tpp (from a saving forward), so
-// the forward recompute is skipped.
+// segment's map, a.f.tw every block's Tpp and a.f.vst every block's Vn (from
+// a saving forward), so the forward recompute is skipped; otherwise the
+// recompute writes the entry states and Vn into a.hst and a.f.vst.
 // phase: PHASE_BEGIN and PHASE_END only with saved.
 template <typename T, int D>
 hipError_t launch_bwd(const BwdArgs& a, bool saved, int phase, hipStream_t st, Profiler* prof);

@@ -337,3 +337,19 @@ def test_one_block_bf16_runs_fp32(oracle_mod, T, D, saved):
     for name, g, r, ax in zip(NAMES, got, ref, HEAD_AXIS):
         tol = 4e-3 if name in ("dq", "dk", "dv") else TOL["f32"]
         assert_close(name, g, r, tol, head_axis=ax)
+
+def test_one_block_bf16_two_batches(oracle_mod):
+    """The same with B = 2, three heads and a ragged block (37 tokens), d = 64,
+    recompute path, and S_in ~ N(0, 0.1) with slow decay."""
+    d = inputs(2, 37, 3, 64, "bf16", seed=9300, s_in_std=0.1, grads=True, decay=0.01)
+    dd = to_dev(d)
+    fa = (dd["q"], dd["k"], dd["v"], dd["alpha"], dd["beta"], dd["S_in"])
+    o, S = gdn.chunk_fwd(*fa)
+    g = gdn.chunk_bwd(*fa, dd["dO"], dd["dS_out"])
+    torch.cuda.synchronize()
+    o_ref, S_ref = oracle_mod.gdn_fwd(*oracle_args(d))
+    assert_close("o", f64(o), o_ref, 4e-3, head_axis=2)
+    assert_close("S_out", f64(S), S_ref, TOL["f32"], head_axis=1)
+    for name, x, r, ax in zip(NAMES, g, oracle_bwd(oracle_mod, d), HEAD_AXIS):
+        assert_close(name, f64(x), r, 4e-3 if name in ("dq", "dk", "dv") else TOL["f32"],
+                     head_axis=ax)

@@ -35,6 +35,7 @@ PEAK_F32_TFLOPS = 157.3       # MI355X fp32 MFMA / vector
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 
 C = 64  # kernel block
+DEFAULT_WORKLOAD = "fwdbwd_h16_t262144_d128_8skew"
 
 
 def kernel_flops_per_block(name, d):
@@ -103,8 +104,9 @@ def source_hash():
     return h.hexdigest()[:16]
 
 
-def load_traffic(kernel):
-    """HBM bytes per launch of `kernel` recorded from rocprofv3 counter runs
+def load_traffic(kernel, wl_name=None):
+    """HBM bytes per launch of `kernel` in workload wl_name (the benchmark
+    workload when None) recorded from rocprofv3 counter runs
     (profiles/traffic.json), or None when absent or taken on other sources."""
     p = os.path.join(HERE, "profiles", "traffic.json")
     if not os.path.exists(p):
@@ -113,6 +115,8 @@ def load_traffic(kernel):
         rec = json.load(f)
     if rec.get("source_hash") != source_hash():
         return None
+    if wl_name is not None and wl_name != DEFAULT_WORKLOAD:
+        rec = rec.get("workloads", {}).get(wl_name, {})
     k = rec.get("kernels", {}).get(kernel)
     return None if k is None else k.get("bytes_per_launch")
 
@@ -162,10 +166,15 @@ def kernel_label(name):
     return base
 
 
-def write_traffic(fetch_csv, write_csv, calib_fetch_csv, calib_write_csv, calib_bytes):
-    """HBM bytes per launch of every library kernel from FETCH_SIZE and
-    WRITE_SIZE (KiB per dispatch), each scaled by what the same counter reads
-    for a plain device copy of calib_bytes."""
+def write_traffic(fetch_csv, write_csv, calib_fetch_csv, calib_write_csv, calib_bytes,
+                  wl_name=None, stats_csv=None):
+    """HBM bytes per launch of every library kernel of workload wl_name (the
+    benchmark workload when None) from FETCH_SIZE and WRITE_SIZE (KiB per
+    dispatch), each scaled by what the same counter reads for a plain device
+    copy of calib_bytes, into profiles/traffic.json and a table under
+    profiles/ (with each kernel's achieved rate when the kernel-trace
+    statistics of the same workload are given)."""
+    wl_name = wl_name or DEFAULT_WORKLOAD
     fetch = _read_counter_csv(fetch_csv)
     write = _read_counter_csv(write_csv)
     cf = _read_counter_csv(calib_fetch_csv)
@@ -174,24 +183,35 @@ def write_traffic(fetch_csv, write_csv, calib_fetch_csv, calib_write_csv, calib_
     copy_w = max(cw.values())
     sf = calib_bytes / (copy_f * 1024.0)
     sw = calib_bytes / (copy_w * 1024.0)
-    import re
-    out = {"source_hash": source_hash(),
-           "calibration": {"copy_bytes_each_way": calib_bytes,
-                           "fetch_kib_per_copy": copy_f, "write_kib_per_copy": copy_w,
-                           "fetch_scale": sf, "write_scale": sw},
-           "kernels": {}}
+    kernels = {}
     for name in sorted(set(fetch) | set(write)):
         short = kernel_label(name)
         if short is None:
             continue
         fb = fetch.get(name, 0.0) * 1024.0 * sf
         wb = write.get(name, 0.0) * 1024.0 * sw
-        out["kernels"][short] = {"fetch_bytes": fb, "write_bytes": wb, "bytes_per_launch": fb + wb}
+        kernels[short] = {"fetch_bytes": fb, "write_bytes": wb, "bytes_per_launch": fb + wb}
+    calib = {"copy_bytes_each_way": calib_bytes, "fetch_kib_per_copy": copy_f,
+             "write_kib_per_copy": copy_w, "fetch_scale": sf, "write_scale": sw}
     path = os.path.join(HERE, "profiles", "traffic.json")
+    rec = {}
+    if os.path.exists(path):
+        with open(path) as f:
+            rec = json.load(f)
+    if rec.get("source_hash") != source_hash():
+        rec = {"source_hash": source_hash()}
+    if wl_name == DEFAULT_WORKLOAD:
+        rec["calibration"] = calib
+        rec["kernels"] = kernels
+    else:
+        rec.setdefault("workloads", {})[wl_name] = {"calibration": calib, "kernels": kernels}
     with open(path, "w") as f:
-        json.dump(out, f, indent=1)
-    print(json.dumps(out, indent=1))
-    _write_traffic_md(out, os.path.join(HERE, "profiles", "traffic_fwdbwd_h16_t262144_d128.md"))
+        json.dump(rec, f, indent=1)
+    print(json.dumps(rec, indent=1))
+    stats = _read_stats_csv(stats_csv) if stats_csv else None
+    _write_traffic_md(kernels, calib, rec["source_hash"], wl_name, stats,
+                      [fetch_csv, write_csv, calib_fetch_csv, calib_write_csv] +
+                      ([stats_csv] if stats_csv else []))
 
 
 # Bytes per 64-token block that a kernel moves of the method's own tensors
@@ -211,69 +231,96 @@ def method_bytes_per_block(name, d, elem=2):
             }.get(name, 0)
 
 
-def _write_traffic_md(tr, path):
-    """The traffic table of the benchmark workload (8 skewed chunks, H = 16,
-    d = 128, saving forward and saved backward): per launch, the counters'
-    bytes split into the method's tensors and this design's intermediates,
-    and per step (one launch of each kernel per chunk)."""
+def _traffic_blocks(wl_name):
+    """Blocks (of 64 tokens, one head) that one launch of each kernel covers in
+    workload wl_name, averaged over its chunks, and the number of chunks."""
     from linear_recurrence_chunked_gated_amd import _lib
     import torch
-    wl = workload("fwdbwd_h16_t262144_d128_8skew")
-    H, d, chunks = wl["H"], wl["D"], wl["chunks"]
+    wl = workload(wl_name)
+    H, d, chunks, save = wl["H"], wl["D"], wl["chunks"], wl["bwd"]
     nch = len(chunks)
     blocks = {}
     for n in chunks:
         L, P = _lib.segment_plan(_lib.make_shape(1, n, H, d, d, torch.bfloat16, 0))
         nb = (n + C - 1) // C
-        for k in ("gdn_prep", "gdn_fwd_summary", "gdn_fwd_out_save", "gdn_bwd_dscan",
-                  "gdn_bwd_grads"):
-            blocks[k] = blocks.get(k, 0) + H * nb / nch
-        blocks["gdn_bwd_dscan_summary"] = (blocks.get("gdn_bwd_dscan_summary", 0)
-                                           + H * max(nb - min(L, nb), 0) / nch)
+        last = nb - (P - 1) * L  # blocks of the last segment
+        per = {"gdn_prep": nb, "gdn_bwd_dscan": nb, "gdn_bwd_grads": nb,
+               "gdn_fwd_out_save" if save else "gdn_fwd_out": nb,
+               # the saving forward maps every segment, the plain one all but the last
+               "gdn_fwd_summary": nb if save else (nb - last if P > 1 else 0),
+               # the reverse maps skip the first segment
+               "gdn_bwd_dscan_summary": max(nb - min(L, nb), 0)}
+        for k, v in per.items():
+            if k.startswith("gdn_bwd") and not wl["bwd"]:
+                continue
+            blocks[k] = blocks.get(k, 0) + H * v / nch
+    return blocks, nch
+
+
+def _write_traffic_md(kernels, calib, src_hash, wl_name, stats, csvs):
+    """The traffic table of a workload: per launch, the counters' bytes split
+    into the method's tensors and this design's intermediates, the achieved
+    rate (when kernel times are given), and per step (one launch of each
+    kernel per chunk)."""
+    wl = workload(wl_name)
+    H, d, bwd = wl["H"], wl["D"], wl["bwd"]
+    blocks, nch = _traffic_blocks(wl_name)
+    by_th = 2840 if bwd else 1032  # algorithmic bytes per token-head (bf16, d = 128)
     rows, tot_step, meth_step = [], 0.0, 0.0
-    for k, v in sorted(tr["kernels"].items(), key=lambda kv: -kv[1]["bytes_per_launch"]):
+    for k, v in sorted(kernels.items(), key=lambda kv: -kv[1]["bytes_per_launch"]):
         m = method_bytes_per_block(k, d) * blocks.get(k, 0)
         t = v["bytes_per_launch"]
         tot_step += t * nch
         meth_step += m * nch
-        rows.append("| %s | %.1f | %.1f | %.1f | %.1f | %.1f | %.2f |" % (
+        rate = ""
+        if stats and k in stats:
+            rate = " | %.1f | %.2f" % (stats[k], t / (stats[k] * 1e-6) / 1e12)
+        elif stats:
+            rate = " | | "
+        rows.append("| %s | %.1f | %.1f | %.1f | %.1f | %.1f%s | %.2f |" % (
             k, v["fetch_bytes"] / 1e6, v["write_bytes"] / 1e6, t / 1e6, m / 1e6, (t - m) / 1e6,
-            t * nch / 1e9))
-    algo = wl["T"] * H * (2840)  # fwd+bwd algorithmic bytes per token-head (bf16, d = 128)
-    c = tr["calibration"]
-    cmds = ["rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/tr_fetch -o tr_fetch -- "
-            "python -u bench.py --steps 1 --warmup 1 --no-cpu-baseline",
-            "rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/tr_write -o tr_write -- "
-            "python -u bench.py --steps 1 --warmup 1 --no-cpu-baseline",
+            rate, t * nch / 1e9))
+    algo = wl["T"] * H * by_th
+    wl_arg = "" if wl_name == DEFAULT_WORKLOAD else " --workload " + wl_name
+    tag = "fwdbwd" if bwd else "fwd"
+    cmds = ["rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/tr_%s_fetch -o fetch -- "
+            "python -u bench.py%s --steps 1 --warmup 1 --no-cpu-baseline" % (tag, wl_arg),
+            "rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/tr_%s_write -o write -- "
+            "python -u bench.py%s --steps 1 --warmup 1 --no-cpu-baseline" % (tag, wl_arg),
             "rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/tr_cfetch -o tr_cfetch -- "
             "python -u bench.py --copy-calibration",
             "rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/tr_cwrite -o tr_cwrite -- "
             "python -u bench.py --copy-calibration",
-            "python bench.py --write-traffic gpurun_out/tr_fetch/tr_fetch_counter_collection.csv "
-            "gpurun_out/tr_write/tr_write_counter_collection.csv "
-            "gpurun_out/tr_cfetch/tr_cfetch_counter_collection.csv "
-            "gpurun_out/tr_cwrite/tr_cwrite_counter_collection.csv"]
-    text = ["# HBM traffic per launch: chained fwd+bwd, T=262144, H=16, d=128, bf16, 8 skewed chunks",
+            "python bench.py --write-traffic " + " ".join(csvs[:4]) + " " + wl_name
+            + (" " + csvs[4] if len(csvs) > 4 else "")]
+    head = ("| kernel | fetch (MB) | write (MB) | total (MB) | method tensors (MB) | "
+            "intermediates (MB) |" + (" avg (us) | TB/s |" if stats else "") + " per step (GB) |")
+    sep = "|---|---:|---:|---:|---:|---:|" + ("---:|---:|" if stats else "") + "---:|"
+    text = ["# HBM traffic per launch: %s" % wl["desc"],
             "", "Commands (run from the repository root on one MI355X, with `TMPDIR=/tmp`), one "
             "counter per pass:", "", "```"] + cmds + ["```", "",
             "Calibration: a plain 1 GiB device copy (torch `copy_`) reads FETCH_SIZE = %.0f KiB and "
             "WRITE_SIZE = %.0f KiB, so fetch counts are scaled by %.4f and write counts by %.4f."
-            % (c["fetch_kib_per_copy"], c["write_kib_per_copy"], c["fetch_scale"], c["write_scale"]),
-            "", "Bytes are per launch, averaged over every launch of the run (8 chunk sizes; the "
-            "warm-up step, the captured step's replays and the eager step). \"method tensors\" is "
-            "what a kernel moves of q, k, v, dO, o, dq, dk, dv and the gates, counted each time a "
-            "kernel moves them (`method_bytes_per_block` in `bench.py`, times the blocks one launch "
-            "covers); \"intermediates\" is the rest: this design's Tpp, per-block states, V^new, "
-            "state gradients and segment maps (and any re-read). `profiles/traffic.json` holds the "
-            "same figures with the hash of the kernel sources they were taken on; `bench.py` reports "
-            "`roofline.traffic` only while that hash matches.", "",
-            "| kernel | fetch (MB) | write (MB) | total (MB) | method tensors (MB) | "
-            "intermediates (MB) | per step (GB) |",
-            "|---|---:|---:|---:|---:|---:|---:|"] + rows + ["",
-            "Per step: %.1f GB, of which %.1f GB are the method's tensors and %.1f GB intermediates, "
-            "against %.2f GB of algorithmic bytes (each tensor moved once: 2,840 B per token-head); "
+            % (calib["fetch_kib_per_copy"], calib["write_kib_per_copy"], calib["fetch_scale"],
+               calib["write_scale"]),
+            "", "Bytes are per launch, averaged over every launch of the run (the warm-up step, the "
+            "captured step's replays and the eager step, over every chunk size). \"method "
+            "tensors\" is what a kernel moves of q, k, v, dO, o, dq, dk, dv and the gates, counted "
+            "each time a kernel moves them (`method_bytes_per_block` in `bench.py`, times the "
+            "blocks one launch covers); \"intermediates\" is the rest: this design's Tpp, per-block "
+            "states, V^new, state gradients and segment maps (and any re-read)."
+            + (" \"avg\" is the kernel's average duration in the kernel trace of the same "
+               "workload (the `--stats` summary given last on the `--write-traffic` line) and "
+               "TB/s the counted bytes over it; a plain device copy reaches 4.7-5.4 TB/s on this "
+               "part." if stats else "")
+            + " `profiles/traffic.json` holds the same bytes with the hash of the kernel sources "
+            "they were taken on; `bench.py` reports `roofline.traffic` only while that hash "
+            "matches.", "", head, sep] + rows + ["",
+            "Per step: %.2f GB, of which %.2f GB are the method's tensors and %.2f GB intermediates, "
+            "against %.2f GB of algorithmic bytes (each tensor moved once: %s B per token-head); "
             "%.2fx." % (tot_step / 1e9, meth_step / 1e9, (tot_step - meth_step) / 1e9, algo / 1e9,
-                        tot_step / algo), "", "Source hash: `%s`." % tr["source_hash"]]
+                        "{:,}".format(by_th), tot_step / algo), "", "Source hash: `%s`." % src_hash]
+    path = os.path.join(HERE, "profiles", "traffic_%s.md" % wl_file_tag(wl_name))
     with open(path, "w") as f:
         f.write("\n".join(text) + "\n")
 
@@ -373,6 +420,11 @@ def copy_calibration(nbytes=1 << 30, reps=4):
         dst.copy_(src)
     torch.cuda.synchronize()
     print(json.dumps({"copy_bytes_each_way": nbytes, "reps": reps}))
+
+
+def wl_file_tag(name):
+    """The workload part of a profile's file name."""
+    return "fwdbwd_h16_t262144_d128" if name == DEFAULT_WORKLOAD else name
 
 
 def workload(name):
@@ -574,7 +626,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=2)
-    ap.add_argument("--workload", default="fwdbwd_h16_t262144_d128_8skew",
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD,
                     help="fwdbwd_h16_t262144_d128_8skew (default), fwdbwd_h16_t16384_d128, "
                          "fwd_h16_t65536_d128, fwd_h32_t65536_d128, fwd_h16_t8192_d128_8x1024, or "
                          "conv_qkv_h16_t262144_d128_8skew (the short convolution)")
@@ -602,12 +654,17 @@ def main():
     ap.add_argument("--write-counters", nargs="+", metavar="ARG",
                     help="OUT_MD TITLE STATS_CSV PMC_CSV... [CMD COMMAND...]: per-kernel counter "
                          "table from rocprofv3 runs")
-    ap.add_argument("--write-traffic", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "CALIB_FETCH_CSV",
-                                                         "CALIB_WRITE_CSV"),
-                    help="turn rocprofv3 FETCH_SIZE/WRITE_SIZE runs into profiles/traffic.json")
+    ap.add_argument("--write-traffic", nargs="+", metavar="ARG",
+                    help="FETCH_CSV WRITE_CSV CALIB_FETCH_CSV CALIB_WRITE_CSV [WORKLOAD "
+                         "[STATS_CSV]]: turn rocprofv3 FETCH_SIZE/WRITE_SIZE runs into "
+                         "profiles/traffic.json and a table under profiles/")
     args = ap.parse_args()
     if args.write_traffic:
-        write_traffic(*args.write_traffic, calib_bytes=1 << 30)
+        a = args.write_traffic
+        if len(a) not in (4, 5, 6):
+            ap.error("--write-traffic takes 4 to 6 arguments")
+        write_traffic(*a[:4], calib_bytes=1 << 30, wl_name=a[4] if len(a) > 4 else None,
+                      stats_csv=a[5] if len(a) > 5 else None)
         return
     if args.write_counters:
         a = args.write_counters
@@ -800,7 +857,7 @@ def main():
             main, other = hbm, mfma
         else:
             main, other = mfma, hbm
-        roofline = dict(kernel=dom, **main, traffic=load_traffic(dom),
+        roofline = dict(kernel=dom, **main, traffic=load_traffic(dom, args.workload),
                         flops_per_launch=per_launch,
                         bytes_per_launch=None if hbm is None else by, other=other)
     # Whole-path roofline: algorithmic flops and bytes per token-head of the

@@ -42,13 +42,8 @@ __device__ __forceinline__ GateLds gate_lds(unsigned char* base) {
 // rows past the end of the sequence, which then leave the state unchanged).
 __device__ __forceinline__ void block_gates(float la, float be, const GateLds& G) {
   const int lane = lane_id();
-  float x = la;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const float y = __shfl_up(x, off, 64);
-    if (lane >= off) x += y;
-  }
-  const float gC = __shfl(x, 63, 64);
+  const float x = wave_prefix_sum(la);
+  const float gC = lane_f(x, 63);
   const float gm = __expf(x);
   G.g[lane] = x;
   G.gam[lane] = gm;
@@ -348,6 +343,79 @@ __device__ __forceinline__ void block_s_yT(const f32x4 (&St)[NDV][D / 16], const
       const auto a = AccFrag<T>::get(St[b], s);
 #pragma unroll
       for (int j = 0; j < 4; ++j) acc[b][j] = Mma<T>::mma(a, bq[j], acc[b][j]);
+    }
+  }
+}
+
+// z[b][i] (m = s-tile i, n = dv-tile b) += K[s][:] . S[dv][:] and
+// o[b][j] (m = dv-tile b, n = r-tile j) += S[dv][:] . Q[r][:], the state's
+// operand fragments shared by both products.
+template <typename T, int D, int NDV, bool WITH_Q = true>
+__device__ __forceinline__ void block_s_kq(const f32x4 (&St)[NDV][D / 16], const T* Ks,
+                                           const T* Qs, int ldd, f32x4 (&z)[NDV][4],
+                                           f32x4 (&o)[NDV][4]) {
+#pragma unroll
+  for (int s = 0; s < D / Mma<T>::KSTEP; ++s) {
+    typename Mma<T>::frag fk[4], fq[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      fk[i] = frag_row<T, PERM>(Ks + 16 * i * ldd, ldd, s);
+      if constexpr (WITH_Q) fq[i] = frag_row<T, PERM>(Qs + 16 * i * ldd, ldd, s);
+    }
+#pragma unroll
+    for (int b = 0; b < NDV; ++b) {
+      const auto bs = AccFrag<T>::get(St[b], s);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        z[b][i] = Mma<T>::mma(fk[i], bs, z[b][i]);
+        if constexpr (WITH_Q) o[b][i] = Mma<T>::mma(bs, fq[i], o[b][i]);
+      }
+    }
+  }
+}
+
+// Element (m = 4g + e, n = i) of the 16 x 16 tile at rows r0.., columns c0..
+// of a row-major LDS tile, in an accumulator's lane layout.
+template <typename T>
+__device__ __forceinline__ f32x4 tile_acc_layout(const T* p, int ld, int r0, int c0);
+template <>
+__device__ __forceinline__ f32x4 tile_acc_layout<bf16>(const bf16* p, int ld, int r0, int c0) {
+  const bf16x4 x = tr_rows4(p + c0, ld, r0 + 4 * (lane_id() >> 4));
+  return f32x4{(float)x[0], (float)x[1], (float)x[2], (float)x[3]};
+}
+template <>
+__device__ __forceinline__ f32x4 tile_acc_layout<float>(const float* p, int ld, int r0, int c0) {
+  const int l = lane_id(), m = r0 + 4 * (l >> 4), n = c0 + (l & 15);
+  return f32x4{p[m * ld + n], p[(m + 1) * ld + n], p[(m + 2) * ld + n], p[(m + 3) * ld + n]};
+}
+
+// Vn = Tpp (V - diag(gamma) Z) for this wave's dv-tiles, Z = K S^T from
+// block_s_kq (m = s, n = dv): X = V - gamma Z in registers, then the product
+// with Tpp rows read in the accumulators' k order.
+template <typename T, int NDV>
+__device__ __forceinline__ void block_vn_from_z(const T* Tpp, int ldc, const T* Vs, int ldd,
+                                                int dv0, const float* gam, f32x4 (&z)[NDV][4],
+                                                f32x4 (&vn)[NDV][4]) {
+  const int g4 = 4 * (lane_id() >> 4);
+#pragma unroll
+  for (int b = 0; b < NDV; ++b)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const f32x4 v = tile_acc_layout<T>(Vs, ldd, 16 * i, 16 * (dv0 + b));
+#pragma unroll
+      for (int e = 0; e < 4; ++e) z[b][i][e] = v[e] - gam[16 * i + g4 + e] * z[b][i][e];
+      vn[b][i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+  for (int s = 0; s < BLK / Mma<T>::KSTEP; ++s) {
+    typename Mma<T>::frag bx[NDV];
+#pragma unroll
+    for (int b = 0; b < NDV; ++b) bx[b] = AccFrag<T>::get(z[b], s);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const auto a = frag_row<T, PERM>(Tpp + 16 * i * ldc, ldc, s);
+#pragma unroll
+      for (int b = 0; b < NDV; ++b) vn[b][i] = Mma<T>::mma(a, bx[b], vn[b][i]);
     }
   }
 }

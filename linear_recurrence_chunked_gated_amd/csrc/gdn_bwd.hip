@@ -399,29 +399,6 @@ static hipError_t launch_dscan(const BwdArgs& a, int seg0, int nseg, const float
 // Sums of a 16x16 accumulator tile C[m][n] (lane: m = 4 g + e, n = i):
 // over n for each m (result valid in lanes with i == 0, element e), and over
 // m for each n (result valid in lanes 0..15).
-// Cross-lane sums without an LDS round trip: DPP within a 16-lane row, and
-// the gfx950 lane swaps (v_permlane16/32_swap) across rows.  Every lane of a
-// group ends with the same total.
-template <int CTRL>
-__device__ __forceinline__ float dpp_f(float x) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
-}
-// sum over the 16 lanes of a row (quad_perm [1,0,3,2], [2,3,0,1], half-row
-// mirror, row mirror)
-__device__ __forceinline__ float sum_row16(float x) {
-  x += dpp_f<0xB1>(x);
-  x += dpp_f<0x4E>(x);
-  x += dpp_f<0x141>(x);
-  x += dpp_f<0x140>(x);
-  return x;
-}
-// sum over the 4 rows (lanes l, l^16, l^32, l^48)
-__device__ __forceinline__ float sum_rows4(float x) {
-  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
-  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
-}
 __device__ __forceinline__ f32x4 tile_sum_over_n(f32x4 v) {
 #pragma unroll
   for (int e = 0; e < 4; ++e) v[e] = sum_row16(v[e]);
@@ -674,9 +651,7 @@ __device__ __forceinline__ void grads_block(const BwdArgs& a, int id, unsigned c
     f32x4 p = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int aa = 0; aa < DKT; ++aa) p += Sx[aa] * dSx[aa];
-    float x = (p[0] + p[1]) + (p[2] + p[3]);
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) x += __shfl_xor(x, off, 64);
+    const float x = wave_sum((p[0] + p[1]) + (p[2] + p[3]));
     if (lane == 0) dgc[w] = x;
   }
   // dVn = P^T dO + D (K dS'^T)
@@ -1019,18 +994,10 @@ __device__ __forceinline__ void grads_block(const BwdArgs& a, int id, unsigned c
     }
     const float dj = G.dec[j] * dd;
     dg -= dj;
-    float tot = dj;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) tot += __shfl_xor(tot, off, 64);
-    const float dgC = tot + G.gC[0] * gcs;
+    const float dgC = wave_sum(dj) + G.gC[0] * gcs;
     if (j == BLK - 1) dg += dgC;
     // reverse inclusive cumsum over the block: dlog alpha_j = sum_{r >= j} dg_r
-    float x = dg;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const float y = __shfl_down(x, off, 64);
-      if (j + off < 64) x += y;
-    }
+    const float x = wave_suffix_sum(dg);
     if (j < nv) {
       const size_t idx = gofs + (size_t)j * f.H;
       a.dalpha[idx] = x / ra;

@@ -60,6 +60,57 @@ __device__ __forceinline__ void full_barrier() {
 }
 __device__ __forceinline__ void vm_wait() { __asm__ __volatile__("s_waitcnt vmcnt(0)" ::: "memory"); }
 
+// Cross-lane sums without an LDS round trip: DPP within a 16-lane row, and
+// across rows the gfx950 lane swaps (v_permlane16/32_swap) or lane reads.
+// dpp_f: lanes whose DPP source lies outside their row receive 0.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float lane_f(float x, int l) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), l));
+}
+// sum over the 16 lanes of a row (quad_perm [1,0,3,2], [2,3,0,1], half-row
+// mirror, row mirror); every lane of the row ends with the total
+__device__ __forceinline__ float sum_row16(float x) {
+  x += dpp_f<0xB1>(x);
+  x += dpp_f<0x4E>(x);
+  x += dpp_f<0x141>(x);
+  x += dpp_f<0x140>(x);
+  return x;
+}
+// sum over the 4 rows (lanes l, l^16, l^32, l^48)
+__device__ __forceinline__ float sum_rows4(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+// sum over the 64 lanes of the wave, in every lane
+__device__ __forceinline__ float wave_sum(float x) { return sum_rows4(sum_row16(x)); }
+// Inclusive prefix sum over lanes 0..l: row shifts right by 1, 2, 4, 8 within
+// each row, then the totals of the rows below (lanes 15, 31, 47).
+__device__ __forceinline__ float wave_prefix_sum(float x) {
+  x += dpp_f<0x111>(x);
+  x += dpp_f<0x112>(x);
+  x += dpp_f<0x114>(x);
+  x += dpp_f<0x118>(x);
+  const float r0 = lane_f(x, 15), r1 = lane_f(x, 31), r2 = lane_f(x, 47);
+  const int row = lane_id() >> 4;
+  return x + (row == 0 ? 0.f : row == 1 ? r0 : row == 2 ? r0 + r1 : (r0 + r1) + r2);
+}
+// Inclusive suffix sum over lanes l..63: row shifts left by 1, 2, 4, 8, then
+// the totals of the rows above (lanes 16, 32, 48).
+__device__ __forceinline__ float wave_suffix_sum(float x) {
+  x += dpp_f<0x101>(x);
+  x += dpp_f<0x102>(x);
+  x += dpp_f<0x104>(x);
+  x += dpp_f<0x108>(x);
+  const float r1 = lane_f(x, 16), r2 = lane_f(x, 32), r3 = lane_f(x, 48);
+  const int row = lane_id() >> 4;
+  return x + (row == 3 ? 0.f : row == 2 ? r3 : row == 1 ? r2 + r3 : r1 + (r2 + r3));
+}
+
 enum KOrder { STD = 0, PERM = 1 };
 
 template <typename T> struct Mma;

@@ -57,21 +57,21 @@ template <typename T, int D> struct FwdLds {
                                    oQ % 4096 == 0 && oP % 4096 == 0), "swizzled tiles 4 KiB aligned");
 };
 
-// Fused out kernel, two blocks in flight: block b's state work reads K, W, P
-// and gates of buffer b % 2 while block b+1's state-free work fills the other
-// buffer.  Q, V and Tpp are single (consumed within one phase; the first half
-// of the T region is unused).
+// Fused out kernel, two blocks in flight: block b's state work (O += Vn^T P^T
+// and the state update) reads K, P and gates of buffer b % 2 while block b+1
+// forms P, S Q^T and Vn from the other buffer.  Q, V and Tpp are single: they
+// are consumed in the iteration that stages them.
 template <typename T, int D> struct OutLds {
   static constexpr int LDD = D + Lay<T>::PAD;
   static constexpr int LDC = BLK + Lay<T>::PAD;
   static constexpr size_t rowD = (size_t)BLK * LDD * sizeof(T);
   static constexpr size_t sq = (size_t)BLK * LDC * sizeof(T);
-  static constexpr size_t oQ = 0, oV = oQ + rowD, oT = oV + rowD, oK = oT + 2 * sq,
-                          oW = oK + 2 * rowD, oP = oW + 2 * rowD, oG = oP + 2 * sq;
+  static constexpr size_t oQ = 0, oV = oQ + rowD, oT = oV + rowD, oK = oT + sq,
+                          oP = oK + 2 * rowD, oG = oP + 2 * sq;
   static constexpr size_t bytes = oG + 2 * kGateBytes;
   static constexpr bool fits = bytes <= 160 * 1024;
   static_assert(sizeof(T) != 2 || (oV % 4096 == 0 && oT % 4096 == 0 && oK % 4096 == 0 &&
-                                   oW % 4096 == 0 && oP % 4096 == 0), "swizzled tiles 4 KiB aligned");
+                                   oP % 4096 == 0), "swizzled tiles 4 KiB aligned");
 };
 
 // Pre kernel: RK K -> Tm (fp32 T, solve scratch; K is dead once A is formed)
@@ -346,11 +346,9 @@ __global__ __launch_bounds__(64 * fwd_nw<D>(), 2) void gdn_fwd_out2_kernel(FwdAr
   extern __shared__ __align__(16) unsigned char smem[];
   T* Qs = reinterpret_cast<T*>(smem + Lz::oQ);
   T* Vs = reinterpret_cast<T*>(smem + Lz::oV);
-  T* Tp = reinterpret_cast<T*>(smem + Lz::oT);
-  T* Tpp = Tp + BLK * LDC;
+  T* Tpp = reinterpret_cast<T*>(smem + Lz::oT);
   // double buffers, by parity n
   auto Kb = [&](int n) { return reinterpret_cast<T*>(smem + Lz::oK + n * Lz::rowD); };
-  auto Wb = [&](int n) { return reinterpret_cast<T*>(smem + Lz::oW + n * Lz::rowD); };
   auto Pb = [&](int n) { return reinterpret_cast<T*>(smem + Lz::oP + n * Lz::sq); };
   auto Gb = [&](int n) { return gate_lds(smem + Lz::oG + n * kGateBytes); };
 
@@ -390,19 +388,22 @@ __global__ __launch_bounds__(64 * fwd_nw<D>(), 2) void gdn_fwd_out2_kernel(FwdAr
     pf.template fetch<decltype(part)::value>(q, k, v, al, bt, tw_block<T>(a.tw, a.nblk, bh, blk),
                                              rs, a.H, blk * BLK, min(BLK, a.T - blk * BLK));
   };
-  // State-free work of a block whose inputs sit in Q, K[n], V, Tpp and
-  // gates G[n]: P -> P[n], Wn -> W[n], U (registers).
-  auto pre = [&](int n, f32x4 (&U)[NDV][4]) {
+  // The state-free work of a block whose inputs sit in Q, K[n], V, Tpp and
+  // gates G[n]: its masked decayed scores P -> P[n].
+  auto pre_pw = [&](int n) {
     if constexpr (OUT) block_scores<T, D, NW, true, false>(Qs, Kb(n), LDD, Gb(n), nullptr, 0, Pb(n), LDC);
-    block_w<T, D, NW>(Kb(n), LDD, Tpp, LDC, Wb(n), Gb(n).gam);
-    block_u<T, NDV>(Tpp, LDC, Vs, LDD, dv0, U);
   };
-  // O^T = diag(gamma) S Q^T of the block in Q with gates G[n].
+  // With S the entry state of the block staged in Q, K[n], V, Tpp, G[n]:
+  // O^T = diag(gamma) S Q^T and, from Z = K S^T in the same pass over the
+  // state's fragments, Vn = U - W S^T = Tpp (V - diag(gamma) Z) -> U, since
+  // W = Tpp diag(gamma) K.  No W tile is formed.
   f32x4 O[NDV][4];
-  auto out_state_part = [&](int n) {
+  auto state_in_part = [&](int n, f32x4 (&U)[NDV][4]) {
+    f32x4 Z[NDV][4];
+    zero_acc(Z);
+    zero_acc(O);
+    block_s_kq<T, D, NDV, OUT>(St, Kb(n), Qs, LDD, Z, O);
     if constexpr (OUT) {
-      zero_acc(O);
-      block_s_yT<T, D, NDV>(St, Qs, LDD, O);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const float gr = Gb(n).gam[16 * j + li];
@@ -410,6 +411,7 @@ __global__ __launch_bounds__(64 * fwd_nw<D>(), 2) void gdn_fwd_out2_kernel(FwdAr
         for (int bb = 0; bb < NDV; ++bb) O[bb][j] *= gr;
       }
     }
+    block_vn_from_z<T, NDV>(Tpp, LDC, Vs, LDD, dv0, Gb(n).gam, Z, U);
   };
 
   Prefetch<T, D, OUT> pf;
@@ -418,8 +420,8 @@ __global__ __launch_bounds__(64 * fwd_nw<D>(), 2) void gdn_fwd_out2_kernel(FwdAr
   if (blk0 + 1 < blk1) fetch(pf, blk0 + 1);
   lds_barrier();
   f32x4 U[NDV][4];
-  pre(0, U);
-  out_state_part(0);
+  pre_pw(0);
+  state_in_part(0, U);
   lds_barrier();
 
   for (int blk = blk0; blk < blk1; ++blk) {
@@ -436,8 +438,7 @@ __global__ __launch_bounds__(64 * fwd_nw<D>(), 2) void gdn_fwd_out2_kernel(FwdAr
       if (next2) fetch_part(std::integral_constant<int, 1>{}, pf, blk + 2);
     }
     lds_barrier();
-    // block blk, state part: Vn = U - W S^T; O^T += Vn^T P^T; S' = gamma_C S + Vn^T D K
-    block_x_st<T, D, NDV, true>(Wb(c), LDD, St, U);
+    // block blk, state part (U holds its Vn): O^T += Vn^T P^T; S' = gamma_C S + Vn^T D K
     if constexpr (STATES)
       StateTiles<T, BLK>::store(vn_block<T, D>(a, bh, blk), dv0, lane, U[0]);
     if (next2) fetch_part(std::integral_constant<int, 2>{}, pf, blk + 2);
@@ -468,10 +469,10 @@ __global__ __launch_bounds__(64 * fwd_nw<D>(), 2) void gdn_fwd_out2_kernel(FwdAr
           }
         }
     }
-    // block blk+1, state-free part and its S Q^T (S is now its entry state)
+    // block blk+1: P, then S Q^T and Vn (S is now its entry state)
     if (next) {
-      pre(n, U);
-      out_state_part(n);
+      pre_pw(n);
+      state_in_part(n, U);
     }
     lds_barrier();
   }

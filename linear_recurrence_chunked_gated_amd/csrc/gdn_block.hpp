@@ -61,8 +61,9 @@ __device__ __forceinline__ void block_gates(float la, float be, const GateLds& G
 //   Af[r][s] = (s < r) beta_r Gamma_rs k_r.k_s      (fp32, strictly lower), if WITH_A
 //   Pl[r][s] = (s <= r) Gamma_rs q_r.k_s            (operand type), if WITH_Q
 // Computed as K K^T and K Q^T with s on the accumulator's m index so each
-// lane stores 4 consecutive s.
-template <typename T, int D, int NW, bool WITH_Q, bool WITH_A = true>
+// lane stores 4 consecutive s.  A_OVER_K: Af lies over the K tile (a barrier
+// separates the last K read from the first A write).
+template <typename T, int D, int NW, bool WITH_Q, bool WITH_A = true, bool A_OVER_K = false>
 __device__ __forceinline__ void block_scores(const T* Qs, const T* Ks, int ldd, const GateLds& G,
                                              float* Af, int ldf, T* Pl, int ldc,
                                              f32x4* kk = nullptr) {
@@ -83,6 +84,8 @@ __device__ __forceinline__ void block_scores(const T* Qs, const T* Ks, int ldd, 
         accP[j] = Mma<T>::mma(a, frag_row<T, STD>(Qs + 16 * (r0 + j) * ldd, ldd, s), accP[j]);
     }
   }
+  // Af takes the K tile's region: every wave's K reads end before any A write
+  if constexpr (A_OVER_K) lds_barrier();
   if (kk) {  // the raw K K^T tiles (m = st, n = r0 + j), for callers that need them later
 #pragma unroll
     for (int j = 0; j < NJ; ++j) kk[j] = accA[j];
@@ -115,6 +118,9 @@ __device__ __forceinline__ void block_scores(const T* Qs, const T* Ks, int ldd, 
 // first for the pairs (1,0) and (3,2), then for rows 32..63 x cols 0..31.
 // The upper blocks of Tm are never part of T; they serve as scratch here and
 // must be treated as zero by readers.  Ends with a workgroup barrier.
+// Tm may be Af (T over A in place): each block of A is read by the wave that
+// then writes the block of T in its place, or before a barrier that precedes
+// that write, and the scratch lies in the upper blocks, which A leaves unused.
 // Wave SUBW does the substitution while the other waves run side(), work of
 // their own that needs neither A nor T; wave SUBW runs its side() during the
 // first block step, which occupies waves 0 and 1 only (SUBW >= 2 then).

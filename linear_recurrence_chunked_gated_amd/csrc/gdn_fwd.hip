@@ -392,7 +392,7 @@ __global__ __launch_bounds__(64 * fwd_nw<D>(), 2) void gdn_fwd_out2_kernel(FwdAr
   };
   // The state-free work of a block whose inputs sit in Q, K[n], V, Tpp and
   // gates G[n]: its masked decayed scores P -> P[n].
-  auto pre_pw = [&](int n) {
+  auto block_p = [&](int n) {
     if constexpr (OUT) block_scores<T, D, NW, true, false>(Qs, Kb(n), LDD, Gb(n), nullptr, 0, Pb(n), LDC);
   };
   // With S the entry state of the block staged in Q, K[n], V, Tpp, G[n]:
@@ -422,7 +422,7 @@ __global__ __launch_bounds__(64 * fwd_nw<D>(), 2) void gdn_fwd_out2_kernel(FwdAr
   if (blk0 + 1 < blk1) fetch(pf, blk0 + 1);
   lds_barrier();
   f32x4 U[NDV][4];
-  pre_pw(0);
+  block_p(0);
   state_in_part(0, U);
   lds_barrier();
 
@@ -473,7 +473,7 @@ __global__ __launch_bounds__(64 * fwd_nw<D>(), 2) void gdn_fwd_out2_kernel(FwdAr
     }
     // block blk+1: P, then S Q^T and Vn (S is now its entry state)
     if (next) {
-      pre_pw(n);
+      block_p(n);
       state_in_part(n, U);
     }
     lds_barrier();

@@ -678,7 +678,7 @@ def main():
         copy_calibration()
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU; runs on several GPUs are not part of this build "
+        print("bench.py measures one GPU; runs on several GPUs are not implemented "
               "(the chunk path shards by heads with no exchange, or along the sequence with one "
               "boundary-state exchange per chunk)", file=sys.stderr)
         sys.exit(2)

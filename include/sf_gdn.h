@@ -63,7 +63,7 @@ extern "C" {
 typedef enum {
   SF_OK = 0,
   SF_ERR_INVALID_ARG = 1,  /* null pointer, bad dimension, misalignment, aliasing */
-  SF_ERR_UNSUPPORTED = 2,  /* valid request this build does not implement */
+  SF_ERR_UNSUPPORTED = 2,  /* valid request that the library does not implement */
   SF_ERR_WORKSPACE = 3,    /* workspace missing or smaller than required */
   SF_ERR_HIP = 4           /* a HIP runtime call or kernel launch failed */
 } sf_status;

@@ -334,6 +334,26 @@ __device__ __forceinline__ void block_x_st(const T* X, int ldd, const f32x4 (&St
   }
 }
 
+// block_x_st with the first NPF k-steps' X fragments read beforehand.
+template <typename T, int D, int NDV, int NPF>
+__device__ __forceinline__ void block_x_st_ra(const T* X, int ldd, const f32x4 (&St)[NDV][D / 16],
+                                              const typename Mma<T>::frag (&a0)[NPF][4],
+                                              f32x4 (&acc)[NDV][4]) {
+  constexpr int KS = D / Mma<T>::KSTEP;
+#pragma unroll
+  for (int s = 0; s < KS; ++s) {
+    typename Mma<T>::frag bs[NDV];
+#pragma unroll
+    for (int b = 0; b < NDV; ++b) bs[b] = AccFrag<T>::get(St[b], s);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const auto a = s < NPF ? a0[s < NPF ? s : 0][i] : frag_row<T, PERM>(X + 16 * i * ldd, ldd, s);
+#pragma unroll
+      for (int b = 0; b < NDV; ++b) acc[b][i] = Mma<T>::mma(a, bs[b], acc[b][i]);
+    }
+  }
+}
+
 // acc[b][j] (m = dv-tile b, n = r-tile j) += S[dv][:] . Y[r][:] with S from the
 // register state tiles and Y a row-major [r][dk] LDS tile (Q):  (S Y^T).
 template <typename T, int D, int NDV>

@@ -315,6 +315,20 @@ __global__ __launch_bounds__(4 * D, 2) void gdn_bwd_dscan2_kernel(BwdArgs a, int
     if constexpr (MAIN)
       StateTiles<T, D>::store(reinterpret_cast<T*>(a.dhst) + ((size_t)bh * f.nblk + blk) * D * D,
                               w, lane, dSv);
+    // This block's first operands (its buffers were published by the last
+    // barrier), read before the next block's staging so that their LDS
+    // latency overlaps it (bf16: dscan 154 -> 148 us, dscan summary 146 -> 140
+    // us per launch on the benchmark).
+    constexpr bool RA = sizeof(T) == 2;
+    typename Mma<T>::frag rbo, rp[4], rk[4];
+    if constexpr (RA) {
+      rbo = frag_tr<T, STD>(Ob(c) + 16 * w, LDD, 0);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        rp[i] = frag_tr<T, STD>(Pb(c) + 16 * i, LDC, 0);
+        rk[i] = frag_row<T, PERM>(Kb(c) + 16 * i * LDD, LDD, 0);
+      }
+    }
     // the next block (blk - 1) into the other buffers; the one after it goes
     // out in three parts over this block
     if (next) {
@@ -330,17 +344,19 @@ __global__ __launch_bounds__(4 * D, 2) void gdn_bwd_dscan2_kernel(BwdArgs a, int
       for (int i = 0; i < 4; ++i) dvn[i] = kd[i] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int s = 0; s < BLK / Mma<T>::KSTEP; ++s) {
-        const auto bo = frag_tr<T, STD>(Ob(c) + 16 * w, LDD, s);
+        const auto bo = (RA && s == 0) ? rbo : frag_tr<T, STD>(Ob(c) + 16 * w, LDD, s);
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-          dvn[i] = Mma<T>::mma(frag_tr<T, STD>(Pb(c) + 16 * i, LDC, s), bo, dvn[i]);
+          dvn[i] = Mma<T>::mma((RA && s == 0) ? rp[i] : frag_tr<T, STD>(Pb(c) + 16 * i, LDC, s),
+                               bo, dvn[i]);
       }
 #pragma unroll
       for (int s = 0; s < D / Mma<T>::KSTEP; ++s) {
         const auto bs = AccFrag<T>::get(dSv, s);
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-          kd[i] = Mma<T>::mma(frag_row<T, PERM>(Kb(c) + 16 * i * LDD, LDD, s), bs, kd[i]);
+          kd[i] = Mma<T>::mma((RA && s == 0) ? rk[i] : frag_row<T, PERM>(Kb(c) + 16 * i * LDD, LDD, s),
+                              bs, kd[i]);
       }
       if (next2) fetch_part(std::integral_constant<int, 2>{}, blk - 2);
 #pragma unroll
@@ -695,6 +711,19 @@ __device__ __forceinline__ void grads_block(const BwdArgs& a, int id, unsigned c
 #pragma unroll
   for (int i = 0; i < 4; ++i) store_tile_N(dvn[i], dVns, LDD, 16 * i, 16 * w);
   bar();
+  // Operands read ahead (bf16, where registers are spare): phase H's dO
+  // fragments here, phase I's first two k-steps of dVn and Vn fragments at the
+  // start of H.  Their LDS reads then overlap the phase before instead of
+  // stalling every wave at once after the barrier (gdn_bwd_grads 722 -> 710 us
+  // per launch on the benchmark).
+  constexpr bool READ_AHEAD = sizeof(T) == 2;
+  typename Mma<T>::frag hO[READ_AHEAD ? D / Mma<T>::KSTEP : 1][4];
+  if constexpr (READ_AHEAD) {
+#pragma unroll
+    for (int s = 0; s < D / Mma<T>::KSTEP; ++s)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) hO[s][j] = frag_row<T, PERM>(Os + 16 * j * LDD, LDD, s);
+  }
   // ---- G: dP^T (m = s, n = r) = Vn dO^T ; P-term of dg ; dPm = dP o Gamma o mask in place of P
   {
     const int st = w & 3, r0 = (w >> 2) * NJ;
@@ -730,6 +759,17 @@ __device__ __forceinline__ void grads_block(const BwdArgs& a, int id, unsigned c
     add_rows(dgp, 16 * st, pgs, -1.f);         // dg_s -= sum_r
   }
   bar();
+  constexpr int NPI = READ_AHEAD ? 2 : 1;
+  typename Mma<T>::frag iV[NPI][2][4];
+  if constexpr (READ_AHEAD) {
+#pragma unroll
+    for (int s = 0; s < NPI; ++s)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        iV[s][0][j] = frag_row<T, PERM>(dVns + 16 * j * LDD, LDD, s);
+        iV[s][1][j] = frag_row<T, PERM>(Vns + 16 * j * LDD, LDD, s);
+      }
+  }
   // ---- H: dQ^T = diag-scaled (S^T dO^T) + K^T dPm^T  (wave: dk-tile w); dK^T starts
   f32x4 dKt[4];
   {
@@ -739,8 +779,10 @@ __device__ __forceinline__ void grads_block(const BwdArgs& a, int id, unsigned c
 #pragma unroll
     for (int s = 0; s < D / Mma<T>::KSTEP; ++s) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        acc[j] = Mma<T>::mma(skf[s], frag_row<T, PERM>(Os + 16 * j * LDD, LDD, s), acc[j]);
+      for (int j = 0; j < 4; ++j) {
+        if constexpr (READ_AHEAD) acc[j] = Mma<T>::mma(skf[s], hO[s][j], acc[j]);
+        else acc[j] = Mma<T>::mma(skf[s], frag_row<T, PERM>(Os + 16 * j * LDD, LDD, s), acc[j]);
+      }
     }
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -780,8 +822,13 @@ __device__ __forceinline__ void grads_block(const BwdArgs& a, int id, unsigned c
     for (int s = 0; s < D / Mma<T>::KSTEP; ++s) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        acc[j] = Mma<T>::mma(skf[s], frag_row<T, PERM>(dVns + 16 * j * LDD, LDD, s), acc[j]);
-        x2[j] = Mma<T>::mma(gkf[s], frag_row<T, PERM>(Vns + 16 * j * LDD, LDD, s), x2[j]);
+        if (READ_AHEAD && s < NPI) {
+          acc[j] = Mma<T>::mma(skf[s], iV[s < NPI ? s : 0][0][j], acc[j]);
+          x2[j] = Mma<T>::mma(gkf[s], iV[s < NPI ? s : 0][1][j], x2[j]);
+        } else {
+          acc[j] = Mma<T>::mma(skf[s], frag_row<T, PERM>(dVns + 16 * j * LDD, LDD, s), acc[j]);
+          x2[j] = Mma<T>::mma(gkf[s], frag_row<T, PERM>(Vns + 16 * j * LDD, LDD, s), x2[j]);
+        }
       }
     }
 #pragma unroll

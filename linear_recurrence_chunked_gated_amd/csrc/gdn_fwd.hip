@@ -677,6 +677,11 @@ __global__ __launch_bounds__(64 * fwd_nw<D>(), 2) void gdn_fwd_summary2_kernel(F
   for (int blk = blk0; blk < blk1; ++blk) {
     const int c = (blk - blk0) & 1, n = c ^ 1;
     const bool next = blk + 1 < blk1, next2 = blk + 2 < blk1;
+    // this block's first W operands (published by the last barrier), read
+    // before the next block's staging so that their LDS latency overlaps it
+    typename Mma<T>::frag rW[1][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) rW[0][i] = frag_row<T, PERM>(Wb(c) + 16 * i * LDD, LDD, 0);
     if (next) {
       pf.stage(nullptr, Kb(n), Vs, Tpp, LDD, LDC, min(BLK, a.T - (blk + 1) * BLK), Gb(n));
       if (next2) fetch_part(std::integral_constant<int, 1>{}, blk + 2);
@@ -700,7 +705,7 @@ __global__ __launch_bounds__(64 * fwd_nw<D>(), 2) void gdn_fwd_summary2_kernel(F
           X2[bb][i] = U[bb][i];
           X2[NDV + bb][i] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
-      block_x_st<T, D, 2 * NDV>(Wb(c), LDD, NM, X2);
+      block_x_st_ra<T, D, 2 * NDV, 1>(Wb(c), LDD, NM, rW, X2);
 #pragma unroll
       for (int bb = 0; bb < 2 * NDV; ++bb)
 #pragma unroll

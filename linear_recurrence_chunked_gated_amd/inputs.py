@@ -10,7 +10,8 @@ on long sequences; no dataset is involved):
   v ~ N(0, 1);
   beta = sigmoid(N(0, 1));
   alpha = exp(-decay * softplus(N(0, 1)))   (decay = 1, or 0.01 for the
-          slow-decay variant in which the carried state matters);
+          slow-decay variant in which the carried state matters; 10 and 0
+          for the strong-decay and no-decay ends of the gate range);
   S_in ~ N(0, s_in_std) when requested, else absent (zeros);
   dO ~ N(0, 1), dS_out ~ N(0, ds_std) for backward runs.
 Draw order: q, k, v, beta-logit, alpha-logit, S_in, dO, dS_out.

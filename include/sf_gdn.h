@@ -106,12 +106,9 @@ sf_status sf_gdn_chunk_fwd(const sf_gdn_shape* shape, const void* q, const void*
  * forward's inputs (the chunk's state trajectory is recomputed from them);
  * dS_out NULL means zeros.  Writes dq, dk, dv (dtype), dalpha, dbeta (fp32,
  * gradients with respect to alpha and beta themselves) and dS_in (fp32, may
- * be NULL when not wanted).  The kernels work with block-local cumulative
- * sums of log alpha: they form the gradient with respect to log alpha and
- * divide by alpha last, so dalpha's absolute error is that of d log alpha over
- * alpha.  Where alpha is far below 1e-2, alpha * dalpha (the log-gate
- * gradient) keeps the accuracy of the other outputs and dalpha alone does
- * not. */
+ * be NULL when not wanted).  dalpha keeps its accuracy down to the smallest
+ * alpha: every term of d log alpha_t is formed with alpha_t as a factor
+ * before the division by alpha_t (tested to alpha ~ 1e-15). */
 sf_status sf_gdn_chunk_bwd(const sf_gdn_shape* shape, const void* q, const void* k, const void* v,
                            const float* alpha, const float* beta, const float* S_in,
                            const void* dO, const float* dS_out, void* dq, void* dk, void* dv,

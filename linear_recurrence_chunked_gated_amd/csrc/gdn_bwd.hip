@@ -464,6 +464,111 @@ __device__ __forceinline__ void add_cols(float* part, int n0, f32x4 v, float sig
   if (lane < 16) lds_add(part + n0 + lane, sign * x);
 }
 
+// Pair terms of d log alpha.  A term X_rs (s <= r, one block) that carries the
+// gate ratio Gamma_rs = exp(g_r - g_s) moves d log alpha_i for s < i <= r: the
+// gradient of g_r minus that of g_s.  Summed as those two per-token sums and a
+// suffix sum over the block, the terms with i <= s cancel only up to rounding,
+// which leaves an error of the block's scale in d log alpha_i; where alpha_i is
+// tiny, d log alpha_i = alpha_i dL/dalpha_i is tiny too and dalpha = d log
+// alpha / alpha is lost.  Summed over the rectangle s < i <= r instead, every
+// term of d log alpha_i contains alpha_i as a factor, so the sum keeps its
+// relative accuracy.  pair_rect adds, for one 16 x 16 tile (row tile a =
+// r-tile, column tile b = s-tile, b <= a) and every i, the tile's share of
+// the rectangle sum to F[i] (this wave's partial, 64 floats): column
+// prefixes for i inside the s-tile, the whole tile for i between the tiles,
+// row suffixes for i inside the r-tile, and both for a diagonal tile.  Every
+// partial sum adds only terms of its own rectangle.  Layout SR: lane (i, g)
+// holds X[16a + i][16b + 4g + e]; RS: X[16a + 4g + e][16b + i].
+// The gradient kernel sums a block's pair terms over rectangles where some
+// alpha of the block is below this (measured: the per-token sums keep dalpha
+// within 4e-5 (fp32) and 2e-3 (bf16) of the head's scale down to it).
+constexpr float kRectAlpha = 0.02f;
+template <bool SR>
+__device__ __forceinline__ void pair_rect(float* F, int a, int b, const f32x4& v) {
+  const int lane = lane_id(), li = lane & 15, g = lane >> 4;
+  if (b > a) return;
+  if (b < a) {
+    float cpre, full;  // column prefix (sigma <= this lane's) and the tile's sum
+    if constexpr (SR) {
+      f32x4 cp;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) cp[e] = sum_row16(v[e]);
+      cp[1] += cp[0];
+      cp[2] += cp[1];
+      cp[3] += cp[2];
+      const float t0 = lane_f(cp[3], 0), t1 = lane_f(cp[3], 16), t2 = lane_f(cp[3], 32),
+                  t3 = lane_f(cp[3], 48);
+      const float off = g == 0 ? 0.f : g == 1 ? t0 : g == 2 ? t0 + t1 : (t0 + t1) + t2;
+      if (li == 0) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) lds_add(F + 16 * b + 4 * g + e + 1, off + cp[e]);
+      }
+      full = ((t0 + t1) + t2) + t3;
+      // row suffixes: rows rho >= i of the whole tile
+      float x = sum_rows4((v[0] + v[1]) + (v[2] + v[3]));
+      x += dpp_f<0x101>(x);
+      x += dpp_f<0x102>(x);
+      x += dpp_f<0x104>(x);
+      x += dpp_f<0x108>(x);
+      if (g == 0 && li >= 1) lds_add(F + 16 * a + li, x);
+      (void)cpre;
+    } else {
+      float x = sum_rows4((v[0] + v[1]) + (v[2] + v[3]));  // column sum, sigma = li
+      x += dpp_f<0x111>(x);
+      x += dpp_f<0x112>(x);
+      x += dpp_f<0x114>(x);
+      x += dpp_f<0x118>(x);
+      if (g == 0) lds_add(F + 16 * b + li + 1, x);
+      full = lane_f(x, 15);
+      f32x4 q;  // row sums, suffix over rho: in the lane over e, then the higher row groups
+#pragma unroll
+      for (int e = 0; e < 4; ++e) q[e] = sum_row16(v[e]);
+      q[2] += q[3];
+      q[1] += q[2];
+      q[0] += q[1];
+      const float t1 = lane_f(q[0], 16), t2 = lane_f(q[0], 32), t3 = lane_f(q[0], 48);
+      const float up = g == 3 ? 0.f : g == 2 ? t3 : g == 1 ? t2 + t3 : t1 + (t2 + t3);
+      if (li == 0) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (4 * g + e >= 1) lds_add(F + 16 * a + 4 * g + e, up + q[e]);
+      }
+      (void)cpre;
+    }
+    // whole tile for 16 b + 16 < i <= 16 a
+    if (lane < 16 * (a - b - 1)) lds_add(F + 16 * b + 17 + lane, full);
+  } else {
+    // diagonal tile: sum over rho >= k, sigma < k for k = 1 .. 15
+    if constexpr (SR) {
+      f32x4 p = v;  // row prefixes over this lane's 4 columns
+      p[1] += p[0];
+      p[2] += p[1];
+      p[3] += p[2];
+      const float u0 = __shfl(p[3], li), u1 = __shfl(p[3], li + 16), u2 = __shfl(p[3], li + 32);
+      const float off = g == 0 ? 0.f : g == 1 ? u0 : g == 2 ? u0 + u1 : (u0 + u1) + u2;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int k = 4 * g + e + 1;
+        const float d = sum_row16(li >= k ? off + p[e] : 0.f);
+        if (li == 0 && k <= 15) lds_add(F + 16 * a + k, d);
+      }
+    } else {
+      f32x4 q = v;  // column suffixes over this lane's 4 rows
+      q[2] += q[3];
+      q[1] += q[2];
+      q[0] += q[1];
+      const float u1 = __shfl(q[0], li + 16), u2 = __shfl(q[0], li + 32), u3 = __shfl(q[0], li + 48);
+      const float up = g == 3 ? 0.f : g == 2 ? u3 : g == 1 ? u2 + u3 : u1 + (u2 + u3);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int k = 4 * g + e;
+        const float d = sum_row16(li < k ? up + q[e] : 0.f);
+        if (li == 0 && k >= 1) lds_add(F + 16 * a + k, d);
+      }
+    }
+  }
+}
+
 // LDS plan of the gradient kernel (regions reused by phase):
 //   RQ Q | RK K | RV V -> Y | RO dO -> dW | RT Tm | RA Af -> Tp, Tpp (-> dVn, dKK
 //   for fp32 at d = 64) | RP P -> dPm | RW Vn -> dT | RD dVn -> dKK |
@@ -490,7 +595,7 @@ template <typename T, int D> struct GradLds {
   static constexpr size_t zA = cmax(f64x64, 2 * sq64);
   static constexpr size_t zW = BF ? cmax(rowD, zSplit) : cmax(rowD, f64x64);
   static constexpr size_t zD = DVN_IN_A ? 0 : cmax(rowD, sq64);
-  static constexpr size_t zPart = (3 * NW * BLK + NW + 4) * sizeof(float);
+  static constexpr size_t zPart = (4 * NW * BLK + NW + 4) * sizeof(float);
   // the input regions, from the start of their area (LDS, or the global area)
   static constexpr size_t oQ = 0, oK = oQ + zR, oV = oK + zR, oO = oV + zR, zIn = oO + zR;
   static constexpr size_t rest(size_t o0) {
@@ -551,7 +656,8 @@ __device__ __forceinline__ void grads_block(const BwdArgs& a, int id, unsigned c
   float* dgp = part + w * BLK;                // dg per token, this wave's share
   float* dbp = part + NW * BLK + w * BLK;     // dbeta per token
   float* ddp = part + 2 * NW * BLK + w * BLK; // dD per token
-  float* dgc = part + 3 * NW * BLK;           // per-wave <dS', S>
+  float* dfp = part + 3 * NW * BLK + w * BLK; // pair-term rectangle sums per token (pair_rect)
+  float* dgc = part + 4 * NW * BLK;           // per-wave <dS', S>
   // Consecutive workgroups take the heads of one token block, so the rows
   // of [B, T, H, D] that run concurrently are read whole (H * D elements).
   const int BH = f.B * f.H;
@@ -590,16 +696,24 @@ __device__ __forceinline__ void grads_block(const BwdArgs& a, int id, unsigned c
     uint4 r0[Tl::NCH], r1[Tl::NCH];
     Tl::load(r0, q, rs, nv);
     Tl::load(r1, k, rs, nv);
-    for (int i = threadIdx.x; i < 3 * NW * BLK + NW + 4; i += 64 * NW) part[i] = 0.f;
+    for (int i = threadIdx.x; i < 4 * NW * BLK + NW + 4; i += 64 * NW) part[i] = 0.f;
     Tl::to_lds(r0, Qs, LDD, nv);
     Tl::to_lds(r1, Ks, LDD, nv);
-    if (w == 0) block_gates(lane < nv ? __logf(ra) : 0.f, lane < nv ? rb : 0.f, G);
+    if (w == 0) {
+      block_gates(lane < nv ? __logf(ra) : 0.f, lane < nv ? rb : 0.f, G);
+      const bool tiny = __ballot(lane < nv && ra < kRectAlpha) != 0;
+      if (lane == 0) G.gC[2] = tiny ? 1.f : 0.f;
+    }
     __builtin_amdgcn_sched_barrier(0);
     StateTiles<T, D>::load(hS, w, lane, Sx);
     StateTiles<T, D>::load(hG, w, lane, dSx);
     __builtin_amdgcn_sched_barrier(0);
   }
   bar();
+  // the pair terms of d log alpha as rectangle sums (pair_rect) where the
+  // block has a small alpha, else as per-token sums (the same value up to
+  // rounding, and cheaper)
+  const bool rect = __builtin_amdgcn_readfirstlane(G.gC[2] != 0.f ? 1 : 0) != 0;
   // ---- B: scores
   f32x4 kk[NJ];  // K K^T tiles (m = 16 (w & 3), n = 16 ((w >> 2) NJ + j)), for phase L
   block_scores<T, D, NW, true>(Qs, Ks, LDD, G, Af, LDF, Pl, LDC, kk);
@@ -724,7 +838,7 @@ __device__ __forceinline__ void grads_block(const BwdArgs& a, int id, unsigned c
 #pragma unroll
       for (int j = 0; j < 4; ++j) hO[s][j] = frag_row<T, PERM>(Os + 16 * j * LDD, LDD, s);
   }
-  // ---- G: dP^T (m = s, n = r) = Vn dO^T ; P-term of dg ; dPm = dP o Gamma o mask in place of P
+  // ---- G: dP^T (m = s, n = r) = Vn dO^T ; P-term of d log alpha ; dPm = dP o Gamma o mask in place of P
   {
     const int st = w & 3, r0 = (w >> 2) * NJ;
     f32x4 acc[NJ];
@@ -737,26 +851,35 @@ __device__ __forceinline__ void grads_block(const BwdArgs& a, int id, unsigned c
       for (int j = 0; j < NJ; ++j)
         acc[j] = Mma<T>::mma(av, frag_row<T, STD>(Os + 16 * (r0 + j) * LDD, LDD, s), acc[j]);
     }
-    f32x4 pgs = {0.f, 0.f, 0.f, 0.f};  // pg summed over this wave's r-tiles
     const int s0 = 16 * st + g4;
+    f32x4 pg[NJ];
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
       const int r = 16 * (r0 + j) + li;
       T* pp = lds_sw(Pl + r * LDC + s0, LDC);  // 4 elements of one 16-byte chunk
-      f32x4 pg, dm;
+      f32x4 dm;
       const float gr = G.g[r];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int s = s0 + e;
         const float p = (float)pp[e];
-        pg[e] = acc[j][e] * p;
+        pg[j][e] = acc[j][e] * p;
         dm[e] = (s <= r) ? acc[j][e] * __expf(gr - G.g[s]) : 0.f;
       }
       st4(pp, dm[0], dm[1], dm[2], dm[3]);
-      add_cols(dgp, 16 * (r0 + j), pg, 1.f);   // dg_r += sum_s
-      pgs += pg;
     }
-    add_rows(dgp, 16 * st, pgs, -1.f);         // dg_s -= sum_r
+    if (rect) {
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) pair_rect<true>(dfp, r0 + j, st, pg[j]);
+    } else {
+      f32x4 pgs = {0.f, 0.f, 0.f, 0.f};  // pg summed over this wave's r-tiles
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        add_cols(dgp, 16 * (r0 + j), pg[j], 1.f);  // dg_r += sum_s
+        pgs += pg[j];
+      }
+      add_rows(dgp, 16 * st, pgs, -1.f);  // dg_s -= sum_r
+    }
   }
   bar();
   constexpr int NPI = READ_AHEAD ? 2 : 1;
@@ -947,7 +1070,7 @@ __device__ __forceinline__ void grads_block(const BwdArgs& a, int id, unsigned c
     }
   }
   bar();
-  // ---- L: dA = -T^T Y (strictly lower); A-terms of dbeta, dg; dKK
+  // ---- L: dA = -T^T Y (strictly lower); A-terms of dbeta and d log alpha; dKK
   {
     const int rt = w & 3, s0t = (w >> 2) * NJ;
     f32x4 acc[NJ];
@@ -974,14 +1097,15 @@ __device__ __forceinline__ void grads_block(const BwdArgs& a, int id, unsigned c
           acc[j] = Mma<float>::mma(at, frag_tr<float, STD>(Yf + 16 * (s0t + j), LDF, s), acc[j]);
       }
     }
-    // db's row sums, over this wave's s-tiles, give both the dbeta_r term and
-    // (times beta_r) the row term of dg
-    f32x4 dbr = {0.f, 0.f, 0.f, 0.f};
+    // db's row sums, over this wave's s-tiles, give the dbeta_r term and
+    // (times beta_r) the row term of dg, or the pair terms beta_r db_rs go to
+    // the rectangle sums
+    f32x4 dbr = {0.f, 0.f, 0.f, 0.f}, dag[NJ];
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
       const int s = 16 * (s0t + j) + li;
       const float gs = G.g[s];
-      f32x4 db, dag, dkk;
+      f32x4 db, dkk;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int r = 16 * rt + g4 + e;
@@ -990,12 +1114,18 @@ __device__ __forceinline__ void grads_block(const BwdArgs& a, int id, unsigned c
         const float da = low ? -acc[j][e] : 0.f;
         const float br = G.beta[r];
         db[e] = da * gam * kk[j][e];
-        dag[e] = br * db[e];
+        dag[j][e] = br * db[e];
         dkk[e] = da * br * gam;
       }
       store_tile_N(dkk, dKKs, LDC, 16 * rt, 16 * (s0t + j));
       dbr += db;
-      add_cols(dgp, 16 * (s0t + j), dag, -1.f);
+    }
+    if (rect) {
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) pair_rect<false>(dfp, rt, s0t + j, dag[j]);
+    } else {
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) add_cols(dgp, 16 * (s0t + j), dag[j], -1.f);
     }
     dbr = tile_sum_over_n(dbr);
     if (li == 0) {
@@ -1003,7 +1133,7 @@ __device__ __forceinline__ void grads_block(const BwdArgs& a, int id, unsigned c
       for (int e = 0; e < 4; ++e) {
         const int r = 16 * rt + g4 + e;
         lds_add(dbp + r, dbr[e]);
-        lds_add(dgp + r, G.beta[r] * dbr[e]);
+        if (!rect) lds_add(dgp + r, G.beta[r] * dbr[e]);
       }
     }
   }
@@ -1028,23 +1158,39 @@ __device__ __forceinline__ void grads_block(const BwdArgs& a, int id, unsigned c
     }
   }
   bar();
-  // ---- N: gate gradients
+  // ---- N: gate gradients.  d log alpha_j collects the terms through gamma_r
+  // for r >= j (dg: the O-term of dQ and the gamma of Tp), the terms through
+  // D_i = exp(g_C - g_i) for i < j (dj), the state's decay gamma_C, and the
+  // pair terms.  With the pair terms as rectangle sums each of these carries
+  // alpha_j as a factor, so d log alpha_j keeps its relative accuracy however
+  // small alpha_j is, and so does dalpha_j = d log alpha_j / alpha_j.  Else
+  // (no alpha below kRectAlpha in the block) the pair terms are in dg, and
+  // d log alpha is the suffix sum of dg with dj moved to the block's end.
   if (w == 0) {
     const int j = lane;
-    float dg = 0.f, dbv = 0.f, dd = 0.f, gcs = 0.f;
+    float dg = 0.f, dbv = 0.f, dd = 0.f, gcs = 0.f, fr = 0.f;
 #pragma unroll
     for (int ww = 0; ww < NW; ++ww) {
       dg += part[ww * BLK + j];
       dbv += part[NW * BLK + ww * BLK + j];
       dd += part[2 * NW * BLK + ww * BLK + j];
+      fr += part[3 * NW * BLK + ww * BLK + j];
       gcs += dgc[ww];
     }
     const float dj = G.dec[j] * dd;
-    dg -= dj;
-    const float dgC = wave_sum(dj) + G.gC[0] * gcs;
-    if (j == BLK - 1) dg += dgC;
-    // reverse inclusive cumsum over the block: dlog alpha_j = sum_{r >= j} dg_r
-    const float x = wave_suffix_sum(dg);
+    float x;
+    if (rect) {
+      // dj of token j - 1 (the shuffle runs in every lane: a lane that sat
+      // out would hand its neighbour nothing)
+      const float dj_up = __shfl_up(dj, 1);
+      const float dj_prev = j == 0 ? 0.f : dj_up;
+      x = ((wave_suffix_sum(dg) + wave_prefix_sum(dj_prev)) + G.gC[0] * gcs) + fr;
+    } else {
+      dg -= dj;
+      const float dgC = wave_sum(dj) + G.gC[0] * gcs;
+      if (j == BLK - 1) dg += dgC;
+      x = wave_suffix_sum(dg);  // dlog alpha_j = sum_{r >= j} dg_r
+    }
     if (j < nv) {
       const size_t idx = gofs + (size_t)j * f.H;
       a.dalpha[idx] = x / ra;

@@ -480,15 +480,16 @@ __device__ __forceinline__ void add_cols(float* part, int n0, f32x4 v, float sig
 // partial sum adds only terms of its own rectangle.  Layout SR: lane (i, g)
 // holds X[16a + i][16b + 4g + e]; RS: X[16a + 4g + e][16b + i].
 // The gradient kernel sums a block's pair terms over rectangles where some
-// alpha of the block is below this (measured: the per-token sums keep dalpha
-// within 4e-5 (fp32) and 2e-3 (bf16) of the head's scale down to it).
+// alpha of the block is below this.  Above it the per-token sums were measured
+// within 7e-6 (fp32) of the head's largest dalpha, and bf16 within its
+// operands' own rounding (3e-3); below it they lose accuracy as 1/alpha.
 constexpr float kRectAlpha = 0.02f;
 template <bool SR>
 __device__ __forceinline__ void pair_rect(float* F, int a, int b, const f32x4& v) {
   const int lane = lane_id(), li = lane & 15, g = lane >> 4;
   if (b > a) return;
   if (b < a) {
-    float cpre, full;  // column prefix (sigma <= this lane's) and the tile's sum
+    float full;  // the tile's sum
     if constexpr (SR) {
       f32x4 cp;
 #pragma unroll
@@ -511,7 +512,6 @@ __device__ __forceinline__ void pair_rect(float* F, int a, int b, const f32x4& v
       x += dpp_f<0x104>(x);
       x += dpp_f<0x108>(x);
       if (g == 0 && li >= 1) lds_add(F + 16 * a + li, x);
-      (void)cpre;
     } else {
       float x = sum_rows4((v[0] + v[1]) + (v[2] + v[3]));  // column sum, sigma = li
       x += dpp_f<0x111>(x);
@@ -533,7 +533,6 @@ __device__ __forceinline__ void pair_rect(float* F, int a, int b, const f32x4& v
         for (int e = 0; e < 4; ++e)
           if (4 * g + e >= 1) lds_add(F + 16 * a + 4 * g + e, up + q[e]);
       }
-      (void)cpre;
     }
     // whole tile for 16 b + 16 < i <= 16 a
     if (lane < 16 * (a - b - 1)) lds_add(F + 16 * b + 17 + lane, full);

@@ -1,5 +1,6 @@
-"""Parity at the ends of the gates' range: the HIP forward and backward through
-the C ABI against the fp64 oracle with
+"""Parity at the ends of the gates' range, and fp32 through a long segment
+chain: the HIP forward and backward through the C ABI against the fp64 oracle
+with
 
   strong  alpha = exp(-10 softplus(z)), down to about 1e-13: the decay inside
           one 64-token block spans hundreds of e-folds, so Gamma and gamma
@@ -68,3 +69,24 @@ def test_gate_extremes_fwd_bwd(oracle_mod, mode, B, T, H, D, dtype, seg):
     assert_close("alpha * dalpha", alpha * f64(grads[3]), alpha * ref[3], tol, head_axis=2)
     for name, g, r, ax in zip(NAMES, grads, ref, HEAD_AXIS):
         assert_close(name, f64(g), r, tol, head_axis=ax)
+
+
+@pytest.mark.parametrize("D,decay", [(64, 0.0), (128, 0.0), (128, 0.01)])
+def test_fp32_long_chain(oracle_mod, D, decay):
+    """fp32 within 1e-4 through 128 segments of one block each (127 steps of
+    the in-chunk segment chain, whose products run on split bf16 operands),
+    with no decay, so nothing of an early segment's state fades before the
+    chunk's end, and with slow decay."""
+    d = inputs(1, 8192, 2, D, "f32", seed=9900 + D, s_in_std=0.1, grads=True, decay=decay)
+    dd = to_dev(d)
+    o, S = gdn.chunk_fwd(dd["q"], dd["k"], dd["v"], dd["alpha"], dd["beta"], dd["S_in"],
+                         seg_blocks=1)
+    grads = gdn.chunk_bwd(dd["q"], dd["k"], dd["v"], dd["alpha"], dd["beta"], dd["S_in"],
+                          dd["dO"], dd["dS_out"], seg_blocks=1)
+    torch.cuda.synchronize()
+    o_ref, S_ref = oracle_mod.gdn_fwd(*oracle_args(d))
+    assert_close("o", f64(o), o_ref, TOL["f32"], head_axis=2)
+    assert_close("S_out", f64(S), S_ref, TOL["f32"], head_axis=1)
+    ref = oracle_mod.gdn_bwd(*oracle_args(d), as_f64(d["dO"]), as_f64(d["dS_out"]))
+    for name, g, r, ax in zip(NAMES, grads, ref, HEAD_AXIS):
+        assert_close(name, f64(g), r, TOL["f32"], head_axis=ax)

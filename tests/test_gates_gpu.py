@@ -48,6 +48,12 @@ CASES = [
     (mode, B, T, H, D, dtype, seg)
     for mode in ("strong", "none", "beta0", "beta1")
     for (B, T, H, D, dtype, seg) in ((1, 1000, 2, 128, "bf16", 3), (2, 333, 2, 64, "f32", 2))
+] + [
+    # strong decay on the other two kernel forms: four waves per workgroup
+    # (d = 64), and the gradient kernel with its tiles in global memory (fp32
+    # at d = 128)
+    ("strong", 1, 700, 2, 64, "bf16", 2),
+    ("strong", 1, 333, 2, 128, "f32", 2),
 ]
 
 

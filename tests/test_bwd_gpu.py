@@ -353,3 +353,21 @@ def test_one_block_bf16_two_batches(oracle_mod):
     for name, x, r, ax in zip(NAMES, g, oracle_bwd(oracle_mod, d), HEAD_AXIS):
         assert_close(name, f64(x), r, 4e-3 if name in ("dq", "dk", "dv") else TOL["f32"],
                      head_axis=ax)
+
+
+def test_single_head_long_chunk(oracle_mod):
+    """One sequence (B = H = 1) of 65,537 tokens at d = 128, bf16, slow decay
+    and a carried state, in the default plan: 57 segments of 18 blocks, so
+    the segment chains run 56 steps on a grid that is mostly padding
+    workgroups, and the last block holds one token.  Forward and backward,
+    whole, against the oracle."""
+    d = inputs(1, 65537, 1, 128, "bf16", seed=20261201, s_in_std=0.1, grads=True, decay=0.01)
+    from linear_recurrence_chunked_gated_amd import _lib
+    assert _lib.segment_plan(_lib.make_shape(1, 65537, 1, 128, 128, torch.bfloat16)) == (18, 57)
+    dd = to_dev(d)
+    o, S = gdn.chunk_fwd(dd["q"], dd["k"], dd["v"], dd["alpha"], dd["beta"], dd["S_in"])
+    torch.cuda.synchronize()
+    o_ref, S_ref = oracle_mod.gdn_fwd(*oracle_args(d))
+    assert_close("o", f64(o), o_ref, TOL["bf16"], head_axis=2)
+    assert_close("S_out", f64(S), S_ref, TOL["bf16"], head_axis=1)
+    check_all(run_bwd(d), oracle_bwd(oracle_mod, d), TOL["bf16"])

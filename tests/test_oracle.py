@@ -294,6 +294,63 @@ def test_backward_closed_form_state_gradient_when_beta_zero(oracle_mod):
     np.testing.assert_allclose(dk, 0.0, atol=0)
 
 
+def test_dalpha_at_tiny_alpha_finite_differences(oracle_mod):
+    """Strong decay (alpha = exp(-10 softplus(z)), down to about 1e-13).  Each
+    state is affine in each alpha_t, and so is the loss, so a central
+    difference in alpha_t is exact up to rounding for any step; a step of
+    0.25 (the affine extension past alpha = 0 included) resolves dalpha at
+    the tokens with the smallest alpha, where dalpha stays of the order of
+    the other gradients while d log alpha = alpha dalpha vanishes."""
+    rng = np.random.default_rng(14)
+    q, k, v, a, b, S0 = rand_inputs(rng, 1, 80, 1, 6, 5, decay=10.0)
+    dO = rng.standard_normal(v.shape)
+    dSo = rng.standard_normal(S0.shape)
+    da = oracle_mod.gdn_bwd(q, k, v, a, b, S0, dO, dSo)[3]
+
+    def loss(a):
+        o, S = oracle_mod.gdn_fwd(q, k, v, a, b, S0)
+        return float(np.sum(dO * o) + np.sum(dSo * S))
+
+    order = np.argsort(a[0, :, 0])
+    assert a[0, order[0], 0] < 1e-10
+    scale = np.abs(da).max()
+    for t in order[:6]:
+        h = 0.25
+        ap, am = a.copy(), a.copy()
+        ap[0, t, 0] += h
+        am[0, t, 0] -= h
+        fd = (loss(ap) - loss(am)) / (2 * h)
+        assert abs(fd - da[0, t, 0]) <= 1e-6 * scale, (t, a[0, t, 0], fd, da[0, t, 0])
+
+
+def test_tiny_alpha_resets_the_state(oracle_mod):
+    """With alpha_R = 1e-30 the state carried into token R is scaled away:
+    from R on, outputs and the exit state equal those of the sequence
+    restarted at R from a zero state, and the gradients of the tokens before
+    R equal those of the prefix with no exit gradient (dalpha_R, which reads
+    the state before R, excepted)."""
+    rng = np.random.default_rng(15)
+    q, k, v, a, b, S0 = rand_inputs(rng, 1, 90, 2, 5, 4, decay=0.3)
+    R = 37
+    a[:, R] = 1e-30
+    dO = rng.standard_normal(v.shape)
+    dSo = rng.standard_normal(S0.shape)
+    o, S = oracle_mod.gdn_fwd(q, k, v, a, b, S0)
+    o2, S2 = oracle_mod.gdn_fwd(q[:, R:], k[:, R:], v[:, R:], a[:, R:], b[:, R:], None)
+    np.testing.assert_allclose(o[:, R:], o2, rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(S, S2, rtol=1e-12, atol=1e-14)
+    g = oracle_mod.gdn_bwd(q, k, v, a, b, S0, dO, dSo)
+    g1 = oracle_mod.gdn_bwd(q[:, :R], k[:, :R], v[:, :R], a[:, :R], b[:, :R], S0, dO[:, :R], None)
+    g2 = oracle_mod.gdn_bwd(q[:, R:], k[:, R:], v[:, R:], a[:, R:], b[:, R:], None, dO[:, R:], dSo)
+    for i in range(5):
+        np.testing.assert_allclose(g[i][:, :R], g1[i], rtol=1e-12, atol=1e-14)
+        if i == 3:
+            np.testing.assert_allclose(g[i][:, R + 1:], g2[i][:, 1:], rtol=1e-12, atol=1e-14)
+        else:
+            np.testing.assert_allclose(g[i][:, R:], g2[i], rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(g[5], g1[5], rtol=1e-12, atol=1e-14)
+
+
 # ------------------------------------------------------------- chaining ----
 
 @pytest.mark.parametrize("lengths", [[64, 64, 64, 64], [10, 100, 1, 45]])

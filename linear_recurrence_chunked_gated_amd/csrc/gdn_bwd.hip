@@ -757,8 +757,8 @@ __device__ __forceinline__ void grads_block(const BwdArgs& a, int id, unsigned c
   typename Mma<T>::frag skf[KST], gkf[KST];
 #pragma unroll
   for (int s = 0; s < KST; ++s) {
-    skf[s] = frag_tr<T, PERM>(Sc + 16 * w, LDD, s);
-    gkf[s] = frag_tr<T, PERM>(Gc + 16 * w, LDD, s);
+    skf[s] = frag_tr<T, STD>(Sc + 16 * w, LDD, s);
+    gkf[s] = frag_tr<T, STD>(Gc + 16 * w, LDD, s);
   }
   block_tprime<T, 64 * NW, true>(Tm, LDF, G, Tp, Tpp, LDC);
   bar();  // copies read before V, dO and Vn replace them
@@ -835,7 +835,7 @@ __device__ __forceinline__ void grads_block(const BwdArgs& a, int id, unsigned c
 #pragma unroll
     for (int s = 0; s < D / Mma<T>::KSTEP; ++s)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) hO[s][j] = frag_row<T, PERM>(Os + 16 * j * LDD, LDD, s);
+      for (int j = 0; j < 4; ++j) hO[s][j] = frag_row<T, STD>(Os + 16 * j * LDD, LDD, s);
   }
   // ---- G: dP^T (m = s, n = r) = Vn dO^T ; P-term of d log alpha ; dPm = dP o Gamma o mask in place of P
   {
@@ -888,8 +888,8 @@ __device__ __forceinline__ void grads_block(const BwdArgs& a, int id, unsigned c
     for (int s = 0; s < NPI; ++s)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        iV[s][0][j] = frag_row<T, PERM>(dVns + 16 * j * LDD, LDD, s);
-        iV[s][1][j] = frag_row<T, PERM>(Vns + 16 * j * LDD, LDD, s);
+        iV[s][0][j] = frag_row<T, STD>(dVns + 16 * j * LDD, LDD, s);
+        iV[s][1][j] = frag_row<T, STD>(Vns + 16 * j * LDD, LDD, s);
       }
   }
   // ---- H: dQ^T = diag-scaled (S^T dO^T) + K^T dPm^T  (wave: dk-tile w); dK^T starts
@@ -903,7 +903,7 @@ __device__ __forceinline__ void grads_block(const BwdArgs& a, int id, unsigned c
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         if constexpr (READ_AHEAD) acc[j] = Mma<T>::mma(skf[s], hO[s][j], acc[j]);
-        else acc[j] = Mma<T>::mma(skf[s], frag_row<T, PERM>(Os + 16 * j * LDD, LDD, s), acc[j]);
+        else acc[j] = Mma<T>::mma(skf[s], frag_row<T, STD>(Os + 16 * j * LDD, LDD, s), acc[j]);
       }
     }
 #pragma unroll
@@ -948,8 +948,8 @@ __device__ __forceinline__ void grads_block(const BwdArgs& a, int id, unsigned c
           acc[j] = Mma<T>::mma(skf[s], iV[s < NPI ? s : 0][0][j], acc[j]);
           x2[j] = Mma<T>::mma(gkf[s], iV[s < NPI ? s : 0][1][j], x2[j]);
         } else {
-          acc[j] = Mma<T>::mma(skf[s], frag_row<T, PERM>(dVns + 16 * j * LDD, LDD, s), acc[j]);
-          x2[j] = Mma<T>::mma(gkf[s], frag_row<T, PERM>(Vns + 16 * j * LDD, LDD, s), x2[j]);
+          acc[j] = Mma<T>::mma(skf[s], frag_row<T, STD>(dVns + 16 * j * LDD, LDD, s), acc[j]);
+          x2[j] = Mma<T>::mma(gkf[s], frag_row<T, STD>(Vns + 16 * j * LDD, LDD, s), x2[j]);
         }
       }
     }

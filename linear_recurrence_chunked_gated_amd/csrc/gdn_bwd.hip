@@ -1069,7 +1069,7 @@ __device__ __forceinline__ void grads_block(const BwdArgs& a, int id, unsigned c
     }
   }
   bar();
-  // ---- L: dA = -T^T Y (strictly lower); A-terms of dbeta and d log alpha; dKK
+  // ---- L: dA = -T^T Y (strictly lower); A-terms of dbeta and d log alpha; dKK + dKK^T
   {
     const int rt = w & 3, s0t = (w >> 2) * NJ;
     f32x4 acc[NJ];
@@ -1116,7 +1116,19 @@ __device__ __forceinline__ void grads_block(const BwdArgs& a, int id, unsigned c
         dag[j][e] = br * db[e];
         dkk[e] = da * br * gam;
       }
-      store_tile_N(dkk, dKKs, LDC, 16 * rt, 16 * (s0t + j));
+      // dKK + dKK^T in place of dKK (dKK is strictly lower, so the two never
+      // overlap): a tile on or below the diagonal goes to its mirror
+      // transposed, then its lower part to its place (on the diagonal, over
+      // the zeros its transpose carried there); the tiles above the
+      // diagonal are other waves' mirrors
+      if (s0t + j <= rt) {
+        store_tile_T(dkk, dKKs, LDC, 16 * rt, 16 * (s0t + j));
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 16 * rt + g4 + e;
+          if (s < r) *lds_sw(dKKs + r * LDC + s, LDC) = from_f<T>(dkk[e]);
+        }
+      }
       dbr += db;
     }
     if (rect) {
@@ -1137,26 +1149,6 @@ __device__ __forceinline__ void grads_block(const BwdArgs& a, int id, unsigned c
     }
   }
   bar();
-  // ---- M: dK^T += K^T (dKK + dKK^T)^T-terms + dW^T Tp ; store dk
-  {
-#pragma unroll
-    for (int s = 0; s < BLK / Mma<T>::KSTEP; ++s) {
-      const auto ak = frag_tr<T, STD>(Ks + 16 * w, LDD, s);
-      const auto aw = frag_tr<T, STD>(dWs + 16 * w, LDD, s);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        dKt[j] = Mma<T>::mma(ak, frag_row<T, STD>(dKKs + 16 * j * LDC, LDC, s), dKt[j]);
-        dKt[j] = Mma<T>::mma(ak, frag_tr<T, STD>(dKKs + 16 * j, LDC, s), dKt[j]);
-        dKt[j] = Mma<T>::mma(aw, frag_tr<T, STD>(Tp + 16 * j, LDC, s), dKt[j]);
-      }
-    }
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int s = 16 * j + li;
-      if (s < nv) st4(dk + (size_t)s * rs + 16 * w + g4, dKt[j][0], dKt[j][1], dKt[j][2], dKt[j][3]);
-    }
-  }
-  bar();
   // ---- N: gate gradients.  d log alpha_j collects the terms through gamma_r
   // for r >= j (dg: the O-term of dQ and the gamma of Tp), the terms through
   // D_i = exp(g_C - g_i) for i < j (dj), the state's decay gamma_C, and the
@@ -1165,6 +1157,9 @@ __device__ __forceinline__ void grads_block(const BwdArgs& a, int id, unsigned c
   // small alpha_j is, and so does dalpha_j = d log alpha_j / alpha_j.  Else
   // (no alpha below kRectAlpha in the block) the pair terms are in dg, and
   // d log alpha is the suffix sum of dg with dj moved to the block's end.
+  // Every term is in place after phase L, and phase M writes no LDS, so
+  // wave 0 forms them ahead of its share of M, beside the other waves'
+  // (the workgroup ends when its last wave does).
   if (w == 0) {
     const int j = lane;
     float dg = 0.f, dbv = 0.f, dd = 0.f, gcs = 0.f, fr = 0.f;
@@ -1194,6 +1189,24 @@ __device__ __forceinline__ void grads_block(const BwdArgs& a, int id, unsigned c
       const size_t idx = gofs + (size_t)j * f.H;
       a.dalpha[idx] = x / ra;
       a.dbeta[idx] = dbv;
+    }
+  }
+  // ---- M: dK^T += K^T (dKK + dKK^T) + dW^T Tp ; store dk
+  {
+#pragma unroll
+    for (int s = 0; s < BLK / Mma<T>::KSTEP; ++s) {
+      const auto ak = frag_tr<T, STD>(Ks + 16 * w, LDD, s);
+      const auto aw = frag_tr<T, STD>(dWs + 16 * w, LDD, s);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        dKt[j] = Mma<T>::mma(ak, frag_row<T, STD>(dKKs + 16 * j * LDC, LDC, s), dKt[j]);
+        dKt[j] = Mma<T>::mma(aw, frag_tr<T, STD>(Tp + 16 * j, LDC, s), dKt[j]);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int s = 16 * j + li;
+      if (s < nv) st4(dk + (size_t)s * rs + 16 * w + g4, dKt[j][0], dKt[j][1], dKt[j][2], dKt[j][3]);
     }
   }
 }

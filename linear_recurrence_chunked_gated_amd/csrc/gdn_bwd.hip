@@ -934,7 +934,10 @@ __device__ __forceinline__ void grads_block(const BwdArgs& a, int id, unsigned c
       if (r < nv) st4(dq + (size_t)r * rs + 16 * w + g4, acc[j][0], acc[j][1], acc[j][2], acc[j][3]);
     }
   }
-  bar();  // dO reads done: its region takes dW
+  // dW takes the dO region: where dO's operands were read ahead (bf16), every
+  // read of dO was before phase G's barrier, so only phase H's own reads of
+  // dO need one here
+  if constexpr (!READ_AHEAD) bar();
   // ---- I: dW^T = -(S^T dVn^T) -> dW row-major ; dK2^T = dS'^T Vn^T scaled by D ; D-term
   {
     f32x4 acc[4], x2[4];
@@ -995,7 +998,6 @@ __device__ __forceinline__ void grads_block(const BwdArgs& a, int id, unsigned c
         a2[j] = Mma<T>::mma(au, frag_row<T, STD>(Vs + 16 * (s0t + j) * LDD, LDD, s), a2[j]);
       }
     }
-    bar();  // Vn (region RW) and V reads done before dT overwrites RW
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
       const int s = 16 * (s0t + j) + li;

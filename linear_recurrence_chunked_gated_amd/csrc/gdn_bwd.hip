@@ -934,9 +934,9 @@ __device__ __forceinline__ void grads_block(const BwdArgs& a, int id, unsigned c
       if (r < nv) st4(dq + (size_t)r * rs + 16 * w + g4, acc[j][0], acc[j][1], acc[j][2], acc[j][3]);
     }
   }
-  // dW takes the dO region: where dO's operands were read ahead (bf16), every
-  // read of dO was before phase G's barrier, so only phase H's own reads of
-  // dO need one here
+  // dW takes the dO region.  Where dO's operands were read ahead (bf16), every
+  // read of dO ended before phase G's barrier; else phase H reads dO from LDS,
+  // and this barrier keeps dW out until every wave has.
   if constexpr (!READ_AHEAD) bar();
   // ---- I: dW^T = -(S^T dVn^T) -> dW row-major ; dK2^T = dS'^T Vn^T scaled by D ; D-term
   {

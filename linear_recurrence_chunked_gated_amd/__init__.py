@@ -7,13 +7,14 @@ in include/sf_gdn.h.
                                  -> (dq, dk, dv, dalpha, dbeta, dS_in)
     chain_fwd / chain_bwd: consecutive chunks through their boundary states.
     gated_delta_chunk(q, k, v, alpha, beta, S_in)    -> (o, S_out), torch autograd
+    short_conv(x, w, conv_in)                        -> (y, conv_out), torch autograd
     shortconv_fwd(x, w, conv_in)                     -> (y, conv_out)
     shortconv_bwd(x, w, conv_in, dy, dconv_out)      -> (dx, dw, dconv_in)
 
 Imports are lazy so that the input generator and the planner load without the
 HIP library.
 """
-__all__ = ["chunk_fwd", "chunk_bwd", "chain_fwd", "chain_bwd", "gated_delta_chunk",
+__all__ = ["chunk_fwd", "chunk_bwd", "chain_fwd", "chain_bwd", "gated_delta_chunk", "short_conv",
            "shortconv_fwd", "shortconv_bwd", "profile", "GDNError"]
 
 
@@ -24,7 +25,7 @@ def __getattr__(name):
     if name in ("chain_fwd", "chain_bwd"):
         from . import chain
         return getattr(chain, name)
-    if name == "gated_delta_chunk":
+    if name in ("gated_delta_chunk", "short_conv"):
         from . import autograd
-        return autograd.gated_delta_chunk
+        return getattr(autograd, name)
     raise AttributeError(name)

@@ -1,7 +1,9 @@
-"""The autograd wrapper (gated_delta_chunk): its gradients are exactly those of
-the saving forward and saved backward called directly, chunks chained through
-S_in = previous S_out differentiate as one sequence (against the fp64
-oracle), and an output left out of the loss contributes a zero gradient."""
+"""The autograd wrappers.  gated_delta_chunk: its gradients are exactly those
+of the saving forward and saved backward called directly, chunks chained
+through S_in = previous S_out differentiate as one sequence (against the fp64
+oracle), and an output left out of the loss contributes a zero gradient.
+short_conv: exactly the direct forward and backward calls, with and without a
+boundary state, and for a window of one token."""
 import pytest
 import torch
 
@@ -92,3 +94,37 @@ def test_autograd_refuses_cpu_tensors():
     d = inputs(1, 64, 1, 64, "f32", seed=4400)
     with pytest.raises(ValueError):
         gdn.gated_delta_chunk(d["q"], d["k"], d["v"], d["alpha"], d["beta"])
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("dtype,W,act,state", [("bf16", 4, 1, True), ("f32", 4, 0, False),
+                                               ("bf16", 1, 1, False)])
+def test_short_conv_autograd_equals_direct_calls(dtype, W, act, state):
+    from linear_recurrence_chunked_gated_amd.inputs import conv_inputs
+    d = conv_inputs(2, 333, 136, W, dtype, seed=4500 + W, state_std=1.0 if state else None,
+                    grads=True, device="cuda")
+    x = d["x"].clone().requires_grad_(True)
+    w = d["w"].clone().requires_grad_(True)
+    ci = d["conv_in"].clone().requires_grad_(True) if state else None
+    y, cout = gdn.short_conv(x, w, ci, act)
+    loss = (y.float() * d["dy"].float()).sum()
+    if W > 1:
+        loss = loss + (cout.float() * d["dconv_out"].float()).sum()
+    loss.backward()
+    y2, c2 = gdn.shortconv_fwd(d["x"], d["w"], d["conv_in"] if state else None, act)
+    ref = gdn.shortconv_bwd(d["x"], d["w"], d["conv_in"] if state else None, d["dy"],
+                            d["dconv_out"] if W > 1 else None, act)
+    torch.cuda.synchronize()
+    assert torch.equal(y.detach(), y2)
+    if W > 1:
+        assert torch.equal(cout.detach(), c2)
+    assert torch.equal(x.grad, ref[0]) and torch.equal(w.grad, ref[1])
+    if state:
+        assert torch.equal(ci.grad, ref[2])
+
+
+def test_short_conv_refuses_cpu_tensors():
+    from linear_recurrence_chunked_gated_amd.inputs import conv_inputs
+    d = conv_inputs(1, 16, 64, 4, "f32", seed=4600)
+    with pytest.raises(ValueError):
+        gdn.short_conv(d["x"], d["w"], d["conv_in"])

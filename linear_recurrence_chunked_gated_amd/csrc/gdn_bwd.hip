@@ -977,10 +977,19 @@ __device__ __forceinline__ void grads_block(const BwdArgs& a, int id, unsigned c
   bf16* YTx = reinterpret_cast<bf16*>(in + Lz::oV);   // Y^T, split (in place of Yf)
   static_assert(Lz::zR >= BLK * SPLIT_LD * 2 && Lz::zW >= BLK * SPLIT_LD * 2, "split tiles");
   if constexpr (SPLIT) {
+    // eight consecutive elements per thread: one 16-byte chunk of hi and one
+    // of lo (the swizzle moves whole chunks)
     for (int i = threadIdx.x; i < BLK * BLK / 8; i += 64 * NW) {
       const int r = i >> 3, c0 = 8 * (i & 7);
+      bf16x8 h, l;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) split_store(Tx + r * SPLIT_LD, c0 + e, Tm[r * LDF + c0 + e]);
+      for (int e = 0; e < 8; ++e) {
+        const float x = Tm[r * LDF + c0 + e];
+        h[e] = (bf16)x;
+        l[e] = (bf16)(x - (float)h[e]);
+      }
+      *reinterpret_cast<bf16x8*>(lds_sw(Tx + r * SPLIT_LD + c0, SPLIT_LD)) = h;
+      *reinterpret_cast<bf16x8*>(lds_sw(Tx + r * SPLIT_LD + BLK + c0, SPLIT_LD)) = l;
     }
   }
   {

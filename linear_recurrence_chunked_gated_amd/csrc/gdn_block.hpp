@@ -134,6 +134,9 @@ __device__ __forceinline__ void block_solve(const float* Af, float* Tm, int ldf,
   const int w = wave_id(), lane = lane_id();
   if (w != SUBW) side();
   if (w == SUBW) {
+    // the substitution is the workgroup's critical path here: its wave goes
+    // ahead of the side work of the wave it shares a SIMD with
+    __builtin_amdgcn_s_setprio(2);
     const int base = 16 * (lane >> 4), c = lane & 15;
     float x[16];
 #pragma unroll
@@ -145,6 +148,7 @@ __device__ __forceinline__ void block_solve(const float* Af, float* Tm, int ldf,
     }
 #pragma unroll
     for (int r = 0; r < 16; ++r) Tm[(base + r) * ldf + base + c] = x[r];
+    __builtin_amdgcn_s_setprio(0);
   }
   lds_barrier();
   float* X = Tm + 16;  // blocks (0,1) and (0,2) as scratch: X_w at column 16 (w + 1)

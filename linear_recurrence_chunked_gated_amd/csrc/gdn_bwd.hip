@@ -1172,6 +1172,9 @@ __device__ __forceinline__ void grads_block(const BwdArgs& a, int id, unsigned c
   // wave 0 forms them ahead of its share of M, beside the other waves'
   // (the workgroup ends when its last wave does).
   if (w == 0) {
+    // wave 0 ends last (the gates, then its share of dK): it goes ahead of
+    // the wave it shares a SIMD with for the rest of the block
+    __builtin_amdgcn_s_setprio(2);
     const int j = lane;
     float dg = 0.f, dbv = 0.f, dd = 0.f, gcs = 0.f, fr = 0.f;
 #pragma unroll

@@ -1173,7 +1173,7 @@ __device__ __forceinline__ void grads_block(const BwdArgs& a, int id, unsigned c
   // (the workgroup ends when its last wave does).
   if (w == 0) {
     // wave 0 ends last (the gates, then its share of dK): it goes ahead of
-    // the wave it shares a SIMD with for the rest of the block
+    // the wave it shares a SIMD with until the block's end
     __builtin_amdgcn_s_setprio(2);
     const int j = lane;
     float dg = 0.f, dbv = 0.f, dd = 0.f, gcs = 0.f, fr = 0.f;
@@ -1223,6 +1223,7 @@ __device__ __forceinline__ void grads_block(const BwdArgs& a, int id, unsigned c
       if (s < nv) st4(dk + (size_t)s * rs + 16 * w + g4, dKt[j][0], dKt[j][1], dKt[j][2], dKt[j][3]);
     }
   }
+  if (w == 0) __builtin_amdgcn_s_setprio(0);  // (the strided form runs further blocks)
 }
 
 template <typename T, int D>
